@@ -1,0 +1,45 @@
+"""fp64 CPU oracle for the Krea 2 single-stream DiT block -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import anything from this package.  The HIP library never
+links, loads or calls it, and it imports nothing from the HIP side: the two
+share only the seeded input generators of ``datagen``, which hold none of
+the block's arithmetic.
+
+Parity status (what pins each function; see the tests under
+``tests/test_oracle_*.py``):
+
+* ``modulated_rmsnorm``, ``gated_gqa_attention``, ``swiglu_mlp``,
+  ``gated_residual``, ``block_forward``, ``block_forward_rows``,
+  ``stack_forward``: pinned by an independent scalar-loop brute force
+  (``oracle.bruteforce``), by torch's own float64 CPU routines
+  (``scaled_dot_product_attention``, ``rms_norm``, ``silu``, ``linear``)
+  and by closed forms and invariants (one-key sequence returns the gated
+  V, two-key softmax is a logistic, GQA equals MHA with replicated K/V
+  heads, zero gates give the identity, scale = -1 gives h = shift,
+  permutation equivariance, batch independence).
+* ``time_embedding``: pinned by closed forms of the sinusoid at chosen t.
+* ``timestep_modulation``: parity unpinned.  The pages name a sinusoidal
+  time embedding and a per-block bias replacing per-block MLPs, but do not
+  give the shared map from t to the modulation vector; the oracle's
+  two-layer bias-free MLP is a reading, and the HIP path implements the
+  same reading.
+* The zero-centred gain form ``(1 + w)`` of the RMSNorm is a reading of
+  the pages (weight decay on a zero-centred parameter); parity of that
+  convention is unpinned by the pages, though the arithmetic under it is
+  pinned as above.
+"""
+from .dit_oracle import (  # noqa: F401
+    OracleConfig,
+    block_forward,
+    block_forward_rows,
+    gated_gqa_attention,
+    gated_residual,
+    modulated_rmsnorm,
+    qkvg_projection,
+    split_modulation,
+    stack_forward,
+    swiglu_mlp,
+    time_embedding,
+    timestep_modulation,
+)

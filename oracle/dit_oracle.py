@@ -1,0 +1,231 @@
+"""Plain float64 oracle of the Krea 2 single-stream DiT block forward.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring for who may use it and
+for the parity status of each function).  Everything is computed in numpy
+float64 from float64 copies of the inputs; nothing is rounded, blocked,
+fused or reordered beyond the definitions written out below.  Matrix
+products use ``np.matmul`` (BLAS dgemm) as a library primitive.
+
+Sources.  The pages are web pages about Krea 2.  The block is described on
+the page "Krea 2 技术报告" (a Chinese translation of the Krea 2 technical
+report), section 架构 (architecture):
+
+* 架构 › Transformer块 -- SwiGLU MLP with 4x expansion replaces the GeLU
+  MLP; grouped-query attention (GQA, the report's reference 45) with the
+  sigmoid-gated attention of "Gated Attention for LLMs" (reference 47);
+  single-stream block = one set of attention and MLP weights shared by
+  text and image tokens, run over the joint sequence.
+* 架构 › 时间步条件化 -- AdaLN-style timestep conditioning is kept, but
+  the per-block MLPs that produce shift/scale/gate are replaced by a
+  per-block tunable bias; sinusoidal time embeddings are named.
+* 架构 › 残差设计 -- standard residual connections.
+* 架构 › 归一化 -- all norms are RMSNorm (the report's reference 51),
+  zero-centred, with weight decay on the learnable parameters.
+
+The page "Krea 2: Laporan teknis model gambar open-weight 12B" (section
+"Pemilihan arsitektur dan ablation") lists the same final choices.
+
+Readings where the pages leave a step open (each is also a test):
+
+* Modulation vector per block: mod = m[b] + bias_block, split in the order
+  shift1, scale1, gate1, shift2, scale2, gate2.
+* Zero-centred RMSNorm: gain (1 + w) with w stored around zero (w = 0 is
+  the identity gain; weight decay pulls the gain towards 1).  Not a mean
+  subtraction: that would be the LayerNorm the report replaced.
+* Modulated norm: h = rmsnorm(x) * (1 + w) * (1 + scale) + shift, eps
+  inside the square root.
+* Gated residual: x + gate * branch (zero gates give the identity block).
+* Gated attention: softmax attention per query head, then an elementwise
+  sigmoid gate over the H*d output channels, computed from the same
+  normalised input as Q/K/V, applied before the output projection.
+* Softmax scale 1/sqrt(head_dim); query head h reads KV head
+  h // (H / Hkv) (contiguous groups); no mask, no positional terms.
+* No linear biases; SwiGLU: silu(h W1^T) * (h W3^T), then W2.
+* Timestep map (parity unpinned): e = [cos(1000 t f_i), sin(1000 t f_i)],
+  f_i = 10000^(-i/(n/2)), m = W_t2 silu(W_t1 e), bias-free, shared by all
+  blocks.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Callable, Iterable, Sequence
+
+import numpy as np
+
+F64 = np.float64
+
+
+@dataclasses.dataclass(frozen=True)
+class OracleConfig:
+    hidden: int
+    n_heads: int
+    n_kv_heads: int
+    head_dim: int
+    ffn: int
+    eps: float = 1e-6
+
+    @classmethod
+    def of(cls, cfg) -> "OracleConfig":
+        """Take the model dimensions from any object that carries them."""
+        return cls(cfg.hidden, cfg.n_heads, cfg.n_kv_heads, cfg.head_dim, cfg.ffn, cfg.eps)
+
+
+def _f64(a) -> np.ndarray:
+    return np.asarray(a, dtype=F64)
+
+
+def silu(z: np.ndarray) -> np.ndarray:
+    return z / (1.0 + np.exp(-z))
+
+
+def sigmoid(z: np.ndarray) -> np.ndarray:
+    return 1.0 / (1.0 + np.exp(-z))
+
+
+# ------------------------------------------------------------------ timestep
+def time_embedding(t, dim: int = 256, t_scale: float = 1000.0, max_period: float = 10000.0) -> np.ndarray:
+    """Sinusoidal embedding [B, dim]: cos of the scaled time at dim/2
+    geometric frequencies, then sin at the same frequencies (page
+    "Krea 2 技术报告", 架构 › 时间步条件化 names sinusoidal time embeddings;
+    width, scale and frequency ladder are this build's reading)."""
+    t = _f64(t).reshape(-1)
+    half = dim // 2
+    freqs = max_period ** (-np.arange(half, dtype=F64) / half)
+    arg = t_scale * t[:, None] * freqs[None, :]
+    return np.concatenate([np.cos(arg), np.sin(arg)], axis=1)
+
+
+def timestep_modulation(t, w_t1, w_t2, hidden: int) -> np.ndarray:
+    """m = W_t2 silu(W_t1 e(t)), reshaped to [B, 6, D] (parity unpinned:
+    the shared map from t to the modulation vector is a reading)."""
+    w_t1, w_t2 = _f64(w_t1), _f64(w_t2)
+    e = time_embedding(t, dim=w_t1.shape[1])
+    z = e @ w_t1.T
+    m = silu(z) @ w_t2.T
+    return m.reshape(-1, 6, hidden)
+
+
+def split_modulation(mod_b, bias) -> tuple:
+    """Per-block modulation of one sample: m[b] + block bias, split into
+    shift1, scale1, gate1, shift2, scale2, gate2 (page "Krea 2 技术报告",
+    架构 › 时间步条件化: per-block tunable bias instead of per-block MLP)."""
+    v = _f64(mod_b) + _f64(bias)
+    return tuple(v[i] for i in range(6))
+
+
+# ------------------------------------------------------------------ steps
+def modulated_rmsnorm(x, w, shift, scale, eps: float) -> np.ndarray:
+    """Zero-centred RMSNorm with adaLN shift/scale over the last axis:
+    x / sqrt(mean(x^2) + eps) * (1 + w) * (1 + scale) + shift
+    (page "Krea 2 技术报告", 架构 › 归一化 and 架构 › 时间步条件化)."""
+    x = _f64(x)
+    w = np.zeros(x.shape[-1]) if w is None else _f64(w)
+    rms = np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    return x / rms * (1.0 + w) * (1.0 + _f64(scale)) + _f64(shift)
+
+
+def qkvg_projection(h, w_qkvg, oc: OracleConfig):
+    """Z = h W_qkvg^T, split by columns into Q [.., H, d], K [.., Hkv, d],
+    V [.., Hkv, d], G [.., H, d] (row blocks of W_qkvg: Q | K | V | G)."""
+    z = _f64(h) @ _f64(w_qkvg).T
+    H, Hk, d = oc.n_heads, oc.n_kv_heads, oc.head_dim
+    lead = z.shape[:-1]
+    q = z[..., : H * d].reshape(*lead, H, d)
+    k = z[..., H * d : (H + Hk) * d].reshape(*lead, Hk, d)
+    v = z[..., (H + Hk) * d : (H + 2 * Hk) * d].reshape(*lead, Hk, d)
+    g = z[..., (H + 2 * Hk) * d :].reshape(*lead, H, d)
+    return q, k, v, g
+
+
+def gated_gqa_attention(q, k, v, g) -> np.ndarray:
+    """One sample.  q, g: [Lq, H, d]; k, v: [Lk, Hkv, d].  Returns [Lq, H*d].
+
+    For query head h with KV head j = h // (H/Hkv):
+    O_h = softmax(Q_h K_j^T / sqrt(d)) V_j  (max-subtracted softmax over
+    all keys, no mask, no positions), then O_h * sigmoid(G_h)
+    (page "Krea 2 技术报告", 架构 › Transformer块: GQA with a sigmoid
+    output gate).
+    """
+    q, k, v, g = _f64(q), _f64(k), _f64(v), _f64(g)
+    lq, H, d = q.shape
+    Hk = k.shape[1]
+    group = H // Hk
+    out = np.empty((lq, H, d))
+    for h in range(H):
+        j = h // group
+        s = (q[:, h, :] @ k[:, j, :].T) / np.sqrt(d)
+        s = s - s.max(axis=1, keepdims=True)
+        p = np.exp(s)
+        p = p / p.sum(axis=1, keepdims=True)
+        out[:, h, :] = (p @ v[:, j, :]) * sigmoid(g[:, h, :])
+    return out.reshape(lq, H * d)
+
+
+def swiglu_mlp(h, w_13, w_2, ffn: int) -> np.ndarray:
+    """silu(h W1^T) * (h W3^T), then W2 (page "Krea 2 技术报告",
+    架构 › Transformer块: SwiGLU, the report's reference 44).  W_13 holds
+    W1 in its first ffn rows and W3 in the next ffn rows."""
+    u = swiglu_hidden(h, w_13, ffn)
+    return u @ _f64(w_2).T
+
+
+def swiglu_hidden(h, w_13, ffn: int) -> np.ndarray:
+    w_13 = _f64(w_13)
+    a = _f64(h) @ w_13[:ffn].T
+    b = _f64(h) @ w_13[ffn:].T
+    return silu(a) * b
+
+
+def gated_residual(x, gate, y) -> np.ndarray:
+    """x + gate * y (page "Krea 2 技术报告", 架构 › 残差设计: standard
+    residual; the adaLN gate scales the branch)."""
+    return _f64(x) + _f64(gate) * _f64(y)
+
+
+# ------------------------------------------------------------------ block
+def _sample_forward(x, mod_b, wts, oc: OracleConfig, rows=None):
+    """Block forward of one sample x [L, D]; outputs for ``rows`` (all if None)."""
+    shift1, scale1, gate1, shift2, scale2, gate2 = split_modulation(mod_b, wts.mod_bias)
+    x = _f64(x)
+    h1 = modulated_rmsnorm(x, wts.norm1_w, shift1, scale1, oc.eps)
+    w_qkvg = _f64(wts.w_qkvg)
+    H, Hk, d = oc.n_heads, oc.n_kv_heads, oc.head_dim
+    # keys and values need every token; queries and gates only the rows asked for
+    kv = h1 @ w_qkvg[H * d : (H + 2 * Hk) * d].T
+    k = kv[:, : Hk * d].reshape(-1, Hk, d)
+    v = kv[:, Hk * d :].reshape(-1, Hk, d)
+    xr = x if rows is None else x[rows]
+    hr = h1 if rows is None else h1[rows]
+    q = (hr @ w_qkvg[: H * d].T).reshape(-1, H, d)
+    g = (hr @ w_qkvg[(H + 2 * Hk) * d :].T).reshape(-1, H, d)
+    og = gated_gqa_attention(q, k, v, g)
+    a = og @ _f64(wts.w_o).T
+    x1 = gated_residual(xr, gate1, a)
+    h2 = modulated_rmsnorm(x1, wts.norm2_w, shift2, scale2, oc.eps)
+    mlp = swiglu_mlp(h2, wts.w_13, wts.w_2, oc.ffn)
+    return gated_residual(x1, gate2, mlp)
+
+
+def block_forward(x, mod, wts, oc: OracleConfig) -> np.ndarray:
+    """x [B, L, D], mod [B, 6, D] -> [B, L, D]; samples are independent."""
+    x = _f64(x)
+    return np.stack([_sample_forward(x[b], mod[b], wts, oc) for b in range(x.shape[0])])
+
+
+def block_forward_rows(x, mod, wts, oc: OracleConfig, b: int, rows: Sequence[int]) -> np.ndarray:
+    """The same definition evaluated only at query tokens ``rows`` of sample b."""
+    return _sample_forward(_f64(x[b]), mod[b], wts, oc, rows=np.asarray(rows))
+
+
+def stack_forward(x, mod, weights: Iterable | Callable[[int], object], n_blocks: int,
+                  oc: OracleConfig) -> np.ndarray:
+    """Apply blocks 0..n_blocks-1 in order with one shared modulation m.
+
+    ``weights`` is either a sequence of per-block weights or a function
+    block index -> weights, so large stacks can be streamed one block at a
+    time."""
+    get = weights if callable(weights) else (lambda i, _w=list(weights): _w[i])
+    y = _f64(x)
+    for i in range(n_blocks):
+        y = block_forward(y, mod, get(i), oc)
+    return y

@@ -1,0 +1,320 @@
+"""Pins of the fp64 oracle against things other than itself (CPU only).
+
+* an independent scalar-loop brute force on tiny shapes;
+* torch's own float64 CPU routines (rms_norm, linear,
+  scaled_dot_product_attention, silu, sigmoid) composed per the readings;
+* closed forms and invariants the definitions fix.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import datagen
+from oracle import bruteforce
+from oracle import dit_oracle as O
+
+
+def tiny_cfg(batch=1, L=5, hkv=2, seed=7, D=8, H=2, d=4, ffn=8):
+    return datagen.Config("tiny", batch=batch, n_image=L, n_text=0, hidden=D, n_heads=H,
+                          n_kv_heads=hkv, head_dim=d, ffn=ffn, dtype="f32", seed=seed,
+                          w_std=0.5, out_std=0.5, mod_std=1.0)
+
+
+def inputs(cfg, strong=True):
+    x = datagen.activations(cfg)
+    w = datagen.block_weights(cfg, 0)
+    mod = datagen.block_mod(cfg, strong=strong)
+    return x, w, mod
+
+
+def oc(cfg):
+    return O.OracleConfig.of(cfg)
+
+
+# ------------------------------------------------------------------ brute force
+@pytest.mark.parametrize("batch", [1, 2])
+@pytest.mark.parametrize("L", [1, 2, 3, 5, 7])
+@pytest.mark.parametrize("hkv", [1, 2])
+def test_block_matches_bruteforce(batch, L, hkv):
+    cfg = tiny_cfg(batch=batch, L=L, hkv=hkv, seed=100 + 10 * L + hkv)
+    x, w, mod = inputs(cfg)
+    ref = O.block_forward(x, mod, w, oc(cfg))
+    bf = np.array(bruteforce.block(x, mod, w, cfg.n_heads, cfg.n_kv_heads, cfg.head_dim, cfg.ffn, cfg.eps))
+    assert np.max(np.abs(ref - bf)) <= 1e-12 * max(1.0, np.max(np.abs(bf)))
+    # the update itself (not just x + small) must agree as well
+    dref, dbf = ref - x, bf - x
+    assert np.max(np.abs(dref - dbf)) <= 1e-12 * max(1.0, np.max(np.abs(dbf)))
+    assert np.max(np.abs(dbf)) > 1e-2  # the block did real work
+
+
+def test_bruteforce_four_heads_two_groups():
+    cfg = tiny_cfg(batch=1, L=4, hkv=2, H=4, D=16, d=4, ffn=12, seed=5)
+    x, w, mod = inputs(cfg)
+    ref = O.block_forward(x, mod, w, oc(cfg))
+    bf = np.array(bruteforce.block(x, mod, w, 4, 2, 4, 12, cfg.eps))
+    assert np.max(np.abs(ref - bf)) <= 1e-12 * np.max(np.abs(bf))
+
+
+def test_time_embedding_matches_bruteforce():
+    t = np.array([0.0, 0.25, 0.731, 1.0])
+    ref = O.time_embedding(t, 256)
+    bf = np.array(bruteforce.time_embedding(t, 256))
+    assert np.max(np.abs(ref - bf)) <= 1e-9  # arguments up to 1000 rad
+
+
+# ------------------------------------------------------------------ torch library routines
+def torch_block(x, mod, w, cfg):
+    """The block composed of torch float64 CPU library routines."""
+    t = lambda a: torch.as_tensor(np.asarray(a, dtype=np.float64))
+    X, M = t(x), t(mod)
+    bias = t(w.mod_bias)
+    H, Hk, d, D, Fn = cfg.n_heads, cfg.n_kv_heads, cfg.head_dim, cfg.hidden, cfg.ffn
+    out = []
+    for b in range(X.shape[0]):
+        m = M[b] + bias
+        xb = X[b]
+        h1 = F.rms_norm(xb, (D,), weight=1 + t(w.norm1_w), eps=cfg.eps) * (1 + m[1]) + m[0]
+        z = F.linear(h1, t(w.w_qkvg))
+        q = z[:, : H * d].reshape(-1, H, d).transpose(0, 1)
+        k = z[:, H * d:(H + Hk) * d].reshape(-1, Hk, d).transpose(0, 1)
+        v = z[:, (H + Hk) * d:(H + 2 * Hk) * d].reshape(-1, Hk, d).transpose(0, 1)
+        g = z[:, (H + 2 * Hk) * d:]
+        k = k.repeat_interleave(H // Hk, dim=0)
+        v = v.repeat_interleave(H // Hk, dim=0)
+        o = F.scaled_dot_product_attention(q[None], k[None], v[None])[0]
+        o = o.transpose(0, 1).reshape(-1, H * d) * torch.sigmoid(g)
+        x1 = xb + m[2] * F.linear(o, t(w.w_o))
+        h2 = F.rms_norm(x1, (D,), weight=1 + t(w.norm2_w), eps=cfg.eps) * (1 + m[4]) + m[3]
+        up = F.linear(h2, t(w.w_13))
+        u = F.silu(up[:, :Fn]) * up[:, Fn:]
+        out.append(x1 + m[5] * F.linear(u, t(w.w_2)))
+    return torch.stack(out).numpy()
+
+
+@pytest.mark.parametrize("name", ["c0"])
+@pytest.mark.parametrize("strong", [False, True])
+def test_block_matches_torch_routines(name, strong):
+    cfg = datagen.get_config(name).replace(batch=2)
+    x, w, mod = inputs(cfg, strong=strong)
+    ref = O.block_forward(x, mod, w, oc(cfg))
+    lib = torch_block(x, mod, w, cfg)
+    assert np.max(np.abs(ref - lib)) <= 1e-12 * np.max(np.abs(lib))
+    d1, d2 = ref - x, lib - x
+    assert np.max(np.abs(d1 - d2)) <= 1e-11 * np.max(np.abs(d2))
+
+
+def test_attention_matches_sdpa_gqa():
+    rng = np.random.default_rng(3)
+    L, H, Hk, d = 37, 8, 2, 16
+    q, g = rng.standard_normal((L, H, d)), rng.standard_normal((L, H, d))
+    k, v = rng.standard_normal((L, Hk, d)), rng.standard_normal((L, Hk, d))
+    ref = O.gated_gqa_attention(q, k, v, g).reshape(L, H, d)
+    T = lambda a: torch.as_tensor(a).transpose(0, 1)[None]
+    o = F.scaled_dot_product_attention(T(q), T(k), T(v), enable_gqa=True)[0].transpose(0, 1)
+    lib = o.numpy() * (1 / (1 + np.exp(-g)))
+    assert np.max(np.abs(ref - lib)) <= 1e-13
+
+
+# ------------------------------------------------------------------ closed forms / invariants
+def test_one_key_returns_gated_value():
+    rng = np.random.default_rng(1)
+    q, g = rng.standard_normal((1, 4, 8)), rng.standard_normal((1, 4, 8))
+    k, v = rng.standard_normal((1, 2, 8)), rng.standard_normal((1, 2, 8))
+    og = O.gated_gqa_attention(q, k, v, g).reshape(1, 4, 8)
+    for h in range(4):
+        np.testing.assert_allclose(og[0, h], v[0, h // 2] / (1 + np.exp(-g[0, h])), rtol=0, atol=1e-15)
+
+
+def test_two_keys_weights_are_logistic():
+    rng = np.random.default_rng(2)
+    d = 16
+    q = rng.standard_normal((1, 1, d))
+    k = rng.standard_normal((2, 1, d))
+    v = rng.standard_normal((2, 1, d))
+    g = np.full((1, 1, d), 50.0)  # sigmoid(50) = 1 - 2e-22 -> 1 in fp64
+    s = k[:, 0, :] @ q[0, 0] / math.sqrt(d)
+    w0 = 1 / (1 + math.exp(-(s[0] - s[1])))
+    expect = w0 * v[0, 0] + (1 - w0) * v[1, 0]
+    np.testing.assert_allclose(O.gated_gqa_attention(q, k, v, g)[0], expect, rtol=0, atol=1e-14)
+
+
+def test_identical_keys_give_mean_value():
+    rng = np.random.default_rng(4)
+    L, d = 9, 8
+    q = rng.standard_normal((L, 2, d))
+    k = np.repeat(rng.standard_normal((1, 1, d)), L, axis=0)
+    v = rng.standard_normal((L, 1, d))
+    g = np.full((L, 2, d), 60.0)
+    og = O.gated_gqa_attention(q, k, v, g).reshape(L, 2, d)
+    np.testing.assert_allclose(og, np.broadcast_to(v.mean(axis=0)[None], (L, 2, d)), atol=1e-14)
+
+
+def test_gqa_equals_mha_with_replicated_kv():
+    cfg = tiny_cfg(batch=2, L=6, hkv=2, H=4, D=16, d=4, ffn=12, seed=9)
+    x, w, mod = inputs(cfg)
+    ref = O.block_forward(x, mod, w, oc(cfg))
+    H, Hk, d = 4, 2, 4
+    wq = w.w_qkvg
+    q_rows, k_rows = wq[: H * d], wq[H * d:(H + Hk) * d]
+    v_rows, g_rows = wq[(H + Hk) * d:(H + 2 * Hk) * d], wq[(H + 2 * Hk) * d:]
+    rep = lambda r: np.concatenate([r[(h // (H // Hk)) * d:(h // (H // Hk) + 1) * d] for h in range(H)])
+    w_mha = datagen.BlockWeights(np.concatenate([q_rows, rep(k_rows), rep(v_rows), g_rows]),
+                                 w.w_o, w.w_13, w.w_2, w.mod_bias, w.norm1_w, w.norm2_w)
+    mha = O.block_forward(x, mod, w_mha, oc(cfg.replace(n_kv_heads=4)))
+    assert np.max(np.abs(ref - mha)) <= 1e-13 * np.max(np.abs(ref))
+
+
+def test_group_size_one_is_mha_per_head():
+    rng = np.random.default_rng(5)
+    L, H, d = 7, 3, 8
+    q, k, v, g = (rng.standard_normal((L, H, d)) for _ in range(4))
+    og = O.gated_gqa_attention(q, k, v, g).reshape(L, H, d)
+    for h in range(H):
+        s = q[:, h] @ k[:, h].T / math.sqrt(d)
+        p = np.exp(s - s.max(1, keepdims=True))
+        p /= p.sum(1, keepdims=True)
+        np.testing.assert_allclose(og[:, h], (p @ v[:, h]) / (1 + np.exp(-g[:, h])), atol=1e-14)
+
+
+def test_zero_gates_make_block_identity():
+    cfg = datagen.get_config("c0")
+    x, w, mod = inputs(cfg)
+    mod = mod.copy()
+    w.mod_bias = w.mod_bias.copy()
+    for i in (2, 5):
+        mod[:, i, :] = 0
+        w.mod_bias[i] = 0
+    np.testing.assert_array_equal(O.block_forward(x, mod, w, oc(cfg)), x.astype(np.float64))
+
+
+def test_gate_logits_to_minus_inf_zero_the_attention_branch():
+    cfg = tiny_cfg(batch=1, L=5, hkv=1, seed=11)
+    x, w, mod = inputs(cfg)
+    H, Hk, d = cfg.n_heads, cfg.n_kv_heads, cfg.head_dim
+    w.w_qkvg = w.w_qkvg.copy()
+    w.w_qkvg[(H + 2 * Hk) * d:] = 0
+    oc_ = oc(cfg)
+    # with G = -inf the attention output is exactly zero, so x1 = x
+    q, k, v, g = O.qkvg_projection(np.ones((5, cfg.hidden)), w.w_qkvg, oc_)
+    with np.errstate(over="ignore"):
+        og = O.gated_gqa_attention(q, k, v, np.full_like(g, -1e4))
+    assert np.all(og == 0)
+    # and gate1 = 0 gives the same x1: compare two blocks that differ only in W_o
+    mod2 = mod.copy()
+    mod2[:, 2, :] = -w.mod_bias[2]
+    w_b = datagen.BlockWeights(w.w_qkvg, w.w_o * 3.0, w.w_13, w.w_2, w.mod_bias, w.norm1_w, w.norm2_w)
+    np.testing.assert_array_equal(O.block_forward(x, mod2, w, oc_), O.block_forward(x, mod2, w_b, oc_))
+
+
+def test_scale_minus_one_gives_shift():
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal((5, 32))
+    shift = rng.standard_normal(32)
+    h = O.modulated_rmsnorm(x, rng.standard_normal(32), shift, -np.ones(32), 1e-6)
+    np.testing.assert_array_equal(h, np.broadcast_to(shift, h.shape))
+
+
+def test_rmsnorm_unit_rms_and_scale_invariance():
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((6, 64)) * 3.0
+    z = np.zeros(64)
+    h = O.modulated_rmsnorm(x, None, z, z, 0.0)
+    np.testing.assert_allclose(np.sqrt(np.mean(h * h, axis=1)), 1.0, atol=1e-14)
+    np.testing.assert_allclose(O.modulated_rmsnorm(5.5 * x, None, z, z, 0.0), h, atol=1e-14)
+    # eps sits inside the square root: a zero row stays finite and maps to shift
+    shift = rng.standard_normal(64)
+    np.testing.assert_array_equal(O.modulated_rmsnorm(np.zeros((1, 64)), None, shift, z, 1e-6)[0], shift)
+    # the zero-centred gain: w multiplies as (1 + w)
+    w = rng.standard_normal(64)
+    np.testing.assert_allclose(O.modulated_rmsnorm(x, w, z, z, 0.0), h * (1 + w), atol=1e-14)
+    np.testing.assert_allclose(np.sqrt(np.mean(x[:1] ** 2)) * h[0], x[0], atol=1e-13)
+
+
+def test_swiglu_zero_w1_is_zero_and_scalar_formula():
+    rng = np.random.default_rng(8)
+    h = rng.standard_normal((3, 8))
+    w13 = rng.standard_normal((10, 8))
+    w2 = rng.standard_normal((8, 5))
+    z13 = w13.copy()
+    z13[:5] = 0
+    assert np.all(O.swiglu_mlp(h, z13, w2, 5) == 0)
+    u = O.swiglu_hidden(h, w13, 5)
+    for r in range(3):
+        for f in range(5):
+            a = float(h[r] @ w13[f])
+            b = float(h[r] @ w13[5 + f])
+            assert abs(u[r, f] - a / (1 + math.exp(-a)) * b) <= 1e-13
+
+
+def test_permutation_equivariance_and_batch_independence():
+    cfg = datagen.get_config("c0").replace(batch=2)
+    x, w, mod = inputs(cfg, strong=True)
+    ref = O.block_forward(x, mod, w, oc(cfg))
+    perm = np.random.default_rng(9).permutation(cfg.seq_len)
+    per = O.block_forward(x[:, perm], mod, w, oc(cfg))
+    assert np.max(np.abs(per - ref[:, perm])) <= 1e-12 * np.max(np.abs(ref))
+    one = O.block_forward(x[1:2], mod[1:2], w, oc(cfg))
+    np.testing.assert_array_equal(one[0], ref[1])
+
+
+def test_rows_and_stack_agree_with_block():
+    cfg = datagen.get_config("c0").replace(batch=2)
+    x, w, mod = inputs(cfg, strong=True)
+    ref = O.block_forward(x, mod, w, oc(cfg))
+    rows = [0, 17, 63, 64, 79]
+    r = O.block_forward_rows(x, mod, w, oc(cfg), 1, rows)
+    assert np.max(np.abs(r - ref[1, rows])) <= 1e-13 * np.max(np.abs(ref))
+    w1 = datagen.block_weights(cfg, 1)
+    two = O.stack_forward(x, mod, [w, w1], 2, oc(cfg))
+    np.testing.assert_array_equal(two, O.block_forward(ref, mod, w1, oc(cfg)))
+
+
+def test_time_embedding_closed_forms():
+    e = O.time_embedding([0.0], 256)[0]
+    np.testing.assert_array_equal(e, np.r_[np.ones(128), np.zeros(128)])
+    # lowest-index frequency is 1 rad per unit of scaled time: t = pi/1000 gives cos = -1
+    e = O.time_embedding([math.pi / 1000], 256)[0]
+    assert abs(e[0] + 1) < 1e-15 and abs(e[128]) < 1e-15
+    # the frequency ladder is geometric down to 10000^(-127/128); at i = 64, f = 1e-2
+    t = 0.5 * math.pi / 1000 / 1e-2
+    e = O.time_embedding([t], 256)[0]
+    assert abs(e[64]) < 1e-12 and abs(e[128 + 64] - 1) < 1e-12
+    e = O.time_embedding(np.linspace(0, 1, 11), 256)
+    np.testing.assert_allclose(e[:, :128] ** 2 + e[:, 128:] ** 2, 1.0, atol=1e-15)
+
+
+def test_timestep_modulation_structure():
+    rng = np.random.default_rng(10)
+    D = 16
+    t = np.array([0.3, 0.9])
+    w1 = rng.standard_normal((D, 256)) * 0.1
+    w2 = rng.standard_normal((6 * D, D)) * 0.1
+    m = O.timestep_modulation(t, w1, w2, D)
+    assert m.shape == (2, 6, D)
+    e = np.array(bruteforce.time_embedding(t, 256))
+    z = np.array([[sum(w1[r, c] * e[b, c] for c in range(256)) for r in range(D)] for b in range(2)])
+    s = z / (1 + np.exp(-z))
+    expect = np.array([[sum(w2[o, r] * s[b, r] for r in range(D)) for o in range(6 * D)] for b in range(2)])
+    np.testing.assert_allclose(m.reshape(2, -1), expect, atol=1e-12)
+    assert np.all(O.timestep_modulation(t, w1, np.zeros_like(w2), D) == 0)
+
+
+def test_parameter_count_pins_elementwise_gate():
+    """An elementwise sigmoid gate (H*d extra output rows of W_qkvg) gives the
+    ~11.7B parameters of the 60-block stack; the 12B model of the page
+    "Krea 2: Laporan teknis model gambar open-weight 12B" (title)."""
+    c4 = datagen.get_config("c4")
+    stack = c4.n_blocks * c4.block_params()
+    assert abs(stack - 11.64e9) < 0.01e9
+    total = stack + c4.timestep_params()
+    assert abs(total - 11.74e9) < 0.01e9
+    assert abs(2 * stack / 1e9 - 23.28) < 0.01  # bf16 bytes of the block weights
+    # a per-head gate (H outputs instead of H*d) would give ~10.7B: not ~11.7B
+    per_head = stack - c4.n_blocks * (c4.n_heads * c4.head_dim - c4.n_heads) * c4.hidden
+    assert per_head < 10.8e9
+    # SwiGLU width: 2/3 * 4 * D rounded up to a multiple of 256
+    assert c4.ffn == int(math.ceil(2 / 3 * 4 * 4096 / 256) * 256)
+    assert datagen.get_config("c0").ffn == int(math.ceil(2 / 3 * 4 * 256 / 16) * 16)
