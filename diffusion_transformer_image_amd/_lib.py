@@ -1,0 +1,212 @@
+"""ctypes binding of libdit.so (argument marshalling only).
+
+Every function here forwards to the C ABI declared in ``include/dit.h``;
+all arithmetic runs in the library's gfx950 kernels.  Torch tensors are used
+for device memory and streams only: their ``data_ptr()`` and the current
+HIP stream are passed through.  If the library has not been built the first
+call raises ``RuntimeError``: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Mapping, Sequence
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libdit.so")
+
+DIT_F32, DIT_BF16 = 0, 1
+STATUS = {0: "DIT_OK", 1: "DIT_ERR_NULL", 2: "DIT_ERR_SHAPE", 3: "DIT_ERR_UNSUPPORTED",
+          4: "DIT_ERR_ALIGN", 5: "DIT_ERR_WORKSPACE", 6: "DIT_ERR_DTYPE", 7: "DIT_ERR_HIP"}
+KERNEL_KINDS = {"modnorm": 0, "gemm_qkvg": 1, "attn": 2, "gemm_o": 3, "resid": 4,
+                "gemm_w13": 5, "gemm_w2": 6, "tmod": 7}
+
+EXPORTS = (
+    "dit_workspace_size", "dit_stack_workspace_size", "dit_block_fwd", "dit_stack_fwd",
+    "dit_timestep_mod", "dit_modnorm", "dit_gemm", "dit_gemm_swiglu", "dit_attention",
+    "dit_gated_residual", "dit_status_str", "dit_last_hip_error", "dit_timer_start",
+    "dit_timer_stop",
+)
+
+
+class DitError(RuntimeError):
+    def __init__(self, status: int, where: str, hip: int = 0):
+        self.status = status
+        self.name = STATUS.get(status, str(status))
+        msg = f"{where}: {self.name}"
+        if status == 7:
+            msg += f" (hipError {hip})"
+        super().__init__(msg)
+
+
+class Config(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("seq_len", ctypes.c_int32), ("hidden", ctypes.c_int32),
+                ("n_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("ffn", ctypes.c_int32), ("eps", ctypes.c_float),
+                ("dtype", ctypes.c_int32)]
+
+
+class BlockWeights(ctypes.Structure):
+    _fields_ = [("w_qkvg", ctypes.c_void_p), ("w_o", ctypes.c_void_p), ("w_13", ctypes.c_void_p),
+                ("w_2", ctypes.c_void_p), ("mod_bias", ctypes.c_void_p),
+                ("norm1_w", ctypes.c_void_p), ("norm2_w", ctypes.c_void_p)]
+
+
+_LIB = None
+
+
+def lib() -> ctypes.CDLL:
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m diffusion_transformer_image_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        cfgp = ctypes.POINTER(Config)
+        wp = ctypes.POINTER(BlockWeights)
+        sig = {
+            "dit_workspace_size": (sz, [cfgp]),
+            "dit_stack_workspace_size": (sz, [cfgp]),
+            "dit_block_fwd": (i32, [cfgp, wp, vp, vp, vp, vp, sz, vp]),
+            "dit_stack_fwd": (i32, [cfgp, i32, wp, vp, vp, vp, vp, sz, vp]),
+            "dit_timestep_mod": (i32, [cfgp, i32, vp, vp, vp, vp, vp, sz, vp]),
+            "dit_modnorm": (i32, [cfgp, vp, i32, vp, vp, vp, vp, i32, vp]),
+            "dit_gemm": (i32, [i32, i32, i32, i32, vp, vp, vp, vp]),
+            "dit_gemm_swiglu": (i32, [i32, i32, i32, i32, vp, vp, vp, vp]),
+            "dit_attention": (i32, [cfgp, vp, vp, vp]),
+            "dit_gated_residual": (i32, [cfgp, vp, i32, vp, vp, vp, i32, vp, i32, vp]),
+            "dit_status_str": (ctypes.c_char_p, [i32]),
+            "dit_last_hip_error": (ctypes.c_int, []),
+            "dit_timer_start": (i32, [i32, i32]),
+            "dit_timer_stop": (i32, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32)]),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype, f.argtypes = res, args
+        _LIB = L
+    return _LIB
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise DitError(status, where, lib().dit_last_hip_error() if status == 7 else 0)
+
+
+# ------------------------------------------------------------------ marshalling
+def _dtype_code(t) -> int:
+    import torch
+    if t == torch.bfloat16 or t == "bf16" or t == DIT_BF16:
+        return DIT_BF16
+    if t == torch.float32 or t == "f32" or t == DIT_F32:
+        return DIT_F32
+    raise ValueError(f"unsupported dtype {t}")
+
+
+def _ptr(x) -> int | None:
+    """Device address of a tensor (or a raw int address, or None)."""
+    if x is None or isinstance(x, int):
+        return x
+    if not x.is_cuda:
+        raise ValueError("tensor must live on the GPU")
+    if not x.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return x.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def make_config(batch, seq_len, hidden, n_heads, n_kv_heads, head_dim, ffn, eps=1e-6,
+                dtype="bf16") -> Config:
+    return Config(batch, seq_len, hidden, n_heads, n_kv_heads, head_dim, ffn, eps,
+                  _dtype_code(dtype))
+
+
+def config_of(c, batch: int | None = None, seq_len: int | None = None) -> Config:
+    """Config from any object with the block's dimension attributes."""
+    return make_config(batch or c.batch, seq_len or c.seq_len, c.hidden, c.n_heads, c.n_kv_heads,
+                       c.head_dim, c.ffn, c.eps, c.dtype)
+
+
+def make_weights(w: Mapping) -> BlockWeights:
+    return BlockWeights(_ptr(w["w_qkvg"]), _ptr(w["w_o"]), _ptr(w["w_13"]), _ptr(w["w_2"]),
+                        _ptr(w["mod_bias"]), _ptr(w.get("norm1_w")), _ptr(w.get("norm2_w")))
+
+
+# ------------------------------------------------------------------ entry points
+def workspace_size(cfg: Config) -> int:
+    return lib().dit_workspace_size(ctypes.byref(cfg))
+
+
+def stack_workspace_size(cfg: Config) -> int:
+    return lib().dit_stack_workspace_size(ctypes.byref(cfg))
+
+
+def block_fwd(cfg: Config, w: Mapping, x_in, x_out, mod, ws, stream=None) -> None:
+    bw = make_weights(w)
+    nbytes = ws.numel() * ws.element_size() if hasattr(ws, "numel") else 0
+    _check(lib().dit_block_fwd(ctypes.byref(cfg), ctypes.byref(bw), _ptr(x_in), _ptr(x_out),
+                               _ptr(mod), _ptr(ws), nbytes, _stream(stream)), "dit_block_fwd")
+
+
+def stack_fwd(cfg: Config, blocks: Sequence[Mapping], x_in, x_out, mod, ws, stream=None) -> None:
+    arr = (BlockWeights * len(blocks))(*[make_weights(b) for b in blocks])
+    nbytes = ws.numel() * ws.element_size() if hasattr(ws, "numel") else 0
+    _check(lib().dit_stack_fwd(ctypes.byref(cfg), len(blocks), arr, _ptr(x_in), _ptr(x_out),
+                               _ptr(mod), _ptr(ws), nbytes, _stream(stream)), "dit_stack_fwd")
+
+
+def timestep_mod(cfg: Config, t, w_t1, w_t2, mod_out, ws, t_dim: int = 256, stream=None) -> None:
+    nbytes = ws.numel() * ws.element_size() if hasattr(ws, "numel") else 0
+    _check(lib().dit_timestep_mod(ctypes.byref(cfg), t_dim, _ptr(t), _ptr(w_t1), _ptr(w_t2),
+                                  _ptr(mod_out), _ptr(ws), nbytes, _stream(stream)),
+           "dit_timestep_mod")
+
+
+def modnorm(cfg: Config, x, h, mod, bias, gain, which: int, stream=None) -> None:
+    _check(lib().dit_modnorm(ctypes.byref(cfg), _ptr(x), _dtype_code(x.dtype), _ptr(h), _ptr(mod),
+                             _ptr(bias), _ptr(gain), which, _stream(stream)), "dit_modnorm")
+
+
+def gemm(a, w, c, stream=None) -> None:
+    m, k = a.shape
+    n = w.shape[0]
+    _check(lib().dit_gemm(_dtype_code(a.dtype), m, n, k, _ptr(a), _ptr(w), _ptr(c),
+                          _stream(stream)), "dit_gemm")
+
+
+def gemm_swiglu(a, w13, u, stream=None) -> None:
+    m, k = a.shape
+    f = w13.shape[0] // 2
+    _check(lib().dit_gemm_swiglu(_dtype_code(a.dtype), m, f, k, _ptr(a), _ptr(w13), _ptr(u),
+                                 _stream(stream)), "dit_gemm_swiglu")
+
+
+def attention(cfg: Config, qkvg, og, stream=None) -> None:
+    _check(lib().dit_attention(ctypes.byref(cfg), _ptr(qkvg), _ptr(og), _stream(stream)),
+           "dit_attention")
+
+
+def gated_residual(cfg: Config, x, y, mod, bias, which: int, out, stream=None) -> None:
+    _check(lib().dit_gated_residual(ctypes.byref(cfg), _ptr(x), _dtype_code(x.dtype), _ptr(y),
+                                    _ptr(mod), _ptr(bias), which, _ptr(out),
+                                    _dtype_code(out.dtype), _stream(stream)),
+           "dit_gated_residual")
+
+
+def timer_start(kind: str, capacity: int) -> None:
+    _check(lib().dit_timer_start(KERNEL_KINDS[kind], capacity), "dit_timer_start")
+
+
+def timer_stop() -> tuple[float, int]:
+    ms = ctypes.c_double(0.0)
+    n = ctypes.c_int32(0)
+    _check(lib().dit_timer_stop(ctypes.byref(ms), ctypes.byref(n)), "dit_timer_stop")
+    return ms.value, n.value

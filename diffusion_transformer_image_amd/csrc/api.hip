@@ -1,0 +1,425 @@
+// C ABI of libdit: argument checking, workspace carving, the block and
+// stack drivers, and the timing hook.  Every entry point checks all of its
+// arguments before the first HIP call; no exception crosses the ABI.
+#include <mutex>
+#include <vector>
+
+#include "../../include/dit.h"
+#include "dit_kernels.h"
+
+using namespace dit;
+
+namespace {
+
+thread_local int g_last_hip = 0;
+
+dit_status hip_fail(hipError_t e) {
+  g_last_hip = (int)e;
+  return DIT_ERR_HIP;
+}
+
+// ---------------------------------------------------------------- timing hook
+struct Timer {
+  std::mutex mu;
+  bool active = false;
+  int kind = -1;
+  int capacity = 0;
+  int count = 0;
+  std::vector<hipEvent_t> ev0, ev1;
+} g_timer;
+
+template <typename F>
+hipError_t timed(int kind, hipStream_t s, F &&launch) {
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  {
+    std::lock_guard<std::mutex> lk(g_timer.mu);
+    if (g_timer.active && g_timer.kind == kind && g_timer.count < g_timer.capacity) {
+      e0 = g_timer.ev0[g_timer.count];
+      e1 = g_timer.ev1[g_timer.count];
+      ++g_timer.count;
+    }
+  }
+  if (e0) {
+    hipError_t e = hipEventRecord(e0, s);
+    if (e != hipSuccess) return e;
+  }
+  hipError_t e = launch();
+  if (e != hipSuccess) return e;
+  if (e1) return hipEventRecord(e1, s);
+  return hipSuccess;
+}
+
+// ---------------------------------------------------------------- checks
+constexpr size_t kAlign = 256;
+constexpr uint64_t kMaxSpan = 0x7FFFFFF0ull;  // buffer-descriptor byte range
+
+size_t esize(dit_dtype t) { return t == DIT_BF16 ? 2 : 4; }
+bool dtype_ok(int t) { return t == DIT_F32 || t == DIT_BF16; }
+bool aligned(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool overlap(const void *a, size_t na, const void *b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+dit_status check_cfg(const dit_config *c) {
+  if (!c) return DIT_ERR_NULL;
+  if (!dtype_ok(c->dtype)) return DIT_ERR_DTYPE;
+  if (c->batch <= 0 || c->seq_len <= 0 || c->hidden <= 0 || c->n_heads <= 0 ||
+      c->n_kv_heads <= 0 || c->head_dim <= 0 || c->ffn <= 0 || !(c->eps >= 0.f))
+    return DIT_ERR_SHAPE;
+  if ((int64_t)c->n_heads * c->head_dim != c->hidden) return DIT_ERR_SHAPE;
+  if (c->n_heads % c->n_kv_heads != 0) return DIT_ERR_SHAPE;
+  if (c->n_heads / c->n_kv_heads > 4) return DIT_ERR_UNSUPPORTED;
+  if (c->dtype == DIT_BF16 ? c->head_dim != 128 : (c->head_dim != 64 && c->head_dim != 128))
+    return DIT_ERR_UNSUPPORTED;
+  if (c->hidden % 8 || c->ffn % 8) return DIT_ERR_UNSUPPORTED;
+  if (c->hidden > 8 * 64 * 32) return DIT_ERR_UNSUPPORTED;  // modnorm keeps a row in registers
+  const uint64_t es = esize(c->dtype);
+  const uint64_t nqkvg = (uint64_t)(2 * c->n_heads + 2 * c->n_kv_heads) * c->head_dim;
+  // byte ranges addressed through one buffer descriptor must stay below 2^31
+  if ((uint64_t)c->seq_len * nqkvg * es > kMaxSpan) return DIT_ERR_UNSUPPORTED;
+  if ((2ull * c->ffn + 256) * c->hidden * es > kMaxSpan) return DIT_ERR_UNSUPPORTED;
+  if ((uint64_t)c->batch * c->seq_len > 0x7FFFFFFFull) return DIT_ERR_SHAPE;
+  return DIT_OK;
+}
+
+struct Dims {
+  size_t T, D, nqkvg, hd, F, es;
+};
+Dims dims(const dit_config *c) {
+  Dims d;
+  d.T = (size_t)c->batch * c->seq_len;
+  d.D = c->hidden;
+  d.nqkvg = (size_t)(2 * c->n_heads + 2 * c->n_kv_heads) * c->head_dim;
+  d.hd = (size_t)c->n_heads * c->head_dim;
+  d.F = c->ffn;
+  d.es = esize(c->dtype);
+  return d;
+}
+
+struct BlockWs {
+  char *h, *qkvg, *og, *br, *x1;
+  size_t bytes;
+};
+BlockWs carve(const dit_config *c, void *ws) {
+  const Dims d = dims(c);
+  BlockWs w;
+  char *p = (char *)ws;
+  size_t off = 0;
+  auto take = [&](size_t n) {
+    char *r = p ? p + off : nullptr;
+    off += round_up(n);
+    return r;
+  };
+  w.h = take(d.T * d.D * d.es);
+  w.qkvg = take(d.T * (d.nqkvg > d.F ? d.nqkvg : d.F) * d.es);
+  w.og = take(d.T * d.hd * d.es);
+  w.br = take(d.T * d.D * d.es);
+  w.x1 = take(d.T * d.D * d.es);
+  const size_t tmod = (size_t)c->batch * c->hidden * 4;
+  w.bytes = off > tmod ? off : tmod;
+  return w;
+}
+
+dit_status check_weights(const dit_block_weights *w) {
+  if (!w) return DIT_ERR_NULL;
+  if (!w->w_qkvg || !w->w_o || !w->w_13 || !w->w_2 || !w->mod_bias) return DIT_ERR_NULL;
+  if (!aligned(w->w_qkvg) || !aligned(w->w_o) || !aligned(w->w_13) || !aligned(w->w_2) ||
+      !aligned(w->mod_bias) || !aligned(w->norm1_w) || !aligned(w->norm2_w))
+    return DIT_ERR_ALIGN;
+  return DIT_OK;
+}
+
+#define DIT_TRY(expr)                     \
+  do {                                    \
+    hipError_t e_ = (expr);               \
+    if (e_ != hipSuccess) return hip_fail(e_); \
+  } while (0)
+
+// One block, on the carved workspace.  x_in has dtype xin_f32 ? f32 : dtype;
+// x_out has xout_f32 ? f32 : dtype; x1 is stored in x1buf with x1_f32.
+dit_status run_block(const dit_config *c, const dit_block_weights *w, const void *x_in,
+                     bool xin_f32, void *x_out, bool xout_f32, const float *mod,
+                     const BlockWs &ws, void *x1buf, bool x1_f32, hipStream_t s) {
+  const Dims d = dims(c);
+  const bool f32 = c->dtype == DIT_F32;
+  const int T = (int)d.T, D = (int)d.D, L = c->seq_len;
+  DIT_TRY(timed(DIT_K_MODNORM, s, [&] {
+    return launch_modnorm(xin_f32, f32, x_in, ws.h, mod, w->mod_bias, w->norm1_w, T, L, D, c->eps, 0, s);
+  }));
+  DIT_TRY(timed(DIT_K_GEMM_QKVG, s, [&] {
+    return launch_gemm(f32, ws.h, w->w_qkvg, ws.qkvg, T, (int)d.nqkvg, D, s);
+  }));
+  DIT_TRY(timed(DIT_K_ATTN, s, [&] {
+    return launch_attention(f32, c->head_dim, ws.qkvg, ws.og, c->batch, L, c->n_heads, c->n_kv_heads, s);
+  }));
+  DIT_TRY(timed(DIT_K_GEMM_O, s, [&] {
+    return launch_gemm(f32, ws.og, w->w_o, ws.br, T, D, (int)d.hd, s);
+  }));
+  DIT_TRY(timed(DIT_K_RESID, s, [&] {
+    return launch_resid(xin_f32, f32, x1_f32, x_in, ws.br, x1buf, mod, w->mod_bias, T, L, D, 0, s);
+  }));
+  DIT_TRY(timed(DIT_K_MODNORM, s, [&] {
+    return launch_modnorm(x1_f32, f32, x1buf, ws.h, mod, w->mod_bias, w->norm2_w, T, L, D, c->eps, 1, s);
+  }));
+  DIT_TRY(timed(DIT_K_GEMM_W13, s, [&] {
+    return launch_gemm_swiglu(f32, ws.h, w->w_13, ws.qkvg, T, (int)d.F, D, s);
+  }));
+  DIT_TRY(timed(DIT_K_GEMM_W2, s, [&] {
+    return launch_gemm(f32, ws.qkvg, w->w_2, ws.br, T, D, (int)d.F, s);
+  }));
+  DIT_TRY(timed(DIT_K_RESID, s, [&] {
+    return launch_resid(x1_f32, f32, xout_f32, x1buf, ws.br, x_out, mod, w->mod_bias, T, L, D, 1, s);
+  }));
+  return DIT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *dit_status_str(dit_status s) {
+  switch (s) {
+    case DIT_OK: return "ok";
+    case DIT_ERR_NULL: return "null pointer";
+    case DIT_ERR_SHAPE: return "invalid or inconsistent shape (or aliasing buffers)";
+    case DIT_ERR_UNSUPPORTED: return "unsupported configuration";
+    case DIT_ERR_ALIGN: return "device pointer not 16-byte aligned";
+    case DIT_ERR_WORKSPACE: return "workspace missing or too small";
+    case DIT_ERR_DTYPE: return "unknown dtype";
+    case DIT_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+int dit_last_hip_error(void) { return g_last_hip; }
+
+size_t dit_workspace_size(const dit_config *cfg) {
+  if (check_cfg(cfg) != DIT_OK) return 0;
+  return carve(cfg, nullptr).bytes;
+}
+
+size_t dit_stack_workspace_size(const dit_config *cfg) {
+  if (check_cfg(cfg) != DIT_OK) return 0;
+  const Dims d = dims(cfg);
+  return carve(cfg, nullptr).bytes + 2 * round_up(d.T * d.D * 4);
+}
+
+dit_status dit_block_fwd(const dit_config *cfg, const dit_block_weights *w, const void *x_in,
+                         void *x_out, const float *mod, void *ws, size_t ws_bytes, void *stream) {
+  dit_status st = check_cfg(cfg);
+  if (st != DIT_OK) return st;
+  if ((st = check_weights(w)) != DIT_OK) return st;
+  if (!x_in || !x_out || !mod) return DIT_ERR_NULL;
+  if (!ws) return DIT_ERR_WORKSPACE;
+  if (!aligned(x_in) || !aligned(x_out) || !aligned(mod) || !aligned(ws)) return DIT_ERR_ALIGN;
+  const Dims d = dims(cfg);
+  const BlockWs need = carve(cfg, nullptr);
+  if (ws_bytes < need.bytes) return DIT_ERR_WORKSPACE;
+  const size_t xb = d.T * d.D * d.es;
+  if (overlap(x_in, xb, x_out, xb)) return DIT_ERR_SHAPE;
+  if (overlap(ws, need.bytes, x_in, xb) || overlap(ws, need.bytes, x_out, xb) ||
+      overlap(ws, need.bytes, mod, (size_t)cfg->batch * 6 * cfg->hidden * 4))
+    return DIT_ERR_SHAPE;
+  const BlockWs bw = carve(cfg, ws);
+  const bool f32 = cfg->dtype == DIT_F32;
+  return run_block(cfg, w, x_in, f32, x_out, f32, mod, bw, bw.x1, f32, (hipStream_t)stream);
+}
+
+dit_status dit_stack_fwd(const dit_config *cfg, int32_t n_blocks, const dit_block_weights *blocks,
+                         const void *x_in, void *x_out, const float *mod, void *ws, size_t ws_bytes,
+                         void *stream) {
+  dit_status st = check_cfg(cfg);
+  if (st != DIT_OK) return st;
+  if (n_blocks <= 0) return DIT_ERR_SHAPE;
+  if (!blocks) return DIT_ERR_NULL;
+  for (int i = 0; i < n_blocks; ++i)
+    if ((st = check_weights(&blocks[i])) != DIT_OK) return st;
+  if (!x_in || !x_out || !mod) return DIT_ERR_NULL;
+  if (!ws) return DIT_ERR_WORKSPACE;
+  if (!aligned(x_in) || !aligned(x_out) || !aligned(mod) || !aligned(ws)) return DIT_ERR_ALIGN;
+  const Dims d = dims(cfg);
+  const size_t need = dit_stack_workspace_size(cfg);
+  if (ws_bytes < need) return DIT_ERR_WORKSPACE;
+  const size_t xb = d.T * d.D * d.es;
+  if (overlap(x_in, xb, x_out, xb)) return DIT_ERR_SHAPE;
+  if (overlap(ws, need, x_in, xb) || overlap(ws, need, x_out, xb) ||
+      overlap(ws, need, mod, (size_t)cfg->batch * 6 * cfg->hidden * 4))
+    return DIT_ERR_SHAPE;
+  const BlockWs bw = carve(cfg, ws);
+  char *xa = (char *)ws + bw.bytes;  // fp32 residual stream
+  char *xb1 = xa + round_up(d.T * d.D * 4);  // fp32 x1
+  const bool f32 = cfg->dtype == DIT_F32;
+  hipStream_t s = (hipStream_t)stream;
+  for (int i = 0; i < n_blocks; ++i) {
+    const bool first = i == 0, last = i == n_blocks - 1;
+    st = run_block(cfg, &blocks[i], first ? x_in : xa, first ? f32 : true, last ? x_out : xa,
+                   last ? f32 : true, mod, bw, xb1, true, s);
+    if (st != DIT_OK) return st;
+  }
+  return DIT_OK;
+}
+
+dit_status dit_timestep_mod(const dit_config *cfg, int32_t t_dim, const float *t, const float *w_t1,
+                            const float *w_t2, float *mod_out, void *ws, size_t ws_bytes,
+                            void *stream) {
+  dit_status st = check_cfg(cfg);
+  if (st != DIT_OK) return st;
+  if (t_dim < 2 || t_dim > 1024 || (t_dim & 1)) return DIT_ERR_SHAPE;
+  if (!t || !w_t1 || !w_t2 || !mod_out) return DIT_ERR_NULL;
+  if (!ws) return DIT_ERR_WORKSPACE;
+  if (!aligned(t) || !aligned(w_t1) || !aligned(w_t2) || !aligned(mod_out) || !aligned(ws))
+    return DIT_ERR_ALIGN;
+  if (ws_bytes < (size_t)cfg->batch * cfg->hidden * 4) return DIT_ERR_WORKSPACE;
+  if ((uint64_t)6 * cfg->hidden * cfg->hidden > 0x7FFFFFFFull) return DIT_ERR_UNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = timed(DIT_K_TMOD, s, [&] {
+    return launch_tmod(t, w_t1, w_t2, mod_out, (float *)ws, cfg->batch, cfg->hidden, t_dim, s);
+  });
+  return e == hipSuccess ? DIT_OK : hip_fail(e);
+}
+
+dit_status dit_modnorm(const dit_config *cfg, const void *x, dit_dtype x_dtype, void *h,
+                       const float *mod, const float *bias, const float *gain, int32_t which,
+                       void *stream) {
+  dit_status st = check_cfg(cfg);
+  if (st != DIT_OK) return st;
+  if (!dtype_ok(x_dtype)) return DIT_ERR_DTYPE;
+  if (x_dtype != DIT_F32 && x_dtype != cfg->dtype) return DIT_ERR_DTYPE;
+  if (which != 0 && which != 1) return DIT_ERR_SHAPE;
+  if (!x || !h || !mod || !bias) return DIT_ERR_NULL;
+  if (!aligned(x) || !aligned(h) || !aligned(mod) || !aligned(bias) || !aligned(gain))
+    return DIT_ERR_ALIGN;
+  const Dims d = dims(cfg);
+  if (overlap(x, d.T * d.D * esize(x_dtype), h, d.T * d.D * d.es)) return DIT_ERR_SHAPE;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = timed(DIT_K_MODNORM, s, [&] {
+    return launch_modnorm(x_dtype == DIT_F32, cfg->dtype == DIT_F32, x, h, mod, bias, gain, (int)d.T,
+                          cfg->seq_len, (int)d.D, cfg->eps, which, s);
+  });
+  return e == hipSuccess ? DIT_OK : hip_fail(e);
+}
+
+static dit_status check_gemm(dit_dtype dtype, int32_t m, int32_t n, int32_t k, const void *a,
+                             const void *w, void *c, int64_t w_rows) {
+  if (!dtype_ok(dtype)) return DIT_ERR_DTYPE;
+  if (m <= 0 || n <= 0 || k <= 0) return DIT_ERR_SHAPE;
+  if (k % 8) return DIT_ERR_UNSUPPORTED;
+  if (!a || !w || !c) return DIT_ERR_NULL;
+  if (!aligned(a) || !aligned(w) || !aligned(c)) return DIT_ERR_ALIGN;
+  const uint64_t es = esize(dtype);
+  if ((uint64_t)w_rows * k * es > kMaxSpan) return DIT_ERR_UNSUPPORTED;
+  if ((uint64_t)256 * k * es > kMaxSpan) return DIT_ERR_UNSUPPORTED;
+  return DIT_OK;
+}
+
+dit_status dit_gemm(dit_dtype dtype, int32_t m, int32_t n, int32_t k, const void *a, const void *w,
+                    void *c, void *stream) {
+  dit_status st = check_gemm(dtype, m, n, k, a, w, c, 256);  // a tile spans <= 256 W rows
+  if (st != DIT_OK) return st;
+  const size_t es = esize(dtype);
+  if (overlap(c, (size_t)m * n * es, a, (size_t)m * k * es) ||
+      overlap(c, (size_t)m * n * es, w, (size_t)n * k * es))
+    return DIT_ERR_SHAPE;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_gemm(dtype == DIT_F32, a, w, c, m, n, k, s);
+  return e == hipSuccess ? DIT_OK : hip_fail(e);
+}
+
+dit_status dit_gemm_swiglu(dit_dtype dtype, int32_t m, int32_t f, int32_t k, const void *a,
+                           const void *w13, void *u, void *stream) {
+  dit_status st = check_gemm(dtype, m, f, k, a, w13, u, 2 * (int64_t)f + 256);
+  if (st != DIT_OK) return st;
+  const size_t es = esize(dtype);
+  if (overlap(u, (size_t)m * f * es, a, (size_t)m * k * es) ||
+      overlap(u, (size_t)m * f * es, w13, (size_t)2 * f * k * es))
+    return DIT_ERR_SHAPE;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_gemm_swiglu(dtype == DIT_F32, a, w13, u, m, f, k, s);
+  return e == hipSuccess ? DIT_OK : hip_fail(e);
+}
+
+dit_status dit_attention(const dit_config *cfg, const void *qkvg, void *og, void *stream) {
+  dit_status st = check_cfg(cfg);
+  if (st != DIT_OK) return st;
+  if (!qkvg || !og) return DIT_ERR_NULL;
+  if (!aligned(qkvg) || !aligned(og)) return DIT_ERR_ALIGN;
+  const Dims d = dims(cfg);
+  if (overlap(qkvg, d.T * d.nqkvg * d.es, og, d.T * d.hd * d.es)) return DIT_ERR_SHAPE;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = timed(DIT_K_ATTN, s, [&] {
+    return launch_attention(cfg->dtype == DIT_F32, cfg->head_dim, qkvg, og, cfg->batch,
+                            cfg->seq_len, cfg->n_heads, cfg->n_kv_heads, s);
+  });
+  return e == hipSuccess ? DIT_OK : hip_fail(e);
+}
+
+dit_status dit_gated_residual(const dit_config *cfg, const void *x, dit_dtype x_dtype,
+                              const void *y, const float *mod, const float *bias, int32_t which,
+                              void *out, dit_dtype out_dtype, void *stream) {
+  dit_status st = check_cfg(cfg);
+  if (st != DIT_OK) return st;
+  if (!dtype_ok(x_dtype) || !dtype_ok(out_dtype)) return DIT_ERR_DTYPE;
+  if ((x_dtype != DIT_F32 && x_dtype != cfg->dtype) || (out_dtype != DIT_F32 && out_dtype != cfg->dtype))
+    return DIT_ERR_DTYPE;
+  if (which != 0 && which != 1) return DIT_ERR_SHAPE;
+  if (!x || !y || !mod || !bias || !out) return DIT_ERR_NULL;
+  if (!aligned(x) || !aligned(y) || !aligned(mod) || !aligned(bias) || !aligned(out))
+    return DIT_ERR_ALIGN;
+  const Dims d = dims(cfg);
+  const size_t n = d.T * d.D;
+  if (overlap(out, n * esize(out_dtype), y, n * d.es)) return DIT_ERR_SHAPE;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = timed(DIT_K_RESID, s, [&] {
+    return launch_resid(x_dtype == DIT_F32, cfg->dtype == DIT_F32, out_dtype == DIT_F32, x, y, out,
+                        mod, bias, (int)d.T, cfg->seq_len, (int)d.D, which, s);
+  });
+  return e == hipSuccess ? DIT_OK : hip_fail(e);
+}
+
+dit_status dit_timer_start(int32_t kind, int32_t capacity) {
+  if (kind < 0 || kind >= DIT_K_COUNT || capacity <= 0 || capacity > 1 << 16) return DIT_ERR_SHAPE;
+  std::lock_guard<std::mutex> lk(g_timer.mu);
+  for (size_t i = 0; i < g_timer.ev0.size(); ++i) {
+    (void)hipEventDestroy(g_timer.ev0[i]);
+    (void)hipEventDestroy(g_timer.ev1[i]);
+  }
+  g_timer.ev0.assign(capacity, nullptr);
+  g_timer.ev1.assign(capacity, nullptr);
+  for (int i = 0; i < capacity; ++i) {
+    hipError_t e = hipEventCreate(&g_timer.ev0[i]);
+    if (e == hipSuccess) e = hipEventCreate(&g_timer.ev1[i]);
+    if (e != hipSuccess) {
+      g_timer.ev0.resize(i);
+      g_timer.ev1.resize(i);
+      return hip_fail(e);
+    }
+  }
+  g_timer.kind = kind;
+  g_timer.capacity = capacity;
+  g_timer.count = 0;
+  g_timer.active = true;
+  return DIT_OK;
+}
+
+dit_status dit_timer_stop(double *total_ms, int32_t *n_launches) {
+  if (!total_ms || !n_launches) return DIT_ERR_NULL;
+  std::lock_guard<std::mutex> lk(g_timer.mu);
+  double tot = 0.0;
+  for (int i = 0; i < g_timer.count; ++i) {
+    hipError_t e = hipEventSynchronize(g_timer.ev1[i]);
+    float ms = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, g_timer.ev0[i], g_timer.ev1[i]);
+    if (e != hipSuccess) return hip_fail(e);
+    tot += ms;
+  }
+  *total_ms = tot;
+  *n_launches = g_timer.count;
+  g_timer.active = false;
+  g_timer.count = 0;
+  return DIT_OK;
+}
+
+}  // extern "C"

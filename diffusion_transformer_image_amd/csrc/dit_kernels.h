@@ -1,0 +1,23 @@
+// Host-side launchers of the gfx950 kernels (internal to libdit).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace dit {
+
+hipError_t launch_modnorm(bool x_f32, bool h_f32, const void *x, void *h, const float *mod,
+                          const float *bias, const float *gain, int rows, int seq_len, int D,
+                          float eps, int which, hipStream_t s);
+hipError_t launch_resid(bool x_f32, bool y_f32, bool out_f32, const void *x, const void *y,
+                        void *out, const float *mod, const float *bias, int rows, int seq_len,
+                        int D, int which, hipStream_t s);
+hipError_t launch_tmod(const float *t, const float *w1, const float *w2, float *mod, float *zs,
+                       int B, int D, int tdim, hipStream_t s);
+hipError_t launch_gemm(bool f32, const void *a, const void *w, void *c, int M, int N, int K,
+                       hipStream_t s);
+hipError_t launch_gemm_swiglu(bool f32, const void *a, const void *w13, void *u, int M, int F,
+                              int K, hipStream_t s);
+hipError_t launch_attention(bool f32, int head_dim, const void *qkvg, void *og, int B, int L,
+                            int H, int Hkv, hipStream_t s);
+
+}  // namespace dit

@@ -1,0 +1,215 @@
+/*
+ * dit.h -- C ABI of the MI355X (gfx950) forward pass of the Krea 2
+ * single-stream DiT block and of a stack of such blocks.
+ *
+ * The block (page "Krea 2 技术报告", the Chinese translation of the Krea 2
+ * technical report, section 架构 = architecture):
+ *   - 架构 › 时间步条件化: AdaLN-style modulation whose shift/scale/gate come
+ *     from one shared timestep vector plus a per-block tunable bias;
+ *   - 架构 › 归一化: zero-centred RMSNorm as the pre-norm;
+ *   - 架构 › Transformer块: grouped-query attention with a sigmoid output gate,
+ *     single-stream (one set of weights over the joint text+image sequence),
+ *     and a SwiGLU MLP;
+ *   - 架构 › 残差设计: standard (here: gated) residual connections.
+ * Positional terms and QKNorm are not part of this path.
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer argument is a DEVICE pointer unless marked (host).
+ *   - All matrices are row-major.  Projection weights use the nn.Linear
+ *     layout [out_features, in_features]: Y = X * W^T, no bias.
+ *   - Activations are [batch, seq_len, hidden] = [T, hidden] with
+ *     T = batch * seq_len; within a sample the image tokens come first,
+ *     then the text tokens (their order does not change the result).
+ *   - `dtype` (DIT_BF16 or DIT_F32) is the element type of x and of the
+ *     four projection weights; modulation vectors, the modulation bias,
+ *     the norm gains, t and the timestep-MLP weights are always float32.
+ *     Arithmetic: bf16 operands with fp32 accumulation, fp32 softmax and
+ *     norm statistics; the fp32 path computes everything in fp32.
+ *   - Device pointers must be 16-byte aligned.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *     enqueue work: results are valid once the stream has been
+ *     synchronised.  Nothing is allocated or freed by the library, except
+ *     the host-side timing events of dit_timer_*.
+ *   - Every argument is checked before anything is enqueued; on a failed
+ *     check nothing is launched and a status other than DIT_OK comes back.
+ *     No exception or abort crosses the ABI.
+ *   - Identical inputs give bitwise identical outputs (no atomics).
+ *   - Calls on different streams are independent if each has its own
+ *     workspace; one workspace used by two overlapping calls races.
+ */
+#ifndef DIT_H
+#define DIT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DIT_OK = 0,
+  DIT_ERR_NULL = 1,        /* a required pointer is NULL                       */
+  DIT_ERR_SHAPE = 2,       /* inconsistent or non-positive sizes, or aliasing  */
+  DIT_ERR_UNSUPPORTED = 3, /* valid but not implemented (e.g. head_dim 96)     */
+  DIT_ERR_ALIGN = 4,       /* a device pointer is not 16-byte aligned          */
+  DIT_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required          */
+  DIT_ERR_DTYPE = 6,       /* unknown dtype                                    */
+  DIT_ERR_HIP = 7          /* a HIP call failed; see dit_last_hip_error()      */
+} dit_status;
+
+typedef enum { DIT_F32 = 0, DIT_BF16 = 1 } dit_dtype;
+
+/* Block dimensions.  Requirements: all sizes > 0; hidden == n_heads*head_dim;
+ * n_heads % n_kv_heads == 0 and n_heads / n_kv_heads <= 4; head_dim == 128
+ * for bf16, head_dim == 64 or 128 for f32; hidden % 8 == 0; ffn % 8 == 0;
+ * eps >= 0. */
+typedef struct {
+  int32_t batch;      /* B                                                  */
+  int32_t seq_len;    /* L: joint image + text tokens per sample            */
+  int32_t hidden;     /* D                                                  */
+  int32_t n_heads;    /* H query heads (and gate heads)                     */
+  int32_t n_kv_heads; /* Hkv key/value heads; query head h reads KV head    */
+                      /* h / (H / Hkv) (contiguous groups)                  */
+  int32_t head_dim;   /* d                                                  */
+  int32_t ffn;        /* F: SwiGLU hidden width                             */
+  float eps;          /* RMSNorm epsilon, inside the square root            */
+  dit_dtype dtype;    /* element type of x and the projection weights       */
+} dit_config;
+
+/* One block's weights (host struct of device pointers).
+ * w_qkvg rows: Q (H*d rows, head h = rows h*d..h*d+d-1) | K (Hkv*d) |
+ *              V (Hkv*d) | G (H*d, the sigmoid gate logits, elementwise).  */
+typedef struct {
+  const void *w_qkvg;    /* [(2H + 2Hkv) * d, D]                               */
+  const void *w_o;       /* [D, H*d]                                           */
+  const void *w_13;      /* [2F, D]: rows 0..F-1 = W1 (through SiLU),           */
+                         /*          rows F..2F-1 = W3 (linear branch)          */
+  const void *w_2;       /* [D, F]                                             */
+  const float *mod_bias; /* [6, D] fp32 per-block bias added to the shared     */
+                         /* modulation: shift1, scale1, gate1, shift2,         */
+                         /* scale2, gate2                                       */
+  const float *norm1_w;  /* [D] fp32 zero-centred gain w (gain = 1 + w);        */
+  const float *norm2_w;  /* NULL means w = 0                                    */
+} dit_block_weights;
+
+/* Kernel classes, for the timing hook. */
+typedef enum {
+  DIT_K_MODNORM = 0,   /* modulated RMSNorm (both norms)       */
+  DIT_K_GEMM_QKVG = 1, /* h1 * W_qkvg^T                        */
+  DIT_K_ATTN = 2,      /* gated GQA flash attention            */
+  DIT_K_GEMM_O = 3,    /* Og * W_o^T                           */
+  DIT_K_RESID = 4,     /* gated residual adds (both)           */
+  DIT_K_GEMM_W13 = 5,  /* h2 * W_13^T with SwiGLU epilogue     */
+  DIT_K_GEMM_W2 = 6,   /* U * W_2^T                            */
+  DIT_K_TMOD = 7,      /* timestep embedding + modulation MLP  */
+  DIT_K_COUNT = 8
+} dit_kernel_kind;
+
+/* Workspace bytes needed by dit_block_fwd for this configuration
+ * (0 if cfg is invalid).  Holds the normalised activations, the Q|K|V|G
+ * projection (later reused for the SwiGLU hidden U), the gated attention
+ * output, the branch outputs and x1. */
+size_t dit_workspace_size(const dit_config *cfg /* host */);
+
+/* Workspace bytes needed by dit_stack_fwd: the block workspace plus two
+ * fp32 [T, D] buffers that carry the residual stream between blocks. */
+size_t dit_stack_workspace_size(const dit_config *cfg /* host */);
+
+/* One block forward.
+ *   x_in  [T, D] dtype; x_out [T, D] dtype (must not overlap x_in);
+ *   mod   [B, 6, D] fp32: the shared modulation vector m of each sample
+ *         (m[b] + w->mod_bias gives shift1, scale1, gate1, shift2, scale2,
+ *         gate2);
+ *   ws    workspace of at least dit_workspace_size(cfg) bytes, not
+ *         overlapping any other argument.
+ * Computes, per sample b:
+ *   h1 = x / sqrt(mean(x^2) + eps) * (1 + norm1_w) * (1 + scale1) + shift1
+ *   [Q|K|V|G] = h1 * W_qkvg^T
+ *   Og_h = softmax(Q_h K_j^T / sqrt(d)) V_j * sigmoid(G_h),  j = h / (H/Hkv)
+ *   x1 = x + gate1 * (Og * W_o^T)
+ *   h2 = x1 / sqrt(mean(x1^2) + eps) * (1 + norm2_w) * (1 + scale2) + shift2
+ *   x_out = x1 + gate2 * ((SiLU(h2 W1^T) * (h2 W3^T)) * W_2^T)
+ * In the bf16 path the intermediates h, QKVG, Og, the branch outputs, U
+ * and x1 are stored as bf16 between kernels. */
+dit_status dit_block_fwd(const dit_config *cfg /* host */, const dit_block_weights *w /* host */,
+                         const void *x_in, void *x_out, const float *mod, void *ws,
+                         size_t ws_bytes, void *stream);
+
+/* n_blocks blocks applied in order, all with the same modulation vector
+ * mod (one denoising step of the stack).  blocks is a host array of
+ * n_blocks weight structs.  The residual stream between blocks is kept in
+ * fp32 in the workspace and rounded to dtype once, into x_out.  ws needs
+ * dit_stack_workspace_size(cfg) bytes.  n_blocks >= 1. */
+dit_status dit_stack_fwd(const dit_config *cfg /* host */, int32_t n_blocks,
+                         const dit_block_weights *blocks /* host [n_blocks] */, const void *x_in,
+                         void *x_out, const float *mod, void *ws, size_t ws_bytes, void *stream);
+
+/* Shared timestep modulation of every sample:
+ *   e = [cos(1000 t f_i), sin(1000 t f_i)], f_i = 10000^(-i/(t_dim/2)),
+ *   mod_out[b] = W_t2 * SiLU(W_t1 * e)  reshaped to [6, D].
+ *   t [B] fp32; w_t1 [D, t_dim] fp32; w_t2 [6D, D] fp32; mod_out [B, 6, D].
+ * t_dim even, 2 <= t_dim <= 1024.  ws needs B*D*4 bytes (dit_workspace_size
+ * is always enough).  The pages name a sinusoidal time embedding and a
+ * per-block bias in place of per-block MLPs (page "Krea 2 技术报告",
+ * 架构 › 时间步条件化); the shared two-layer map is this library's reading. */
+dit_status dit_timestep_mod(const dit_config *cfg /* host */, int32_t t_dim, const float *t,
+                            const float *w_t1, const float *w_t2, float *mod_out, void *ws,
+                            size_t ws_bytes, void *stream);
+
+/* ---- the individual steps of the block (same kernels dit_block_fwd runs) */
+
+/* Modulated zero-centred RMSNorm over rows of x [T, D] (page
+ * "Krea 2 技术报告", 架构 › 归一化):
+ *   h = x / sqrt(mean(x^2) + eps) * (1 + gain) * (1 + scale) + shift
+ * with shift = mod[b][3*which] + bias[3*which], scale = mod[b][3*which+1]
+ * + bias[3*which+1], b = row / seq_len.  which: 0 = first norm, 1 = second.
+ * x_dtype may be DIT_F32 or cfg->dtype; h has cfg->dtype.  gain may be NULL. */
+dit_status dit_modnorm(const dit_config *cfg /* host */, const void *x, dit_dtype x_dtype, void *h,
+                       const float *mod, const float *bias, const float *gain, int32_t which,
+                       void *stream);
+
+/* C[M, N] = A[M, K] * W[N, K]^T in dtype with fp32 accumulation.
+ * K % 8 == 0; M, N, K > 0; M*K, N*K elements each below 2^30. */
+dit_status dit_gemm(dit_dtype dtype, int32_t m, int32_t n, int32_t k, const void *a, const void *w,
+                    void *c, void *stream);
+
+/* U[M, F] = SiLU(A W1^T) * (A W3^T) with W13 = [W1; W3] of shape [2F, K]
+ * (page "Krea 2 技术报告", 架构 › Transformer块: SwiGLU MLP). */
+dit_status dit_gemm_swiglu(dit_dtype dtype, int32_t m, int32_t f, int32_t k, const void *a,
+                           const void *w13, void *u, void *stream);
+
+/* Gated grouped-query attention over the rows of qkvg [T, (2H+2Hkv)*d]
+ * (column blocks Q | K | V | G, as produced by the QKVG projection):
+ *   og[b, l, h*d:(h+1)*d] = softmax_keys(Q_h K_j^T / sqrt(d)) V_j * sigmoid(G_h)
+ * within each sample, all keys, no mask (page "Krea 2 技术报告",
+ * 架构 › Transformer块).  og [T, H*d] in cfg->dtype. */
+dit_status dit_attention(const dit_config *cfg /* host */, const void *qkvg, void *og,
+                         void *stream);
+
+/* out = x + gate * y over rows of [T, D], gate = mod[b][3*which+2] +
+ * bias[3*which+2] (page "Krea 2 技术报告", 架构 › 残差设计).
+ * x_dtype and out_dtype may be DIT_F32 or cfg->dtype; y has cfg->dtype. */
+dit_status dit_gated_residual(const dit_config *cfg /* host */, const void *x, dit_dtype x_dtype,
+                              const void *y, const float *mod, const float *bias, int32_t which,
+                              void *out, dit_dtype out_dtype, void *stream);
+
+/* ---- diagnostics */
+
+const char *dit_status_str(dit_status s);
+/* hipError_t of this thread's last DIT_ERR_HIP (0 if none). */
+int dit_last_hip_error(void);
+
+/* Timing hook: while started, every launch of kernel class `kind` made by
+ * this library is bracketed by a pair of HIP events recorded on the
+ * launch's own stream (at most `capacity` launches).  dit_timer_stop
+ * synchronises those events and returns the summed duration in ms and the
+ * number of launches.  Global to the process; not for concurrent use. */
+dit_status dit_timer_start(int32_t kind, int32_t capacity);
+dit_status dit_timer_stop(double *total_ms /* host */, int32_t *n_launches /* host */);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DIT_H */

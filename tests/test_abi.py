@@ -1,0 +1,150 @@
+"""The C ABI on the CPU: the library loads, exports every declared symbol,
+and rejects bad arguments before any HIP call (fake device addresses are
+never dereferenced because every call here fails validation)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import diffusion_transformer_image_amd as dit
+from diffusion_transformer_image_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+P = 0x7F0000000000  # a 16-byte aligned fake device address, never touched
+
+
+def declared_symbols():
+    src = open(os.path.join(ROOT, "include", "dit.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dit_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = dit.lib()
+    syms = declared_symbols()
+    assert len(syms) >= 14
+    for s in syms:
+        assert hasattr(L, s), s
+    assert set(syms) == set(dit.EXPORTS)
+
+
+def cfg(**kw):
+    base = dict(batch=2, seq_len=80, hidden=256, n_heads=4, n_kv_heads=2, head_dim=64, ffn=688,
+                eps=1e-6, dtype="f32")
+    base.update(kw)
+    return dit.make_config(**base)
+
+
+def test_status_strings():
+    L = dit.lib()
+    for code in range(8):
+        assert L.dit_status_str(code)
+    assert L.dit_status_str(0) == b"ok"
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(batch=0), "DIT_ERR_SHAPE"),
+    (dict(seq_len=-1), "DIT_ERR_SHAPE"),
+    (dict(hidden=255), "DIT_ERR_SHAPE"),          # != H * d
+    (dict(n_kv_heads=3), "DIT_ERR_SHAPE"),        # H % Hkv != 0
+    (dict(n_heads=8, head_dim=32, n_kv_heads=1), "DIT_ERR_UNSUPPORTED"),  # group 8
+    (dict(head_dim=32, n_heads=8, n_kv_heads=4), "DIT_ERR_UNSUPPORTED"),  # d = 32
+    (dict(dtype="bf16"), "DIT_ERR_UNSUPPORTED"),  # bf16 needs d = 128
+    (dict(ffn=690), "DIT_ERR_UNSUPPORTED"),       # ffn % 8
+    (dict(eps=-1.0), "DIT_ERR_SHAPE"),
+])
+def test_bad_config_is_rejected(kw, expect):
+    c = cfg(**kw)
+    assert dit.workspace_size(c) == 0
+    w = _lib.BlockWeights(P, P, P, P, P, P, P)
+    st = dit.lib().dit_block_fwd(ctypes.byref(c), ctypes.byref(w), P, P + (1 << 30), P + (2 << 30),
+                                 P + (3 << 30), 1 << 40, None)
+    assert _lib.STATUS[st] == expect
+
+
+def test_bad_dtype_code():
+    c = cfg()
+    c.dtype = 7
+    assert dit.lib().dit_workspace_size(ctypes.byref(c)) == 0
+    st = dit.lib().dit_gemm(5, 16, 16, 16, P, P + 4096, P + 8192, None)
+    assert _lib.STATUS[st] == "DIT_ERR_DTYPE"
+
+
+def call_block(c, w, x_in, x_out, mod, ws, ws_bytes):
+    return _lib.STATUS[dit.lib().dit_block_fwd(ctypes.byref(c), ctypes.byref(w) if w else None,
+                                               x_in, x_out, mod, ws, ws_bytes, None)]
+
+
+def test_block_argument_checks():
+    c = cfg()
+    need = dit.workspace_size(c)
+    assert need > 0
+    w = _lib.BlockWeights(P, P, P, P, P, 0, 0)
+    G = 1 << 30
+    X, Y, M, WS = P + G, P + 2 * G, P + 3 * G, P + 4 * G
+    assert call_block(c, None, X, Y, M, WS, need) == "DIT_ERR_NULL"
+    assert call_block(c, _lib.BlockWeights(0, P, P, P, P, 0, 0), X, Y, M, WS, need) == "DIT_ERR_NULL"
+    assert call_block(c, w, 0, Y, M, WS, need) == "DIT_ERR_NULL"
+    assert call_block(c, w, X, Y, 0, WS, need) == "DIT_ERR_NULL"
+    assert call_block(c, w, X, Y, M, 0, need) == "DIT_ERR_WORKSPACE"
+    assert call_block(c, w, X, Y, M, WS, need - 1) == "DIT_ERR_WORKSPACE"
+    assert call_block(c, w, X + 8, Y, M, WS, need) == "DIT_ERR_ALIGN"
+    assert call_block(c, _lib.BlockWeights(P + 4, P, P, P, P, 0, 0), X, Y, M, WS, need) == "DIT_ERR_ALIGN"
+    assert call_block(c, w, X, X + 64, M, WS, need) == "DIT_ERR_SHAPE"  # x_out overlaps x_in
+    assert call_block(c, w, X, Y, M, X, need) == "DIT_ERR_SHAPE"  # workspace overlaps x_in
+
+
+def test_stack_argument_checks():
+    c = cfg()
+    need = dit.stack_workspace_size(c)
+    assert need > dit.workspace_size(c)
+    arr = (_lib.BlockWeights * 2)(_lib.BlockWeights(P, P, P, P, P, 0, 0), _lib.BlockWeights(P, P, 0, P, P, 0, 0))
+    G = 1 << 30
+    L = dit.lib()
+    st = L.dit_stack_fwd(ctypes.byref(c), 0, arr, P + G, P + 2 * G, P + 3 * G, P + 4 * G, need, None)
+    assert _lib.STATUS[st] == "DIT_ERR_SHAPE"
+    st = L.dit_stack_fwd(ctypes.byref(c), 2, arr, P + G, P + 2 * G, P + 3 * G, P + 4 * G, need, None)
+    assert _lib.STATUS[st] == "DIT_ERR_NULL"  # block 1 lacks w_13
+    st = L.dit_stack_fwd(ctypes.byref(c), 1, arr, P + G, P + 2 * G, P + 3 * G, P + 4 * G, need - 16, None)
+    assert _lib.STATUS[st] == "DIT_ERR_WORKSPACE"
+
+
+def test_step_argument_checks():
+    L = dit.lib()
+    c = cfg()
+    G = 1 << 30
+    S = lambda st: _lib.STATUS[st]
+    assert S(L.dit_gemm(0, 0, 16, 16, P, P + G, P + 2 * G, None)) == "DIT_ERR_SHAPE"
+    assert S(L.dit_gemm(0, 16, 16, 12, P, P + G, P + 2 * G, None)) == "DIT_ERR_UNSUPPORTED"  # K % 8
+    assert S(L.dit_gemm(1, 16, 16, 16, P + 2, P + G, P + 2 * G, None)) == "DIT_ERR_ALIGN"
+    assert S(L.dit_gemm(1, 16, 16, 16, P, P + G, P + 64, None)) == "DIT_ERR_SHAPE"  # C overlaps A
+    assert S(L.dit_gemm_swiglu(1, 16, 16, 16, 0, P + G, P + 2 * G, None)) == "DIT_ERR_NULL"
+    assert S(L.dit_attention(ctypes.byref(c), P, 0, None)) == "DIT_ERR_NULL"
+    assert S(L.dit_attention(ctypes.byref(c), P, P + 64, None)) == "DIT_ERR_SHAPE"
+    assert S(L.dit_modnorm(ctypes.byref(c), P, 0, P + G, P + 2 * G, P + 3 * G, 0, 2, None)) == "DIT_ERR_SHAPE"
+    assert S(L.dit_modnorm(ctypes.byref(c), P, 9, P + G, P + 2 * G, P + 3 * G, 0, 0, None)) == "DIT_ERR_DTYPE"
+    cb = cfg(dtype="f32")
+    assert S(L.dit_gated_residual(ctypes.byref(cb), P, 0, P + G, P + 2 * G, 0, 0, P + 3 * G, 0, None)) == "DIT_ERR_NULL"
+    assert S(L.dit_timestep_mod(ctypes.byref(c), 255, P, P + G, P + 2 * G, P + 3 * G, P + 4 * G, 1 << 20, None)) == "DIT_ERR_SHAPE"
+    assert S(L.dit_timestep_mod(ctypes.byref(c), 256, P, P + G, P + 2 * G, P + 3 * G, P + 4 * G, 16, None)) == "DIT_ERR_WORKSPACE"
+    assert S(L.dit_timer_start(99, 4)) == "DIT_ERR_SHAPE"
+
+
+def test_workspace_sizes_cover_the_buffers():
+    import datagen
+    for name in ("c0", "c1", "c3", "c4"):
+        dc = datagen.get_config(name)
+        c = dit.config_of(dc)
+        es = 2 if dc.dtype == "bf16" else 4
+        T, D = dc.tokens, dc.hidden
+        need = T * D * es * 4 + T * max(dc.n_qkvg, dc.ffn) * es
+        assert dit.workspace_size(c) >= need
+        assert dit.stack_workspace_size(c) >= dit.workspace_size(c) + 2 * T * D * 4
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    monkeypatch.setattr(_lib, "_LIB", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", "/nonexistent/libdit.so")
+    with pytest.raises(RuntimeError, match="missing"):
+        _lib.lib()

@@ -1,0 +1,225 @@
+"""GPU parity of the whole block and stack against the fp64 oracle, plus the
+invariants the definitions fix, all through the C ABI."""
+import numpy as np
+import pytest
+
+import datagen
+from oracle import dit_oracle as O
+from tests._parity import assert_parity, assert_update_parity
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    from datagen import device
+    import diffusion_transformer_image_amd as dit
+    dit.lib()
+    return torch, device, dit
+
+
+class Run:
+    """Uploads one configuration's inputs and runs the block on the GPU."""
+
+    def __init__(self, dev, cfg, strong=False, block=0):
+        torch, device, dit = dev
+        self.torch, self.device, self.dit = torch, device, dit
+        self.cfg = cfg
+        self.x = datagen.activations(cfg)
+        self.w = datagen.block_weights(cfg, block)
+        self.mod = datagen.block_mod(cfg, strong=strong)
+        self.c = dit.config_of(cfg)
+        self.X = device.to_device(self.x.reshape(cfg.tokens, cfg.hidden), cfg.dtype)
+        self.W = device.weights_to_device(self.w, cfg.dtype)
+        self.M = device.to_device(self.mod, "f32")
+        self.ws = torch.empty(dit.workspace_size(self.c), dtype=torch.uint8, device="cuda")
+
+    def forward(self, X=None, W=None, M=None):
+        torch = self.torch
+        X = self.X if X is None else X
+        Y = torch.empty_like(X)
+        self.dit.block_fwd(self.c, self.W if W is None else W, X, Y, self.M if M is None else M, self.ws)
+        torch.cuda.synchronize()
+        return self.device.to_numpy(Y).reshape(self.cfg.batch, self.cfg.seq_len, self.cfg.hidden)
+
+
+def check_block(y, ref, x, dtype, what):
+    e, c = assert_parity(y, ref, dtype, what + " output")
+    eu, cu = assert_update_parity(y, ref, x, dtype, what + " update")
+    print(f"{what}: output {e:.2e}/{c:.7f} update {eu:.2e}/{cu:.7f}")
+
+
+@pytest.mark.parametrize("strong", [False, True])
+def test_block_c0_full(dev, strong):
+    cfg = datagen.get_config("c0")
+    r = Run(dev, cfg, strong)
+    y = r.forward()
+    ref = O.block_forward(r.x, r.mod, r.w, O.OracleConfig.of(cfg))
+    check_block(y, ref, r.x, "f32", "c0")
+
+
+def sample_rows(L, seed):
+    rng = np.random.default_rng(seed)
+    return np.unique(np.r_[0, 1, 63, 64, L // 2, L - 65, L - 64, L - 1, rng.integers(0, L, 8)])
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c3b"])
+@pytest.mark.parametrize("strong", [False, True])
+def test_block_full_size_sampled(dev, name, strong):
+    """Full-size block in the launch configuration the benchmark times;
+    the oracle evaluates sampled query tokens of the first and last sample."""
+    cfg = datagen.get_config(name)
+    print(f"block {name} strong={strong}", flush=True)
+    r = Run(dev, cfg, strong)
+    y = r.forward()
+    oc = O.OracleConfig.of(cfg)
+    for b in sorted({0, cfg.batch - 1}):
+        rows = sample_rows(cfg.seq_len, b + 31 * len(name))
+        ref = O.block_forward_rows(r.x, r.mod, r.w, oc, b, rows)
+        check_block(y[b, rows], ref, r.x[b, rows].astype(np.float64), "bf16", f"{name} b={b}")
+
+
+def test_block_bf16_small_full_output(dev):
+    """Every output of a small bf16 block (d = 128, ragged L) against the oracle."""
+    cfg = datagen.get_config("c1").replace(batch=2, n_image=70, n_text=27, hidden=512, n_heads=4,
+                                            n_kv_heads=1, ffn=1368)
+    for strong in (False, True):
+        r = Run(dev, cfg, strong)
+        y = r.forward()
+        ref = O.block_forward(r.x, r.mod, r.w, O.OracleConfig.of(cfg))
+        check_block(y, ref, r.x, "bf16", f"small bf16 strong={strong}")
+
+
+def test_zero_gates_identity_bitwise(dev):
+    for name in ("c0", "c1"):
+        cfg = datagen.get_config(name).replace(batch=2, n_image=100, n_text=20)
+        r = Run(dev, cfg, strong=True)
+        mod = r.mod.copy()
+        mod[:, 2] = -r.w.mod_bias[2]
+        mod[:, 5] = -r.w.mod_bias[5]
+        # m + bias is exactly 0 in fp32 for these rows
+        y = r.forward(M=r.device.to_device(mod, "f32"))
+        np.testing.assert_array_equal(y, r.x.astype(np.float64))
+
+
+def test_gqa_equals_mha_with_replicated_kv(dev):
+    torch, device, dit = dev
+    cfg = datagen.get_config("c1").replace(batch=1, n_image=96, n_text=33, hidden=512, n_heads=4,
+                                            n_kv_heads=1, ffn=1368)
+    r = Run(dev, cfg, strong=True)
+    y = r.forward()
+    H, Hk, d = 4, 1, 128
+    wq = r.w.w_qkvg
+    k_rows, v_rows = wq[H * d:(H + Hk) * d], wq[(H + Hk) * d:(H + 2 * Hk) * d]
+    w_mha = np.concatenate([wq[:H * d], np.tile(k_rows, (4, 1)), np.tile(v_rows, (4, 1)), wq[(H + 2 * Hk) * d:]])
+    W = dict(r.W)
+    W["w_qkvg"] = device.to_device(w_mha, "bf16")
+    cm = dit.config_of(cfg.replace(n_kv_heads=4))
+    Y = torch.empty_like(r.X)
+    ws = torch.empty(dit.workspace_size(cm), dtype=torch.uint8, device="cuda")
+    dit.block_fwd(cm, W, r.X, Y, r.M, ws)
+    torch.cuda.synchronize()
+    ym = device.to_numpy(Y).reshape(y.shape)
+    # same arithmetic per head; only kernel instantiations differ
+    assert_parity(ym - r.x, y - r.x, "bf16", "GQA vs MHA", maxabs=1e-3, cos_min=0.999999)
+
+
+def test_permutation_equivariance(dev):
+    torch, device, dit = dev
+    cfg = datagen.get_config("c0").replace(batch=1)
+    r = Run(dev, cfg, strong=True)
+    y = r.forward()
+    perm = np.random.default_rng(5).permutation(cfg.seq_len)
+    Xp = device.to_device(r.x[:, perm].reshape(cfg.tokens, cfg.hidden), "f32")
+    yp = r.forward(X=Xp)
+    assert np.max(np.abs(yp - y[:, perm])) <= 1e-5 * np.max(np.abs(y))
+
+
+def test_determinism_bitwise(dev):
+    cfg = datagen.get_config("c1").replace(batch=2, n_image=300, n_text=33)
+    r = Run(dev, cfg, strong=True)
+    np.testing.assert_array_equal(r.forward(), r.forward())
+
+
+def test_end_to_end_from_timestep(dev):
+    """t -> timestep modulation -> block, each side with its own a0."""
+    torch, device, dit = dev
+    cfg = datagen.get_config("c0").replace(batch=2)
+    r = Run(dev, cfg)
+    t, w1, w2 = datagen.timestep_inputs(cfg)
+    M = torch.empty((2, 6, cfg.hidden), dtype=torch.float32, device="cuda")
+    dit.timestep_mod(r.c, device.to_device(t, "f32"), device.to_device(w1, "f32"), device.to_device(w2, "f32"), M, r.ws)
+    y = r.forward(M=M)
+    oc = O.OracleConfig.of(cfg)
+    ref = O.block_forward(r.x, O.timestep_modulation(t, w1, w2, cfg.hidden), r.w, oc)
+    check_block(y, ref, r.x, "f32", "t -> block")
+
+
+# ------------------------------------------------------------------ stack
+def run_stack(dev, cfg, blocks_np, x, mod):
+    torch, device, dit = dev
+    c = dit.config_of(cfg)
+    X = device.to_device(x.reshape(cfg.tokens, cfg.hidden), cfg.dtype)
+    Y = torch.empty_like(X)
+    Ws = [device.weights_to_device(w, cfg.dtype) for w in blocks_np]
+    ws = torch.empty(dit.stack_workspace_size(c), dtype=torch.uint8, device="cuda")
+    dit.stack_fwd(c, Ws, X, Y, device.to_device(mod, "f32"), ws)
+    torch.cuda.synchronize()
+    return device.to_numpy(Y).reshape(x.shape)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_stack_60_blocks_small(dev, dtype):
+    """60 blocks with the stack's weight scaling, every output checked."""
+    if dtype == "f32":
+        cfg = datagen.get_config("c0").replace(n_blocks=60, out_std=0.02 / np.sqrt(120), batch=2)
+    else:
+        cfg = datagen.get_config("c4").replace(batch=2, n_image=64, n_text=16, hidden=256, n_heads=2,
+                                                n_kv_heads=1, ffn=688)
+    x = datagen.activations(cfg)
+    mod = datagen.block_mod(cfg, strong=True)
+    blocks = [datagen.block_weights(cfg, i) for i in range(60)]
+    y = run_stack(dev, cfg, blocks, x, mod)
+    ref = O.stack_forward(x, mod, blocks, 60, O.OracleConfig.of(cfg))
+    check_block(y, ref, x, dtype, "stack60")
+
+
+def test_stack_full_dims_three_blocks(dev):
+    cfg = datagen.get_config("c4").replace(n_image=200, n_text=56)
+    x = datagen.activations(cfg)
+    mod = datagen.block_mod(cfg, strong=False)
+    blocks = [datagen.block_weights(cfg, i) for i in range(3)]
+    y = run_stack(dev, cfg, blocks, x, mod)
+    ref = O.stack_forward(x, mod, blocks, 3, O.OracleConfig.of(cfg))
+    check_block(y, ref, x, "bf16", "stack3")
+
+
+@pytest.mark.parametrize("live", [0, 59])
+def test_stack_c4_full_size_one_live_block(dev, live):
+    """The 60-block stack at its full 1024 px shape: 59 blocks run their full
+    compute but have zero gates (exact identity), one block is live, so the
+    oracle can evaluate sampled output tokens of that one block."""
+    torch, device, dit = dev
+    cfg = datagen.get_config("c4")
+    print(f"stack c4 live={live}", flush=True)
+    x = datagen.activations(cfg)
+    mod = datagen.block_mod(cfg)
+    w = datagen.block_weights(cfg, 0)
+    W = device.weights_to_device(w, "bf16")
+    dead_bias = w.mod_bias.copy()
+    dead_bias[2] = -mod[0, 2]
+    dead_bias[5] = -mod[0, 5]
+    Wd = dict(W)
+    Wd["mod_bias"] = device.to_device(dead_bias, "f32")
+    blocks = [W if i == live else Wd for i in range(60)]
+    c = dit.config_of(cfg)
+    X = device.to_device(x.reshape(cfg.tokens, cfg.hidden), "bf16")
+    Y = torch.empty_like(X)
+    ws = torch.empty(dit.stack_workspace_size(c), dtype=torch.uint8, device="cuda")
+    dit.stack_fwd(c, blocks, X, Y, device.to_device(mod, "f32"), ws)
+    torch.cuda.synchronize()
+    y = device.to_numpy(Y).reshape(x.shape)
+    rows = sample_rows(cfg.seq_len, 7 + live)
+    ref = O.block_forward_rows(x, mod, w, O.OracleConfig.of(cfg), 0, rows)
+    check_block(y[0, rows], ref, x[0, rows].astype(np.float64), "bf16", f"c4 live block {live}")

@@ -1,0 +1,180 @@
+"""GPU parity of each step kernel against the fp64 oracle (through the C ABI)."""
+import numpy as np
+import pytest
+
+import datagen
+from oracle import dit_oracle as O
+from tests._parity import assert_parity
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    from datagen import device
+    import diffusion_transformer_image_amd as dit
+    dit.lib()
+    return torch, device, dit
+
+
+def small_cfg(name, **kw):
+    return datagen.get_config(name).replace(**kw)
+
+
+# ------------------------------------------------------------------ GEMM
+GEMM_CASES = [
+    ("f32", 80, 768, 256), ("f32", 80, 256, 688), ("f32", 300, 200, 40), ("f32", 1, 1, 8),
+    ("bf16", 16, 16, 32), ("bf16", 1, 1, 8), ("bf16", 80, 768, 264), ("bf16", 513, 1040, 4096),
+    ("bf16", 1000, 10240, 4096), ("bf16", 300, 4096, 11008), ("bf16", 257, 4096, 4096),
+]
+
+
+@pytest.mark.parametrize("dt,m,n,k", GEMM_CASES)
+def test_gemm(dev, dt, m, n, k):
+    torch, device, dit = dev
+    print(f"gemm {dt} M={m} N={n} K={k}", flush=True)
+    cfg = datagen.get_config("c0" if dt == "f32" else "c1")
+    a, w = datagen.gemm_operands(cfg, m, n, k, tag=m + n + k)
+    A, W = device.to_device(a, dt), device.to_device(w, dt)
+    C = torch.empty((m, n), dtype=A.dtype, device="cuda")
+    dit.gemm(A, W, C)
+    torch.cuda.synchronize()
+    ref = a.astype(np.float64) @ w.astype(np.float64).T
+    y = device.to_numpy(C)
+    # fp32 accumulation; bf16 output rounding (2^-9 relative) dominates
+    assert_parity(y, ref, dt, f"gemm {m}x{n}x{k}", maxabs=1e-5 if dt == "f32" else 8e-3, cos_min=0.99999)
+
+
+SWIGLU_CASES = [("f32", 80, 688, 256), ("f32", 100, 40, 64), ("bf16", 80, 688, 256),
+                ("bf16", 600, 11008, 4096), ("bf16", 300, 200, 128)]
+
+
+@pytest.mark.parametrize("dt,m,f,k", SWIGLU_CASES)
+def test_gemm_swiglu(dev, dt, m, f, k):
+    torch, device, dit = dev
+    print(f"swiglu {dt} M={m} F={f} K={k}", flush=True)
+    cfg = datagen.get_config("c0" if dt == "f32" else "c1")
+    a, w = datagen.gemm_operands(cfg, m, 2 * f, k, tag=7 + m + f + k)
+    A, W = device.to_device(a, dt), device.to_device(w, dt)
+    U = torch.empty((m, f), dtype=A.dtype, device="cuda")
+    dit.gemm_swiglu(A, W, U)
+    torch.cuda.synchronize()
+    ref = O.swiglu_hidden(a, w, f)
+    assert_parity(device.to_numpy(U), ref, dt, "swiglu", maxabs=1e-5 if dt == "f32" else 8e-3, cos_min=0.99999)
+
+
+# ------------------------------------------------------------------ attention
+ATTN_CASES = [
+    ("c0", 1, 80), ("c0", 2, 1), ("c0", 1, 65), ("c0", 3, 200),
+    ("c1", 1, 1), ("c1", 2, 80), ("c1", 2, 512), ("c1", 1, 130), ("c1", 1, 4544), ("c1", 1, 4608),
+]
+
+
+@pytest.mark.parametrize("name,B,L", ATTN_CASES)
+def test_attention(dev, name, B, L):
+    torch, device, dit = dev
+    print(f"attention {name} B={B} L={L}", flush=True)
+    cfg = small_cfg(name, batch=B, n_image=L, n_text=0)
+    z = datagen.qkvg_activations(cfg)
+    Z = device.to_device(z, cfg.dtype)
+    OG = torch.empty((cfg.tokens, cfg.n_heads * cfg.head_dim), dtype=Z.dtype, device="cuda")
+    dit.attention(dit.config_of(cfg), Z, OG)
+    torch.cuda.synchronize()
+    y = device.to_numpy(OG).reshape(B, L, -1)
+    oc = O.OracleConfig.of(cfg)
+    zz = z.reshape(B, L, -1)
+    rows = np.arange(L) if L <= 600 else np.unique(np.r_[0, 1, 63, 64, 65, L // 2, L - 65, L - 64, L - 2, L - 1,
+                                                            np.random.default_rng(L).integers(0, L, 24)])
+    for b in range(B):
+        H, Hk, d = cfg.n_heads, cfg.n_kv_heads, cfg.head_dim
+        zb = zz[b].astype(np.float64)
+        q = zb[rows, : H * d].reshape(len(rows), H, d)
+        k = zb[:, H * d:(H + Hk) * d].reshape(L, Hk, d)
+        v = zb[:, (H + Hk) * d:(H + 2 * Hk) * d].reshape(L, Hk, d)
+        g = zb[rows, (H + 2 * Hk) * d:].reshape(len(rows), H, d)
+        ref = O.gated_gqa_attention(q, k, v, g)
+        assert_parity(y[b, rows], ref, cfg.dtype, f"attention b={b}", maxabs=1e-5 if cfg.dtype == "f32" else 1e-2,
+                      cos_min=0.99999)
+
+
+def test_attention_one_key_returns_gated_value(dev):
+    torch, device, dit = dev
+    cfg = small_cfg("c1", batch=3, n_image=1, n_text=0)
+    z = datagen.qkvg_activations(cfg)
+    Z = device.to_device(z, "bf16")
+    OG = torch.empty((3, 4096), dtype=torch.bfloat16, device="cuda")
+    dit.attention(dit.config_of(cfg), Z, OG)
+    torch.cuda.synchronize()
+    H, Hk, d = 32, 8, 128
+    v = z[:, (H + Hk) * d:(H + 2 * Hk) * d].reshape(3, Hk, d).astype(np.float64)
+    g = z[:, (H + 2 * Hk) * d:].reshape(3, H, d).astype(np.float64)
+    expect = np.stack([v[:, h // 4] / (1 + np.exp(-g[:, h])) for h in range(H)], axis=1).reshape(3, -1)
+    y = device.to_numpy(OG)
+    # only the final bf16 rounding separates the two
+    assert np.max(np.abs(y - expect)) <= 2 ** -8 * np.max(np.abs(expect))
+
+
+# ------------------------------------------------------------------ modnorm / residual
+@pytest.mark.parametrize("name,x_f32", [("c0", True), ("c1", False), ("c1", True)])
+@pytest.mark.parametrize("which", [0, 1])
+def test_modnorm(dev, name, x_f32, which):
+    torch, device, dit = dev
+    cfg = small_cfg(name, batch=3, n_image=37, n_text=0)
+    x = datagen.activations(cfg)
+    w = datagen.block_weights(cfg)
+    mod = datagen.block_mod(cfg, strong=True)
+    X = device.to_device(x, "f32" if x_f32 else cfg.dtype)
+    Hh = torch.empty((cfg.tokens, cfg.hidden), dtype=torch.float32 if cfg.dtype == "f32" else torch.bfloat16, device="cuda")
+    gain = w.norm1_w if which == 0 else w.norm2_w
+    dit.modnorm(dit.config_of(cfg), X, Hh, device.to_device(mod, "f32"), device.to_device(w.mod_bias, "f32"),
+                device.to_device(gain, "f32"), which)
+    torch.cuda.synchronize()
+    ref = []
+    for b in range(3):
+        m = O.split_modulation(mod[b], w.mod_bias)
+        ref.append(O.modulated_rmsnorm(x[b], gain, m[3 * which], m[3 * which + 1], cfg.eps))
+    ref = np.concatenate(ref)
+    y = device.to_numpy(Hh)
+    if cfg.dtype == "f32":
+        assert_parity(y, ref, "f32", "modnorm", maxabs=2e-6)
+    else:
+        assert np.max(np.abs(y - ref) / (np.abs(ref) + 1e-3)) <= 2 ** -8 + 1e-5  # bf16 rounding only
+
+
+@pytest.mark.parametrize("name,xd,od", [("c0", "f32", "f32"), ("c1", "bf16", "bf16"), ("c1", "f32", "f32"),
+                                        ("c1", "bf16", "f32"), ("c1", "f32", "bf16")])
+@pytest.mark.parametrize("which", [0, 1])
+def test_gated_residual(dev, name, xd, od, which):
+    torch, device, dit = dev
+    cfg = small_cfg(name, batch=2, n_image=41, n_text=0)
+    x = datagen.activations(cfg)
+    y = datagen.activations(cfg.replace(seed=cfg.seed + 17))
+    w = datagen.block_weights(cfg)
+    mod = datagen.block_mod(cfg, strong=True)
+    X, Y = device.to_device(x, xd), device.to_device(y, cfg.dtype)
+    out = torch.empty_like(X, dtype=torch.float32 if od == "f32" else torch.bfloat16)
+    dit.gated_residual(dit.config_of(cfg), X, Y, device.to_device(mod, "f32"), device.to_device(w.mod_bias, "f32"),
+                       which, out)
+    torch.cuda.synchronize()
+    gates = [O.split_modulation(mod[b], w.mod_bias)[3 * which + 2] for b in range(2)]
+    ref = np.concatenate([O.gated_residual(x[b], gates[b], y[b]) for b in range(2)])
+    mag = np.concatenate([np.abs(x[b]) + np.abs(gates[b] * y[b]) for b in range(2)])
+    r = device.to_numpy(out).reshape(ref.shape)
+    tol = (2 ** -8 if od == "bf16" else 0.0) * np.abs(ref) + 1e-6 * mag
+    assert np.all(np.abs(r - ref) <= tol)
+
+
+# ------------------------------------------------------------------ timestep modulation
+@pytest.mark.parametrize("name", ["c0", "c3", "c1"])
+def test_timestep_mod(dev, name):
+    torch, device, dit = dev
+    cfg = datagen.get_config(name)
+    t, w1, w2 = datagen.timestep_inputs(cfg)
+    c = dit.config_of(cfg)
+    M = torch.empty((cfg.batch, 6, cfg.hidden), dtype=torch.float32, device="cuda")
+    ws = torch.empty(dit.workspace_size(c), dtype=torch.uint8, device="cuda")
+    dit.timestep_mod(c, device.to_device(t, "f32"), device.to_device(w1, "f32"), device.to_device(w2, "f32"), M, ws)
+    torch.cuda.synchronize()
+    ref = O.timestep_modulation(t, w1, w2, cfg.hidden)
+    assert_parity(device.to_numpy(M), ref, "f32", "timestep modulation", maxabs=2e-5)
