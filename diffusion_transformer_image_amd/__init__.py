@@ -19,6 +19,7 @@ from ._lib import (  # noqa: F401
     gated_residual,
     gemm,
     gemm_swiglu,
+    gemm_variant,
     lib,
     make_config,
     make_weights,

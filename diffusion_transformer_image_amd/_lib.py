@@ -23,7 +23,7 @@ KERNEL_KINDS = {"modnorm": 0, "gemm_qkvg": 1, "attn": 2, "gemm_o": 3, "resid": 4
 
 EXPORTS = (
     "dit_workspace_size", "dit_stack_workspace_size", "dit_block_fwd", "dit_stack_fwd",
-    "dit_timestep_mod", "dit_modnorm", "dit_gemm", "dit_gemm_swiglu", "dit_attention",
+    "dit_timestep_mod", "dit_modnorm", "dit_gemm", "dit_gemm_swiglu", "dit_gemm_variant", "dit_attention",
     "dit_gated_residual", "dit_status_str", "dit_last_hip_error", "dit_timer_start",
     "dit_timer_stop",
 )
@@ -74,6 +74,7 @@ def lib() -> ctypes.CDLL:
             "dit_modnorm": (i32, [cfgp, vp, i32, vp, vp, vp, vp, i32, vp]),
             "dit_gemm": (i32, [i32, i32, i32, i32, vp, vp, vp, vp]),
             "dit_gemm_swiglu": (i32, [i32, i32, i32, i32, vp, vp, vp, vp]),
+            "dit_gemm_variant": (i32, [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp]),
             "dit_attention": (i32, [cfgp, vp, vp, vp]),
             "dit_gated_residual": (i32, [cfgp, vp, i32, vp, vp, vp, i32, vp, i32, vp]),
             "dit_status_str": (ctypes.c_char_p, [i32]),
@@ -187,6 +188,13 @@ def gemm_swiglu(a, w13, u, stream=None) -> None:
     f = w13.shape[0] // 2
     _check(lib().dit_gemm_swiglu(_dtype_code(a.dtype), m, f, k, _ptr(a), _ptr(w13), _ptr(u),
                                  _stream(stream)), "dit_gemm_swiglu")
+
+
+def gemm_variant(variant: int, a, w, c, swiglu: bool = False, stream=None) -> None:
+    m, k = a.shape
+    n = w.shape[0] // 2 if swiglu else w.shape[0]
+    _check(lib().dit_gemm_variant(_dtype_code(a.dtype), variant, int(swiglu), m, n, k, _ptr(a), _ptr(w),
+                                  _ptr(c), _stream(stream)), "dit_gemm_variant")
 
 
 def attention(cfg: Config, qkvg, og, stream=None) -> None:

@@ -117,7 +117,7 @@ BlockWs carve(const dit_config *c, void *ws) {
   w.qkvg = take(d.T * (d.nqkvg > d.F ? d.nqkvg : d.F) * d.es);
   w.og = take(d.T * d.hd * d.es);
   w.br = take(d.T * d.D * d.es);
-  w.x1 = take(d.T * d.D * d.es);
+  w.x1 = take(d.T * d.D * 4);  // x1 = x + gate1 * A stays fp32 (one rounding, at x_out)
   const size_t tmod = (size_t)c->batch * c->hidden * 4;
   w.bytes = off > tmod ? off : tmod;
   return w;
@@ -204,7 +204,7 @@ size_t dit_workspace_size(const dit_config *cfg) {
 size_t dit_stack_workspace_size(const dit_config *cfg) {
   if (check_cfg(cfg) != DIT_OK) return 0;
   const Dims d = dims(cfg);
-  return carve(cfg, nullptr).bytes + 2 * round_up(d.T * d.D * 4);
+  return carve(cfg, nullptr).bytes + round_up(d.T * d.D * 4);
 }
 
 dit_status dit_block_fwd(const dit_config *cfg, const dit_block_weights *w, const void *x_in,
@@ -225,7 +225,7 @@ dit_status dit_block_fwd(const dit_config *cfg, const dit_block_weights *w, cons
     return DIT_ERR_SHAPE;
   const BlockWs bw = carve(cfg, ws);
   const bool f32 = cfg->dtype == DIT_F32;
-  return run_block(cfg, w, x_in, f32, x_out, f32, mod, bw, bw.x1, f32, (hipStream_t)stream);
+  return run_block(cfg, w, x_in, f32, x_out, f32, mod, bw, bw.x1, true, (hipStream_t)stream);
 }
 
 dit_status dit_stack_fwd(const dit_config *cfg, int32_t n_blocks, const dit_block_weights *blocks,
@@ -249,14 +249,13 @@ dit_status dit_stack_fwd(const dit_config *cfg, int32_t n_blocks, const dit_bloc
       overlap(ws, need, mod, (size_t)cfg->batch * 6 * cfg->hidden * 4))
     return DIT_ERR_SHAPE;
   const BlockWs bw = carve(cfg, ws);
-  char *xa = (char *)ws + bw.bytes;  // fp32 residual stream
-  char *xb1 = xa + round_up(d.T * d.D * 4);  // fp32 x1
+  char *xa = (char *)ws + bw.bytes;  // fp32 residual stream between blocks
   const bool f32 = cfg->dtype == DIT_F32;
   hipStream_t s = (hipStream_t)stream;
   for (int i = 0; i < n_blocks; ++i) {
     const bool first = i == 0, last = i == n_blocks - 1;
     st = run_block(cfg, &blocks[i], first ? x_in : xa, first ? f32 : true, last ? x_out : xa,
-                   last ? f32 : true, mod, bw, xb1, true, s);
+                   last ? f32 : true, mod, bw, bw.x1, true, s);
     if (st != DIT_OK) return st;
   }
   return DIT_OK;
@@ -338,6 +337,22 @@ dit_status dit_gemm_swiglu(dit_dtype dtype, int32_t m, int32_t f, int32_t k, con
     return DIT_ERR_SHAPE;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = launch_gemm_swiglu(dtype == DIT_F32, a, w13, u, m, f, k, s);
+  return e == hipSuccess ? DIT_OK : hip_fail(e);
+}
+
+dit_status dit_gemm_variant(dit_dtype dtype, int32_t variant, int32_t swiglu, int32_t m, int32_t n,
+                            int32_t k, const void *a, const void *w, void *c, void *stream) {
+  if (variant < 0 || variant >= kGemmVariants) return DIT_ERR_UNSUPPORTED;
+  if (swiglu != 0 && swiglu != 1) return DIT_ERR_SHAPE;
+  dit_status st = check_gemm(dtype, m, n, k, a, w, c, swiglu ? 2 * (int64_t)n + 256 : 256);
+  if (st != DIT_OK) return st;
+  const size_t es = esize(dtype);
+  const size_t wrows = swiglu ? 2 * (size_t)n : (size_t)n;
+  if (overlap(c, (size_t)m * n * es, a, (size_t)m * k * es) || overlap(c, (size_t)m * n * es, w, wrows * k * es))
+    return DIT_ERR_SHAPE;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = swiglu ? launch_gemm_swiglu(dtype == DIT_F32, a, w, c, m, n, k, s, variant)
+                        : launch_gemm(dtype == DIT_F32, a, w, c, m, n, k, s, variant);
   return e == hipSuccess ? DIT_OK : hip_fail(e);
 }
 

@@ -49,7 +49,8 @@ __global__ __launch_bounds__(512) void attn_kernel(const T *__restrict__ qkvg, T
 
   __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
   const int nthreads = blockDim.x;
   const int group = H / Hkv;
   const int b = blockIdx.z, j = blockIdx.y;

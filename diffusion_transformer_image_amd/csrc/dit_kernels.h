@@ -13,10 +13,12 @@ hipError_t launch_resid(bool x_f32, bool y_f32, bool out_f32, const void *x, con
                         int D, int which, hipStream_t s);
 hipError_t launch_tmod(const float *t, const float *w1, const float *w2, float *mod, float *zs,
                        int B, int D, int tdim, hipStream_t s);
+// variant < 0 picks the default tile configuration for the shape
 hipError_t launch_gemm(bool f32, const void *a, const void *w, void *c, int M, int N, int K,
-                       hipStream_t s);
+                       hipStream_t s, int variant = -1);
 hipError_t launch_gemm_swiglu(bool f32, const void *a, const void *w13, void *u, int M, int F,
-                              int K, hipStream_t s);
+                              int K, hipStream_t s, int variant = -1);
+constexpr int kGemmVariants = 7;
 hipError_t launch_attention(bool f32, int head_dim, const void *qkvg, void *og, int B, int L,
                             int H, int Hkv, hipStream_t s);
 

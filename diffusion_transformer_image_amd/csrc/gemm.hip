@@ -1,21 +1,24 @@
 // MFMA GEMM for the projections of the DiT block: C[M,N] = A[M,K] * W[N,K]^T
 // (nn.Linear layout: both operands K-contiguous), with an optional fused
 // SwiGLU epilogue for the up/gate projection (page "Krea 2 技术报告",
-// 架构 › Transformer块: SwiGLU MLP; grouped-query attention projections).
+// 架构 › Transformer块: SwiGLU MLP; the attention projections).
 //
 // Design for gfx950:
 //  * a workgroup owns a BM x BN output tile; WM x WN waves each own a
 //    (BM/WM) x (BN/WN) sub-tile of 16x16 MFMA blocks with fp32 accumulators;
-//  * K advances 128 bytes per stage (64 bf16 / 32 fp32).  Operands go from
-//    HBM straight into LDS with buffer_load ... lds (no VGPR staging),
-//    double-buffered, one barrier per stage;
-//  * LDS rows are 128 bytes; 16-byte chunk c of row r is stored at chunk
-//    c ^ (r & 7), so the MFMA fragment reads (16 rows x one chunk per lane
-//    group) spread over all banks;
+//  * K advances BKB bytes per stage (64 or 128 bytes of every row).  Operands
+//    go from HBM straight into LDS with buffer_load ... lds (no VGPR
+//    staging) through a STAGES-deep ring: the loads of stage kt+STAGES-1 are
+//    issued while stage kt is multiplied, and each wave waits only for its
+//    own loads of the stage it is about to read (partial vmcnt), so one
+//    barrier per stage is the only synchronisation;
+//  * 16-byte chunk c of LDS row r sits at chunk c ^ swz(r), which spreads
+//    the fragment reads (16 rows x one chunk per lane group) over all banks;
 //  * tails in M, N and K are zero-filled by the buffer descriptor's range
 //    check (out-of-range chunks are given an out-of-range offset);
 //  * workgroup ids are remapped so that each XCD (dispatch is round-robin
-//    over the 8 XCDs) walks a contiguous band of tiles that share A rows.
+//    over the 8 XCDs) walks a contiguous band of tiles, grouped GM row
+//    tiles at a time, so tiles sharing A rows or W rows meet in one L2.
 #include "dit_common.h"
 #include "dit_kernels.h"
 
@@ -23,25 +26,43 @@ namespace dit {
 
 enum { EPI_STORE = 0, EPI_SWIGLU = 1 };
 
-template <typename T, int BM, int BN, int WM, int WN, int EPI>
+template <int CPR>
+__device__ __forceinline__ int chunk_swizzle(int row) {
+  // CPR = 16-byte chunks per LDS row: 8 (128-byte rows) or 4 (64-byte rows)
+  return CPR == 8 ? (row & 7) : ((row >> 1) & 3);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <typename T, int BM, int BN, int BKB, int STAGES, int WM, int WN, int EPI>
 __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(const T *__restrict__ A,
                                                            const T *__restrict__ W,
                                                            T *__restrict__ C, int M, int N, int K,
                                                            int m_tiles, int n_tiles) {
   constexpr int NW = WM * WN;
-  constexpr int ROWB = 128;               // bytes of K per LDS row per stage
-  constexpr int EPC = 16 / sizeof(T);     // elements per 16-byte chunk
-  constexpr int KSTAGE = ROWB / sizeof(T);  // K elements per stage
+  constexpr int CPR = BKB / 16;             // 16-byte chunks per row per stage
+  constexpr int RPB = 1024 / BKB;           // rows per 1 KiB DMA block
+  constexpr int EPC = 16 / sizeof(T);       // elements per chunk
+  constexpr int KSTAGE = BKB / sizeof(T);   // K elements per stage
+  constexpr int KSTEPS = CPR / 4;           // MFMA k-steps per stage (4 chunks each)
   constexpr int TM = BM / WM, TN = BN / WN;  // wave sub-tile
   constexpr int RB = TM / 16, CB = TN / 16;
-  constexpr int ABLK = BM / 8, BBLK = BN / 8;  // 1 KiB blocks (8 rows) per stage
-  constexpr int STAGE_BYTES = (BM + BN) * ROWB;
+  constexpr int ABLK = BM / RPB, BBLK = BN / RPB;  // DMA blocks per stage
+  constexpr int STAGE_BYTES = (BM + BN) * BKB;
+  constexpr int BPW = (ABLK + BBLK) / NW;   // DMA loads per wave per stage
   static_assert((ABLK + BBLK) % NW == 0, "blocks must split evenly over waves");
   static_assert(EPI != EPI_SWIGLU || (CB % 2 == 0), "SwiGLU pairs column blocks");
+  static_assert(STAGES >= 2 && BPW * (STAGES - 2) < 64, "vmcnt range");
+  static_assert(STAGES * STAGE_BYTES <= 160 * 1024, "LDS");
 
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE_BYTES];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
   const int wm = wave / WN, wn = wave % WN;
 
   // ---- tile id: XCD-contiguous remap, then grouped (GM row tiles) order
@@ -56,36 +77,35 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(const T *__restrict__
   const int tm = first_m + in_g % gsz, tn = in_g / gsz;
   const int m0 = tm * BM;
   // SwiGLU: W holds [W1; W3] with N = F rows each; the tile covers F-columns
-  // [f0, f0 + BN/2) and reads those rows of both halves.
+  // [n0, n0 + BN/2) and reads those rows of both halves.
   const int n0 = (EPI == EPI_SWIGLU) ? tn * (BN / 2) : tn * BN;
 
   // Descriptors span only the rows this tile may touch, so 32-bit offsets
-  // suffice for any M (the host checks (2N + BN) * K * sizeof(T) < 2^31).
+  // suffice for any M (the host checks (2N + 256) * K * sizeof(T) < 2^31).
   const uint32_t ldb = (uint32_t)K * sizeof(T);  // row pitch in bytes
   const rsrc_t ra = make_rsrc(A + (size_t)m0 * K, (uint32_t)min(M - m0, BM) * ldb);
   const rsrc_t rw = (EPI == EPI_SWIGLU)
                         ? make_rsrc(W + (size_t)n0 * K, (uint32_t)(N + min(N - n0, BN / 2)) * ldb)
                         : make_rsrc(W + (size_t)n0 * K, (uint32_t)min(N - n0, BN) * ldb);
 
-  // ---- per-lane load offsets: lane writes LDS slot lane of a 1 KiB block =
-  // row lane/8, physical chunk lane%8, which holds logical chunk
-  // (lane%8) ^ (lane/8).
-  const int lrow = lane >> 3;
-  const int lchunk = (lane & 7) ^ lrow;
-  constexpr int BPW = (ABLK + BBLK) / NW;
+  // ---- per-lane DMA offsets: lane writes LDS slot `lane` of a 1 KiB block
+  // = row lane / CPR, physical chunk lane % CPR, which holds logical chunk
+  // (lane % CPR) ^ swz(row).
+  const int lrow = lane / CPR;
+  const int lchunk = (lane % CPR) ^ chunk_swizzle<CPR>(lrow);
   uint32_t goff[BPW];
   bool gval[BPW];
 #pragma unroll
   for (int j = 0; j < BPW; ++j) {
     const int blk = wave + j * NW;
     if (blk < ABLK) {
-      const int r = blk * 8 + lrow;
+      const int r = blk * RPB + lrow;
       gval[j] = (m0 + r) < M;
       goff[j] = (uint32_t)r * ldb + lchunk * 16;
     } else {
-      const int r = (blk - ABLK) * 8 + lrow;
+      const int r = (blk - ABLK) * RPB + lrow;
       if (EPI == EPI_SWIGLU) {
-        // rows [0, BN/2) of the tile: W1 row n0 + r; rows [BN/2, BN): W3 row
+        // tile rows [0, BN/2): W1 row n0 + r; rows [BN/2, BN): W3 row
         // N + n0 + r - BN/2 (offsets relative to the descriptor at row n0)
         const int rr = r < BN / 2 ? r : r - BN / 2;
         gval[j] = n0 + rr < N;
@@ -99,8 +119,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(const T *__restrict__
 
   auto issue_stage = [&](int kt, int buf) {
     const int k0 = kt * KSTAGE;
-    const bool ktail = (k0 + KSTAGE) > K;
-    const int kc_ok = ktail ? (K - k0) / EPC : 8;  // chunks of this stage inside K
+    const int kc_ok = (k0 + KSTAGE > K) ? (K - k0) / EPC : CPR;  // chunks inside K
     char *base = smem + buf * STAGE_BYTES;
 #pragma unroll
     for (int j = 0; j < BPW; ++j) {
@@ -117,49 +136,53 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(const T *__restrict__
 #pragma unroll
     for (int j = 0; j < CB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // fragment rows inside the stage buffer
+  // fragment rows inside a stage buffer (A rows first, then W rows)
   const int g = lane >> 4, r16 = lane & 15;
-  const int swz = lane & 7;  // (row & 7) for every fragment row this lane reads
+  const int swz = chunk_swizzle<CPR>(r16);  // every fragment row this lane reads is r16 mod 16
   int arow[RB], brow[CB];
 #pragma unroll
-  for (int i = 0; i < RB; ++i) arow[i] = wm * TM + i * 16 + r16;
+  for (int i = 0; i < RB; ++i) arow[i] = (wm * TM + i * 16 + r16) * BKB;
 #pragma unroll
   for (int j = 0; j < CB; ++j) {
+    int r;
     if (EPI == EPI_SWIGLU) {
       const int half = CB / 2, jj = j % half;
-      brow[j] = BM + (j < half ? 0 : BN / 2) + wn * (TN / 2) + jj * 16 + r16;
+      r = BM + (j < half ? 0 : BN / 2) + wn * (TN / 2) + jj * 16 + r16;
     } else {
-      brow[j] = BM + wn * TN + j * 16 + r16;
+      r = BM + wn * TN + j * 16 + r16;
     }
+    brow[j] = r * BKB;
   }
 
   const int nk = (K + KSTAGE - 1) / KSTAGE;
-  issue_stage(0, 0);
-  wait_vmem();
-  __syncthreads();
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < nk) issue_stage(s, s);
 
   for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) issue_stage(kt + 1, buf ^ 1);
-    const char *sb = smem + buf * STAGE_BYTES;
+    // this wave's loads of stage kt are done once at most the loads of the
+    // (up to STAGES-2) later stages already issued are still in flight
+    if (kt + STAGES - 2 < nk) wait_vmcnt<BPW * (STAGES - 2)>();
+    else wait_vmcnt<0>();
+    __syncthreads();  // every wave's part of stage kt has landed; stage kt-1 is consumed
+    if (kt + STAGES - 1 < nk) issue_stage(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
+    const char *sb = smem + (kt % STAGES) * STAGE_BYTES;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int ks = 0; ks < KSTEPS; ++ks) {
       const int pc = ((ks * 4 + g) ^ swz) * 16;
       u32x4 af[RB], bfr[CB];
 #pragma unroll
-      for (int i = 0; i < RB; ++i) af[i] = *reinterpret_cast<const u32x4 *>(sb + arow[i] * ROWB + pc);
+      for (int i = 0; i < RB; ++i) af[i] = *reinterpret_cast<const u32x4 *>(sb + arow[i] + pc);
 #pragma unroll
-      for (int j = 0; j < CB; ++j) bfr[j] = *reinterpret_cast<const u32x4 *>(sb + brow[j] * ROWB + pc);
+      for (int j = 0; j < CB; ++j) bfr[j] = *reinterpret_cast<const u32x4 *>(sb + brow[j] + pc);
 #pragma unroll
       for (int i = 0; i < RB; ++i)
 #pragma unroll
         for (int j = 0; j < CB; ++j) acc[i][j] = mma16<T>(af[i], bfr[j], acc[i][j]);
     }
-    wait_vmem();
-    __syncthreads();
   }
 
-  // ---- epilogue: lane holds rows 4g+i of column r16 of every 16x16 block
+  // ---- epilogue: lane holds rows 4g+e of column r16 of every 16x16 block
   if (EPI == EPI_SWIGLU) {
     constexpr int half = CB / 2;
 #pragma unroll
@@ -195,28 +218,42 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(const T *__restrict__
   }
 }
 
-template <typename T, int BM, int BN, int WM, int WN, int EPI>
+template <typename T, int BM, int BN, int BKB, int STAGES, int WM, int WN, int EPI>
 static hipError_t launch_gemm_t(const void *a, const void *w, void *c, int M, int N, int K,
                                 hipStream_t s) {
   const int mt = (M + BM - 1) / BM;
   const int nt = (EPI == EPI_SWIGLU) ? (N + BN / 2 - 1) / (BN / 2) : (N + BN - 1) / BN;
-  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, EPI>), dim3(mt * nt), dim3(WM * WN * 64), 0,
-                     s, (const T *)a, (const T *)w, (T *)c, M, N, K, mt, nt);
+  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, BKB, STAGES, WM, WN, EPI>), dim3(mt * nt),
+                     dim3(WM * WN * 64), 0, s, (const T *)a, (const T *)w, (T *)c, M, N, K, mt, nt);
   return hipGetLastError();
 }
 
+// Tile configurations, selectable for tuning (variant < 0: the default).
+template <int EPI>
+static hipError_t gemm_dispatch(bool f32, int variant, const void *a, const void *w, void *c,
+                                int M, int N, int K, hipStream_t s) {
+  if (f32) return launch_gemm_t<float, 256, 256, 128, 2, 2, 4, EPI>(a, w, c, M, N, K, s);
+  if (variant < 0) variant = 2;  // best measured on the 1024 px shapes (all four projections)
+  switch (variant) {
+    case 0: return launch_gemm_t<bf16, 256, 256, 64, 4, 2, 2, EPI>(a, w, c, M, N, K, s);
+    case 1: return launch_gemm_t<bf16, 256, 256, 64, 4, 2, 4, EPI>(a, w, c, M, N, K, s);
+    case 2: return launch_gemm_t<bf16, 256, 256, 128, 2, 2, 4, EPI>(a, w, c, M, N, K, s);
+    case 3: return launch_gemm_t<bf16, 256, 128, 64, 4, 2, 2, EPI>(a, w, c, M, N, K, s);
+    case 4: return launch_gemm_t<bf16, 256, 128, 128, 3, 2, 2, EPI>(a, w, c, M, N, K, s);
+    case 5: return launch_gemm_t<bf16, 128, 128, 128, 4, 2, 2, EPI>(a, w, c, M, N, K, s);
+    case 6: return launch_gemm_t<bf16, 256, 256, 64, 5, 2, 2, EPI>(a, w, c, M, N, K, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 hipError_t launch_gemm(bool f32, const void *a, const void *w, void *c, int M, int N, int K,
-                       hipStream_t s) {
-  if (f32) return launch_gemm_t<float, 256, 256, 2, 4, EPI_STORE>(a, w, c, M, N, K, s);
-  // narrow outputs (N <= 4096) leave too few 256x256 tiles for 256 CUs
-  if (N <= 4096) return launch_gemm_t<bf16, 256, 128, 4, 2, EPI_STORE>(a, w, c, M, N, K, s);
-  return launch_gemm_t<bf16, 256, 256, 2, 4, EPI_STORE>(a, w, c, M, N, K, s);
+                       hipStream_t s, int variant) {
+  return gemm_dispatch<EPI_STORE>(f32, variant, a, w, c, M, N, K, s);
 }
 
 hipError_t launch_gemm_swiglu(bool f32, const void *a, const void *w13, void *u, int M, int F,
-                              int K, hipStream_t s) {
-  if (f32) return launch_gemm_t<float, 256, 256, 2, 4, EPI_SWIGLU>(a, w13, u, M, F, K, s);
-  return launch_gemm_t<bf16, 256, 256, 2, 4, EPI_SWIGLU>(a, w13, u, M, F, K, s);
+                              int K, hipStream_t s, int variant) {
+  return gemm_dispatch<EPI_SWIGLU>(f32, variant, a, w13, u, M, F, K, s);
 }
 
 }  // namespace dit

@@ -109,11 +109,11 @@ typedef enum {
 /* Workspace bytes needed by dit_block_fwd for this configuration
  * (0 if cfg is invalid).  Holds the normalised activations, the Q|K|V|G
  * projection (later reused for the SwiGLU hidden U), the gated attention
- * output, the branch outputs and x1. */
+ * output, the branch outputs and x1 (fp32). */
 size_t dit_workspace_size(const dit_config *cfg /* host */);
 
-/* Workspace bytes needed by dit_stack_fwd: the block workspace plus two
- * fp32 [T, D] buffers that carry the residual stream between blocks. */
+/* Workspace bytes needed by dit_stack_fwd: the block workspace plus one
+ * fp32 [T, D] buffer that carries the residual stream between blocks. */
 size_t dit_stack_workspace_size(const dit_config *cfg /* host */);
 
 /* One block forward.
@@ -130,8 +130,9 @@ size_t dit_stack_workspace_size(const dit_config *cfg /* host */);
  *   x1 = x + gate1 * (Og * W_o^T)
  *   h2 = x1 / sqrt(mean(x1^2) + eps) * (1 + norm2_w) * (1 + scale2) + shift2
  *   x_out = x1 + gate2 * ((SiLU(h2 W1^T) * (h2 W3^T)) * W_2^T)
- * In the bf16 path the intermediates h, QKVG, Og, the branch outputs, U
- * and x1 are stored as bf16 between kernels. */
+ * In the bf16 path the intermediates h, QKVG, Og, the branch outputs and
+ * U are stored as bf16 between kernels; x1 is kept in fp32, so the
+ * residual stream is rounded once, into x_out. */
 dit_status dit_block_fwd(const dit_config *cfg /* host */, const dit_block_weights *w /* host */,
                          const void *x_in, void *x_out, const float *mod, void *ws,
                          size_t ws_bytes, void *stream);
@@ -178,6 +179,15 @@ dit_status dit_gemm(dit_dtype dtype, int32_t m, int32_t n, int32_t k, const void
  * (page "Krea 2 技术报告", 架构 › Transformer块: SwiGLU MLP). */
 dit_status dit_gemm_swiglu(dit_dtype dtype, int32_t m, int32_t f, int32_t k, const void *a,
                            const void *w13, void *u, void *stream);
+
+/* The same products with an explicit tile configuration, for tuning and
+ * tests: variant 0..6 selects one of the compiled (BM x BN tile, stage
+ * depth, wave grid) configurations; every variant computes the same
+ * result up to fp32 summation order.  swiglu = 0: C[M, N] = A W^T with
+ * W [N, K]; swiglu = 1: as dit_gemm_swiglu with F = n and W = W13 [2n, K].
+ * Variants are ignored by the fp32 path. */
+dit_status dit_gemm_variant(dit_dtype dtype, int32_t variant, int32_t swiglu, int32_t m, int32_t n,
+                            int32_t k, const void *a, const void *w, void *c, void *stream);
 
 /* Gated grouped-query attention over the rows of qkvg [T, (2H+2Hkv)*d]
  * (column blocks Q | K | V | G, as produced by the QKVG projection):

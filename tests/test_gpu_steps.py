@@ -178,3 +178,19 @@ def test_timestep_mod(dev, name):
     torch.cuda.synchronize()
     ref = O.timestep_modulation(t, w1, w2, cfg.hidden)
     assert_parity(device.to_numpy(M), ref, "f32", "timestep modulation", maxabs=2e-5)
+
+
+@pytest.mark.parametrize("variant", list(range(7)))
+@pytest.mark.parametrize("swiglu", [False, True])
+def test_gemm_every_tile_variant(dev, variant, swiglu):
+    """Every compiled tile configuration on ragged M, N and K."""
+    torch, device, dit = dev
+    m, n, k = 300, 200 if swiglu else 520, 328
+    cfg = datagen.get_config("c1")
+    a, w = datagen.gemm_operands(cfg, m, 2 * n if swiglu else n, k, tag=97 + variant)
+    A, W = device.to_device(a, "bf16"), device.to_device(w, "bf16")
+    C = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    dit.gemm_variant(variant, A, W, C, swiglu=swiglu)
+    torch.cuda.synchronize()
+    ref = O.swiglu_hidden(a, w, n) if swiglu else a.astype(np.float64) @ w.astype(np.float64).T
+    assert_parity(device.to_numpy(C), ref, "bf16", f"variant {variant}", maxabs=8e-3, cos_min=0.99999)
