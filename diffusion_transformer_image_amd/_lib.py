@@ -75,7 +75,7 @@ def lib() -> ctypes.CDLL:
             "dit_gemm": (i32, [i32, i32, i32, i32, vp, vp, vp, vp]),
             "dit_gemm_swiglu": (i32, [i32, i32, i32, i32, vp, vp, vp, vp]),
             "dit_gemm_variant": (i32, [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp]),
-            "dit_attention": (i32, [cfgp, vp, vp, vp]),
+            "dit_attention": (i32, [cfgp, vp, vp, vp, sz, vp]),
             "dit_gated_residual": (i32, [cfgp, vp, i32, vp, vp, vp, i32, vp, i32, vp]),
             "dit_status_str": (ctypes.c_char_p, [i32]),
             "dit_last_hip_error": (ctypes.c_int, []),
@@ -197,8 +197,9 @@ def gemm_variant(variant: int, a, w, c, swiglu: bool = False, stream=None) -> No
                                   _ptr(c), _stream(stream)), "dit_gemm_variant")
 
 
-def attention(cfg: Config, qkvg, og, stream=None) -> None:
-    _check(lib().dit_attention(ctypes.byref(cfg), _ptr(qkvg), _ptr(og), _stream(stream)),
+def attention(cfg: Config, qkvg, og, ws, stream=None) -> None:
+    nbytes = ws.numel() * ws.element_size() if hasattr(ws, "numel") else 0
+    _check(lib().dit_attention(ctypes.byref(cfg), _ptr(qkvg), _ptr(og), _ptr(ws), nbytes, _stream(stream)),
            "dit_attention")
 
 

@@ -100,7 +100,7 @@ Dims dims(const dit_config *c) {
 }
 
 struct BlockWs {
-  char *h, *qkvg, *og, *br, *x1;
+  char *h, *qkvg, *og, *br, *x1, *vt;
   size_t bytes;
 };
 BlockWs carve(const dit_config *c, void *ws) {
@@ -118,6 +118,7 @@ BlockWs carve(const dit_config *c, void *ws) {
   w.og = take(d.T * d.hd * d.es);
   w.br = take(d.T * d.D * d.es);
   w.x1 = take(d.T * d.D * 4);  // x1 = x + gate1 * A stays fp32 (one rounding, at x_out)
+  w.vt = take(attention_vt_bytes(c->dtype == DIT_F32, c->batch, c->seq_len, c->n_kv_heads, c->head_dim));
   const size_t tmod = (size_t)c->batch * c->hidden * 4;
   w.bytes = off > tmod ? off : tmod;
   return w;
@@ -153,7 +154,7 @@ dit_status run_block(const dit_config *c, const dit_block_weights *w, const void
     return launch_gemm(f32, ws.h, w->w_qkvg, ws.qkvg, T, (int)d.nqkvg, D, s);
   }));
   DIT_TRY(timed(DIT_K_ATTN, s, [&] {
-    return launch_attention(f32, c->head_dim, ws.qkvg, ws.og, c->batch, L, c->n_heads, c->n_kv_heads, s);
+    return launch_attention(f32, c->head_dim, ws.qkvg, ws.vt, ws.og, c->batch, L, c->n_heads, c->n_kv_heads, s);
   }));
   DIT_TRY(timed(DIT_K_GEMM_O, s, [&] {
     return launch_gemm(f32, ws.og, w->w_o, ws.br, T, D, (int)d.hd, s);
@@ -356,16 +357,23 @@ dit_status dit_gemm_variant(dit_dtype dtype, int32_t variant, int32_t swiglu, in
   return e == hipSuccess ? DIT_OK : hip_fail(e);
 }
 
-dit_status dit_attention(const dit_config *cfg, const void *qkvg, void *og, void *stream) {
+dit_status dit_attention(const dit_config *cfg, const void *qkvg, void *og, void *ws, size_t ws_bytes,
+                         void *stream) {
   dit_status st = check_cfg(cfg);
   if (st != DIT_OK) return st;
   if (!qkvg || !og) return DIT_ERR_NULL;
-  if (!aligned(qkvg) || !aligned(og)) return DIT_ERR_ALIGN;
+  if (!ws) return DIT_ERR_WORKSPACE;
+  if (!aligned(qkvg) || !aligned(og) || !aligned(ws)) return DIT_ERR_ALIGN;
   const Dims d = dims(cfg);
-  if (overlap(qkvg, d.T * d.nqkvg * d.es, og, d.T * d.hd * d.es)) return DIT_ERR_SHAPE;
+  const size_t vtb = attention_vt_bytes(cfg->dtype == DIT_F32, cfg->batch, cfg->seq_len, cfg->n_kv_heads,
+                                        cfg->head_dim);
+  if (ws_bytes < vtb) return DIT_ERR_WORKSPACE;
+  if (overlap(qkvg, d.T * d.nqkvg * d.es, og, d.T * d.hd * d.es) || overlap(ws, vtb, qkvg, d.T * d.nqkvg * d.es) ||
+      overlap(ws, vtb, og, d.T * d.hd * d.es))
+    return DIT_ERR_SHAPE;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = timed(DIT_K_ATTN, s, [&] {
-    return launch_attention(cfg->dtype == DIT_F32, cfg->head_dim, qkvg, og, cfg->batch,
+    return launch_attention(cfg->dtype == DIT_F32, cfg->head_dim, qkvg, ws, og, cfg->batch,
                             cfg->seq_len, cfg->n_heads, cfg->n_kv_heads, s);
   });
   return e == hipSuccess ? DIT_OK : hip_fail(e);

@@ -7,63 +7,140 @@
 //   with j = h / (H / Hkv).
 //
 // Design for gfx950:
-//  * one workgroup = (sample b, KV head j, 64 query tokens) for ALL query
-//    heads of the group: the K / V tiles of head j are brought to LDS once
-//    and read by group * 2 waves (each wave: one query head, 32 queries);
+//  * a small pass first writes V^T ([B][Hkv][d][Lp], keys contiguous, Lp =
+//    L rounded up to the key tile, zero padded), so both operand tiles of
+//    the main loop go HBM -> LDS by DMA (buffer_load ... lds) with no VALU
+//    work, through a 3-deep ring (tile t+2 in flight while t is used; each
+//    wave waits only for its own DMA of tile t, then one barrier);
+//  * one workgroup = (sample b, KV head j, 2*QW query tokens) for ALL query
+//    heads of the group: the K / V^T tiles of head j are brought to LDS once
+//    and read by group * 2 waves (each wave: one query head, QW = 32 or 48
+//    queries; 48 when that fills the 256 CUs in fewer weighted rounds, e.g.
+//    4608 tokens: 768 workgroups = 3 full rounds instead of 4.5);
 //  * scores are computed transposed, S^T = K Q^T (MFMA 16x16), so each
-//    lane owns one query column: the online-softmax statistics of a query
-//    live in 4 lanes (one per lane group) and the probabilities P^T are
-//    already in the register layout of the B operand of O^T = V^T P^T;
-//  * V^T tiles are written to LDS transposed (4 keys x 16 bytes per
-//    thread), with an XOR swizzle of the 4-key units by (d & 15);
-//  * K tiles go HBM -> LDS directly (buffer_load ... lds), double-buffered;
-//  * softmax in fp32 with exp2 and the 1/sqrt(d) scale folded into one FMA;
-//    the running max is shared by the 4 lanes of a query via xor shuffles;
+//    lane owns one query column: the softmax statistics of a query live in
+//    4 lanes (one per lane group) and the probabilities P^T are already in
+//    the register layout of the B operand of O^T = V^T P^T;
+//  * softmax in fp32 base 2 with the 1/sqrt(d) scale folded into one FMA.
+//    The reference maximum is only raised when a tile's maximum exceeds it
+//    by more than 8 (log2 units), so probabilities stay <= 2^8 and the
+//    rescale of the accumulators (a wave-uniform branch) is rare; the
+//    quotient O / l is unchanged by the choice of reference;
+//  * LDS data is XOR-swizzled (K by 16-byte chunk at DMA time, V^T when
+//    the V^T pass writes it, which also groups each lane's keys of one
+//    MFMA into one chunk) so every fragment is one ds_read_b128 and 16
+//    rows hit distinct banks (checked with SQ_LDS_BANK_CONFLICT);
 //  * epilogue: divide by the row sum, multiply by sigmoid(G), store.
+#include <cmath>
+
 #include "dit_common.h"
 #include "dit_kernels.h"
 
 namespace dit {
 
-constexpr int ATT_BQ = 64;   // query tokens per workgroup
-constexpr int ATT_QW = 32;   // query tokens per wave
 constexpr int ATT_BK = 64;   // keys per tile
 
-template <typename T, int HD, int MIN_THREADS>
-__global__ __launch_bounds__(512) void attn_kernel(const T *__restrict__ qkvg, T *__restrict__ og,
-                                                   int L, int H, int Hkv, float sc) {
+__host__ __device__ constexpr int att_lpad(int L) { return (L + ATT_BK - 1) / ATT_BK * ATT_BK; }
+
+// ---------------------------------------------------------------- V^T pass
+// vt[b][j][dd][l] = qkvg[b*L + l][(H + Hkv + j)*HD + dd], zero for l >= L,
+// with the keys of each 64-key tile of a row dd rearranged so that every
+// 16-byte chunk holds exactly the keys one lane feeds one MFMA, and the
+// chunks XOR-swizzled by dd:
+//   bf16: logical chunk c = pr*4 + g holds keys (2pr)*16 + 4g + {0..3} and
+//         (2pr+1)*16 + 4g + {0..3}; it is stored at chunk c ^ (dd & 7);
+//   fp32: logical chunk c holds keys 4c + {0..3}; stored at c ^ (dd & 15).
+// A straight 16-byte DMA copy of a tile row then gives the LDS layout the
+// fragment reads want: one conflict-free ds_read_b128 per fragment.
+template <typename T>
+__device__ __forceinline__ int vt_chunk_key(int c, int e) {  // e < 16 / sizeof(T)
+  if constexpr (sizeof(T) == 2) return (2 * (c >> 2) + (e >> 2)) * 16 + 4 * (c & 3) + (e & 3);
+  else return 4 * c + e;
+}
+template <typename T>
+__device__ __forceinline__ int vt_swizzle(int dd) { return sizeof(T) == 2 ? (dd & 7) : (dd & 15); }
+
+template <typename T, int HD>
+__global__ __launch_bounds__(256) void vtrans_kernel(const T *__restrict__ qkvg, T *__restrict__ vt,
+                                                     int L, int H, int Hkv) {
+  constexpr int EPC = 16 / sizeof(T);  // elements per 16-byte chunk
+  __shared__ T tile[ATT_BK][HD + EPC];
+  const int l0 = blockIdx.x * ATT_BK, j = blockIdx.y, b = blockIdx.z;
+  const int Lp = att_lpad(L);
+  const size_t ldq = (size_t)(2 * H + 2 * Hkv) * HD;
+  const T *src = qkvg + (size_t)b * L * ldq + (size_t)(H + Hkv + j) * HD;
+  for (int idx = threadIdx.x; idx < ATT_BK * (HD / EPC); idx += blockDim.x) {
+    const int r = idx / (HD / EPC), c = (idx % (HD / EPC)) * EPC;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (l0 + r < L) v = *reinterpret_cast<const u32x4 *>(src + (size_t)(l0 + r) * ldq + c);
+    T pv[EPC];
+    __builtin_memcpy(pv, &v, 16);
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) tile[r][c + e] = pv[e];
+  }
+  __syncthreads();
+  T *dst = vt + ((size_t)b * Hkv + j) * HD * Lp + l0;
+  for (int idx = threadIdx.x; idx < HD * (ATT_BK / EPC); idx += blockDim.x) {
+    const int dd = idx % HD, pc = idx / HD;  // physical 16-byte chunk of the row
+    const int lc = pc ^ vt_swizzle<T>(dd);   // logical chunk stored there
+    T w[EPC];
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) w[e] = tile[vt_chunk_key<T>(lc, e)][dd];
+    u32x4 v;
+    __builtin_memcpy(&v, w, 16);
+    *reinterpret_cast<u32x4 *>(dst + (size_t)dd * Lp + pc * EPC) = v;
+  }
+}
+
+// ---------------------------------------------------------------- main kernel
+template <int N>
+__device__ __forceinline__ void att_wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// NW = waves per workgroup (2 per query head of the group); QW = query
+// tokens per wave (32 or 48), so a workgroup covers 2 * QW query tokens.
+template <typename T, int HD, int NW, int QW>
+__global__ __launch_bounds__(NW * 64) void attn_kernel(const T *__restrict__ qkvg, const T *__restrict__ vt,
+                                                       T *__restrict__ og, int L, int H, int Hkv, float sc) {
   constexpr int ES = sizeof(T);
-  constexpr int EPC = 16 / ES;          // elements per 16-byte chunk
   constexpr int KROW = HD * ES;         // bytes of one K row in LDS
-  constexpr int NCK = KROW / 16;        // chunks per K row
+  constexpr int NCK = KROW / 16;        // 16-byte chunks per K row (16 or 32)
   constexpr int KS = KROW / 64;         // MFMA k-steps over d (4 chunks each)
   constexpr int KTILE = ATT_BK * KROW;  // bytes of a K tile
   constexpr int VROW = ATT_BK * ES;     // bytes of one V^T row (64 keys)
-  constexpr int UB = 4 * ES;            // bytes of a 4-key unit of V^T
+  constexpr int VCH = VROW / 16;        // chunks per V^T row (8 or 16)
   constexpr int VTILE = HD * VROW;
   constexpr int STAGE = KTILE + VTILE;
   constexpr int DB = HD / 16;           // 16-row blocks of d
-  constexpr int QB = ATT_QW / 16;       // 16-column blocks of queries per wave
+  constexpr int QB = QW / 16;           // 16-column blocks of queries per wave
   constexpr int KB = ATT_BK / 16;       // 16-key blocks per tile
-  static_assert(NCK >= 8, "K rows need >= 8 chunks for the swizzle");
+  constexpr int NSTAGE = (3 * STAGE <= 160 * 1024) ? 3 : 2;  // K / V^T ring depth
+  constexpr int PD = NSTAGE - 1;        // tiles in flight ahead of the one in use
+  constexpr int KBLK = KTILE / 1024, VBLK = VTILE / 1024;
+  constexpr int DMA_PER_TILE = (KBLK + NW - 1) / NW + (VBLK + NW - 1) / NW;  // per wave
+  static_assert(NCK >= 16, "K rows need >= 16 chunks for the swizzle");
+  static_assert(KBLK % NW == 0 && VBLK % NW == 0, "tile blocks split evenly over the waves");
+  static_assert(NSTAGE * STAGE <= 160 * 1024, "LDS");
 
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
-  const int nthreads = blockDim.x;
   const int group = H / Hkv;
   const int b = blockIdx.z, j = blockIdx.y;
   const int h = j * group + (wave >> 1);
-  const int q0 = blockIdx.x * ATT_BQ + (wave & 1) * ATT_QW;
+  const int q0 = blockIdx.x * (2 * QW) + (wave & 1) * QW;
   const int g = lane >> 4, r16 = lane & 15;
+  const int Lp = att_lpad(L);
 
   const int ldq = (2 * H + 2 * Hkv) * HD;  // elements per token row of qkvg
   const uint32_t ldqb = (uint32_t)ldq * ES;
   const T *base = qkvg + (size_t)b * L * ldq;
   const rsrc_t rq = make_rsrc(base, (uint32_t)L * ldqb);
+  const rsrc_t rv = make_rsrc(vt + ((size_t)b * Hkv + j) * HD * Lp, (uint32_t)HD * Lp * ES);
   const uint32_t kcol = (uint32_t)(H + j) * HD * ES;
-  const uint32_t vcol = (uint32_t)(H + Hkv + j) * HD * ES;
 
   // ---- Q fragments (B operand of S^T = K Q^T), kept in registers
   u32x4 qf[QB][KS];
@@ -77,67 +154,26 @@ __global__ __launch_bounds__(512) void attn_kernel(const T *__restrict__ qkvg, T
     }
   }
 
-  // ---- tile loaders
-  const int nwaves = nthreads >> 6;
-  auto issue_k = [&](int t, int buf) {
-    char *kb = smem + buf * STAGE;
-    constexpr int ROWS_PER_BLK = 1024 / KROW;
-    constexpr int NBLK = KTILE / 1024;
-    for (int blk = wave; blk < NBLK; blk += nwaves) {
-      const int row = blk * ROWS_PER_BLK + lane / NCK;
-      const int pc = lane % NCK;
-      const int lc = pc ^ (row & 7);
+  // ---- tile loaders (DMA; each wave writes whole 1 KiB blocks)
+  auto issue_tile = [&](int t, int buf) {
+    char *kt = smem + buf * STAGE;
+    constexpr int KRPB = 1024 / KROW;
+#pragma unroll
+    for (int blk = wave; blk < KBLK; blk += NW) {
+      const int row = blk * KRPB + lane / NCK;
+      const int lc = (lane % NCK) ^ (row & 15);
       const int key = t * ATT_BK + row;
       const uint32_t off = key < L ? (uint32_t)key * ldqb + kcol + lc * 16 : kOOB;
-      load_lds16(rq, kb + blk * 1024, off);
+      load_lds16(rq, kt + blk * 1024, off);
     }
-  };
-  // V: each unit is 4 keys x EPC d-values; loaded to registers, then
-  // written transposed.  Units per tile = 16 * HD / EPC.
-  constexpr int NVU = (ATT_BK / 4) * (HD / EPC);
-  constexpr int VU_PER_T = (NVU + MIN_THREADS - 1) / MIN_THREADS;
-  u32x4 vreg[VU_PER_T][4];
-  auto load_v = [&](int t) {
+    char *vtl = kt + KTILE;
+    constexpr int VRPB = 1024 / VROW;
 #pragma unroll
-    for (int u = 0; u < VU_PER_T; ++u) {
-      const int unit = tid + u * nthreads;
-      if (unit < NVU) {
-        const int kg = unit % (ATT_BK / 4), dc = unit / (ATT_BK / 4);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = t * ATT_BK + kg * 4 + r;
-          const uint32_t off = key < L ? (uint32_t)key * ldqb + vcol + dc * 16 : kOOB;
-          vreg[u][r] = load16(rq, off);
-        }
-      }
-    }
-  };
-  auto store_vt = [&](int buf) {
-    char *vt = smem + buf * STAGE + KTILE;
-#pragma unroll
-    for (int u = 0; u < VU_PER_T; ++u) {
-      const int unit = tid + u * nthreads;
-      if (unit < NVU) {
-        const int kg = unit % (ATT_BK / 4), dc = unit / (ATT_BK / 4);
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) {
-          const int d = dc * EPC + e;
-          char *dst = vt + d * VROW + ((kg ^ (d & 15)) * UB);
-          if constexpr (ES == 2) {
-            // element e of 4 consecutive key rows -> one 8-byte unit
-            uint32_t w[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const uint32_t word = vreg[u][r][e >> 1];
-              w[r] = (e & 1) ? (word >> 16) : (word & 0xFFFFu);
-            }
-            *reinterpret_cast<u32x2 *>(dst) = u32x2{w[0] | (w[1] << 16), w[2] | (w[3] << 16)};
-          } else {
-            *reinterpret_cast<u32x4 *>(dst) =
-                u32x4{vreg[u][0][e], vreg[u][1][e], vreg[u][2][e], vreg[u][3][e]};
-          }
-        }
-      }
+    for (int blk = wave; blk < VBLK; blk += NW) {
+      // rows of V^T are stored pre-swizzled: copy them verbatim
+      const int d = blk * VRPB + lane / VCH;
+      const uint32_t off = (uint32_t)d * Lp * ES + (uint32_t)t * VROW + (lane % VCH) * 16;
+      load_lds16(rv, vtl + blk * 1024, off);
     }
   };
 
@@ -146,39 +182,43 @@ __global__ __launch_bounds__(512) void attn_kernel(const T *__restrict__ qkvg, T
   for (int i = 0; i < DB; ++i)
 #pragma unroll
     for (int k = 0; k < QB; ++k) o[i][k] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float mrow[QB], lrow[QB];
+  float mref[QB], lrow[QB];
 #pragma unroll
-  for (int k = 0; k < QB; ++k) { mrow[k] = -INFINITY; lrow[k] = 0.f; }
+  for (int k = 0; k < QB; ++k) { mref[k] = -INFINITY; lrow[k] = 0.f; }
+  const float tau = 8.0f / sc;  // raw-score margin: probabilities stay <= 2^8
 
   const int nt = (L + ATT_BK - 1) / ATT_BK;
-  issue_k(0, 0);
-  load_v(0);
-  store_vt(0);
-  wait_vmem();
-  __syncthreads();
+#pragma unroll
+  for (int p = 0; p < PD; ++p)
+    if (p < nt) issue_tile(p, p);
 
   for (int t = 0; t < nt; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < nt) {
-      issue_k(t + 1, buf ^ 1);
-      load_v(t + 1);
-    }
-    const char *kt = smem + buf * STAGE;
-    const char *vt = kt + KTILE;
+    // this wave's DMA of tile t is done once only the (up to PD-1) later
+    // tiles already issued may be pending
+    if (t + PD - 1 < nt) att_wait_vmcnt<DMA_PER_TILE * (PD - 1)>();
+    else att_wait_vmcnt<0>();
+    __syncthreads();  // all of tile t landed; every wave is done with tile t-1
+    if (t + PD < nt) issue_tile(t + PD, (t + PD) % NSTAGE);
+    const char *kt = smem + (t % NSTAGE) * STAGE;
+    const char *vtl = kt + KTILE;
 
-    // S^T[kb][qb]: lane holds keys kb*16 + 4g + i of query qb*16 + r16
+    // S^T[kb][qb]: lane holds keys kb*16 + 4g + i of query qb*16 + r16.
+    // All K fragments of the tile are requested before the first MFMA.
+    u32x4 kf[KB][KS];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)  // row = kb*16 + r16, so (row & 15) = r16
+        kf[kb][ks] = *reinterpret_cast<const u32x4 *>(kt + (kb * 16 + r16) * KROW + (((ks * 4 + g) ^ r16) * 16));
     f32x4 s[KB][QB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) s[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int row = kb * 16 + r16;
-        const u32x4 kf = *reinterpret_cast<const u32x4 *>(kt + row * KROW + (((ks * 4 + g) ^ (row & 7)) * 16));
+      for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) s[kb][qb] = mma16<T>(kf, qf[qb][ks], s[kb][qb]);
-      }
+        for (int qb = 0; qb < QB; ++qb) s[kb][qb] = mma16<T>(kf[kb][ks], qf[qb][ks], s[kb][qb]);
     }
 
     // mask keys past the end of the sequence (last tile only)
@@ -193,7 +233,6 @@ __global__ __launch_bounds__(512) void attn_kernel(const T *__restrict__ qkvg, T
     }
 
     // online softmax per query column
-    float alpha[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       float mx = s[0][qb][0];
@@ -203,10 +242,16 @@ __global__ __launch_bounds__(512) void attn_kernel(const T *__restrict__ qkvg, T
         for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[kb][qb][i]);
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(mrow[qb], mx);
-      alpha[qb] = __builtin_amdgcn_exp2f((mrow[qb] - mnew) * sc);
-      mrow[qb] = mnew;
-      const float msc = mnew * sc;
+      const bool need = mx > mref[qb] + tau;  // always true on the first tile
+      if (__any(need)) {
+        const float mnew = need ? mx : mref[qb];
+        const float alpha = __builtin_amdgcn_exp2f((mref[qb] - mnew) * sc);
+        mref[qb] = mnew;
+        lrow[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[db][qb] *= alpha;
+      }
+      const float msc = mref[qb] * sc;
       float sum = 0.f;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
@@ -216,14 +261,14 @@ __global__ __launch_bounds__(512) void attn_kernel(const T *__restrict__ qkvg, T
           s[kb][qb][i] = p;
           sum += p;
         }
-      lrow[qb] = lrow[qb] * alpha[qb] + sum;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) o[db][qb] *= alpha[qb];
+      lrow[qb] += sum;
     }
 
-    // O^T[db][qb] += V^T[db rows] * P^T
+    // O^T[db][qb] += V^T[db rows] * P^T; the V^T fragment of row
+    // d = db*16 + r16 for k-slice c is one 16-byte chunk at c ^ swizzle(d)
     if constexpr (ES == 2) {
-      // bf16: one MFMA (k = 32) per pair of 16-key blocks
+      // bf16: one MFMA (k = 32) per pair of 16-key blocks; the lane's 8
+      // keys are (2pr)*16 + 4g + {0..3} and (2pr+1)*16 + 4g + {0..3}
 #pragma unroll
       for (int pr = 0; pr < KB / 2; ++pr) {
         u32x4 pf[QB];
@@ -237,19 +282,16 @@ __global__ __launch_bounds__(512) void attn_kernel(const T *__restrict__ qkvg, T
           }
           pf[qb] = __builtin_bit_cast(u32x4, pv);
         }
+        const int cpos = ((pr * 4 + g) ^ (r16 & 7)) * 16;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const int d = db * 16 + r16;
-          const char *rowp = vt + d * VROW;
-          const u32x2 lo = *reinterpret_cast<const u32x2 *>(rowp + ((((2 * pr) * 4 + g) ^ r16) * UB));
-          const u32x2 hi = *reinterpret_cast<const u32x2 *>(rowp + ((((2 * pr + 1) * 4 + g) ^ r16) * UB));
-          const u32x4 vf = u32x4{lo.x, lo.y, hi.x, hi.y};
+          const u32x4 vf = *reinterpret_cast<const u32x4 *>(vtl + (db * 16 + r16) * VROW + cpos);
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) o[db][qb] = mma16<T>(vf, pf[qb], o[db][qb]);
         }
       }
     } else {
-      // fp32: four MFMAs (k = 4 each) per 16-key block
+      // fp32: four MFMAs (k = 4 each) per 16-key block; chunk kb*4 + g
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         u32x4 pf[QB];
@@ -257,17 +299,13 @@ __global__ __launch_bounds__(512) void attn_kernel(const T *__restrict__ qkvg, T
         for (int qb = 0; qb < QB; ++qb) pf[qb] = __builtin_bit_cast(u32x4, s[kb][qb]);
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const int d = db * 16 + r16;
-          const u32x4 vf = *reinterpret_cast<const u32x4 *>(vt + d * VROW + (((kb * 4 + g) ^ r16) * UB));
+          const u32x4 vf = *reinterpret_cast<const u32x4 *>(vtl + (db * 16 + r16) * VROW + (((kb * 4 + g) ^ r16) * 16));
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) o[db][qb] = mma16<T>(vf, pf[qb], o[db][qb]);
         }
       }
     }
 
-    if (t + 1 < nt) store_vt(buf ^ 1);
-    wait_vmem();
-    __syncthreads();
   }
 
   // ---- epilogue: row sums over the 4 lane groups, normalise, gate, store
@@ -285,39 +323,76 @@ __global__ __launch_bounds__(512) void attn_kernel(const T *__restrict__ qkvg, T
       T *orow = og + ((size_t)b * L + q) * ldo + (size_t)h * HD;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const int d = db * 16 + 4 * g;
+        const int d = db * 16 + 4 * g;  // 4 consecutive channels per lane
+        if constexpr (ES == 2) {
+          const bf16x4 gv = *reinterpret_cast<const bf16x4 *>(grow + d);
+          bf16x4 ov;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float gv = to_f32(grow[d + i]);
-          orow[d + i] = from_f32<T>(o[db][qb][i] * inv * sigmoid(gv));
+          for (int i = 0; i < 4; ++i)
+            ov[i] = (bf16)(o[db][qb][i] * inv * __builtin_amdgcn_rcpf(1.0f + __expf(-(float)gv[i])));
+          *reinterpret_cast<bf16x4 *>(orow + d) = ov;
+        } else {
+          const f32x4 gv = *reinterpret_cast<const f32x4 *>(grow + d);
+          f32x4 ov;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ov[i] = o[db][qb][i] * inv / (1.0f + __expf(-gv[i]));
+          *reinterpret_cast<f32x4 *>(orow + d) = ov;
         }
       }
     }
   }
 }
 
+size_t attention_vt_bytes(bool f32, int B, int L, int Hkv, int head_dim) {
+  return (size_t)B * Hkv * head_dim * att_lpad(L) * (f32 ? 4 : 2);
+}
+
+template <typename T, int HD, int QW>
+static void launch_attn_q(const T *q, const T *v, T *og, int B, int L, int H, int Hkv, float sc,
+                          hipStream_t s) {
+  const int group = H / Hkv;
+  dim3 grid((L + 2 * QW - 1) / (2 * QW), Hkv, B);
+  switch (group) {  // 2 waves per query head of the group
+    case 1: hipLaunchKernelGGL((attn_kernel<T, HD, 2, QW>), grid, dim3(128), 0, s, q, v, og, L, H, Hkv, sc); break;
+    case 2: hipLaunchKernelGGL((attn_kernel<T, HD, 4, QW>), grid, dim3(256), 0, s, q, v, og, L, H, Hkv, sc); break;
+    case 4: hipLaunchKernelGGL((attn_kernel<T, HD, 8, QW>), grid, dim3(512), 0, s, q, v, og, L, H, Hkv, sc); break;
+  }
+}
+
+// Work units of a launch, counted in rounds of one workgroup per CU and
+// weighted by the queries per wave: picks 32 or 48 queries per wave.
+static double attn_rounds(int B, int L, int Hkv, int qw) {
+  const double wgs = (double)B * Hkv * ((L + 2 * qw - 1) / (2 * qw));
+  return std::ceil(wgs / 256.0) * qw;
+}
+
 template <typename T, int HD>
-static hipError_t launch_attn_t(const void *qkvg, void *og, int B, int L, int H, int Hkv,
+static hipError_t launch_attn_t(const void *qkvg, void *vt, void *og, int B, int L, int H, int Hkv,
                                 hipStream_t s) {
   const int group = H / Hkv;
-  dim3 grid((L + ATT_BQ - 1) / ATT_BQ, Hkv, B);
-  const int nthr = group * (ATT_BQ / ATT_QW) * 64;
+  if (group != 1 && group != 2 && group != 4) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((vtrans_kernel<T, HD>), dim3(att_lpad(L) / ATT_BK, Hkv, B), dim3(256), 0, s,
+                     (const T *)qkvg, (T *)vt, L, H, Hkv);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   // log2(e) / sqrt(d): softmax in base 2 with the score scale in one FMA
   const float sc = 1.4426950408889634f / sqrtf((float)HD);
-  if (nthr >= 256)
-    hipLaunchKernelGGL((attn_kernel<T, HD, 256>), grid, dim3(nthr), 0, s, (const T *)qkvg, (T *)og, L, H, Hkv, sc);
+  const auto *q = (const T *)qkvg;
+  const auto *v = (const T *)vt;
+  if (sizeof(T) == 2 && attn_rounds(B, L, Hkv, 48) < attn_rounds(B, L, Hkv, 32))
+    launch_attn_q<T, HD, 48>(q, v, (T *)og, B, L, H, Hkv, sc, s);
   else
-    hipLaunchKernelGGL((attn_kernel<T, HD, 128>), grid, dim3(nthr), 0, s, (const T *)qkvg, (T *)og, L, H, Hkv, sc);
+    launch_attn_q<T, HD, 32>(q, v, (T *)og, B, L, H, Hkv, sc, s);
   return hipGetLastError();
 }
 
-hipError_t launch_attention(bool f32, int head_dim, const void *qkvg, void *og, int B, int L, int H,
-                            int Hkv, hipStream_t s) {
+hipError_t launch_attention(bool f32, int head_dim, const void *qkvg, void *vt, void *og, int B,
+                            int L, int H, int Hkv, hipStream_t s) {
   if (f32) {
-    if (head_dim == 64) return launch_attn_t<float, 64>(qkvg, og, B, L, H, Hkv, s);
-    if (head_dim == 128) return launch_attn_t<float, 128>(qkvg, og, B, L, H, Hkv, s);
+    if (head_dim == 64) return launch_attn_t<float, 64>(qkvg, vt, og, B, L, H, Hkv, s);
+    if (head_dim == 128) return launch_attn_t<float, 128>(qkvg, vt, og, B, L, H, Hkv, s);
   } else {
-    if (head_dim == 128) return launch_attn_t<bf16, 128>(qkvg, og, B, L, H, Hkv, s);
+    if (head_dim == 128) return launch_attn_t<bf16, 128>(qkvg, vt, og, B, L, H, Hkv, s);
   }
   return hipErrorInvalidValue;
 }

@@ -233,7 +233,7 @@ template <int EPI>
 static hipError_t gemm_dispatch(bool f32, int variant, const void *a, const void *w, void *c,
                                 int M, int N, int K, hipStream_t s) {
   if (f32) return launch_gemm_t<float, 256, 256, 128, 2, 2, 4, EPI>(a, w, c, M, N, K, s);
-  if (variant < 0) variant = 2;  // best measured on the 1024 px shapes (all four projections)
+  if (variant < 0) variant = (EPI == EPI_SWIGLU) ? 2 : 7;  // best measured on the 1024 px shapes
   switch (variant) {
     case 0: return launch_gemm_t<bf16, 256, 256, 64, 4, 2, 2, EPI>(a, w, c, M, N, K, s);
     case 1: return launch_gemm_t<bf16, 256, 256, 64, 4, 2, 4, EPI>(a, w, c, M, N, K, s);
@@ -242,6 +242,7 @@ static hipError_t gemm_dispatch(bool f32, int variant, const void *a, const void
     case 4: return launch_gemm_t<bf16, 256, 128, 128, 3, 2, 2, EPI>(a, w, c, M, N, K, s);
     case 5: return launch_gemm_t<bf16, 128, 128, 128, 4, 2, 2, EPI>(a, w, c, M, N, K, s);
     case 6: return launch_gemm_t<bf16, 256, 256, 64, 5, 2, 2, EPI>(a, w, c, M, N, K, s);
+    case 7: return launch_gemm_t<bf16, 192, 256, 128, 2, 2, 4, EPI>(a, w, c, M, N, K, s);
     default: return hipErrorInvalidValue;
   }
 }

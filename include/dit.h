@@ -108,8 +108,8 @@ typedef enum {
 
 /* Workspace bytes needed by dit_block_fwd for this configuration
  * (0 if cfg is invalid).  Holds the normalised activations, the Q|K|V|G
- * projection (later reused for the SwiGLU hidden U), the gated attention
- * output, the branch outputs and x1 (fp32). */
+ * projection (later reused for the SwiGLU hidden U), the transposed V, the
+ * gated attention output, the branch outputs and x1 (fp32). */
 size_t dit_workspace_size(const dit_config *cfg /* host */);
 
 /* Workspace bytes needed by dit_stack_fwd: the block workspace plus one
@@ -181,7 +181,7 @@ dit_status dit_gemm_swiglu(dit_dtype dtype, int32_t m, int32_t f, int32_t k, con
                            const void *w13, void *u, void *stream);
 
 /* The same products with an explicit tile configuration, for tuning and
- * tests: variant 0..6 selects one of the compiled (BM x BN tile, stage
+ * tests: variant 0..7 selects one of the compiled (BM x BN tile, stage
  * depth, wave grid) configurations; every variant computes the same
  * result up to fp32 summation order.  swiglu = 0: C[M, N] = A W^T with
  * W [N, K]; swiglu = 1: as dit_gemm_swiglu with F = n and W = W13 [2n, K].
@@ -193,9 +193,11 @@ dit_status dit_gemm_variant(dit_dtype dtype, int32_t variant, int32_t swiglu, in
  * (column blocks Q | K | V | G, as produced by the QKVG projection):
  *   og[b, l, h*d:(h+1)*d] = softmax_keys(Q_h K_j^T / sqrt(d)) V_j * sigmoid(G_h)
  * within each sample, all keys, no mask (page "Krea 2 技术报告",
- * 架构 › Transformer块).  og [T, H*d] in cfg->dtype. */
-dit_status dit_attention(const dit_config *cfg /* host */, const void *qkvg, void *og,
-                         void *stream);
+ * 架构 › Transformer块).  og [T, H*d] in cfg->dtype.  ws receives the
+ * transposed V of every KV head (B*Hkv*d*ceil(L/64)*64 elements;
+ * dit_workspace_size(cfg) is always enough) and must not overlap qkvg or og. */
+dit_status dit_attention(const dit_config *cfg /* host */, const void *qkvg, void *og, void *ws,
+                         size_t ws_bytes, void *stream);
 
 /* out = x + gate * y over rows of [T, D], gate = mod[b][3*which+2] +
  * bias[3*which+2] (page "Krea 2 技术报告", 架构 › 残差设计).
