@@ -75,7 +75,7 @@ dit_status check_cfg(const dit_config *c) {
   if (c->dtype == DIT_BF16 ? c->head_dim != 128 : (c->head_dim != 64 && c->head_dim != 128))
     return DIT_ERR_UNSUPPORTED;
   if (c->hidden % 8 || c->ffn % 8) return DIT_ERR_UNSUPPORTED;
-  if (c->hidden > 8 * 64 * 32) return DIT_ERR_UNSUPPORTED;  // modnorm keeps a row in registers
+  if (c->hidden > 8192) return DIT_ERR_UNSUPPORTED;  // norms keep a row in registers, 3 vectors in LDS
   const uint64_t es = esize(c->dtype);
   const uint64_t nqkvg = (uint64_t)(2 * c->n_heads + 2 * c->n_kv_heads) * c->head_dim;
   // byte ranges addressed through one buffer descriptor must stay below 2^31
@@ -140,10 +140,11 @@ dit_status check_weights(const dit_block_weights *w) {
   } while (0)
 
 // One block, on the carved workspace.  x_in has dtype xin_f32 ? f32 : dtype;
-// x_out has xout_f32 ? f32 : dtype; x1 is stored in x1buf with x1_f32.
+// x_out has xout_f32 ? f32 : dtype; x1 (fp32) is stored in x1buf.
 dit_status run_block(const dit_config *c, const dit_block_weights *w, const void *x_in,
                      bool xin_f32, void *x_out, bool xout_f32, const float *mod,
-                     const BlockWs &ws, void *x1buf, bool x1_f32, hipStream_t s) {
+                     const BlockWs &ws, void *x1buf, hipStream_t s) {
+  const bool x1_f32 = true;
   const Dims d = dims(c);
   const bool f32 = c->dtype == DIT_F32;
   const int T = (int)d.T, D = (int)d.D, L = c->seq_len;
@@ -159,12 +160,20 @@ dit_status run_block(const dit_config *c, const dit_block_weights *w, const void
   DIT_TRY(timed(DIT_K_GEMM_O, s, [&] {
     return launch_gemm(f32, ws.og, w->w_o, ws.br, T, D, (int)d.hd, s);
   }));
-  DIT_TRY(timed(DIT_K_RESID, s, [&] {
-    return launch_resid(xin_f32, f32, x1_f32, x_in, ws.br, x1buf, mod, w->mod_bias, T, L, D, 0, s);
-  }));
-  DIT_TRY(timed(DIT_K_MODNORM, s, [&] {
-    return launch_modnorm(x1_f32, f32, x1buf, ws.h, mod, w->mod_bias, w->norm2_w, T, L, D, c->eps, 1, s);
-  }));
+  if (3 * (size_t)D * sizeof(float) <= 64 * 1024) {
+    // x1 = x + gate1 * A (fp32) fused with h2 = modnorm(x1; norm 2)
+    DIT_TRY(timed(DIT_K_RESID, s, [&] {
+      return launch_resid_modnorm(xin_f32, f32, x_in, ws.br, (float *)x1buf, ws.h, mod, w->mod_bias,
+                                  w->norm2_w, T, L, D, c->eps, s);
+    }));
+  } else {  // the three staged vectors would not fit the default LDS window
+    DIT_TRY(timed(DIT_K_RESID, s, [&] {
+      return launch_resid(xin_f32, f32, x1_f32, x_in, ws.br, x1buf, mod, w->mod_bias, T, L, D, 0, s);
+    }));
+    DIT_TRY(timed(DIT_K_MODNORM, s, [&] {
+      return launch_modnorm(x1_f32, f32, x1buf, ws.h, mod, w->mod_bias, w->norm2_w, T, L, D, c->eps, 1, s);
+    }));
+  }
   DIT_TRY(timed(DIT_K_GEMM_W13, s, [&] {
     return launch_gemm_swiglu(f32, ws.h, w->w_13, ws.qkvg, T, (int)d.F, D, s);
   }));
@@ -226,7 +235,7 @@ dit_status dit_block_fwd(const dit_config *cfg, const dit_block_weights *w, cons
     return DIT_ERR_SHAPE;
   const BlockWs bw = carve(cfg, ws);
   const bool f32 = cfg->dtype == DIT_F32;
-  return run_block(cfg, w, x_in, f32, x_out, f32, mod, bw, bw.x1, true, (hipStream_t)stream);
+  return run_block(cfg, w, x_in, f32, x_out, f32, mod, bw, bw.x1, (hipStream_t)stream);
 }
 
 dit_status dit_stack_fwd(const dit_config *cfg, int32_t n_blocks, const dit_block_weights *blocks,
@@ -256,7 +265,7 @@ dit_status dit_stack_fwd(const dit_config *cfg, int32_t n_blocks, const dit_bloc
   for (int i = 0; i < n_blocks; ++i) {
     const bool first = i == 0, last = i == n_blocks - 1;
     st = run_block(cfg, &blocks[i], first ? x_in : xa, first ? f32 : true, last ? x_out : xa,
-                   last ? f32 : true, mod, bw, bw.x1, true, s);
+                   last ? f32 : true, mod, bw, bw.x1, s);
     if (st != DIT_OK) return st;
   }
   return DIT_OK;

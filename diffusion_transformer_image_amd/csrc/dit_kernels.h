@@ -11,6 +11,10 @@ hipError_t launch_modnorm(bool x_f32, bool h_f32, const void *x, void *h, const 
 hipError_t launch_resid(bool x_f32, bool y_f32, bool out_f32, const void *x, const void *y,
                         void *out, const float *mod, const float *bias, int rows, int seq_len,
                         int D, int which, hipStream_t s);
+// x1 = x + gate1 * y (fp32), h = modnorm of x1 with the second norm
+hipError_t launch_resid_modnorm(bool x_f32, bool f32, const void *x, const void *y, float *x1, void *h,
+                                const float *mod, const float *bias, const float *gain2, int rows,
+                                int seq_len, int D, float eps, hipStream_t s);
 hipError_t launch_tmod(const float *t, const float *w1, const float *w2, float *mod, float *zs,
                        int B, int D, int tdim, hipStream_t s);
 // variant < 0 picks the default tile configuration for the shape

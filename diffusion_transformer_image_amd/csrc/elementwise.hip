@@ -41,78 +41,115 @@ template <> struct Vec8<float> {
 };
 __device__ __forceinline__ void load8f(const float *p, float (&v)[8]) { Vec8<float>::load(p, v); }
 
+// ----------------------------------------------------------------- layout
+// Every elementwise kernel runs one workgroup per (sample b, 16 token rows):
+// the per-sample modulation vectors it needs (combined with the block bias
+// and the norm gain) are computed once into LDS, then each of the 4 waves
+// streams 4 rows, one row per wave at a time, 8 elements per lane-chunk.
+constexpr int EW_ROWS = 16;  // rows per workgroup
+constexpr int EW_WAVES = 4;
+
+__device__ __forceinline__ void lds8(const float *p, float (&v)[8]) {
+  const f32x4 a = *reinterpret_cast<const f32x4 *>(p);
+  const f32x4 b = *reinterpret_cast<const f32x4 *>(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+// A = (1 + gain) * (1 + scale), S = shift of norm `which`; G = gate of
+// residual `which` (all with the per-block bias added to m[b]).
+__device__ __forceinline__ void stage_norm_vectors(float *A, float *S, const float *mod, const float *bias,
+                                                   const float *gain, int b, int D, int which) {
+  const float *msh = mod + ((size_t)b * 6 + 3 * which) * D;
+  const float *bsh = bias + (size_t)(3 * which) * D;
+  for (int i = threadIdx.x * 4; i < D; i += blockDim.x * 4) {
+    const f32x4 sh = *reinterpret_cast<const f32x4 *>(msh + i) + *reinterpret_cast<const f32x4 *>(bsh + i);
+    const f32x4 sc = *reinterpret_cast<const f32x4 *>(msh + D + i) + *reinterpret_cast<const f32x4 *>(bsh + D + i);
+    const f32x4 g = gain ? *reinterpret_cast<const f32x4 *>(gain + i) : f32x4{0.f, 0.f, 0.f, 0.f};
+    *reinterpret_cast<f32x4 *>(A + i) = (1.0f + g) * (1.0f + sc);
+    *reinterpret_cast<f32x4 *>(S + i) = sh;
+  }
+}
+__device__ __forceinline__ void stage_gate_vector(float *G, const float *mod, const float *bias, int b, int D,
+                                                  int which) {
+  const float *mg = mod + ((size_t)b * 6 + 3 * which + 2) * D;
+  const float *bg = bias + (size_t)(3 * which + 2) * D;
+  for (int i = threadIdx.x * 4; i < D; i += blockDim.x * 4)
+    *reinterpret_cast<f32x4 *>(G + i) = *reinterpret_cast<const f32x4 *>(mg + i) + *reinterpret_cast<const f32x4 *>(bg + i);
+}
+
 // ----------------------------------------------------------------- modnorm
-// One wave per token row; the row stays in registers between the
-// sum-of-squares pass and the normalise pass (NCH chunks of 8 per lane).
-// h = x * rsqrt(mean(x^2) + eps) * (1 + gain) * (1 + scale) + shift.
+// h = x * rsqrt(mean(x^2) + eps) * A + S; the row stays in registers
+// (NCH chunks of 8 per lane) between the sum of squares and the output.
 template <typename Tx, typename Th, int NCH>
 __global__ __launch_bounds__(256) void modnorm_kernel(const Tx *__restrict__ x, Th *__restrict__ h,
                                                       const float *__restrict__ mod,
                                                       const float *__restrict__ bias,
-                                                      const float *__restrict__ gain, int rows,
-                                                      int seq_len, int D, float eps, int which) {
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
+                                                      const float *__restrict__ gain, int seq_len, int D,
+                                                      float eps, int which) {
+  extern __shared__ float ew_lds[];
+  float *A = ew_lds, *S = ew_lds + D;
+  const int b = blockIdx.y;
+  stage_norm_vectors(A, S, mod, bias, gain, b, D, which);
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nch = D >> 3;
-  const Tx *xr = x + (size_t)row * D;
-  float v[NCH][8];
-  float ss = 0.f;
+  for (int rr = 0; rr < EW_ROWS / EW_WAVES; ++rr) {
+    const int l = blockIdx.x * EW_ROWS + rr * EW_WAVES + wave;
+    if (l >= seq_len) break;
+    const size_t row = (size_t)b * seq_len + l;
+    const Tx *xr = x + row * D;
+    float v[NCH][8];
+    float ss = 0.f;
 #pragma unroll
-  for (int c = 0; c < NCH; ++c) {
-    const int ch = lane + 64 * c;
-    if (ch < nch) {
-      Vec8<Tx>::load(xr + ch * 8, v[c]);
+    for (int c = 0; c < NCH; ++c) {
+      const int ch = lane + 64 * c;
+      if (ch < nch) {
+        Vec8<Tx>::load(xr + ch * 8, v[c]);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) ss += v[c][i] * v[c][i];
-    }
-  }
-  ss = wave_sum(ss);
-  const float inv = rsqrtf(ss / (float)D + eps);
-  const int b = row / seq_len;
-  const float *msh = mod + ((size_t)b * 6 + 3 * which) * D;
-  const float *bsh = bias + (size_t)(3 * which) * D;
-  Th *hr = h + (size_t)row * D;
-#pragma unroll
-  for (int c = 0; c < NCH; ++c) {
-    const int ch = lane + 64 * c;
-    if (ch < nch) {
-      float sh[8], sc[8], bs0[8], bs1[8], g[8], o[8];
-      load8f(msh + ch * 8, sh);
-      load8f(msh + D + ch * 8, sc);
-      load8f(bsh + ch * 8, bs0);
-      load8f(bsh + D + ch * 8, bs1);
-      if (gain) {
-        load8f(gain + ch * 8, g);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) g[i] = 0.f;
+        for (int i = 0; i < 8; ++i) ss += v[c][i] * v[c][i];
       }
+    }
+    const float inv = rsqrtf(wave_sum(ss) / (float)D + eps);
+    Th *hr = h + row * D;
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        o[i] = v[c][i] * inv * (1.f + g[i]) * (1.f + (sc[i] + bs1[i])) + (sh[i] + bs0[i]);
-      Vec8<Th>::store(hr + ch * 8, o);
+    for (int c = 0; c < NCH; ++c) {
+      const int ch = lane + 64 * c;
+      if (ch < nch) {
+        float a[8], sh[8], o[8];
+        lds8(A + ch * 8, a);
+        lds8(S + ch * 8, sh);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[i] = v[c][i] * inv * a[i] + sh[i];
+        Vec8<Th>::store(hr + ch * 8, o);
+      }
     }
   }
+}
+
+static int nch_bucket(int D) {
+  const int per = (D / 8 + 63) / 64;
+  return per <= 1 ? 1 : per <= 2 ? 2 : per <= 4 ? 4 : per <= 8 ? 8 : per <= 16 ? 16 : -1;
 }
 
 template <typename Tx, typename Th>
 static hipError_t launch_modnorm_t(const void *x, void *h, const float *mod, const float *bias,
                                    const float *gain, int rows, int seq_len, int D, float eps,
                                    int which, hipStream_t s) {
-  const int nch = D / 8;
-  const int per = (nch + 63) / 64;
-  dim3 grid((rows + 3) / 4), block(256);
+  const int B = rows / seq_len;
+  dim3 grid((seq_len + EW_ROWS - 1) / EW_ROWS, B), block(256);
+  const size_t lds = 2 * (size_t)D * sizeof(float);
 #define DIT_MN(N)                                                                                  \
-  hipLaunchKernelGGL((modnorm_kernel<Tx, Th, N>), grid, block, 0, s, (const Tx *)x, (Th *)h, mod,  \
-                     bias, gain, rows, seq_len, D, eps, which)
-  if (per <= 1) DIT_MN(1);
-  else if (per <= 2) DIT_MN(2);
-  else if (per <= 4) DIT_MN(4);
-  else if (per <= 8) DIT_MN(8);
-  else if (per <= 16) DIT_MN(16);
-  else if (per <= 32) DIT_MN(32);
-  else return hipErrorInvalidValue;
+  hipLaunchKernelGGL((modnorm_kernel<Tx, Th, N>), grid, block, lds, s, (const Tx *)x, (Th *)h, mod, \
+                     bias, gain, seq_len, D, eps, which)
+  switch (nch_bucket(D)) {
+    case 1: DIT_MN(1); break;
+    case 2: DIT_MN(2); break;
+    case 4: DIT_MN(4); break;
+    case 8: DIT_MN(8); break;
+    case 16: DIT_MN(16); break;
+    default: return hipErrorInvalidValue;
+  }
 #undef DIT_MN
   return hipGetLastError();
 }
@@ -127,28 +164,31 @@ hipError_t launch_modnorm(bool x_f32, bool h_f32, const void *x, void *h, const 
 }
 
 // ----------------------------------------------------------------- residual
-// out = x + gate * y, one 8-element chunk per thread (grid-stride).
+// out = x + G * y, G the gate of residual `which`.
 template <typename Tx, typename Ty, typename To>
 __global__ __launch_bounds__(256) void resid_kernel(const Tx *__restrict__ x, const Ty *__restrict__ y,
-                                                    To *__restrict__ out,
-                                                    const float *__restrict__ mod,
-                                                    const float *__restrict__ bias, int rows,
-                                                    int seq_len, int D, int which) {
-  const int nch_row = D >> 3;
-  const size_t total = (size_t)rows * nch_row;
-  for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
-       idx += (size_t)gridDim.x * blockDim.x) {
-    const int row = (int)(idx / nch_row);
-    const int col = (int)(idx - (size_t)row * nch_row) * 8;
-    const int b = row / seq_len;
-    float xv[8], yv[8], gm[8], gb[8], o[8];
-    Vec8<Tx>::load(x + (size_t)row * D + col, xv);
-    Vec8<Ty>::load(y + (size_t)row * D + col, yv);
-    load8f(mod + ((size_t)b * 6 + 3 * which + 2) * D + col, gm);
-    load8f(bias + (size_t)(3 * which + 2) * D + col, gb);
+                                                    To *__restrict__ out, const float *__restrict__ mod,
+                                                    const float *__restrict__ bias, int seq_len, int D,
+                                                    int which) {
+  extern __shared__ float ew_lds[];
+  float *G = ew_lds;
+  const int b = blockIdx.y;
+  stage_gate_vector(G, mod, bias, b, D, which);
+  __syncthreads();
+  const int nch = D >> 3;
+  const int l0 = blockIdx.x * EW_ROWS;
+  const int nrows = min(EW_ROWS, seq_len - l0);
+  // flat walk over (row, chunk) of this workgroup's rows: fully coalesced
+  for (int idx = threadIdx.x; idx < nrows * nch; idx += blockDim.x) {
+    const int r = idx / nch, ch = idx - r * nch;
+    const size_t off = ((size_t)b * seq_len + l0 + r) * D + ch * 8;
+    float xv[8], yv[8], gv[8], o[8];
+    Vec8<Tx>::load(x + off, xv);
+    Vec8<Ty>::load(y + off, yv);
+    lds8(G + ch * 8, gv);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] = xv[i] + (gm[i] + gb[i]) * yv[i];
-    Vec8<To>::store(out + (size_t)row * D + col, o);
+    for (int i = 0; i < 8; ++i) o[i] = xv[i] + gv[i] * yv[i];
+    Vec8<To>::store(out + off, o);
   }
 }
 
@@ -156,11 +196,10 @@ template <typename Tx, typename Ty, typename To>
 static hipError_t launch_resid_t(const void *x, const void *y, void *out, const float *mod,
                                  const float *bias, int rows, int seq_len, int D, int which,
                                  hipStream_t s) {
-  const size_t total = (size_t)rows * (D / 8);
-  size_t blocks = (total + 255) / 256;
-  if (blocks > 256 * 64) blocks = 256 * 64;
-  hipLaunchKernelGGL((resid_kernel<Tx, Ty, To>), dim3((unsigned)blocks), dim3(256), 0, s,
-                     (const Tx *)x, (const Ty *)y, (To *)out, mod, bias, rows, seq_len, D, which);
+  const int B = rows / seq_len;
+  dim3 grid((seq_len + EW_ROWS - 1) / EW_ROWS, B);
+  hipLaunchKernelGGL((resid_kernel<Tx, Ty, To>), grid, dim3(256), (size_t)D * sizeof(float), s,
+                     (const Tx *)x, (const Ty *)y, (To *)out, mod, bias, seq_len, D, which);
   return hipGetLastError();
 }
 
@@ -176,6 +215,94 @@ hipError_t launch_resid(bool x_f32, bool y_f32, bool out_f32, const void *x, con
     else { if (out_f32) DIT_R(bf16, bf16, float); else DIT_R(bf16, bf16, bf16); }
   }
 #undef DIT_R
+}
+
+// ----------------------------------------------------------------- residual + norm
+// The first gated residual fused with the second modulated norm:
+//   x1 = x + gate1 * y   (stored fp32),   h2 = modnorm(x1; norm 2).
+// Saves writing x1 and reading it back between two passes.
+template <typename Tx, typename Ty, typename Th, int NCH>
+__global__ __launch_bounds__(256) void resid_modnorm_kernel(const Tx *__restrict__ x, const Ty *__restrict__ y,
+                                                            float *__restrict__ x1, Th *__restrict__ h,
+                                                            const float *__restrict__ mod,
+                                                            const float *__restrict__ bias,
+                                                            const float *__restrict__ gain2, int seq_len,
+                                                            int D, float eps) {
+  extern __shared__ float ew_lds[];
+  float *G = ew_lds, *A = ew_lds + D, *S = ew_lds + 2 * D;
+  const int b = blockIdx.y;
+  stage_gate_vector(G, mod, bias, b, D, 0);
+  stage_norm_vectors(A, S, mod, bias, gain2, b, D, 1);
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nch = D >> 3;
+  for (int rr = 0; rr < EW_ROWS / EW_WAVES; ++rr) {
+    const int l = blockIdx.x * EW_ROWS + rr * EW_WAVES + wave;
+    if (l >= seq_len) break;
+    const size_t row = (size_t)b * seq_len + l;
+    float v[NCH][8];
+    float ss = 0.f;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int ch = lane + 64 * c;
+      if (ch < nch) {
+        float xv[8], yv[8], gv[8];
+        Vec8<Tx>::load(x + row * D + ch * 8, xv);
+        Vec8<Ty>::load(y + row * D + ch * 8, yv);
+        lds8(G + ch * 8, gv);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          v[c][i] = xv[i] + gv[i] * yv[i];
+          ss += v[c][i] * v[c][i];
+        }
+        Vec8<float>::store(x1 + row * D + ch * 8, v[c]);
+      }
+    }
+    const float inv = rsqrtf(wave_sum(ss) / (float)D + eps);
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int ch = lane + 64 * c;
+      if (ch < nch) {
+        float a[8], sh[8], o[8];
+        lds8(A + ch * 8, a);
+        lds8(S + ch * 8, sh);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[i] = v[c][i] * inv * a[i] + sh[i];
+        Vec8<Th>::store(h + row * D + ch * 8, o);
+      }
+    }
+  }
+}
+
+template <typename Tx, typename Ty, typename Th>
+static hipError_t launch_resid_modnorm_t(const void *x, const void *y, float *x1, void *h, const float *mod,
+                                         const float *bias, const float *gain2, int rows, int seq_len,
+                                         int D, float eps, hipStream_t s) {
+  const int B = rows / seq_len;
+  dim3 grid((seq_len + EW_ROWS - 1) / EW_ROWS, B), block(256);
+  const size_t lds = 3 * (size_t)D * sizeof(float);
+#define DIT_RMN(N)                                                                                   \
+  hipLaunchKernelGGL((resid_modnorm_kernel<Tx, Ty, Th, N>), grid, block, lds, s, (const Tx *)x,     \
+                     (const Ty *)y, x1, (Th *)h, mod, bias, gain2, seq_len, D, eps)
+  switch (nch_bucket(D)) {
+    case 1: DIT_RMN(1); break;
+    case 2: DIT_RMN(2); break;
+    case 4: DIT_RMN(4); break;
+    case 8: DIT_RMN(8); break;
+    case 16: DIT_RMN(16); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef DIT_RMN
+  return hipGetLastError();
+}
+
+hipError_t launch_resid_modnorm(bool x_f32, bool f32, const void *x, const void *y, float *x1, void *h,
+                                const float *mod, const float *bias, const float *gain2, int rows,
+                                int seq_len, int D, float eps, hipStream_t s) {
+  // y and h have the compute dtype (f32 ? fp32 : bf16); x is fp32 or that dtype
+  if (f32) return launch_resid_modnorm_t<float, float, float>(x, y, x1, h, mod, bias, gain2, rows, seq_len, D, eps, s);
+  if (x_f32) return launch_resid_modnorm_t<float, bf16, bf16>(x, y, x1, h, mod, bias, gain2, rows, seq_len, D, eps, s);
+  return launch_resid_modnorm_t<bf16, bf16, bf16>(x, y, x1, h, mod, bias, gain2, rows, seq_len, D, eps, s);
 }
 
 // ----------------------------------------------------------------- timestep MLP
