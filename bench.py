@@ -217,7 +217,7 @@ def main() -> int:
     dom_avg = dom_ms / max(dom_n, 1)
     dom_flops = fpt[dom] * cfg.tokens
     achieved = dom_flops / (dom_avg * 1e-3) / 1e12
-    roofline = {"bound": "mfma", "kernel": "gemm_kernel<bf16,256,256,2,4,SWIGLU> (h2 * W13^T + SwiGLU)",
+    roofline = {"bound": "mfma", "kernel": "gemm_kernel (h2 * W13^T with the SwiGLU epilogue)",
                 "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / PEAK_BF16_TFLOPS, "traffic": load_traffic("gemm.hip"),
                 "flops_per_launch": dom_flops, "avg_launch_ms": dom_avg, "launches": dom_n}

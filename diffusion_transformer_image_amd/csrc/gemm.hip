@@ -19,6 +19,8 @@
 //  * workgroup ids are remapped so that each XCD (dispatch is round-robin
 //    over the 8 XCDs) walks a contiguous band of tiles, grouped GM row
 //    tiles at a time, so tiles sharing A rows or W rows meet in one L2.
+#include <cmath>
+
 #include "dit_common.h"
 #include "dit_kernels.h"
 
@@ -38,7 +40,14 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <typename T, int BM, int BN, int BKB, int STAGES, int WM, int WN, int EPI>
+// PIPE (two-stage ring only): software-pipelined main loop.  The fragments
+// of k-step ks+1 are read from LDS while the MFMAs of k-step ks run, and the
+// stage barrier sits between the last two MFMA bursts of a stage: the wave
+// first reads its last fragments of stage kt, issues the MFMAs of the
+// previous k-step, then waits for stage kt+1 and the barrier, refills the
+// buffer stage kt used and reads the first fragments of stage kt+1 while its
+// last MFMAs of stage kt execute.
+template <typename T, int BM, int BN, int BKB, int STAGES, int WM, int WN, int EPI, bool PIPE = false>
 __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(const T *__restrict__ A,
                                                            const T *__restrict__ W,
                                                            T *__restrict__ C, int M, int N, int K,
@@ -155,6 +164,42 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(const T *__restrict__
   }
 
   const int nk = (K + KSTAGE - 1) / KSTAGE;
+
+  auto load_frags = [&](const char *sb, int ks, u32x4(&af)[RB], u32x4(&bf)[CB]) {
+    const int pc = ((ks * 4 + g) ^ swz) * 16;
+#pragma unroll
+    for (int i = 0; i < RB; ++i) af[i] = *reinterpret_cast<const u32x4 *>(sb + arow[i] + pc);
+#pragma unroll
+    for (int j = 0; j < CB; ++j) bf[j] = *reinterpret_cast<const u32x4 *>(sb + brow[j] + pc);
+  };
+  auto mmas = [&](const u32x4(&af)[RB], const u32x4(&bf)[CB]) {
+#pragma unroll
+    for (int i = 0; i < RB; ++i)
+#pragma unroll
+      for (int j = 0; j < CB; ++j) acc[i][j] = mma16<T>(af[i], bf[j], acc[i][j]);
+  };
+
+  if constexpr (PIPE) {
+    static_assert(STAGES == 2 && KSTEPS == 2, "pipelined loop: two stages of two k-steps");
+    issue_stage(0, 0);
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (nk > 1) issue_stage(1, 1);
+    u32x4 a0[RB], b0[CB], a1[RB], b1[CB];
+    load_frags(smem, 0, a0, b0);
+    for (int kt = 0; kt < nk; ++kt) {
+      const char *sb = smem + (kt & 1) * STAGE_BYTES;
+      load_frags(sb, 1, a1, b1);
+      mmas(a0, b0);
+      if (kt + 1 < nk) {
+        wait_vmcnt<0>();  // this wave's DMA of stage kt+1
+        __syncthreads();  // stage kt+1 visible; every wave holds its stage-kt fragments
+        if (kt + 2 < nk) issue_stage(kt + 2, kt & 1);
+        load_frags(smem + ((kt + 1) & 1) * STAGE_BYTES, 0, a0, b0);
+      }
+      mmas(a1, b1);
+    }
+  } else {
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s)
     if (s < nk) issue_stage(s, s);
@@ -181,49 +226,79 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(const T *__restrict__
         for (int j = 0; j < CB; ++j) acc[i][j] = mma16<T>(af[i], bfr[j], acc[i][j]);
     }
   }
+  }
 
   // ---- epilogue: lane holds rows 4g+e of column r16 of every 16x16 block
-  if (EPI == EPI_SWIGLU) {
-    constexpr int half = CB / 2;
+  constexpr int TNO = (EPI == EPI_SWIGLU) ? TN / 2 : TN;  // output columns per wave
+  const int col0 = (EPI == EPI_SWIGLU) ? n0 + wn * (TN / 2) : n0 + wn * TN;
+  const int row0 = m0 + wm * TM;
+  auto out_val = [&](int i, int j, int e) -> float {
+    if constexpr (EPI == EPI_SWIGLU) return silu(acc[i][j][e]) * acc[i][j + CB / 2][e];
+    else return acc[i][j][e];
+  };
+  if constexpr (sizeof(T) == 2 && (TNO * 2) % 64 == 0 && NW * TM * TNO * 2 <= STAGES * STAGE_BYTES) {
+    // bf16: stage the wave's TM x TNO output tile in LDS (16-byte chunks
+    // XOR-swizzled by row), then write whole 16-byte chunks: each row of the
+    // tile goes out as TNO*2 contiguous bytes instead of 2-byte pieces.
+    constexpr int PITCH = TNO * 2;       // bytes per tile row in LDS
+    constexpr int CPRO = PITCH / 16;     // 16-byte chunks per row (4 or 8)
+    __syncthreads();  // all waves are done reading the operand stages
+    char *tile = smem + wave * (TM * PITCH);
 #pragma unroll
-    for (int j = 0; j < half; ++j) {
-      const int col = n0 + wn * (TN / 2) + j * 16 + r16;
-      if (col >= N) continue;
+    for (int j = 0; j < CB / ((EPI == EPI_SWIGLU) ? 2 : 1); ++j) {
+      const int col = j * 16 + r16;  // column inside the wave tile
 #pragma unroll
       for (int i = 0; i < RB; ++i) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int row = m0 + wm * TM + i * 16 + 4 * g + e;
-          if (row < M) {
-            const float a = acc[i][j][e], b = acc[i][j + half][e];
-            C[(size_t)row * N + col] = from_f32<T>(silu(a) * b);
-          }
+          const int row = i * 16 + 4 * g + e;
+          const int off = row * PITCH + (((col >> 3) ^ (row & (CPRO - 1))) << 4) + (col & 7) * 2;
+          *reinterpret_cast<bf16 *>(tile + off) = (bf16)out_val(i, j, e);
+        }
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int q = lane; q < TM * CPRO; q += 64) {
+      const int row = q / CPRO, c = q % CPRO;
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(tile + row * PITCH + ((c ^ (row & (CPRO - 1))) << 4));
+      const int gr = row0 + row, gc = col0 + c * 8;
+      if (gr < M) {
+        T *dst = C + (size_t)gr * N + gc;
+        if (gc + 8 <= N && (N & 7) == 0) {
+          *reinterpret_cast<u32x4 *>(dst) = v;
+        } else {
+          const bf16x8 vb = __builtin_bit_cast(bf16x8, v);
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (gc + e < N) dst[e] = vb[e];
         }
       }
     }
   } else {
 #pragma unroll
-    for (int j = 0; j < CB; ++j) {
-      const int col = n0 + wn * TN + j * 16 + r16;
+    for (int j = 0; j < CB / ((EPI == EPI_SWIGLU) ? 2 : 1); ++j) {
+      const int col = col0 + j * 16 + r16;
       if (col >= N) continue;
 #pragma unroll
       for (int i = 0; i < RB; ++i) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int row = m0 + wm * TM + i * 16 + 4 * g + e;
-          if (row < M) C[(size_t)row * N + col] = from_f32<T>(acc[i][j][e]);
+          const int row = row0 + i * 16 + 4 * g + e;
+          if (row < M) C[(size_t)row * N + col] = from_f32<T>(out_val(i, j, e));
         }
       }
     }
   }
 }
 
-template <typename T, int BM, int BN, int BKB, int STAGES, int WM, int WN, int EPI>
+template <typename T, int BM, int BN, int BKB, int STAGES, int WM, int WN, int EPI, bool PIPE = false>
 static hipError_t launch_gemm_t(const void *a, const void *w, void *c, int M, int N, int K,
                                 hipStream_t s) {
   const int mt = (M + BM - 1) / BM;
   const int nt = (EPI == EPI_SWIGLU) ? (N + BN / 2 - 1) / (BN / 2) : (N + BN - 1) / BN;
-  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, BKB, STAGES, WM, WN, EPI>), dim3(mt * nt),
+  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, BKB, STAGES, WM, WN, EPI, PIPE>), dim3(mt * nt),
                      dim3(WM * WN * 64), 0, s, (const T *)a, (const T *)w, (T *)c, M, N, K, mt, nt);
   return hipGetLastError();
 }
@@ -233,7 +308,17 @@ template <int EPI>
 static hipError_t gemm_dispatch(bool f32, int variant, const void *a, const void *w, void *c,
                                 int M, int N, int K, hipStream_t s) {
   if (f32) return launch_gemm_t<float, 256, 256, 128, 2, 2, 4, EPI>(a, w, c, M, N, K, s);
-  if (variant < 0) variant = (EPI == EPI_SWIGLU) ? 2 : 7;  // best measured on the 1024 px shapes
+  if (variant < 0) {
+    // software-pipelined 8-wave tiles; 192 x 256 instead of 256 x 256 when
+    // its tile count fills the 256 CUs in noticeably fuller rounds (e.g.
+    // N = 4096 at 9216 rows: 768 tiles = 3 full rounds vs 576 = 2.25)
+    const int ncols = (EPI == EPI_SWIGLU) ? 128 : 256;
+    auto fill = [&](int bm) {
+      const double tiles = (double)((M + bm - 1) / bm) * ((N + ncols - 1) / ncols);
+      return tiles / (std::ceil(tiles / 256.0) * 256.0);
+    };
+    variant = (fill(192) > fill(256) + 0.05) ? 9 : 8;
+  }
   switch (variant) {
     case 0: return launch_gemm_t<bf16, 256, 256, 64, 4, 2, 2, EPI>(a, w, c, M, N, K, s);
     case 1: return launch_gemm_t<bf16, 256, 256, 64, 4, 2, 4, EPI>(a, w, c, M, N, K, s);
@@ -243,6 +328,8 @@ static hipError_t gemm_dispatch(bool f32, int variant, const void *a, const void
     case 5: return launch_gemm_t<bf16, 128, 128, 128, 4, 2, 2, EPI>(a, w, c, M, N, K, s);
     case 6: return launch_gemm_t<bf16, 256, 256, 64, 5, 2, 2, EPI>(a, w, c, M, N, K, s);
     case 7: return launch_gemm_t<bf16, 192, 256, 128, 2, 2, 4, EPI>(a, w, c, M, N, K, s);
+    case 8: return launch_gemm_t<bf16, 256, 256, 128, 2, 2, 4, EPI, true>(a, w, c, M, N, K, s);
+    case 9: return launch_gemm_t<bf16, 192, 256, 128, 2, 2, 4, EPI, true>(a, w, c, M, N, K, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -184,7 +184,7 @@ def test_timestep_mod(dev, name):
     assert_parity(device.to_numpy(M), ref, "f32", "timestep modulation", maxabs=2e-5)
 
 
-@pytest.mark.parametrize("variant", list(range(8)))
+@pytest.mark.parametrize("variant", list(range(10)))
 @pytest.mark.parametrize("swiglu", [False, True])
 def test_gemm_every_tile_variant(dev, variant, swiglu):
     """Every compiled tile configuration on ragged M, N and K."""
