@@ -1,0 +1,120 @@
+"""HBM traffic of the dominant kernel (the SwiGLU up/gate GEMM at 1024 px).
+
+Two steps:
+
+1. ``python bench_traffic.py run`` -- launched under rocprofv3 with one
+   counter per run, e.g.
+
+       rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/fetch -o p -- python3 bench_traffic.py run
+       rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/write -o p -- python3 bench_traffic.py run
+
+   It runs, in this order, a plain elementwise copy with conversion (128 Mi
+   float32 read = 512 MiB, 128 Mi bf16 written = 256 MiB, ordinary vector
+   loads and stores) and the W13 GEMM with the SwiGLU epilogue
+   on the 1024 px shapes (h2 [9216, 4096], W13 [22016, 4096], U [9216,
+   11008], bf16), a few times each.
+
+2. ``python bench_traffic.py summarize OUT/fetch OUT/write`` -- reads the
+   two counter CSVs, scales each counter by what it reads for the copy
+   (FETCH_SIZE and WRITE_SIZE are in KiB; the copy moves a known byte
+   count), and writes profiles/traffic_gemm_w13_1024px.json (+ .md) with
+   the per-launch HBM bytes and the sha256 of gemm.hip, so bench.py
+   reports the figure only while the kernel source is unchanged.
+"""
+from __future__ import annotations
+
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+COPY_N = 128 << 20  # elements of the calibration copy
+COPY_READ, COPY_WRITE = 4 * COPY_N, 2 * COPY_N
+T, D, F = 9216, 4096, 11008
+
+
+def run() -> None:
+    import torch
+
+    import diffusion_transformer_image_amd as dit
+    torch.cuda.set_device(0)
+    src = torch.empty(COPY_N, dtype=torch.float32, device="cuda")
+    dst = torch.empty(COPY_N, dtype=torch.bfloat16, device="cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(3)
+    a = (torch.randn(T, D, generator=g, device="cuda")).to(torch.bfloat16)
+    w = (torch.randn(2 * F, D, generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+    u = torch.empty(T, F, dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dit.gemm_swiglu(a, w, u)
+    torch.cuda.synchronize()
+    print("done", flush=True)
+
+
+def _counter(d: str, name: str):
+    f = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not f:
+        raise SystemExit(f"no counter CSV under {d}")
+    copy, gemm = [], []
+    for r in csv.DictReader(open(f[0])):
+        if r["Counter_Name"] != name:
+            continue
+        v = float(r["Counter_Value"]) * 1024.0  # KiB -> bytes
+        k = r["Kernel_Name"]
+        if "gemm_kernel" in k:
+            gemm.append(v)
+        elif "copy" in k.lower() and "distribution" not in k:
+            copy.append(v)
+    if not copy or not gemm:
+        raise SystemExit(f"{name}: copy={len(copy)} gemm={len(gemm)} dispatches found")
+    return sum(copy) / len(copy), sum(gemm) / len(gemm), f[0]
+
+
+def summarize(fetch_dir: str, write_dir: str) -> None:
+    cf, gf, _ = _counter(fetch_dir, "FETCH_SIZE")
+    cw, gw, _ = _counter(write_dir, "WRITE_SIZE")
+    kf, kw = cf / COPY_READ, cw / COPY_WRITE  # counter bytes per real byte
+    fetch, write = gf / kf, gw / kw
+    algorithmic = 2 * (T * D + 2 * F * D + T * F)
+    sha = hashlib.sha256(open(os.path.join(ROOT, "diffusion_transformer_image_amd", "csrc", "gemm.hip"),
+                              "rb").read()).hexdigest()[:16]
+    rec = {"kernel": "gemm_kernel (h2 * W13^T with the SwiGLU epilogue), 1024 px shapes",
+           "bytes_per_launch": fetch + write, "fetch_bytes": fetch, "write_bytes": write,
+           "algorithmic_bytes": algorithmic, "ratio_to_algorithmic": (fetch + write) / algorithmic,
+           "copy_calibration": {"read_bytes": COPY_READ, "write_bytes": COPY_WRITE,
+                                "fetch_counter_per_byte": kf, "write_counter_per_byte": kw},
+           "source_sha256_16": sha}
+    out = os.path.join(ROOT, "profiles", "traffic_gemm_w13_1024px")
+    json.dump(rec, open(out + ".json", "w"), indent=1)
+    md = [f"# HBM traffic of the W13 GEMM (SwiGLU epilogue), 1024 px shapes\n\n",
+          "Commands (R = repository root on the GPU box):\n\n```\n",
+          "cd /tmp && export TMPDIR=/tmp\n",
+          "rocprofv3 --pmc FETCH_SIZE --output-format csv -d $R/gpurun_out/traffic/fetch -o p -- python3 $R/bench_traffic.py run\n",
+          "rocprofv3 --pmc WRITE_SIZE --output-format csv -d $R/gpurun_out/traffic/write -o p -- python3 $R/bench_traffic.py run\n",
+          "python3 bench_traffic.py summarize gpurun_out/traffic/fetch gpurun_out/traffic/write\n```\n\n",
+          f"| Quantity | Bytes per launch |\n|---|---|\n",
+          f"| FETCH (calibrated) | {fetch:.4g} |\n| WRITE (calibrated) | {write:.4g} |\n",
+          f"| total | {fetch + write:.4g} |\n| algorithmic (h2 + W13 + U) | {algorithmic:.4g} |\n\n",
+          f"Copy calibration (float32 -> bf16 elementwise copy, {COPY_READ >> 20} MiB read, "
+          f"{COPY_WRITE >> 20} MiB written): FETCH_SIZE reads {kf:.3f} and WRITE_SIZE {kw:.3f} "
+          f"counter-bytes per byte.  gemm.hip sha256 prefix {sha}.\n"]
+    open(out + ".md", "w").write("".join(md))
+    print(json.dumps(rec, indent=1))
+
+
+if __name__ == "__main__":
+    if sys.argv[1:2] == ["run"]:
+        run()
+    elif sys.argv[1:2] == ["summarize"]:
+        summarize(sys.argv[2], sys.argv[3])
+    else:
+        raise SystemExit(__doc__)

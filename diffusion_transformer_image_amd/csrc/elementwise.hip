@@ -394,12 +394,78 @@ __global__ __launch_bounds__(256) void tmod_stage2(const float *__restrict__ zs,
   }
 }
 
+// Stage 2 for few samples (B <= 4): the whole SiLU'd hidden of every sample
+// sits in LDS, so each wave streams 4 rows of W_t2 at a time over the full K
+// with 16 independent 16-byte loads in flight per lane and no barrier; a
+// workgroup covers 64 rows so the staging is amortised.
+constexpr int TM_NB = 4;
+__global__ __launch_bounds__(256) void tmod_stage2_fewb(const float *__restrict__ zs,
+                                                        const float *__restrict__ w2,
+                                                        float *__restrict__ mod, int B, int D) {
+  extern __shared__ float zl[];  // [B][D]
+  for (int i = threadIdx.x * 4; i < B * D; i += blockDim.x * 4)
+    *reinterpret_cast<f32x4 *>(zl + i) = *reinterpret_cast<const f32x4 *>(zs + i);
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int O = 6 * D;
+  // 64 rows per workgroup (4 passes of 4 rows per wave) amortise the staging
+  for (int pass = 0; pass < 4; ++pass) {
+  const int o0 = ((blockIdx.x * 4 + pass) * 4 + wave) * 4;
+  if (o0 >= O) break;
+  float acc[4][TM_NB];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int b = 0; b < TM_NB; ++b) acc[r][b] = 0.f;
+  for (int k0 = 0; k0 < D; k0 += 4 * 256) {
+    f32x4 w[4][4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int k = k0 + u * 256 + lane * 4;
+        w[u][r] = (k < D && o0 + r < O) ? *reinterpret_cast<const f32x4 *>(w2 + (size_t)(o0 + r) * D + k)
+                                         : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int k = k0 + u * 256 + lane * 4;
+      if (k < D) {
+#pragma unroll
+        for (int b = 0; b < TM_NB; ++b) {
+          if (b < B) {
+            const f32x4 z = *reinterpret_cast<const f32x4 *>(zl + b * D + k);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              acc[r][b] += w[u][r].x * z.x + w[u][r].y * z.y + w[u][r].z * z.z + w[u][r].w * z.w;
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int b = 0; b < TM_NB; ++b) {
+    if (b < B) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float sum = wave_sum(acc[r][b]);
+        if (lane == 0 && o0 + r < O) mod[(size_t)b * O + o0 + r] = sum;
+      }
+    }
+  }
+  }
+}
+
 hipError_t launch_tmod(const float *t, const float *w1, const float *w2, float *mod, float *zs,
                        int B, int D, int tdim, hipStream_t s) {
   hipLaunchKernelGGL(tmod_stage1, dim3((D + 15) / 16), dim3(256), 0, s, t, w1, zs, B, D, tdim);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(tmod_stage2, dim3((6 * D + 7) / 8), dim3(256), 0, s, zs, w2, mod, B, D);
+  if (B <= TM_NB && (size_t)B * D * sizeof(float) <= 64 * 1024)
+    hipLaunchKernelGGL(tmod_stage2_fewb, dim3((6 * D + 63) / 64), dim3(256), (size_t)B * D * sizeof(float), s,
+                       zs, w2, mod, B, D);
+  else
+    hipLaunchKernelGGL(tmod_stage2, dim3((6 * D + 7) / 8), dim3(256), 0, s, zs, w2, mod, B, D);
   return hipGetLastError();
 }
 

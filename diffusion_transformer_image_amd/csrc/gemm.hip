@@ -330,6 +330,7 @@ static hipError_t gemm_dispatch(bool f32, int variant, const void *a, const void
     case 7: return launch_gemm_t<bf16, 192, 256, 128, 2, 2, 4, EPI>(a, w, c, M, N, K, s);
     case 8: return launch_gemm_t<bf16, 256, 256, 128, 2, 2, 4, EPI, true>(a, w, c, M, N, K, s);
     case 9: return launch_gemm_t<bf16, 192, 256, 128, 2, 2, 4, EPI, true>(a, w, c, M, N, K, s);
+    case 10: return launch_gemm_t<bf16, 256, 256, 128, 2, 2, 2, EPI, true>(a, w, c, M, N, K, s);
     default: return hipErrorInvalidValue;
   }
 }

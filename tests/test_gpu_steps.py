@@ -170,10 +170,13 @@ def test_gated_residual(dev, name, xd, od, which):
 
 
 # ------------------------------------------------------------------ timestep modulation
-@pytest.mark.parametrize("name", ["c0", "c3", "c1"])
-def test_timestep_mod(dev, name):
+@pytest.mark.parametrize("name,batch", [("c0", None), ("c0", 3), ("c3", None), ("c3", 4), ("c3", 5),
+                                        ("c1", None)])
+def test_timestep_mod(dev, name, batch):
     torch, device, dit = dev
     cfg = datagen.get_config(name)
+    if batch:
+        cfg = cfg.replace(batch=batch)
     t, w1, w2 = datagen.timestep_inputs(cfg)
     c = dit.config_of(cfg)
     M = torch.empty((cfg.batch, 6, cfg.hidden), dtype=torch.float32, device="cuda")
@@ -184,7 +187,7 @@ def test_timestep_mod(dev, name):
     assert_parity(device.to_numpy(M), ref, "f32", "timestep modulation", maxabs=2e-5)
 
 
-@pytest.mark.parametrize("variant", list(range(10)))
+@pytest.mark.parametrize("variant", list(range(11)))
 @pytest.mark.parametrize("swiglu", [False, True])
 def test_gemm_every_tile_variant(dev, variant, swiglu):
     """Every compiled tile configuration on ragged M, N and K."""
