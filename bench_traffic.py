@@ -20,6 +20,10 @@ Two steps:
    count), and writes profiles/traffic_gemm_w13_1024px.json (+ .md) with
    the per-launch HBM bytes and the sha256 of gemm.hip, so bench.py
    reports the figure only while the kernel source is unchanged.
+
+``python bench_traffic.py stats <run_kernel_stats.csv> <out.md> <title> <command>``
+renders a rocprofv3 ``--stats`` kernel summary CSV as the markdown table kept
+under profiles/.
 """
 from __future__ import annotations
 
@@ -111,10 +115,26 @@ def summarize(fetch_dir: str, write_dir: str) -> None:
     print(json.dumps(rec, indent=1))
 
 
+def stats(src: str, dst: str, title: str, command: str) -> None:
+    rows = list(csv.DictReader(open(src)))
+    out = [f"# {title}\n\n", "Command (R = repository root on the GPU box):\n\n```\n", command, "\n```\n\n",
+           "| Kernel | Calls | Total (us) | Average (us) | Min (us) | Max (us) | % |\n"
+           "|---|---|---|---|---|---|---|\n"]
+    for r in rows:
+        name = r["Name"]
+        short = name if len(name) < 90 else name[:87] + "..."
+        us = lambda k: float(r[k]) / 1e3
+        out.append(f"| `{short}` | {r['Calls']} | {us('TotalDurationNs'):.1f} | {us('AverageNs'):.1f} | "
+                   f"{us('MinNs'):.1f} | {us('MaxNs'):.1f} | {float(r['Percentage']):.2f} |\n")
+    open(dst, "w").write("".join(out))
+
+
 if __name__ == "__main__":
     if sys.argv[1:2] == ["run"]:
         run()
     elif sys.argv[1:2] == ["summarize"]:
         summarize(sys.argv[2], sys.argv[3])
+    elif sys.argv[1:2] == ["stats"]:
+        stats(*sys.argv[2:6])
     else:
         raise SystemExit(__doc__)

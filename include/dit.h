@@ -181,7 +181,7 @@ dit_status dit_gemm_swiglu(dit_dtype dtype, int32_t m, int32_t f, int32_t k, con
                            const void *w13, void *u, void *stream);
 
 /* The same products with an explicit tile configuration, for tuning and
- * tests: variant 0..9 selects one of the compiled (BM x BN tile, stage
+ * tests: variant 0..10 selects one of the compiled (BM x BN tile, stage
  * depth, wave grid) configurations; every variant computes the same
  * result up to fp32 summation order.  swiglu = 0: C[M, N] = A W^T with
  * W [N, K]; swiglu = 1: as dit_gemm_swiglu with F = n and W = W13 [2n, K].
