@@ -40,6 +40,15 @@ __device__ __forceinline__ u32x2 load8(rsrc_t r, uint32_t voff) {
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// s_waitcnt lgkmcnt(0) as a real instruction (not inline asm), so the
+// compiler's wait-insertion pass sees it.  Placed before a main loop, it
+// retires the scalar kernel-argument loads the scheduler tends to leave in
+// flight: scalar loads return out of order, and while one is pending every
+// LDS wait in the loop degrades to lgkmcnt(0), which serialises the
+// software-pipelined fragment reads with the MFMAs.
+// Encoding (gfx9): vmcnt = 63 (bits 3:0, 15:14), expcnt = 7, lgkmcnt = 0.
+__device__ __forceinline__ void drain_lgkm() { __builtin_amdgcn_s_waitcnt(0xc07f); }
+
 template <typename T> struct is_bf16 { static constexpr bool value = false; };
 template <> struct is_bf16<bf16> { static constexpr bool value = true; };
 

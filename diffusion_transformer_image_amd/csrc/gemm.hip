@@ -187,18 +187,29 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(const T *__restrict__
     if (nk > 1) issue_stage(1, 1);
     u32x4 a0[RB], b0[CB], a1[RB], b1[CB];
     load_frags(smem, 0, a0, b0);
-    for (int kt = 0; kt < nk; ++kt) {
+    drain_lgkm();
+    // The last stage is peeled so the loop body is straight-line: a branch
+    // inside it would merge a path with the next stage's fragment reads in
+    // flight into the wait before the second MFMA burst.
+    // sched_barrier(0) keeps the instruction scheduler from moving the
+    // fragment reads next to the MFMAs that consume them.
+    for (int kt = 0; kt < nk - 1; ++kt) {
       const char *sb = smem + (kt & 1) * STAGE_BYTES;
       load_frags(sb, 1, a1, b1);
+      __builtin_amdgcn_sched_barrier(0);
       mmas(a0, b0);
-      if (kt + 1 < nk) {
-        wait_vmcnt<0>();  // this wave's DMA of stage kt+1
-        __syncthreads();  // stage kt+1 visible; every wave holds its stage-kt fragments
-        if (kt + 2 < nk) issue_stage(kt + 2, kt & 1);
-        load_frags(smem + ((kt + 1) & 1) * STAGE_BYTES, 0, a0, b0);
-      }
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmcnt<0>();  // this wave's DMA of stage kt+1
+      __syncthreads();  // stage kt+1 visible; every wave holds its stage-kt fragments
+      if (kt + 2 < nk) issue_stage(kt + 2, kt & 1);
+      load_frags(smem + ((kt + 1) & 1) * STAGE_BYTES, 0, a0, b0);
+      __builtin_amdgcn_sched_barrier(0);
       mmas(a1, b1);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    load_frags(smem + ((nk - 1) & 1) * STAGE_BYTES, 1, a1, b1);
+    mmas(a0, b0);
+    mmas(a1, b1);
   } else {
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s)
