@@ -74,7 +74,7 @@ def lib() -> ctypes.CDLL:
             "dit_modnorm": (i32, [cfgp, vp, i32, vp, vp, vp, vp, i32, vp]),
             "dit_gemm": (i32, [i32, i32, i32, i32, vp, vp, vp, vp]),
             "dit_gemm_swiglu": (i32, [i32, i32, i32, i32, vp, vp, vp, vp]),
-            "dit_gemm_variant": (i32, [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp]),
+            "dit_gemm_variant": (i32, [i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp]),
             "dit_attention": (i32, [cfgp, vp, vp, vp, sz, vp]),
             "dit_gated_residual": (i32, [cfgp, vp, i32, vp, vp, vp, i32, vp, i32, vp]),
             "dit_status_str": (ctypes.c_char_p, [i32]),
@@ -190,11 +190,11 @@ def gemm_swiglu(a, w13, u, stream=None) -> None:
                                  _stream(stream)), "dit_gemm_swiglu")
 
 
-def gemm_variant(variant: int, a, w, c, swiglu: bool = False, stream=None) -> None:
+def gemm_variant(variant: int, a, w, c, swiglu: bool = False, group_m: int = 0, stream=None) -> None:
     m, k = a.shape
     n = w.shape[0] // 2 if swiglu else w.shape[0]
-    _check(lib().dit_gemm_variant(_dtype_code(a.dtype), variant, int(swiglu), m, n, k, _ptr(a), _ptr(w),
-                                  _ptr(c), _stream(stream)), "dit_gemm_variant")
+    _check(lib().dit_gemm_variant(_dtype_code(a.dtype), variant, group_m, int(swiglu), m, n, k, _ptr(a),
+                                  _ptr(w), _ptr(c), _stream(stream)), "dit_gemm_variant")
 
 
 def attention(cfg: Config, qkvg, og, ws, stream=None) -> None:

@@ -350,9 +350,11 @@ dit_status dit_gemm_swiglu(dit_dtype dtype, int32_t m, int32_t f, int32_t k, con
   return e == hipSuccess ? DIT_OK : hip_fail(e);
 }
 
-dit_status dit_gemm_variant(dit_dtype dtype, int32_t variant, int32_t swiglu, int32_t m, int32_t n,
-                            int32_t k, const void *a, const void *w, void *c, void *stream) {
+dit_status dit_gemm_variant(dit_dtype dtype, int32_t variant, int32_t group_m, int32_t swiglu,
+                            int32_t m, int32_t n, int32_t k, const void *a, const void *w, void *c,
+                            void *stream) {
   if (variant < 0 || variant >= kGemmVariants) return DIT_ERR_UNSUPPORTED;
+  if (group_m < 0 || group_m > 64) return DIT_ERR_SHAPE;
   if (swiglu != 0 && swiglu != 1) return DIT_ERR_SHAPE;
   dit_status st = check_gemm(dtype, m, n, k, a, w, c, swiglu ? 2 * (int64_t)n + 256 : 256);
   if (st != DIT_OK) return st;
@@ -361,8 +363,8 @@ dit_status dit_gemm_variant(dit_dtype dtype, int32_t variant, int32_t swiglu, in
   if (overlap(c, (size_t)m * n * es, a, (size_t)m * k * es) || overlap(c, (size_t)m * n * es, w, wrows * k * es))
     return DIT_ERR_SHAPE;
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = swiglu ? launch_gemm_swiglu(dtype == DIT_F32, a, w, c, m, n, k, s, variant)
-                        : launch_gemm(dtype == DIT_F32, a, w, c, m, n, k, s, variant);
+  hipError_t e = swiglu ? launch_gemm_swiglu(dtype == DIT_F32, a, w, c, m, n, k, s, variant, group_m)
+                        : launch_gemm(dtype == DIT_F32, a, w, c, m, n, k, s, variant, group_m);
   return e == hipSuccess ? DIT_OK : hip_fail(e);
 }
 

@@ -17,11 +17,12 @@ hipError_t launch_resid_modnorm(bool x_f32, bool f32, const void *x, const void 
                                 int seq_len, int D, float eps, hipStream_t s);
 hipError_t launch_tmod(const float *t, const float *w1, const float *w2, float *mod, float *zs,
                        int B, int D, int tdim, hipStream_t s);
-// variant < 0 picks the default tile configuration for the shape
+// variant < 0 picks the default tile configuration for the shape; group_m
+// <= 0 the default tile-grouping width (row tiles per L2 group)
 hipError_t launch_gemm(bool f32, const void *a, const void *w, void *c, int M, int N, int K,
-                       hipStream_t s, int variant = -1);
+                       hipStream_t s, int variant = -1, int group_m = 0);
 hipError_t launch_gemm_swiglu(bool f32, const void *a, const void *w13, void *u, int M, int F,
-                              int K, hipStream_t s, int variant = -1);
+                              int K, hipStream_t s, int variant = -1, int group_m = 0);
 constexpr int kGemmVariants = 11;
 // vt: scratch of attention_vt_bytes() for the transposed V of every KV head
 size_t attention_vt_bytes(bool f32, int B, int L, int Hkv, int head_dim);

@@ -17,8 +17,9 @@
 //  * tails in M, N and K are zero-filled by the buffer descriptor's range
 //    check (out-of-range chunks are given an out-of-range offset);
 //  * workgroup ids are remapped so that each XCD (dispatch is round-robin
-//    over the 8 XCDs) walks a contiguous band of tiles, grouped GM row
-//    tiles at a time, so tiles sharing A rows or W rows meet in one L2.
+//    over the 8 XCDs) walks a contiguous band of tiles, grouped gm row
+//    tiles at a time, so tiles sharing A rows or W rows meet in one L2
+//    (gm is chosen per shape by the host).
 #include <cmath>
 
 #include "dit_common.h"
@@ -51,7 +52,7 @@ template <typename T, int BM, int BN, int BKB, int STAGES, int WM, int WN, int E
 __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(const T *__restrict__ A,
                                                            const T *__restrict__ W,
                                                            T *__restrict__ C, int M, int N, int K,
-                                                           int m_tiles, int n_tiles) {
+                                                           int m_tiles, int n_tiles, int gm) {
   constexpr int NW = WM * WN;
   constexpr int CPR = BKB / 16;             // 16-byte chunks per row per stage
   constexpr int RPB = 1024 / BKB;           // rows per 1 KiB DMA block
@@ -78,11 +79,10 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(const T *__restrict__
   const int nwg = m_tiles * n_tiles;
   int pid = blockIdx.x;
   if ((nwg & 7) == 0) pid = (pid & 7) * (nwg >> 3) + (pid >> 3);
-  constexpr int GM = 8;
-  const int group = pid / (GM * n_tiles);
-  const int first_m = group * GM;
-  const int gsz = min(m_tiles - first_m, GM);
-  const int in_g = pid - group * GM * n_tiles;
+  const int group = pid / (gm * n_tiles);
+  const int first_m = group * gm;
+  const int gsz = min(m_tiles - first_m, gm);
+  const int in_g = pid - group * gm * n_tiles;
   const int tm = first_m + in_g % gsz, tn = in_g / gsz;
   const int m0 = tm * BM;
   // SwiGLU: W holds [W1; W3] with N = F rows each; the tile covers F-columns
@@ -306,54 +306,58 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(const T *__restrict__
 
 template <typename T, int BM, int BN, int BKB, int STAGES, int WM, int WN, int EPI, bool PIPE = false>
 static hipError_t launch_gemm_t(const void *a, const void *w, void *c, int M, int N, int K,
-                                hipStream_t s) {
+                                hipStream_t s, int gm) {
   const int mt = (M + BM - 1) / BM;
   const int nt = (EPI == EPI_SWIGLU) ? (N + BN / 2 - 1) / (BN / 2) : (N + BN - 1) / BN;
   hipLaunchKernelGGL((gemm_kernel<T, BM, BN, BKB, STAGES, WM, WN, EPI, PIPE>), dim3(mt * nt),
-                     dim3(WM * WN * 64), 0, s, (const T *)a, (const T *)w, (T *)c, M, N, K, mt, nt);
+                     dim3(WM * WN * 64), 0, s, (const T *)a, (const T *)w, (T *)c, M, N, K, mt, nt,
+                     gm);
   return hipGetLastError();
 }
 
 // Tile configurations, selectable for tuning (variant < 0: the default).
 template <int EPI>
-static hipError_t gemm_dispatch(bool f32, int variant, const void *a, const void *w, void *c,
-                                int M, int N, int K, hipStream_t s) {
-  if (f32) return launch_gemm_t<float, 256, 256, 128, 2, 2, 4, EPI>(a, w, c, M, N, K, s);
+static hipError_t gemm_dispatch(bool f32, int variant, int gm, const void *a, const void *w,
+                                void *c, int M, int N, int K, hipStream_t s) {
+  if (gm <= 0) gm = 8;
+  if (f32) return launch_gemm_t<float, 256, 256, 128, 2, 2, 4, EPI>(a, w, c, M, N, K, s, gm);
   if (variant < 0) {
     // software-pipelined 8-wave tiles; 192 x 256 instead of 256 x 256 when
-    // its tile count fills the 256 CUs in noticeably fuller rounds (e.g.
-    // N = 4096 at 9216 rows: 768 tiles = 3 full rounds vs 576 = 2.25)
+    // its tile count fills the 256 CUs in fuller rounds (e.g. N = 4096 at
+    // 9216 rows: 768 tiles = 3 full rounds vs 576 = 2.25).  Below a 2 %
+    // fill advantage the larger tile wins: it moves fewer operand bytes
+    // per FLOP.
     const int ncols = (EPI == EPI_SWIGLU) ? 128 : 256;
     auto fill = [&](int bm) {
       const double tiles = (double)((M + bm - 1) / bm) * ((N + ncols - 1) / ncols);
       return tiles / (std::ceil(tiles / 256.0) * 256.0);
     };
-    variant = (fill(192) > fill(256) + 0.05) ? 9 : 8;
+    variant = (fill(192) > fill(256) + 0.02) ? 9 : 8;
   }
   switch (variant) {
-    case 0: return launch_gemm_t<bf16, 256, 256, 64, 4, 2, 2, EPI>(a, w, c, M, N, K, s);
-    case 1: return launch_gemm_t<bf16, 256, 256, 64, 4, 2, 4, EPI>(a, w, c, M, N, K, s);
-    case 2: return launch_gemm_t<bf16, 256, 256, 128, 2, 2, 4, EPI>(a, w, c, M, N, K, s);
-    case 3: return launch_gemm_t<bf16, 256, 128, 64, 4, 2, 2, EPI>(a, w, c, M, N, K, s);
-    case 4: return launch_gemm_t<bf16, 256, 128, 128, 3, 2, 2, EPI>(a, w, c, M, N, K, s);
-    case 5: return launch_gemm_t<bf16, 128, 128, 128, 4, 2, 2, EPI>(a, w, c, M, N, K, s);
-    case 6: return launch_gemm_t<bf16, 256, 256, 64, 5, 2, 2, EPI>(a, w, c, M, N, K, s);
-    case 7: return launch_gemm_t<bf16, 192, 256, 128, 2, 2, 4, EPI>(a, w, c, M, N, K, s);
-    case 8: return launch_gemm_t<bf16, 256, 256, 128, 2, 2, 4, EPI, true>(a, w, c, M, N, K, s);
-    case 9: return launch_gemm_t<bf16, 192, 256, 128, 2, 2, 4, EPI, true>(a, w, c, M, N, K, s);
-    case 10: return launch_gemm_t<bf16, 256, 256, 128, 2, 2, 2, EPI, true>(a, w, c, M, N, K, s);
+    case 0: return launch_gemm_t<bf16, 256, 256, 64, 4, 2, 2, EPI>(a, w, c, M, N, K, s, gm);
+    case 1: return launch_gemm_t<bf16, 256, 256, 64, 4, 2, 4, EPI>(a, w, c, M, N, K, s, gm);
+    case 2: return launch_gemm_t<bf16, 256, 256, 128, 2, 2, 4, EPI>(a, w, c, M, N, K, s, gm);
+    case 3: return launch_gemm_t<bf16, 256, 128, 64, 4, 2, 2, EPI>(a, w, c, M, N, K, s, gm);
+    case 4: return launch_gemm_t<bf16, 256, 128, 128, 3, 2, 2, EPI>(a, w, c, M, N, K, s, gm);
+    case 5: return launch_gemm_t<bf16, 128, 128, 128, 4, 2, 2, EPI>(a, w, c, M, N, K, s, gm);
+    case 6: return launch_gemm_t<bf16, 256, 256, 64, 5, 2, 2, EPI>(a, w, c, M, N, K, s, gm);
+    case 7: return launch_gemm_t<bf16, 192, 256, 128, 2, 2, 4, EPI>(a, w, c, M, N, K, s, gm);
+    case 8: return launch_gemm_t<bf16, 256, 256, 128, 2, 2, 4, EPI, true>(a, w, c, M, N, K, s, gm);
+    case 9: return launch_gemm_t<bf16, 192, 256, 128, 2, 2, 4, EPI, true>(a, w, c, M, N, K, s, gm);
+    case 10: return launch_gemm_t<bf16, 256, 256, 128, 2, 2, 2, EPI, true>(a, w, c, M, N, K, s, gm);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_gemm(bool f32, const void *a, const void *w, void *c, int M, int N, int K,
-                       hipStream_t s, int variant) {
-  return gemm_dispatch<EPI_STORE>(f32, variant, a, w, c, M, N, K, s);
+                       hipStream_t s, int variant, int group_m) {
+  return gemm_dispatch<EPI_STORE>(f32, variant, group_m, a, w, c, M, N, K, s);
 }
 
 hipError_t launch_gemm_swiglu(bool f32, const void *a, const void *w13, void *u, int M, int F,
-                              int K, hipStream_t s, int variant) {
-  return gemm_dispatch<EPI_SWIGLU>(f32, variant, a, w13, u, M, F, K, s);
+                              int K, hipStream_t s, int variant, int group_m) {
+  return gemm_dispatch<EPI_SWIGLU>(f32, variant, group_m, a, w13, u, M, F, K, s);
 }
 
 }  // namespace dit

@@ -182,12 +182,15 @@ dit_status dit_gemm_swiglu(dit_dtype dtype, int32_t m, int32_t f, int32_t k, con
 
 /* The same products with an explicit tile configuration, for tuning and
  * tests: variant 0..10 selects one of the compiled (BM x BN tile, stage
- * depth, wave grid) configurations; every variant computes the same
- * result up to fp32 summation order.  swiglu = 0: C[M, N] = A W^T with
- * W [N, K]; swiglu = 1: as dit_gemm_swiglu with F = n and W = W13 [2n, K].
- * Variants are ignored by the fp32 path. */
-dit_status dit_gemm_variant(dit_dtype dtype, int32_t variant, int32_t swiglu, int32_t m, int32_t n,
-                            int32_t k, const void *a, const void *w, void *c, void *stream);
+ * depth, wave grid) configurations; group_m (0 = default, else 1..64) is
+ * the number of row tiles walked together so their operands share an L2.
+ * Every choice computes the same result up to fp32 summation order.
+ * swiglu = 0: C[M, N] = A W^T with W [N, K]; swiglu = 1: as
+ * dit_gemm_swiglu with F = n and W = W13 [2n, K].  The tile variant is
+ * ignored by the fp32 path.  group_m outside 0..64 -> DIT_ERR_SHAPE. */
+dit_status dit_gemm_variant(dit_dtype dtype, int32_t variant, int32_t group_m, int32_t swiglu,
+                            int32_t m, int32_t n, int32_t k, const void *a, const void *w, void *c,
+                            void *stream);
 
 /* Gated grouped-query attention over the rows of qkvg [T, (2H+2Hkv)*d]
  * (column blocks Q | K | V | G, as produced by the QKVG projection):

@@ -187,6 +187,24 @@ def test_timestep_mod(dev, name, batch):
     assert_parity(device.to_numpy(M), ref, "f32", "timestep modulation", maxabs=2e-5)
 
 
+@pytest.mark.parametrize("group_m", [1, 3, 64])
+@pytest.mark.parametrize("variant", [8, 9])
+def test_gemm_tile_grouping(dev, variant, group_m):
+    """The L2 grouping width reorders tiles only: ragged M with fewer row
+    tiles than one group, and several groups with a partial last one."""
+    torch, device, dit = dev
+    m, n, k = 1100, 776, 264
+    cfg = datagen.get_config("c1")
+    a, w = datagen.gemm_operands(cfg, m, n, k, tag=61 + group_m)
+    A, W = device.to_device(a, "bf16"), device.to_device(w, "bf16")
+    C = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    dit.gemm_variant(variant, A, W, C, group_m=group_m)
+    torch.cuda.synchronize()
+    ref = a.astype(np.float64) @ w.astype(np.float64).T
+    assert_parity(device.to_numpy(C), ref, "bf16", f"variant {variant} group {group_m}", maxabs=8e-3,
+                  cos_min=0.99999)
+
+
 @pytest.mark.parametrize("variant", list(range(11)))
 @pytest.mark.parametrize("swiglu", [False, True])
 def test_gemm_every_tile_variant(dev, variant, swiglu):
