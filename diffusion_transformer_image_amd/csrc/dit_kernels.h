@@ -23,7 +23,7 @@ hipError_t launch_gemm(bool f32, const void *a, const void *w, void *c, int M, i
                        hipStream_t s, int variant = -1, int group_m = 0);
 hipError_t launch_gemm_swiglu(bool f32, const void *a, const void *w13, void *u, int M, int F,
                               int K, hipStream_t s, int variant = -1, int group_m = 0);
-constexpr int kGemmVariants = 11;
+constexpr int kGemmVariants = 15;
 // vt: scratch of attention_vt_bytes() for the transposed V of every KV head
 size_t attention_vt_bytes(bool f32, int B, int L, int Hkv, int head_dim);
 hipError_t launch_attention(bool f32, int head_dim, const void *qkvg, void *vt, void *og, int B,

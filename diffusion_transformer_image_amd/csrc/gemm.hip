@@ -21,6 +21,7 @@
 //    tiles at a time, so tiles sharing A rows or W rows meet in one L2
 //    (gm is chosen per shape by the host).
 #include <cmath>
+#include <type_traits>
 
 #include "dit_common.h"
 #include "dit_kernels.h"
@@ -39,6 +40,83 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Epilogue shared by the GEMM kernels: lane holds rows 4g+e of column r16 of
+// every 16x16 block of its wave's TM x TN sub-tile.  bf16 output goes through
+// LDS (16-byte chunks XOR-swizzled by row) and leaves as whole 16-byte chunks.
+template <typename T, int BM, int BN, int NW, int WM, int WN, int EPI, int SMEM>
+__device__ __forceinline__ void gemm_epilogue(const f32x4 (&acc)[BM / WM / 16][BN / WN / 16], char *smem,
+                                              T *__restrict__ C, int M, int N, int m0, int n0,
+                                              int wave, int lane) {
+  constexpr int TM = BM / WM, TN = BN / WN;
+  constexpr int RB = TM / 16, CB = TN / 16;
+  const int wm = wave / WN, wn = wave % WN;
+  const int g = lane >> 4, r16 = lane & 15;
+  constexpr int TNO = (EPI == EPI_SWIGLU) ? TN / 2 : TN;  // output columns per wave
+  const int col0 = (EPI == EPI_SWIGLU) ? n0 + wn * (TN / 2) : n0 + wn * TN;
+  const int row0 = m0 + wm * TM;
+  auto out_val = [&](int i, int j, int e) -> float {
+    if constexpr (EPI == EPI_SWIGLU) return silu(acc[i][j][e]) * acc[i][j + CB / 2][e];
+    else return acc[i][j][e];
+  };
+  // (the XOR swizzle needs a power-of-two number of 16-byte chunks per row)
+  if constexpr (sizeof(T) == 2 && (TNO * 2) % 64 == 0 && ((TNO / 8) & (TNO / 8 - 1)) == 0 &&
+                NW * TM * TNO * 2 <= SMEM) {
+    // bf16: stage the wave's TM x TNO output tile in LDS (16-byte chunks
+    // XOR-swizzled by row), then write whole 16-byte chunks: each row of the
+    // tile goes out as TNO*2 contiguous bytes instead of 2-byte pieces.
+    constexpr int PITCH = TNO * 2;       // bytes per tile row in LDS
+    constexpr int CPRO = PITCH / 16;     // 16-byte chunks per row (4 or 8)
+    __syncthreads();  // all waves are done reading the operand stages
+    char *tile = smem + wave * (TM * PITCH);
+#pragma unroll
+    for (int j = 0; j < CB / ((EPI == EPI_SWIGLU) ? 2 : 1); ++j) {
+      const int col = j * 16 + r16;  // column inside the wave tile
+#pragma unroll
+      for (int i = 0; i < RB; ++i) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int row = i * 16 + 4 * g + e;
+          const int off = row * PITCH + (((col >> 3) ^ (row & (CPRO - 1))) << 4) + (col & 7) * 2;
+          *reinterpret_cast<bf16 *>(tile + off) = (bf16)out_val(i, j, e);
+        }
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int q = lane; q < TM * CPRO; q += 64) {
+      const int row = q / CPRO, c = q % CPRO;
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(tile + row * PITCH + ((c ^ (row & (CPRO - 1))) << 4));
+      const int gr = row0 + row, gc = col0 + c * 8;
+      if (gr < M) {
+        T *dst = C + (size_t)gr * N + gc;
+        if (gc + 8 <= N && (N & 7) == 0) {
+          *reinterpret_cast<u32x4 *>(dst) = v;
+        } else {
+          const bf16x8 vb = __builtin_bit_cast(bf16x8, v);
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (gc + e < N) dst[e] = vb[e];
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < CB / ((EPI == EPI_SWIGLU) ? 2 : 1); ++j) {
+      const int col = col0 + j * 16 + r16;
+      if (col >= N) continue;
+#pragma unroll
+      for (int i = 0; i < RB; ++i) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int row = row0 + i * 16 + 4 * g + e;
+          if (row < M) C[(size_t)row * N + col] = from_f32<T>(out_val(i, j, e));
+        }
+      }
+    }
+  }
 }
 
 // PIPE (two-stage ring only): software-pipelined main loop.  The fragments
@@ -239,69 +317,209 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(const T *__restrict__
   }
   }
 
-  // ---- epilogue: lane holds rows 4g+e of column r16 of every 16x16 block
-  constexpr int TNO = (EPI == EPI_SWIGLU) ? TN / 2 : TN;  // output columns per wave
-  const int col0 = (EPI == EPI_SWIGLU) ? n0 + wn * (TN / 2) : n0 + wn * TN;
-  const int row0 = m0 + wm * TM;
-  auto out_val = [&](int i, int j, int e) -> float {
-    if constexpr (EPI == EPI_SWIGLU) return silu(acc[i][j][e]) * acc[i][j + CB / 2][e];
-    else return acc[i][j][e];
-  };
-  if constexpr (sizeof(T) == 2 && (TNO * 2) % 64 == 0 && NW * TM * TNO * 2 <= STAGES * STAGE_BYTES) {
-    // bf16: stage the wave's TM x TNO output tile in LDS (16-byte chunks
-    // XOR-swizzled by row), then write whole 16-byte chunks: each row of the
-    // tile goes out as TNO*2 contiguous bytes instead of 2-byte pieces.
-    constexpr int PITCH = TNO * 2;       // bytes per tile row in LDS
-    constexpr int CPRO = PITCH / 16;     // 16-byte chunks per row (4 or 8)
-    __syncthreads();  // all waves are done reading the operand stages
-    char *tile = smem + wave * (TM * PITCH);
-#pragma unroll
-    for (int j = 0; j < CB / ((EPI == EPI_SWIGLU) ? 2 : 1); ++j) {
-      const int col = j * 16 + r16;  // column inside the wave tile
-#pragma unroll
-      for (int i = 0; i < RB; ++i) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int row = i * 16 + 4 * g + e;
-          const int off = row * PITCH + (((col >> 3) ^ (row & (CPRO - 1))) << 4) + (col & 7) * 2;
-          *reinterpret_cast<bf16 *>(tile + off) = (bf16)out_val(i, j, e);
-        }
-      }
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int q = lane; q < TM * CPRO; q += 64) {
-      const int row = q / CPRO, c = q % CPRO;
-      const u32x4 v = *reinterpret_cast<const u32x4 *>(tile + row * PITCH + ((c ^ (row & (CPRO - 1))) << 4));
-      const int gr = row0 + row, gc = col0 + c * 8;
-      if (gr < M) {
-        T *dst = C + (size_t)gr * N + gc;
-        if (gc + 8 <= N && (N & 7) == 0) {
-          *reinterpret_cast<u32x4 *>(dst) = v;
-        } else {
-          const bf16x8 vb = __builtin_bit_cast(bf16x8, v);
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (gc + e < N) dst[e] = vb[e];
-        }
-      }
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < CB / ((EPI == EPI_SWIGLU) ? 2 : 1); ++j) {
-      const int col = col0 + j * 16 + r16;
-      if (col >= N) continue;
-#pragma unroll
-      for (int i = 0; i < RB; ++i) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int row = row0 + i * 16 + 4 * g + e;
-          if (row < M) C[(size_t)row * N + col] = from_f32<T>(out_val(i, j, e));
-        }
-      }
-    }
+  gemm_epilogue<T, BM, BN, NW, WM, WN, EPI, STAGES * STAGE_BYTES>(acc, smem, C, M, N, m0, n0, wave,
+                                                                 lane);
+}
+
+// Calls f(integral_constant<I>) for I = B..E-1 in order while f returns true.
+template <int B, int E, typename F>
+__device__ __forceinline__ bool static_for(F &&f) {
+  if constexpr (B < E) {
+    if (!f(std::integral_constant<int, B>{})) return false;
+    return static_for<B + 1, E>(f);
   }
+  return true;
+}
+
+// ---------------------------------------------------------------------------
+// Ring kernel (bf16): 8 waves (2 x 4), BM x BN output tile, K advanced 32
+// elements (64 bytes of every row) per stage through an R-deep LDS ring fed
+// by LDS DMA.
+//  * stage s lives in buffer s % R.  At step kt the wave multiplies the
+//    fragments of stage kt (already in registers), reads the fragments of
+//    stage kt+1 from LDS and issues the DMA of stage kt+R into the buffer of
+//    stage kt, so each DMA has R-1 steps to land;
+//  * the one barrier per step sits between the two halves of the step's
+//    MFMAs.  Before it each wave waits only for its own DMA of stage kt+1
+//    (partial vmcnt: the later stages stay in flight) and for its own LDS
+//    reads of stage kt; a bare s_barrier follows (no memory fence, which
+//    would wait for every DMA in flight);
+//  * the K offset of a stage is the scalar soffset of the DMA, so the loop
+//    does no per-lane address arithmetic; the LDS addresses of a buffer are
+//    fixed because the step loop is unrolled over the R buffers;
+//  * a 64-byte LDS row holds 4 chunks; chunk c of row r sits at
+//    c ^ (((r >> 1) ^ (r >> 2)) & 3), which keeps the 16 rows x one chunk of
+//    a fragment read on distinct banks for 8- and 16-lane access groups.
+__device__ __forceinline__ int swz64(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+
+__device__ __forceinline__ void load_lds16_k(rsrc_t r, const void *lds_wave_base, uint32_t voff,
+                                             uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds_wave_base, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void barrier_only() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+template <int BM, int BN, int R, int WM, int WN, int EPI>
+__global__ __launch_bounds__(WM *WN * 64) void gemm_ring_kernel(const bf16 *__restrict__ A,
+                                                        const bf16 *__restrict__ W,
+                                                        bf16 *__restrict__ C, int M, int N, int K,
+                                                        int m_tiles, int n_tiles, int gm) {
+  constexpr int NW = WM * WN;
+  constexpr int TM = BM / WM, TN = BN / WN;
+  constexpr int RB = TM / 16, CB = TN / 16;
+  constexpr int ABLK = BM / 16, BBLK = BN / 16, NBLK = ABLK + BBLK;  // 1 KiB blocks per stage
+  constexpr int STAGE = NBLK * 1024;
+  constexpr int LPW = (NBLK + NW - 1) / NW;  // DMA loads per wave per stage (waves >= NBLK % NW: one less)
+  constexpr bool EVEN = (NBLK % NW) == 0;
+  static_assert(R >= 3 && LPW * (R - 1) < 64, "ring depth / vmcnt range");
+  static_assert(R * STAGE <= 160 * 1024, "LDS");
+  static_assert(RB % 2 == 0, "two MFMA halves");
+  static_assert(EPI != EPI_SWIGLU || (CB % 2 == 0), "SwiGLU pairs column blocks");
+
+  __shared__ __attribute__((aligned(1024))) char smem[R * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+
+  const int nwg = m_tiles * n_tiles;
+  int pid = blockIdx.x;
+  if ((nwg & 7) == 0) pid = (pid & 7) * (nwg >> 3) + (pid >> 3);
+  const int group = pid / (gm * n_tiles);
+  const int first_m = group * gm;
+  const int gsz = min(m_tiles - first_m, gm);
+  const int in_g = pid - group * gm * n_tiles;
+  const int tm = first_m + in_g % gsz, tn = in_g / gsz;
+  const int m0 = tm * BM;
+  const int n0 = (EPI == EPI_SWIGLU) ? tn * (BN / 2) : tn * BN;
+
+  const uint32_t ldb = (uint32_t)K * 2;
+  const rsrc_t ra = make_rsrc(A + (size_t)m0 * K, (uint32_t)min(M - m0, BM) * ldb);
+  const rsrc_t rw = (EPI == EPI_SWIGLU)
+                        ? make_rsrc(W + (size_t)n0 * K, (uint32_t)(N + min(N - n0, BN / 2)) * ldb)
+                        : make_rsrc(W + (size_t)n0 * K, (uint32_t)min(N - n0, BN) * ldb);
+
+  // ---- DMA: lane fills slot `lane` of a 1 KiB block = row lane / 4 of the
+  // block, physical chunk lane % 4, which holds logical chunk (lane % 4) ^ swz
+  const int lrow = lane >> 2;
+  const int lchunk = (lane & 3) ^ swz64(lrow);
+  const bool full = EVEN || wave < NBLK % NW;  // this wave issues LPW loads per stage (else LPW - 1)
+  uint32_t goff[LPW];
+#pragma unroll
+  for (int j = 0; j < LPW; ++j) {
+    const int blk = wave + j * NW;
+    bool ok = false;
+    uint32_t off = 0;
+    if (blk < ABLK) {
+      const int r = blk * 16 + lrow;
+      ok = (m0 + r) < M;
+      off = (uint32_t)r * ldb;
+    } else if (blk < NBLK) {
+      const int r = (blk - ABLK) * 16 + lrow;
+      if (EPI == EPI_SWIGLU) {
+        const int rr = r < BN / 2 ? r : r - BN / 2;
+        ok = n0 + rr < N;
+        off = (uint32_t)(r < BN / 2 ? rr : N + rr) * ldb;
+      } else {
+        ok = (n0 + r) < N;
+        off = (uint32_t)r * ldb;
+      }
+    }
+    // rows outside the operand keep an out-of-range offset at every stage
+    goff[j] = ok ? off + lchunk * 16 : kOOB;
+  }
+  const int nk = K / 32;  // the host guarantees K % (32 R) == 0
+  // Stage s >= nk (past the end of K) is issued too, with an out-of-range
+  // scalar offset: its loads return zeros into a buffer nobody reads, which
+  // keeps every step identical (no branches, constant wait counts).
+  auto issue = [&](int s, char *buf) {
+    const uint32_t kb = s < nk ? (uint32_t)s * 64 : kOOB;
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) {
+      const int blk = wave + j * NW;
+      if (j < LPW - 1 || full) load_lds16_k(blk < ABLK ? ra : rw, buf + blk * 1024, goff[j], kb);
+    }
+  };
+  // this wave's DMA of a stage is complete once at most P later stages are in flight
+  auto wait_stages = [&](auto Pc) {
+    constexpr int P = decltype(Pc)::value;
+    if (EVEN || full) wait_vmcnt<LPW * P>();
+    else wait_vmcnt<(LPW - 1) * P>();
+  };
+
+  // ---- fragment addresses: row r16 of each 16-row block, chunk g ^ swz
+  const int g = lane >> 4, r16 = lane & 15;
+  const int fch = (g ^ swz64(r16)) * 16;
+  const int aoff = (wm * TM + r16) * 64 + fch;
+  const int boff = (BM + wn * ((EPI == EPI_SWIGLU) ? TN / 2 : TN) + r16) * 64 + fch;
+  auto bblk = [](int j) {  // 1 KiB offset of column block j from boff
+    if (EPI == EPI_SWIGLU) return (j < CB / 2 ? j : (BN / 2) / 16 + j - CB / 2) * 1024;
+    return j * 1024;
+  };
+
+  f32x4 acc[RB][CB];
+#pragma unroll
+  for (int i = 0; i < RB; ++i)
+#pragma unroll
+    for (int j = 0; j < CB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  u32x4 fa0[RB], fb0[CB], fa1[RB], fb1[CB];
+  auto load_frags = [&](const char *sb, u32x4(&af)[RB], u32x4(&bf)[CB]) {
+#pragma unroll
+    for (int i = 0; i < RB; ++i) af[i] = *reinterpret_cast<const u32x4 *>(sb + aoff + i * 1024);
+#pragma unroll
+    for (int j = 0; j < CB; ++j) bf[j] = *reinterpret_cast<const u32x4 *>(sb + boff + bblk(j));
+  };
+  auto mmas = [&](const u32x4(&af)[RB], const u32x4(&bf)[CB], auto I0) {
+    constexpr int i0 = decltype(I0)::value;
+#pragma unroll
+    for (int i = i0; i < i0 + RB / 2; ++i)
+#pragma unroll
+      for (int j = 0; j < CB; ++j) acc[i][j] = mma16<bf16>(af[i], bf[j], acc[i][j]);
+  };
+
+  // prologue: stages 0 .. R-1 in flight, stage 0 in registers
+#pragma unroll
+  for (int st = 0; st < R; ++st) issue(st, smem + st * STAGE);
+  wait_stages(std::integral_constant<int, R - 1>{});
+  barrier_only();
+  load_frags(smem, fa0, fb0);
+  drain_lgkm();
+
+  // step kt: multiply stage kt (register set cur), fetch stage kt+1 (set nxt)
+  // from buffer (kt+1) % R, refill buffer kt % R with stage kt+R
+  auto step = [&](int kt, auto Uc, u32x4(&ca)[RB], u32x4(&cb)[CB], u32x4(&na)[RB], u32x4(&nb)[CB]) {
+    constexpr int u = decltype(Uc)::value;  // kt % R
+    mmas(ca, cb, std::integral_constant<int, 0>{});
+    __builtin_amdgcn_sched_barrier(0);
+    wait_stages(std::integral_constant<int, R - 2>{});
+    wait_lgkm0();
+    barrier_only();
+    issue(kt + R, smem + u * STAGE);
+    load_frags(smem + ((u + 1) % R) * STAGE, na, nb);
+    __builtin_amdgcn_sched_barrier(0);
+    mmas(ca, cb, std::integral_constant<int, RB / 2>{});
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // unrolled over R steps (R even) so buffer offsets and register sets are
+  // constants; one loop exit keeps the accumulators in registers (the host
+  // guarantees nk % R == 0)
+  static_assert(R % 2 == 0, "register sets alternate with the buffer index");
+  for (int kt0 = 0; kt0 < nk; kt0 += R) {
+    static_for<0, R>([&](auto V) {
+      constexpr int v = decltype(V)::value;
+      if constexpr (v % 2 == 0) step(kt0 + v, std::integral_constant<int, v>{}, fa0, fb0, fa1, fb1);
+      else step(kt0 + v, std::integral_constant<int, v>{}, fa1, fb1, fa0, fb0);
+      return true;
+    });
+  }
+  wait_vmcnt<0>();
+
+  gemm_epilogue<bf16, BM, BN, NW, WM, WN, EPI, R * STAGE>(acc, smem, C, M, N, m0, n0, wave, lane);
 }
 
 template <typename T, int BM, int BN, int BKB, int STAGES, int WM, int WN, int EPI, bool PIPE = false>
@@ -312,6 +530,16 @@ static hipError_t launch_gemm_t(const void *a, const void *w, void *c, int M, in
   hipLaunchKernelGGL((gemm_kernel<T, BM, BN, BKB, STAGES, WM, WN, EPI, PIPE>), dim3(mt * nt),
                      dim3(WM * WN * 64), 0, s, (const T *)a, (const T *)w, (T *)c, M, N, K, mt, nt,
                      gm);
+  return hipGetLastError();
+}
+
+template <int BM, int BN, int R, int WM, int WN, int EPI>
+static hipError_t launch_ring_t(const void *a, const void *w, void *c, int M, int N, int K,
+                                hipStream_t s, int gm) {
+  const int mt = (M + BM - 1) / BM;
+  const int nt = (EPI == EPI_SWIGLU) ? (N + BN / 2 - 1) / (BN / 2) : (N + BN - 1) / BN;
+  hipLaunchKernelGGL((gemm_ring_kernel<BM, BN, R, WM, WN, EPI>), dim3(mt * nt), dim3(WM * WN * 64), 0, s,
+                     (const bf16 *)a, (const bf16 *)w, (bf16 *)c, M, N, K, mt, nt, gm);
   return hipGetLastError();
 }
 
@@ -346,6 +574,10 @@ static hipError_t gemm_dispatch(bool f32, int variant, int gm, const void *a, co
     case 8: return launch_gemm_t<bf16, 256, 256, 128, 2, 2, 4, EPI, true>(a, w, c, M, N, K, s, gm);
     case 9: return launch_gemm_t<bf16, 192, 256, 128, 2, 2, 4, EPI, true>(a, w, c, M, N, K, s, gm);
     case 10: return launch_gemm_t<bf16, 256, 256, 128, 2, 2, 2, EPI, true>(a, w, c, M, N, K, s, gm);
+    case 11: return (K % 128) ? launch_gemm_t<bf16, 256, 256, 128, 2, 2, 4, EPI, true>(a, w, c, M, N, K, s, gm) : launch_ring_t<256, 256, 4, 2, 4, EPI>(a, w, c, M, N, K, s, gm);
+    case 12: return (K % 128) ? launch_gemm_t<bf16, 192, 256, 128, 2, 2, 4, EPI, true>(a, w, c, M, N, K, s, gm) : launch_ring_t<192, 256, 4, 2, 4, EPI>(a, w, c, M, N, K, s, gm);
+    case 13: return (K % 128) ? launch_gemm_t<bf16, 256, 256, 128, 2, 2, 4, EPI, true>(a, w, c, M, N, K, s, gm) : launch_ring_t<256, 256, 4, 2, 2, EPI>(a, w, c, M, N, K, s, gm);
+    case 14: return (K % 128) ? launch_gemm_t<bf16, 192, 256, 128, 2, 2, 4, EPI, true>(a, w, c, M, N, K, s, gm) : launch_ring_t<256, 192, 4, 2, 2, EPI>(a, w, c, M, N, K, s, gm);
     default: return hipErrorInvalidValue;
   }
 }

@@ -120,7 +120,7 @@ def test_step_argument_checks():
     assert S(L.dit_gemm(1, 16, 16, 16, P + 2, P + G, P + 2 * G, None)) == "DIT_ERR_ALIGN"
     assert S(L.dit_gemm(1, 16, 16, 16, P, P + G, P + 64, None)) == "DIT_ERR_SHAPE"  # C overlaps A
     assert S(L.dit_gemm_swiglu(1, 16, 16, 16, 0, P + G, P + 2 * G, None)) == "DIT_ERR_NULL"
-    assert S(L.dit_gemm_variant(1, 11, 0, 0, 16, 16, 16, P, P + G, P + 2 * G, None)) == "DIT_ERR_UNSUPPORTED"
+    assert S(L.dit_gemm_variant(1, 15, 0, 0, 16, 16, 16, P, P + G, P + 2 * G, None)) == "DIT_ERR_UNSUPPORTED"
     assert S(L.dit_gemm_variant(1, 8, 65, 0, 16, 16, 16, P, P + G, P + 2 * G, None)) == "DIT_ERR_SHAPE"
     assert S(L.dit_gemm_variant(1, 8, -1, 0, 16, 16, 16, P, P + G, P + 2 * G, None)) == "DIT_ERR_SHAPE"
     assert S(L.dit_gemm_variant(1, 8, 4, 2, 16, 16, 16, P, P + G, P + 2 * G, None)) == "DIT_ERR_SHAPE"

@@ -205,7 +205,7 @@ def test_gemm_tile_grouping(dev, variant, group_m):
                   cos_min=0.99999)
 
 
-@pytest.mark.parametrize("variant", list(range(11)))
+@pytest.mark.parametrize("variant", list(range(15)))
 @pytest.mark.parametrize("swiglu", [False, True])
 def test_gemm_every_tile_variant(dev, variant, swiglu):
     """Every compiled tile configuration on ragged M, N and K."""
@@ -219,3 +219,22 @@ def test_gemm_every_tile_variant(dev, variant, swiglu):
     torch.cuda.synchronize()
     ref = O.swiglu_hidden(a, w, n) if swiglu else a.astype(np.float64) @ w.astype(np.float64).T
     assert_parity(device.to_numpy(C), ref, "bf16", f"variant {variant}", maxabs=8e-3, cos_min=0.99999)
+
+
+@pytest.mark.parametrize("k", [128, 384, 1152])
+@pytest.mark.parametrize("variant", [11, 12, 13, 14])
+@pytest.mark.parametrize("swiglu", [False, True])
+def test_gemm_ring_variants(dev, variant, swiglu, k):
+    """The LDS-ring tiles (K a multiple of 128): ragged M and N, K from one
+    ring's worth of stages (every step past the end issues empty loads) to
+    several trips round the ring."""
+    torch, device, dit = dev
+    m, n = 300, 200 if swiglu else 520
+    cfg = datagen.get_config("c1")
+    a, w = datagen.gemm_operands(cfg, m, 2 * n if swiglu else n, k, tag=131 + variant + k)
+    A, W = device.to_device(a, "bf16"), device.to_device(w, "bf16")
+    C = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    dit.gemm_variant(variant, A, W, C, swiglu=swiglu)
+    torch.cuda.synchronize()
+    ref = O.swiglu_hidden(a, w, n) if swiglu else a.astype(np.float64) @ w.astype(np.float64).T
+    assert_parity(device.to_numpy(C), ref, "bf16", f"variant {variant} k {k}", maxabs=8e-3, cos_min=0.99999)
