@@ -25,7 +25,7 @@ EXPORTS = (
     "dit_workspace_size", "dit_stack_workspace_size", "dit_block_fwd", "dit_stack_fwd",
     "dit_timestep_mod", "dit_modnorm", "dit_gemm", "dit_gemm_swiglu", "dit_gemm_variant", "dit_attention",
     "dit_gated_residual", "dit_status_str", "dit_last_hip_error", "dit_timer_start",
-    "dit_timer_stop",
+    "dit_timer_stop", "dit_gemm_splitk",
 )
 
 
@@ -75,6 +75,7 @@ def lib() -> ctypes.CDLL:
             "dit_gemm": (i32, [i32, i32, i32, i32, vp, vp, vp, vp]),
             "dit_gemm_swiglu": (i32, [i32, i32, i32, i32, vp, vp, vp, vp]),
             "dit_gemm_variant": (i32, [i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp]),
+            "dit_gemm_splitk": (i32, [i32, i32, i32, i32, i32, vp, vp, vp, i32, i32, vp, sz, vp]),
             "dit_attention": (i32, [cfgp, vp, vp, vp, sz, vp]),
             "dit_gated_residual": (i32, [cfgp, vp, i32, vp, vp, vp, i32, vp, i32, vp]),
             "dit_status_str": (ctypes.c_char_p, [i32]),
@@ -195,6 +196,16 @@ def gemm_variant(variant: int, a, w, c, swiglu: bool = False, group_m: int = 0, 
     n = w.shape[0] // 2 if swiglu else w.shape[0]
     _check(lib().dit_gemm_variant(_dtype_code(a.dtype), variant, group_m, int(swiglu), m, n, k, _ptr(a),
                                   _ptr(w), _ptr(c), _stream(stream)), "dit_gemm_variant")
+
+
+def gemm_splitk(a, w, c, sk_tiles: int, segs: int, ws=None, swiglu: bool = False, stream=None) -> None:
+    """256 x 256 tiles with the last sk_tiles tiles split into segs K ranges
+    (fp32 partials in ws: sk_tiles * segs * 256 * 256 floats)."""
+    m, k = a.shape
+    n = w.shape[0] // 2 if swiglu else w.shape[0]
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().dit_gemm_splitk(_dtype_code(a.dtype), int(swiglu), m, n, k, _ptr(a), _ptr(w), _ptr(c),
+                                 sk_tiles, segs, _ptr(ws), nbytes, _stream(stream)), "dit_gemm_splitk")
 
 
 def attention(cfg: Config, qkvg, og, ws, stream=None) -> None:

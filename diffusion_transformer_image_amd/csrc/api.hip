@@ -1,6 +1,7 @@
 // C ABI of libdit: argument checking, workspace carving, the block and
 // stack drivers, and the timing hook.  Every entry point checks all of its
 // arguments before the first HIP call; no exception crosses the ABI.
+#include <algorithm>
 #include <mutex>
 #include <vector>
 
@@ -101,8 +102,22 @@ Dims dims(const dit_config *c) {
 
 struct BlockWs {
   char *h, *qkvg, *og, *br, *x1, *vt;
+  float *part;        // fp32 K-split partials of the projections (bf16 only)
+  size_t part_bytes;
   size_t bytes;
 };
+
+// fp32 partial bytes the default GEMM choices of one block need
+size_t block_part_bytes(const dit_config *c) {
+  if (c->dtype != DIT_BF16) return 0;
+  const int T = c->batch * c->seq_len, D = c->hidden, F = c->ffn;
+  const int nq = (2 * c->n_heads + 2 * c->n_kv_heads) * c->head_dim, hd = c->n_heads * c->head_dim;
+  size_t b = gemm_choose(T, nq, D, false).part_bytes;
+  b = std::max(b, gemm_choose(T, D, hd, false).part_bytes);
+  b = std::max(b, gemm_choose(T, F, D, true).part_bytes);
+  b = std::max(b, gemm_choose(T, D, F, false).part_bytes);
+  return b;
+}
 BlockWs carve(const dit_config *c, void *ws) {
   const Dims d = dims(c);
   BlockWs w;
@@ -119,6 +134,8 @@ BlockWs carve(const dit_config *c, void *ws) {
   w.br = take(d.T * d.D * d.es);
   w.x1 = take(d.T * d.D * 4);  // x1 = x + gate1 * A stays fp32 (one rounding, at x_out)
   w.vt = take(attention_vt_bytes(c->dtype == DIT_F32, c->batch, c->seq_len, c->n_kv_heads, c->head_dim));
+  w.part_bytes = block_part_bytes(c);
+  w.part = (float *)take(w.part_bytes);
   const size_t tmod = (size_t)c->batch * c->hidden * 4;
   w.bytes = off > tmod ? off : tmod;
   return w;
@@ -152,13 +169,13 @@ dit_status run_block(const dit_config *c, const dit_block_weights *w, const void
     return launch_modnorm(xin_f32, f32, x_in, ws.h, mod, w->mod_bias, w->norm1_w, T, L, D, c->eps, 0, s);
   }));
   DIT_TRY(timed(DIT_K_GEMM_QKVG, s, [&] {
-    return launch_gemm(f32, ws.h, w->w_qkvg, ws.qkvg, T, (int)d.nqkvg, D, s);
+    return launch_gemm(f32, ws.h, w->w_qkvg, ws.qkvg, T, (int)d.nqkvg, D, s, -1, 0, ws.part, ws.part_bytes);
   }));
   DIT_TRY(timed(DIT_K_ATTN, s, [&] {
     return launch_attention(f32, c->head_dim, ws.qkvg, ws.vt, ws.og, c->batch, L, c->n_heads, c->n_kv_heads, s);
   }));
   DIT_TRY(timed(DIT_K_GEMM_O, s, [&] {
-    return launch_gemm(f32, ws.og, w->w_o, ws.br, T, D, (int)d.hd, s);
+    return launch_gemm(f32, ws.og, w->w_o, ws.br, T, D, (int)d.hd, s, -1, 0, ws.part, ws.part_bytes);
   }));
   if (3 * (size_t)D * sizeof(float) <= 64 * 1024) {
     // x1 = x + gate1 * A (fp32) fused with h2 = modnorm(x1; norm 2)
@@ -175,10 +192,10 @@ dit_status run_block(const dit_config *c, const dit_block_weights *w, const void
     }));
   }
   DIT_TRY(timed(DIT_K_GEMM_W13, s, [&] {
-    return launch_gemm_swiglu(f32, ws.h, w->w_13, ws.qkvg, T, (int)d.F, D, s);
+    return launch_gemm_swiglu(f32, ws.h, w->w_13, ws.qkvg, T, (int)d.F, D, s, -1, 0, ws.part, ws.part_bytes);
   }));
   DIT_TRY(timed(DIT_K_GEMM_W2, s, [&] {
-    return launch_gemm(f32, ws.qkvg, w->w_2, ws.br, T, D, (int)d.F, s);
+    return launch_gemm(f32, ws.qkvg, w->w_2, ws.br, T, D, (int)d.F, s, -1, 0, ws.part, ws.part_bytes);
   }));
   DIT_TRY(timed(DIT_K_RESID, s, [&] {
     return launch_resid(x1_f32, f32, xout_f32, x1buf, ws.br, x_out, mod, w->mod_bias, T, L, D, 1, s);
@@ -365,6 +382,30 @@ dit_status dit_gemm_variant(dit_dtype dtype, int32_t variant, int32_t group_m, i
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = swiglu ? launch_gemm_swiglu(dtype == DIT_F32, a, w, c, m, n, k, s, variant, group_m)
                         : launch_gemm(dtype == DIT_F32, a, w, c, m, n, k, s, variant, group_m);
+  return e == hipSuccess ? DIT_OK : hip_fail(e);
+}
+
+dit_status dit_gemm_splitk(dit_dtype dtype, int32_t swiglu, int32_t m, int32_t n, int32_t k, const void *a,
+                           const void *w, void *c, int32_t sk_tiles, int32_t segs, void *ws, size_t ws_bytes,
+                           void *stream) {
+  if (dtype != DIT_BF16) return dtype_ok(dtype) ? DIT_ERR_UNSUPPORTED : DIT_ERR_DTYPE;
+  if (swiglu != 0 && swiglu != 1) return DIT_ERR_SHAPE;
+  dit_status st = check_gemm(dtype, m, n, k, a, w, c, swiglu ? 2 * (int64_t)n + 256 : 256);
+  if (st != DIT_OK) return st;
+  const int64_t tiles = (int64_t)((m + 255) / 256) * ((n + (swiglu ? 127 : 255)) / (swiglu ? 128 : 256));
+  const int nk = (k + 63) / 64;
+  if (sk_tiles < 0 || sk_tiles > tiles || segs < 1 || segs > 64 || segs > nk) return DIT_ERR_SHAPE;
+  const size_t need = (size_t)sk_tiles * segs * 256 * 256 * sizeof(float);
+  if (need && !ws) return DIT_ERR_WORKSPACE;
+  if (ws_bytes < need) return DIT_ERR_WORKSPACE;
+  if (ws && !aligned(ws)) return DIT_ERR_ALIGN;
+  const size_t wrows = swiglu ? 2 * (size_t)n : (size_t)n;
+  if (overlap(c, (size_t)m * n * 2, a, (size_t)m * k * 2) || overlap(c, (size_t)m * n * 2, w, wrows * k * 2))
+    return DIT_ERR_SHAPE;
+  if (need && (overlap(ws, need, a, (size_t)m * k * 2) || overlap(ws, need, w, wrows * k * 2) ||
+               overlap(ws, need, c, (size_t)m * n * 2)))
+    return DIT_ERR_SHAPE;
+  hipError_t e = launch_gemm_split(swiglu == 1, a, w, c, m, n, k, sk_tiles, segs, (float *)ws, (hipStream_t)stream);
   return e == hipSuccess ? DIT_OK : hip_fail(e);
 }
 

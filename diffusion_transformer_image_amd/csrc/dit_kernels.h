@@ -18,11 +18,25 @@ hipError_t launch_resid_modnorm(bool x_f32, bool f32, const void *x, const void 
 hipError_t launch_tmod(const float *t, const float *w1, const float *w2, float *mod, float *zs,
                        int B, int D, int tdim, hipStream_t s);
 // variant < 0 picks the default tile configuration for the shape; group_m
-// <= 0 the default tile-grouping width (row tiles per L2 group)
+// <= 0 the default tile-grouping width (row tiles per L2 group).  part (fp32,
+// part_bytes) lets the default configuration split the tail tiles along K.
 hipError_t launch_gemm(bool f32, const void *a, const void *w, void *c, int M, int N, int K,
-                       hipStream_t s, int variant = -1, int group_m = 0);
+                       hipStream_t s, int variant = -1, int group_m = 0, float *part = nullptr,
+                       size_t part_bytes = 0);
 hipError_t launch_gemm_swiglu(bool f32, const void *a, const void *w13, void *u, int M, int F,
-                              int K, hipStream_t s, int variant = -1, int group_m = 0);
+                              int K, hipStream_t s, int variant = -1, int group_m = 0,
+                              float *part = nullptr, size_t part_bytes = 0);
+// The default choice for a bf16 product (256 x 256 tiles, variant 8, when
+// sk_tiles > 0) and the fp32 partial bytes its K split needs.
+struct GemmChoice {
+  int variant, sk_tiles, segs;
+  size_t part_bytes;
+};
+GemmChoice gemm_choose(int M, int N, int K, bool swiglu);
+// 256 x 256 tiles (bf16) with the last sk_tiles tiles split into segs K
+// segments; part holds sk_tiles * segs * 256 * 256 floats.
+hipError_t launch_gemm_split(bool swiglu, const void *a, const void *w, void *c, int M, int N, int K,
+                             int sk_tiles, int segs, float *part, hipStream_t s);
 constexpr int kGemmVariants = 15;
 // vt: scratch of attention_vt_bytes() for the transposed V of every KV head
 size_t attention_vt_bytes(bool f32, int B, int L, int Hkv, int head_dim);

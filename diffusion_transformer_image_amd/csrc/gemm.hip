@@ -42,6 +42,54 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Split of the last tiles along K (stream-K style tail): tiles dp_tiles ..
+// end of the grouped tile order are each computed by `segs` workgroups, one
+// per contiguous range of K stages; those store fp32 partial tiles in `part`
+// (slot = (tile - dp_tiles) * segs + segment, BM*BN floats each, in the
+// accumulator register layout) and gemm_sk_fixup sums the segments of a tile
+// in segment order and applies the epilogue.  segs == 1: no split.
+struct SkPlan {
+  int dp_tiles;
+  int segs;
+  float *part;
+};
+
+// Linear tile id -> (row tile, column tile): walks gm row tiles at a time,
+// column-major inside a group, so tiles sharing operands run together.
+__device__ __forceinline__ void tile_coords(int pid, int m_tiles, int n_tiles, int gm, int &tm, int &tn) {
+  const int group = pid / (gm * n_tiles);
+  const int first_m = group * gm;
+  const int gsz = min(m_tiles - first_m, gm);
+  const int in_g = pid - group * gm * n_tiles;
+  tm = first_m + in_g % gsz;
+  tn = in_g / gsz;
+}
+
+// One wave's TM x TN sub-tile straight to C (element stores), with the
+// SwiGLU pairing of column blocks j and j + CB/2.
+template <typename T, int TM, int TN, int EPI>
+__device__ __forceinline__ void gemm_store_direct(const f32x4 (&acc)[TM / 16][TN / 16], T *__restrict__ C,
+                                                  int M, int N, int row0, int col0, int lane) {
+  constexpr int RB = TM / 16, CB = TN / 16;
+  const int g = lane >> 4, r16 = lane & 15;
+#pragma unroll
+  for (int j = 0; j < CB / ((EPI == EPI_SWIGLU) ? 2 : 1); ++j) {
+    const int col = col0 + j * 16 + r16;
+    if (col >= N) continue;
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = row0 + i * 16 + 4 * g + e;
+        float v;
+        if constexpr (EPI == EPI_SWIGLU) v = silu(acc[i][j][e]) * acc[i][j + CB / 2][e];
+        else v = acc[i][j][e];
+        if (row < M) C[(size_t)row * N + col] = from_f32<T>(v);
+      }
+    }
+  }
+}
+
 // Epilogue shared by the GEMM kernels: lane holds rows 4g+e of column r16 of
 // every 16x16 block of its wave's TM x TN sub-tile.  bf16 output goes through
 // LDS (16-byte chunks XOR-swizzled by row) and leaves as whole 16-byte chunks.
@@ -103,19 +151,7 @@ __device__ __forceinline__ void gemm_epilogue(const f32x4 (&acc)[BM / WM / 16][B
       }
     }
   } else {
-#pragma unroll
-    for (int j = 0; j < CB / ((EPI == EPI_SWIGLU) ? 2 : 1); ++j) {
-      const int col = col0 + j * 16 + r16;
-      if (col >= N) continue;
-#pragma unroll
-      for (int i = 0; i < RB; ++i) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int row = row0 + i * 16 + 4 * g + e;
-          if (row < M) C[(size_t)row * N + col] = from_f32<T>(out_val(i, j, e));
-        }
-      }
-    }
+    gemm_store_direct<T, TM, TN, EPI>(acc, C, M, N, row0, col0, lane);
   }
 }
 
@@ -130,7 +166,7 @@ template <typename T, int BM, int BN, int BKB, int STAGES, int WM, int WN, int E
 __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(const T *__restrict__ A,
                                                            const T *__restrict__ W,
                                                            T *__restrict__ C, int M, int N, int K,
-                                                           int m_tiles, int n_tiles, int gm) {
+                                                           int m_tiles, int n_tiles, int gm, SkPlan sk) {
   constexpr int NW = WM * WN;
   constexpr int CPR = BKB / 16;             // 16-byte chunks per row per stage
   constexpr int RPB = 1024 / BKB;           // rows per 1 KiB DMA block
@@ -153,15 +189,23 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(const T *__restrict__
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
   const int wm = wave / WN, wn = wave % WN;
 
-  // ---- tile id: XCD-contiguous remap, then grouped (GM row tiles) order
-  const int nwg = m_tiles * n_tiles;
-  int pid = blockIdx.x;
-  if ((nwg & 7) == 0) pid = (pid & 7) * (nwg >> 3) + (pid >> 3);
-  const int group = pid / (gm * n_tiles);
-  const int first_m = group * gm;
-  const int gsz = min(m_tiles - first_m, gm);
-  const int in_g = pid - group * gm * n_tiles;
-  const int tm = first_m + in_g % gsz, tn = in_g / gsz;
+  // ---- tile id: whole tiles first (XCD-contiguous remap, then grouped
+  // order), then the K segments of the split tail tiles
+  const int nk_all = (K + KSTAGE - 1) / KSTAGE;
+  int pid, kb = 0, nk = nk_all, slot = -1;
+  if ((int)blockIdx.x < sk.dp_tiles) {
+    const int nwg = sk.dp_tiles;
+    pid = blockIdx.x;
+    if ((nwg & 7) == 0) pid = (pid & 7) * (nwg >> 3) + (pid >> 3);
+  } else {
+    slot = blockIdx.x - sk.dp_tiles;
+    const int seg = slot % sk.segs;
+    pid = sk.dp_tiles + slot / sk.segs;
+    kb = seg * nk_all / sk.segs;
+    nk = (seg + 1) * nk_all / sk.segs - kb;
+  }
+  int tm, tn;
+  tile_coords(pid, m_tiles, n_tiles, gm, tm, tn);
   const int m0 = tm * BM;
   // SwiGLU: W holds [W1; W3] with N = F rows each; the tile covers F-columns
   // [n0, n0 + BN/2) and reads those rows of both halves.
@@ -205,7 +249,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(const T *__restrict__
   }
 
   auto issue_stage = [&](int kt, int buf) {
-    const int k0 = kt * KSTAGE;
+    const int k0 = (kb + kt) * KSTAGE;
     const int kc_ok = (k0 + KSTAGE > K) ? (K - k0) / EPC : CPR;  // chunks inside K
     char *base = smem + buf * STAGE_BYTES;
 #pragma unroll
@@ -240,8 +284,6 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(const T *__restrict__
     }
     brow[j] = r * BKB;
   }
-
-  const int nk = (K + KSTAGE - 1) / KSTAGE;
 
   auto load_frags = [&](const char *sb, int ks, u32x4(&af)[RB], u32x4(&bf)[CB]) {
     const int pc = ((ks * 4 + g) ^ swz) * 16;
@@ -317,8 +359,45 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(const T *__restrict__
   }
   }
 
+  if (slot >= 0) {  // a K segment of a split tile: fp32 partial, register layout
+    float *dst = sk.part + (size_t)slot * BM * BN + (size_t)wave * RB * CB * 256 + lane * 4;
+#pragma unroll
+    for (int i = 0; i < RB; ++i)
+#pragma unroll
+      for (int j = 0; j < CB; ++j) *reinterpret_cast<f32x4 *>(dst + (i * CB + j) * 256) = acc[i][j];
+    return;
+  }
   gemm_epilogue<T, BM, BN, NW, WM, WN, EPI, STAGES * STAGE_BYTES>(acc, smem, C, M, N, m0, n0, wave,
                                                                  lane);
+}
+
+// Sums the K-segment partials of each split tile in segment order and
+// stores the result through the kernel's epilogue (one workgroup = one wave
+// sub-tile of one split tile).
+template <typename T, int BM, int BN, int WM, int WN, int EPI>
+__global__ __launch_bounds__(64) void gemm_sk_fixup(const float *__restrict__ part, T *__restrict__ C,
+                                                    int M, int N, int m_tiles, int n_tiles, int gm,
+                                                    int dp_tiles, int segs) {
+  constexpr int NW = WM * WN, TM = BM / WM, TN = BN / WN, RB = TM / 16, CB = TN / 16;
+  const int t = blockIdx.x / NW, wave = blockIdx.x % NW, lane = threadIdx.x;
+  const int wm = wave / WN, wn = wave % WN;
+  f32x4 acc[RB][CB];
+#pragma unroll
+  for (int i = 0; i < RB; ++i)
+#pragma unroll
+    for (int j = 0; j < CB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int sgm = 0; sgm < segs; ++sgm) {
+    const float *src = part + (size_t)(t * segs + sgm) * BM * BN + (size_t)wave * RB * CB * 256 + lane * 4;
+#pragma unroll
+    for (int i = 0; i < RB; ++i)
+#pragma unroll
+      for (int j = 0; j < CB; ++j) acc[i][j] += *reinterpret_cast<const f32x4 *>(src + (i * CB + j) * 256);
+  }
+  int tm, tn;
+  tile_coords(dp_tiles + t, m_tiles, n_tiles, gm, tm, tn);
+  const int row0 = tm * BM + wm * TM;
+  const int col0 = (EPI == EPI_SWIGLU) ? tn * (BN / 2) + wn * (TN / 2) : tn * BN + wn * TN;
+  gemm_store_direct<T, TM, TN, EPI>(acc, C, M, N, row0, col0, lane);
 }
 
 // Calls f(integral_constant<I>) for I = B..E-1 in order while f returns true.
@@ -524,12 +603,18 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_ring_kernel(const bf16 *__re
 
 template <typename T, int BM, int BN, int BKB, int STAGES, int WM, int WN, int EPI, bool PIPE = false>
 static hipError_t launch_gemm_t(const void *a, const void *w, void *c, int M, int N, int K,
-                                hipStream_t s, int gm) {
+                                hipStream_t s, int gm, int sk_tiles = 0, int segs = 1, float *part = nullptr) {
   const int mt = (M + BM - 1) / BM;
   const int nt = (EPI == EPI_SWIGLU) ? (N + BN / 2 - 1) / (BN / 2) : (N + BN - 1) / BN;
-  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, BKB, STAGES, WM, WN, EPI, PIPE>), dim3(mt * nt),
-                     dim3(WM * WN * 64), 0, s, (const T *)a, (const T *)w, (T *)c, M, N, K, mt, nt,
-                     gm);
+  if (segs <= 1 || !part) sk_tiles = 0;
+  const SkPlan plan{mt * nt - sk_tiles, sk_tiles ? segs : 1, part};
+  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, BKB, STAGES, WM, WN, EPI, PIPE>),
+                     dim3(plan.dp_tiles + sk_tiles * plan.segs), dim3(WM * WN * 64), 0, s, (const T *)a,
+                     (const T *)w, (T *)c, M, N, K, mt, nt, gm, plan);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || sk_tiles == 0) return e;
+  hipLaunchKernelGGL((gemm_sk_fixup<T, BM, BN, WM, WN, EPI>), dim3(sk_tiles * WM * WN), dim3(64), 0, s,
+                     (const float *)part, (T *)c, M, N, mt, nt, gm, plan.dp_tiles, plan.segs);
   return hipGetLastError();
 }
 
@@ -543,24 +628,60 @@ static hipError_t launch_ring_t(const void *a, const void *w, void *c, int M, in
   return hipGetLastError();
 }
 
+// Default configuration of a bf16 product, in units of one round of
+// 256 x 256 tiles over the 256 CUs:
+//  * whole 256 x 256 tiles: ceil(tiles / 256) rounds;
+//  * whole 192 x 256 tiles: ceil(tiles192 / 256) rounds of ~0.85 (measured
+//    per-round cost of the smaller tile);
+//  * 256 x 256 tiles with the partial last round split along K into `segs`
+//    segments per tile (segs = 256 / tail tiles, at most 8 and at most
+//    nk / 2): full rounds + 1/segs + the fp32 partials and the fixup pass,
+//    ~5 us + 0.13 us per 256 KiB partial (written once, read once), against
+//    a round of ~97 us per 4096 of K (measured on the block's shapes).
+//    Needs the partial buffer (segs * tail * 256 KiB).
+GemmChoice gemm_choose(int M, int N, int K, bool swiglu) {
+  GemmChoice ch{8, 0, 1, 0};
+  const int ncols = swiglu ? 128 : 256;  // output columns per tile
+  const long nt = (N + ncols - 1) / ncols;
+  const long t256 = (long)((M + 255) / 256) * nt, t192 = (long)((M + 191) / 192) * nt;
+  const double r256 = std::ceil(t256 / 256.0), r192 = std::ceil(t192 / 256.0) * 0.85;
+  double best = r256;
+  if (r192 < best) { best = r192; ch.variant = 9; }
+  const long full = t256 / 256, tail = t256 % 256;
+  const int nk = (K + 63) / 64;
+  if (full >= 1 && tail > 0) {
+    int segs = (int)std::min<long>(8, 256 / tail);
+    segs = std::min(segs, nk / 2);
+    if (segs >= 2) {
+      const double round_us = 97.0 * K / 4096.0;
+      const double rsk = full + 1.0 / segs + (5.0 + 0.131 * tail * segs) / round_us;
+      if (rsk < best) {
+        ch = GemmChoice{8, (int)tail, segs, (size_t)tail * segs * 256 * 256 * sizeof(float)};
+      }
+    }
+  }
+  return ch;
+}
+
 // Tile configurations, selectable for tuning (variant < 0: the default).
 template <int EPI>
 static hipError_t gemm_dispatch(bool f32, int variant, int gm, const void *a, const void *w,
-                                void *c, int M, int N, int K, hipStream_t s) {
+                                void *c, int M, int N, int K, hipStream_t s, float *part,
+                                size_t part_bytes) {
   if (gm <= 0) gm = 8;
   if (f32) return launch_gemm_t<float, 256, 256, 128, 2, 2, 4, EPI>(a, w, c, M, N, K, s, gm);
   if (variant < 0) {
-    // software-pipelined 8-wave tiles; 192 x 256 instead of 256 x 256 when
-    // its tile count fills the 256 CUs in fuller rounds (e.g. N = 4096 at
-    // 9216 rows: 768 tiles = 3 full rounds vs 576 = 2.25).  Below a 2 %
-    // fill advantage the larger tile wins: it moves fewer operand bytes
-    // per FLOP.
+    const GemmChoice ch = gemm_choose(M, N, K, EPI == EPI_SWIGLU);
+    if (ch.sk_tiles > 0 && part && part_bytes >= ch.part_bytes)
+      return launch_gemm_t<bf16, 256, 256, 128, 2, 2, 4, EPI, true>(a, w, c, M, N, K, s, gm, ch.sk_tiles,
+                                                                    ch.segs, part);
+    // without the partial buffer: whole tiles, the fuller of 192 / 256 rows
     const int ncols = (EPI == EPI_SWIGLU) ? 128 : 256;
     auto fill = [&](int bm) {
       const double tiles = (double)((M + bm - 1) / bm) * ((N + ncols - 1) / ncols);
       return tiles / (std::ceil(tiles / 256.0) * 256.0);
     };
-    variant = (fill(192) > fill(256) + 0.02) ? 9 : 8;
+    variant = ch.sk_tiles > 0 ? ((fill(192) > fill(256) + 0.02) ? 9 : 8) : ch.variant;
   }
   switch (variant) {
     case 0: return launch_gemm_t<bf16, 256, 256, 64, 4, 2, 2, EPI>(a, w, c, M, N, K, s, gm);
@@ -583,13 +704,23 @@ static hipError_t gemm_dispatch(bool f32, int variant, int gm, const void *a, co
 }
 
 hipError_t launch_gemm(bool f32, const void *a, const void *w, void *c, int M, int N, int K,
-                       hipStream_t s, int variant, int group_m) {
-  return gemm_dispatch<EPI_STORE>(f32, variant, group_m, a, w, c, M, N, K, s);
+                       hipStream_t s, int variant, int group_m, float *part, size_t part_bytes) {
+  return gemm_dispatch<EPI_STORE>(f32, variant, group_m, a, w, c, M, N, K, s, part, part_bytes);
 }
 
 hipError_t launch_gemm_swiglu(bool f32, const void *a, const void *w13, void *u, int M, int F,
-                              int K, hipStream_t s, int variant, int group_m) {
-  return gemm_dispatch<EPI_SWIGLU>(f32, variant, group_m, a, w13, u, M, F, K, s);
+                              int K, hipStream_t s, int variant, int group_m, float *part,
+                              size_t part_bytes) {
+  return gemm_dispatch<EPI_SWIGLU>(f32, variant, group_m, a, w13, u, M, F, K, s, part, part_bytes);
+}
+
+hipError_t launch_gemm_split(bool swiglu, const void *a, const void *w, void *c, int M, int N, int K,
+                             int sk_tiles, int segs, float *part, hipStream_t s) {
+  if (swiglu)
+    return launch_gemm_t<bf16, 256, 256, 128, 2, 2, 4, EPI_SWIGLU, true>(a, w, c, M, N, K, s, 8, sk_tiles,
+                                                                         segs, part);
+  return launch_gemm_t<bf16, 256, 256, 128, 2, 2, 4, EPI_STORE, true>(a, w, c, M, N, K, s, 8, sk_tiles, segs,
+                                                                      part);
 }
 
 }  // namespace dit

@@ -109,7 +109,9 @@ typedef enum {
 /* Workspace bytes needed by dit_block_fwd for this configuration
  * (0 if cfg is invalid).  Holds the normalised activations, the Q|K|V|G
  * projection (later reused for the SwiGLU hidden U), the transposed V, the
- * gated attention output, the branch outputs and x1 (fp32). */
+ * gated attention output, the branch outputs, x1 (fp32) and, for bf16,
+ * the fp32 partial tiles of projections whose last round of output tiles
+ * is split along K (at most 256 tiles' worth, 64 MiB). */
 size_t dit_workspace_size(const dit_config *cfg /* host */);
 
 /* Workspace bytes needed by dit_stack_fwd: the block workspace plus one
@@ -193,6 +195,25 @@ dit_status dit_gemm_swiglu(dit_dtype dtype, int32_t m, int32_t f, int32_t k, con
 dit_status dit_gemm_variant(dit_dtype dtype, int32_t variant, int32_t group_m, int32_t swiglu,
                             int32_t m, int32_t n, int32_t k, const void *a, const void *w, void *c,
                             void *stream);
+
+/* The bf16 product (swiglu = 0: C = A W^T; 1: the SwiGLU hidden as in
+ * dit_gemm_swiglu with F = n) on 256 x 256 output tiles (256 x 128 output
+ * columns for SwiGLU), with the last sk_tiles tiles of the tile order each
+ * split into segs contiguous ranges of K (64-element stages, segs <= the
+ * stage count): every range is one workgroup that stores an fp32 partial
+ * tile in ws, and a second pass sums the partials of each tile in range
+ * order and applies the output step, so the result is deterministic.  This
+ * is how the block keeps all CUs busy when the tile count leaves a mostly
+ * empty last round; the block chooses sk_tiles and segs itself and this
+ * entry point exposes the split for tests and tuning.
+ * ws: sk_tiles * segs * 256 * 256 floats (may be NULL when that is 0),
+ * 16-byte aligned, overlapping no operand.  dtype must be DIT_BF16
+ * (DIT_F32 -> DIT_ERR_UNSUPPORTED).  sk_tiles outside 0..tiles, segs
+ * outside 1..min(64, stages) -> DIT_ERR_SHAPE; ws too small ->
+ * DIT_ERR_WORKSPACE. */
+dit_status dit_gemm_splitk(dit_dtype dtype, int32_t swiglu, int32_t m, int32_t n, int32_t k, const void *a,
+                           const void *w, void *c, int32_t sk_tiles, int32_t segs, void *ws, size_t ws_bytes,
+                           void *stream);
 
 /* Gated grouped-query attention over the rows of qkvg [T, (2H+2Hkv)*d]
  * (column blocks Q | K | V | G, as produced by the QKVG projection):

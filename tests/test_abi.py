@@ -124,6 +124,16 @@ def test_step_argument_checks():
     assert S(L.dit_gemm_variant(1, 8, 65, 0, 16, 16, 16, P, P + G, P + 2 * G, None)) == "DIT_ERR_SHAPE"
     assert S(L.dit_gemm_variant(1, 8, -1, 0, 16, 16, 16, P, P + G, P + 2 * G, None)) == "DIT_ERR_SHAPE"
     assert S(L.dit_gemm_variant(1, 8, 4, 2, 16, 16, 16, P, P + G, P + 2 * G, None)) == "DIT_ERR_SHAPE"
+    # split-K tail: dtype, tile / segment ranges, workspace size and overlap
+    sk = lambda *a: S(L.dit_gemm_splitk(*a))
+    assert sk(0, 0, 512, 512, 256, P, P + G, P + 2 * G, 1, 2, P + 3 * G, 1 << 20, None) == "DIT_ERR_UNSUPPORTED"
+    assert sk(1, 0, 512, 512, 256, P, P + G, P + 2 * G, 5, 2, P + 3 * G, 1 << 24, None) == "DIT_ERR_SHAPE"  # 4 tiles
+    assert sk(1, 0, 512, 512, 256, P, P + G, P + 2 * G, 2, 5, P + 3 * G, 1 << 24, None) == "DIT_ERR_SHAPE"  # 4 stages
+    assert sk(1, 0, 512, 512, 256, P, P + G, P + 2 * G, 2, 0, P + 3 * G, 1 << 24, None) == "DIT_ERR_SHAPE"
+    assert sk(1, 0, 512, 512, 256, P, P + G, P + 2 * G, 2, 2, P + 3 * G, 4 * 65536 * 4 - 4, None) == "DIT_ERR_WORKSPACE"
+    assert sk(1, 0, 512, 512, 256, P, P + G, P + 2 * G, 2, 2, 0, 1 << 24, None) == "DIT_ERR_WORKSPACE"
+    assert sk(1, 0, 512, 512, 256, P, P + G, P + 2 * G, 2, 2, P + 2 * G + 64, 1 << 24, None) == "DIT_ERR_SHAPE"
+    assert sk(1, 2, 512, 512, 256, P, P + G, P + 2 * G, 0, 1, 0, 0, None) == "DIT_ERR_SHAPE"
     assert S(L.dit_attention(ctypes.byref(c), P, 0, P + 2 * G, 1 << 30, None)) == "DIT_ERR_NULL"
     assert S(L.dit_attention(ctypes.byref(c), P, P + 64, P + 2 * G, 1 << 30, None)) == "DIT_ERR_SHAPE"
     assert S(L.dit_attention(ctypes.byref(c), P, P + G, P + 2 * G, 16, None)) == "DIT_ERR_WORKSPACE"

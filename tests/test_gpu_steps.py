@@ -238,3 +238,32 @@ def test_gemm_ring_variants(dev, variant, swiglu, k):
     torch.cuda.synchronize()
     ref = O.swiglu_hidden(a, w, n) if swiglu else a.astype(np.float64) @ w.astype(np.float64).T
     assert_parity(device.to_numpy(C), ref, "bf16", f"variant {variant} k {k}", maxabs=8e-3, cos_min=0.99999)
+
+
+@pytest.mark.parametrize("swiglu", [False, True])
+@pytest.mark.parametrize("m,n,k,sk_tiles,segs", [
+    (300, 520, 328, 6, 3),     # every tile split, ragged M, N and K (K tail in the last segment)
+    (600, 776, 1024, 2, 7),    # only the last two tiles split, uneven segment lengths
+    (256, 256, 128, 1, 2),     # one tile, two one-stage segments
+    (513, 264, 4096, 3, 8),    # ragged row tile among the split ones, long K
+])
+def test_gemm_split_tail(dev, m, n, k, sk_tiles, segs, swiglu):
+    """K-split tail tiles: fp32 partials summed in segment order by the fixup
+    pass, whole tiles as before, SwiGLU applied after the sum."""
+    torch, device, dit = dev
+    if swiglu:
+        n = (n // 2 + 7) // 8 * 8
+    tiles = ((m + 255) // 256) * ((n + (127 if swiglu else 255)) // (128 if swiglu else 256))
+    sk_tiles = min(sk_tiles, tiles)
+    cfg = datagen.get_config("c1")
+    a, w = datagen.gemm_operands(cfg, m, 2 * n if swiglu else n, k, tag=171 + segs + k)
+    A, W = device.to_device(a, "bf16"), device.to_device(w, "bf16")
+    C = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(max(sk_tiles * segs * 65536, 1), dtype=torch.float32, device="cuda")
+    dit.gemm_splitk(A, W, C, sk_tiles, segs, ws, swiglu=swiglu)
+    C2 = torch.empty_like(C)
+    dit.gemm_splitk(A, W, C2, sk_tiles, segs, ws, swiglu=swiglu)
+    torch.cuda.synchronize()
+    ref = O.swiglu_hidden(a, w, n) if swiglu else a.astype(np.float64) @ w.astype(np.float64).T
+    assert_parity(device.to_numpy(C), ref, "bf16", f"split {sk_tiles}x{segs}", maxabs=8e-3, cos_min=0.99999)
+    assert torch.equal(C, C2), "split-K tail is not deterministic"
