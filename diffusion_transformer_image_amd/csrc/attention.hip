@@ -21,11 +21,15 @@
 //    lane owns one query column: the softmax statistics of a query live in
 //    4 lanes (one per lane group) and the probabilities P^T are already in
 //    the register layout of the B operand of O^T = V^T P^T;
-//  * softmax in fp32 base 2 with the 1/sqrt(d) scale folded into one FMA.
-//    The reference maximum is only raised when a tile's maximum exceeds it
-//    by more than 8 (log2 units), so probabilities stay <= 2^8 and the
-//    rescale of the accumulators (a wave-uniform branch) is rare; the
-//    quotient O / l is unchanged by the choice of reference;
+//  * softmax in fp32 base 2 with the 1/sqrt(d) scale folded into one FMA,
+//    against a lazy reference: the numerators of a tile are computed with
+//    the current reference and packed to bf16 (the B operand of P V), and
+//    the row sums are taken from the packed values with v_dot2 (two keys
+//    per instruction).  Only if a lane's partial sum leaves [0, 2^30] (a
+//    score > 30 log2 units above the reference, or no reference yet) does
+//    the wave recompute the tile's scores, take their maximum, rescale the
+//    accumulators and redo the numerators; the quotient O / l does not
+//    depend on the reference.  No per-tile maximum, no shuffles;
 //  * LDS data is XOR-swizzled (K by 16-byte chunk at DMA time, V^T when
 //    the V^T pass writes it, which also groups each lane's keys of one
 //    MFMA into one chunk) so every fragment is one ds_read_b128 and 16
@@ -185,32 +189,30 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const T *__restrict__ qkv
   float mref[QB], lrow[QB];
 #pragma unroll
   for (int k = 0; k < QB; ++k) { mref[k] = -INFINITY; lrow[k] = 0.f; }
-  const float tau = 8.0f / sc;  // raw-score margin: probabilities stay <= 2^8
 
   const int nt = (L + ATT_BK - 1) / ATT_BK;
 #pragma unroll
   for (int p = 0; p < PD; ++p)
     if (p < nt) issue_tile(p, p);
 
-  for (int t = 0; t < nt; ++t) {
-    // this wave's DMA of tile t is done once only the (up to PD-1) later
-    // tiles already issued may be pending
-    if (t + PD - 1 < nt) att_wait_vmcnt<DMA_PER_TILE * (PD - 1)>();
-    else att_wait_vmcnt<0>();
-    __syncthreads();  // all of tile t landed; every wave is done with tile t-1
-    if (t + PD < nt) issue_tile(t + PD, (t + PD) % NSTAGE);
-    const char *kt = smem + (t % NSTAGE) * STAGE;
-    const char *vtl = kt + KTILE;
+  // lane-dependent parts of the fragment addresses inside a stage buffer
+  // (the 16-row block and the buffer base are added as immediates / one
+  // uniform offset per tile)
+  int koff[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) koff[ks] = r16 * KROW + (((ks * 4 + g) ^ r16) * 16);
+  const int vrow = KTILE + r16 * VROW;
 
-    // S^T[kb][qb]: lane holds keys kb*16 + 4g + i of query qb*16 + r16.
-    // All K fragments of the tile are requested before the first MFMA.
+  // S^T[kb][qb] = K Q^T for the tile in buffer kt: lane holds keys
+  // kb*16 + 4g + i of query qb*16 + r16 (all K fragments requested first);
+  // keys past the end of the sequence get -inf.
+  auto scores = [&](const char *kt, int t, f32x4(&s)[KB][QB]) {
     u32x4 kf[KB][KS];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)  // row = kb*16 + r16, so (row & 15) = r16
-        kf[kb][ks] = *reinterpret_cast<const u32x4 *>(kt + (kb * 16 + r16) * KROW + (((ks * 4 + g) ^ r16) * 16));
-    f32x4 s[KB][QB];
+      for (int ks = 0; ks < KS; ++ks)
+        kf[kb][ks] = *reinterpret_cast<const u32x4 *>(kt + koff[ks] + kb * 16 * KROW);
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
@@ -220,9 +222,10 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const T *__restrict__ qkv
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) s[kb][qb] = mma16<T>(kf[kb][ks], qf[qb][ks], s[kb][qb]);
     }
-
-    // mask keys past the end of the sequence (last tile only)
     if ((t + 1) * ATT_BK > L) {
+      // a real branch (the empty volatile asm cannot be speculated): without
+      // it the compiler turns the mask into selects on every tile
+      asm volatile("" ::: "memory");
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -231,38 +234,95 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const T *__restrict__ qkv
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) s[kb][qb][i] = -INFINITY;
     }
+  };
 
-    // online softmax per query column
+  // Numerators p = 2^(s*sc - mref*sc) against the running reference, as the
+  // B operand of O^T += V^T P^T (bf16: one 16-byte fragment per pair of
+  // 16-key blocks; fp32: the values themselves), and this lane's partial row
+  // sums, taken from the values the MFMA will use.
+  constexpr int NPF = (ES == 2) ? KB / 2 : KB;
+  auto numerators = [&](f32x4(&s)[KB][QB], u32x4(&pf)[NPF][QB], float (&lp)[QB]) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      float mx = s[0][qb][0];
+      const float msc = mref[qb] * sc;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[kb][qb][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const bool need = mx > mref[qb] + tau;  // always true on the first tile
-      if (__any(need)) {
-        const float mnew = need ? mx : mref[qb];
-        const float alpha = __builtin_amdgcn_exp2f((mref[qb] - mnew) * sc);
+        for (int i = 0; i < 4; ++i) s[kb][qb][i] = __builtin_amdgcn_exp2f(fmaf(s[kb][qb][i], sc, -msc));
+      float sum = 0.f;
+      if constexpr (ES == 2) {
+#pragma unroll
+        for (int pr = 0; pr < KB / 2; ++pr) {
+          bf16x8 pv;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            pv[i] = (bf16)s[2 * pr][qb][i];
+            pv[4 + i] = (bf16)s[2 * pr + 1][qb][i];
+          }
+          pf[pr][qb] = __builtin_bit_cast(u32x4, pv);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const bf16x2 two = {pv[2 * i], pv[2 * i + 1]};
+            sum = __builtin_amdgcn_fdot2_f32_bf16(two, bf16x2{(bf16)1.0f, (bf16)1.0f}, sum, false);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          pf[kb][qb] = __builtin_bit_cast(u32x4, s[kb][qb]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sum += s[kb][qb][i];
+        }
+      }
+      lp[qb] = sum;
+    }
+  };
+
+  for (int t = 0; t < nt; ++t) {
+    // this wave's DMA of tile t is done once only the (up to PD-1) later
+    // tiles already issued may be pending
+    if (t + PD - 1 < nt) att_wait_vmcnt<DMA_PER_TILE * (PD - 1)>();
+    else att_wait_vmcnt<0>();
+    __syncthreads();  // all of tile t landed; every wave is done with tile t-1
+    if (t + PD < nt) issue_tile(t + PD, (t + PD) % NSTAGE);
+    const char *kt = smem + (t % NSTAGE) * STAGE;
+
+    f32x4 s[KB][QB];
+    scores(kt, t, s);
+    u32x4 pf[NPF][QB];
+    float lp[QB];
+    numerators(s, pf, lp);
+    // Lazy reference: a lane's partial row sum above 2^30 (or not finite)
+    // means a score more than 30 (log2 units) above the reference, or no
+    // reference yet (first tile).  Then the wave recomputes the tile's
+    // scores, raises the reference to the running maximum, rescales the
+    // accumulators and redoes the numerators; O / l does not depend on the
+    // reference, which only keeps the numerators in range.
+    bool big = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) big |= !(lp[qb] <= 0x1p30f);
+    if (__any(big)) {
+      scores(kt, t, s);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        float mx = s[0][qb][0];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[kb][qb][i]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mnew = fmaxf(mref[qb], mx);
+        const float alpha = __builtin_amdgcn_exp2f((mref[qb] - mnew) * sc);  // 0 when mref = -inf
         mref[qb] = mnew;
         lrow[qb] *= alpha;
 #pragma unroll
         for (int db = 0; db < DB; ++db) o[db][qb] *= alpha;
       }
-      const float msc = mref[qb] * sc;
-      float sum = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][qb][i], sc, -msc));
-          s[kb][qb][i] = p;
-          sum += p;
-        }
-      lrow[qb] += sum;
+      numerators(s, pf, lp);
     }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) lrow[qb] += lp[qb];
 
     // O^T[db][qb] += V^T[db rows] * P^T; the V^T fragment of row
     // d = db*16 + r16 for k-slice c is one 16-byte chunk at c ^ swizzle(d)
@@ -271,41 +331,27 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const T *__restrict__ qkv
       // keys are (2pr)*16 + 4g + {0..3} and (2pr+1)*16 + 4g + {0..3}
 #pragma unroll
       for (int pr = 0; pr < KB / 2; ++pr) {
-        u32x4 pf[QB];
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          bf16x8 pv;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            pv[i] = (bf16)s[2 * pr][qb][i];
-            pv[4 + i] = (bf16)s[2 * pr + 1][qb][i];
-          }
-          pf[qb] = __builtin_bit_cast(u32x4, pv);
-        }
         const int cpos = ((pr * 4 + g) ^ (r16 & 7)) * 16;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const u32x4 vf = *reinterpret_cast<const u32x4 *>(vtl + (db * 16 + r16) * VROW + cpos);
+          const u32x4 vf = *reinterpret_cast<const u32x4 *>(kt + vrow + db * 16 * VROW + cpos);
 #pragma unroll
-          for (int qb = 0; qb < QB; ++qb) o[db][qb] = mma16<T>(vf, pf[qb], o[db][qb]);
+          for (int qb = 0; qb < QB; ++qb) o[db][qb] = mma16<T>(vf, pf[pr][qb], o[db][qb]);
         }
       }
     } else {
       // fp32: four MFMAs (k = 4 each) per 16-key block; chunk kb*4 + g
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        u32x4 pf[QB];
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) pf[qb] = __builtin_bit_cast(u32x4, s[kb][qb]);
+        const int cpos = ((kb * 4 + g) ^ r16) * 16;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const u32x4 vf = *reinterpret_cast<const u32x4 *>(vtl + (db * 16 + r16) * VROW + (((kb * 4 + g) ^ r16) * 16));
+          const u32x4 vf = *reinterpret_cast<const u32x4 *>(kt + vrow + db * 16 * VROW + cpos);
 #pragma unroll
-          for (int qb = 0; qb < QB; ++qb) o[db][qb] = mma16<T>(vf, pf[qb], o[db][qb]);
+          for (int qb = 0; qb < QB; ++qb) o[db][qb] = mma16<T>(vf, pf[kb][qb], o[db][qb]);
         }
       }
     }
-
   }
 
   // ---- epilogue: row sums over the 4 lane groups, normalise, gate, store
