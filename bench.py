@@ -9,9 +9,10 @@ SwiGLU width 11008, bf16 with fp32 accumulation.  Inputs are seeded
 synthetic arrays, resident in HBM before timing starts.
 
 Prints one JSON line.  ``value`` is tokens/s of the whole step.  The
-``roofline`` object is for the dominant kernel (the SwiGLU up/gate GEMM),
-timed with HIP events recorded around each of its launches on its own
-stream inside the timed region.  ``cpu_baseline`` times the fp64 oracle on
+``roofline`` object is for the dominant kernel (the SwiGLU up/gate GEMM:
+the tile kernel and, when the last round of tiles is split along K, its
+fixup pass), timed with HIP events recorded around each of its launches on
+its own stream inside the timed region.  ``cpu_baseline`` times the fp64 oracle on
 one sample of the same workload on the host cores.
 """
 from __future__ import annotations
@@ -217,7 +218,8 @@ def main() -> int:
     dom_avg = dom_ms / max(dom_n, 1)
     dom_flops = fpt[dom] * cfg.tokens
     achieved = dom_flops / (dom_avg * 1e-3) / 1e12
-    roofline = {"bound": "mfma", "kernel": "gemm_kernel (h2 * W13^T with the SwiGLU epilogue)",
+    roofline = {"bound": "mfma", "kernel": "gemm_kernel + gemm_sk_fixup (h2 * W13^T with the SwiGLU "
+                                           "epilogue; last round of tiles split along K, fixup pass)",
                 "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / PEAK_BF16_TFLOPS, "traffic": load_traffic("gemm.hip"),
                 "flops_per_launch": dom_flops, "avg_launch_ms": dom_avg, "launches": dom_n}

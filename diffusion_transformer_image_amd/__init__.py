@@ -18,6 +18,7 @@ from ._lib import (  # noqa: F401
     config_of,
     gated_residual,
     gemm,
+    gemm_plan,
     gemm_splitk,
     gemm_swiglu,
     gemm_variant,

@@ -25,7 +25,7 @@ EXPORTS = (
     "dit_workspace_size", "dit_stack_workspace_size", "dit_block_fwd", "dit_stack_fwd",
     "dit_timestep_mod", "dit_modnorm", "dit_gemm", "dit_gemm_swiglu", "dit_gemm_variant", "dit_attention",
     "dit_gated_residual", "dit_status_str", "dit_last_hip_error", "dit_timer_start",
-    "dit_timer_stop", "dit_gemm_splitk",
+    "dit_timer_stop", "dit_gemm_splitk", "dit_gemm_plan",
 )
 
 
@@ -76,6 +76,8 @@ def lib() -> ctypes.CDLL:
             "dit_gemm_swiglu": (i32, [i32, i32, i32, i32, vp, vp, vp, vp]),
             "dit_gemm_variant": (i32, [i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp]),
             "dit_gemm_splitk": (i32, [i32, i32, i32, i32, i32, vp, vp, vp, i32, i32, vp, sz, vp]),
+            "dit_gemm_plan": (i32, [i32, i32, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32),
+                                    ctypes.POINTER(i32), ctypes.POINTER(sz)]),
             "dit_attention": (i32, [cfgp, vp, vp, vp, sz, vp]),
             "dit_gated_residual": (i32, [cfgp, vp, i32, vp, vp, vp, i32, vp, i32, vp]),
             "dit_status_str": (ctypes.c_char_p, [i32]),
@@ -206,6 +208,14 @@ def gemm_splitk(a, w, c, sk_tiles: int, segs: int, ws=None, swiglu: bool = False
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().dit_gemm_splitk(_dtype_code(a.dtype), int(swiglu), m, n, k, _ptr(a), _ptr(w), _ptr(c),
                                  sk_tiles, segs, _ptr(ws), nbytes, _stream(stream)), "dit_gemm_splitk")
+
+
+def gemm_plan(m: int, n: int, k: int, swiglu: bool = False) -> dict:
+    """The tile configuration the block uses for a bf16 product of this shape."""
+    v, t, sg, pb = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32(), ctypes.c_size_t()
+    _check(lib().dit_gemm_plan(m, n, k, int(swiglu), ctypes.byref(v), ctypes.byref(t), ctypes.byref(sg),
+                               ctypes.byref(pb)), "dit_gemm_plan")
+    return {"variant": v.value, "sk_tiles": t.value, "segs": sg.value, "part_bytes": pb.value}
 
 
 def attention(cfg: Config, qkvg, og, ws, stream=None) -> None:

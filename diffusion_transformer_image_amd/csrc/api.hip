@@ -385,6 +385,18 @@ dit_status dit_gemm_variant(dit_dtype dtype, int32_t variant, int32_t group_m, i
   return e == hipSuccess ? DIT_OK : hip_fail(e);
 }
 
+dit_status dit_gemm_plan(int32_t m, int32_t n, int32_t k, int32_t swiglu, int32_t *variant, int32_t *sk_tiles,
+                         int32_t *segs, size_t *part_bytes) {
+  if (m <= 0 || n <= 0 || k <= 0 || (swiglu != 0 && swiglu != 1)) return DIT_ERR_SHAPE;
+  if (!variant || !sk_tiles || !segs || !part_bytes) return DIT_ERR_NULL;
+  const GemmChoice ch = gemm_choose(m, n, k, swiglu == 1);
+  *variant = ch.variant;
+  *sk_tiles = ch.sk_tiles;
+  *segs = ch.segs;
+  *part_bytes = ch.part_bytes;
+  return DIT_OK;
+}
+
 dit_status dit_gemm_splitk(dit_dtype dtype, int32_t swiglu, int32_t m, int32_t n, int32_t k, const void *a,
                            const void *w, void *c, int32_t sk_tiles, int32_t segs, void *ws, size_t ws_bytes,
                            void *stream) {

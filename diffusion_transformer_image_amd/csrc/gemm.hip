@@ -372,32 +372,37 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(const T *__restrict__
 }
 
 // Sums the K-segment partials of each split tile in segment order and
-// stores the result through the kernel's epilogue (one workgroup = one wave
-// sub-tile of one split tile).
-template <typename T, int BM, int BN, int WM, int WN, int EPI>
+// stores the result through the epilogue.  One workgroup (one wave) covers
+// FRB of the RB row blocks of one wave sub-tile of one split tile, so the
+// pass runs RB / FRB times more waves than the tiles have sub-tiles.
+template <typename T, int BM, int BN, int WM, int WN, int EPI, int FRB>
 __global__ __launch_bounds__(64) void gemm_sk_fixup(const float *__restrict__ part, T *__restrict__ C,
                                                     int M, int N, int m_tiles, int n_tiles, int gm,
                                                     int dp_tiles, int segs) {
   constexpr int NW = WM * WN, TM = BM / WM, TN = BN / WN, RB = TM / 16, CB = TN / 16;
-  const int t = blockIdx.x / NW, wave = blockIdx.x % NW, lane = threadIdx.x;
+  static_assert(RB % FRB == 0, "row-block split");
+  constexpr int NP = RB / FRB;  // workgroups per wave sub-tile
+  const int lane = threadIdx.x;
+  const int piece = blockIdx.x % NP, wave = (blockIdx.x / NP) % NW, t = blockIdx.x / (NP * NW);
   const int wm = wave / WN, wn = wave % WN;
-  f32x4 acc[RB][CB];
+  f32x4 acc[FRB][CB];
 #pragma unroll
-  for (int i = 0; i < RB; ++i)
+  for (int i = 0; i < FRB; ++i)
 #pragma unroll
     for (int j = 0; j < CB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int sgm = 0; sgm < segs; ++sgm) {
     const float *src = part + (size_t)(t * segs + sgm) * BM * BN + (size_t)wave * RB * CB * 256 + lane * 4;
 #pragma unroll
-    for (int i = 0; i < RB; ++i)
+    for (int i = 0; i < FRB; ++i)
 #pragma unroll
-      for (int j = 0; j < CB; ++j) acc[i][j] += *reinterpret_cast<const f32x4 *>(src + (i * CB + j) * 256);
+      for (int j = 0; j < CB; ++j)
+        acc[i][j] += *reinterpret_cast<const f32x4 *>(src + ((piece * FRB + i) * CB + j) * 256);
   }
   int tm, tn;
   tile_coords(dp_tiles + t, m_tiles, n_tiles, gm, tm, tn);
-  const int row0 = tm * BM + wm * TM;
+  const int row0 = tm * BM + wm * TM + piece * FRB * 16;
   const int col0 = (EPI == EPI_SWIGLU) ? tn * (BN / 2) + wn * (TN / 2) : tn * BN + wn * TN;
-  gemm_store_direct<T, TM, TN, EPI>(acc, C, M, N, row0, col0, lane);
+  gemm_store_direct<T, FRB * 16, TN, EPI>(acc, C, M, N, row0, col0, lane);
 }
 
 // Calls f(integral_constant<I>) for I = B..E-1 in order while f returns true.
@@ -613,8 +618,9 @@ static hipError_t launch_gemm_t(const void *a, const void *w, void *c, int M, in
                      (const T *)w, (T *)c, M, N, K, mt, nt, gm, plan);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || sk_tiles == 0) return e;
-  hipLaunchKernelGGL((gemm_sk_fixup<T, BM, BN, WM, WN, EPI>), dim3(sk_tiles * WM * WN), dim3(64), 0, s,
-                     (const float *)part, (T *)c, M, N, mt, nt, gm, plan.dp_tiles, plan.segs);
+  constexpr int FRB = (BM / WM / 16) % 2 == 0 ? 2 : 1;  // row blocks per fixup wave
+  hipLaunchKernelGGL((gemm_sk_fixup<T, BM, BN, WM, WN, EPI, FRB>), dim3(sk_tiles * WM * WN * (BM / WM / 16 / FRB)),
+                     dim3(64), 0, s, (const float *)part, (T *)c, M, N, mt, nt, gm, plan.dp_tiles, plan.segs);
   return hipGetLastError();
 }
 

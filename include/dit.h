@@ -196,6 +196,15 @@ dit_status dit_gemm_variant(dit_dtype dtype, int32_t variant, int32_t group_m, i
                             int32_t m, int32_t n, int32_t k, const void *a, const void *w, void *c,
                             void *stream);
 
+/* (host only, no GPU call) The configuration dit_block_fwd uses for a bf16
+ * product of this shape when its workspace holds the partial tiles: tile
+ * variant (as in dit_gemm_variant) and, when sk_tiles > 0, the split tail
+ * of dit_gemm_splitk (256 x 256 tiles) with its fp32 partial bytes.  Non-
+ * positive sizes or swiglu outside 0..1 -> DIT_ERR_SHAPE; NULL outputs ->
+ * DIT_ERR_NULL. */
+dit_status dit_gemm_plan(int32_t m, int32_t n, int32_t k, int32_t swiglu, int32_t *variant, int32_t *sk_tiles,
+                         int32_t *segs, size_t *part_bytes);
+
 /* The bf16 product (swiglu = 0: C = A W^T; 1: the SwiGLU hidden as in
  * dit_gemm_swiglu with F = n) on 256 x 256 output tiles (256 x 128 output
  * columns for SwiGLU), with the last sk_tiles tiles of the tile order each

@@ -164,3 +164,22 @@ def test_missing_library_fails_loudly(monkeypatch):
     monkeypatch.setattr(_lib, "LIB_PATH", "/nonexistent/libdit.so")
     with pytest.raises(RuntimeError, match="missing"):
         _lib.lib()
+
+
+def test_gemm_plan_choices():
+    """The block's GEMM choices at the 1024 px shapes: the W13 and W2 tails
+    are split along K, QKVG runs whole 256-row tiles, O whole 192-row tiles;
+    a split always fits its stated partial buffer."""
+    T, D, F = 9216, 4096, 11008
+    w13 = dit.gemm_plan(T, F, D, swiglu=True)
+    assert (w13["sk_tiles"], w13["segs"]) == (24, 8) and w13["part_bytes"] == 24 * 8 * 65536 * 4
+    assert dit.gemm_plan(T, D, F)["sk_tiles"] == 64
+    assert dit.gemm_plan(T, 10240, D) == {"variant": 8, "sk_tiles": 0, "segs": 1, "part_bytes": 0}
+    assert dit.gemm_plan(T, D, D)["variant"] == 9 and dit.gemm_plan(T, D, D)["sk_tiles"] == 0
+    for m in (80, 1000, 4608, 9088, 16384):
+        for n, k, sw in ((10240, 4096, False), (4096, 11008, False), (11008, 4096, True)):
+            p = dit.gemm_plan(m, n, k, swiglu=sw)
+            assert p["part_bytes"] == p["sk_tiles"] * p["segs"] * 65536 * 4
+            assert p["sk_tiles"] == 0 or 2 <= p["segs"] <= 8
+    with pytest.raises(dit.DitError):
+        dit.gemm_plan(0, 16, 16)
