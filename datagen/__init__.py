@@ -34,12 +34,13 @@ import numpy as np
 __all__ = [
     "Config", "CONFIGS", "get_config", "bf16_bits", "bf16_round", "bits_to_f32",
     "BlockWeights", "block_weights", "activations", "block_mod", "timestep_inputs",
-    "qkvg_activations", "rng",
+    "qkvg_activations", "rng", "qk_norm_weights",
 ]
 
 # tensor ids used in the spawn keys (stable: changing one changes the data)
 TID_X, TID_T, TID_WT1, TID_WT2, TID_MOD = 0, 1, 2, 3, 4
 TID_WQKVG, TID_WO, TID_W13, TID_W2, TID_MODBIAS, TID_NORM1, TID_NORM2 = 10, 11, 12, 13, 14, 15, 16
+TID_QNORM, TID_KNORM = 17, 18
 TID_QKVG_ACT = 20
 TID_GEMM_A, TID_GEMM_W = 30, 31
 
@@ -65,6 +66,8 @@ class Config:
     out_std: float = 0.02  # W_o and W_2 ~ N(0, out_std)
     mod_std: float = 0.15  # synthetic modulation vector for block-level inputs
     t_dim: int = 256  # sinusoidal timestep-embedding width
+    grid_h: int = 0  # latent patch grid of the image tokens (grid_h * grid_w = n_image)
+    grid_w: int = 0
 
     @property
     def seq_len(self) -> int:
@@ -96,18 +99,19 @@ _BIG = dict(hidden=4096, n_heads=32, n_kv_heads=8, head_dim=128, ffn=11008, dtyp
 CONFIGS = {
     # tiny fp32 block: 64 image + 16 text tokens
     "c0": Config("c0-tiny-f32", batch=1, n_image=64, n_text=16, hidden=256, n_heads=4,
-                 n_kv_heads=2, head_dim=64, ffn=688, dtype="f32", seed=0, mod_std=0.04),
+                 n_kv_heads=2, head_dim=64, ffn=688, dtype="f32", seed=0, mod_std=0.04, grid_h=8, grid_w=8),
     # 256 px stage: 16x16 latent patches + 256 text tokens
-    "c1": Config("c1-256px", batch=32, n_image=256, n_text=256, seed=1, **_BIG),
+    "c1": Config("c1-256px", batch=32, n_image=256, n_text=256, seed=1, grid_h=16, grid_w=16, **_BIG),
     # 512 px stage: 32x32 + 256
-    "c2": Config("c2-512px", batch=8, n_image=1024, n_text=256, seed=2, **_BIG),
+    "c2": Config("c2-512px", batch=8, n_image=1024, n_text=256, seed=2, grid_h=32, grid_w=32, **_BIG),
     # 1024 px stage: 64x64 + 512
-    "c3": Config("c3-1024px", batch=2, n_image=4096, n_text=512, seed=3, **_BIG),
+    "c3": Config("c3-1024px", batch=2, n_image=4096, n_text=512, seed=3, grid_h=64, grid_w=64, **_BIG),
     # non-square 768x1344: 48x84 + 512
-    "c3b": Config("c3b-768x1344", batch=2, n_image=4032, n_text=512, seed=1003, **_BIG),
+    "c3b": Config("c3b-768x1344", batch=2, n_image=4032, n_text=512, seed=1003, grid_h=48, grid_w=84,
+                  **_BIG),
     # 60-block stack, one denoising step at 1024 px, batch 1
     "c4": Config("c4-stack60-1024px", batch=1, n_image=4096, n_text=512, seed=4, n_blocks=60,
-                 out_std=0.02 / math.sqrt(2 * 60), **_BIG),
+                 out_std=0.02 / math.sqrt(2 * 60), grid_h=64, grid_w=64, **_BIG),
 }
 
 
@@ -161,6 +165,8 @@ class BlockWeights:
     mod_bias: np.ndarray  # [6, D] fp32: shift1, scale1, gate1, shift2, scale2, gate2
     norm1_w: np.ndarray  # [D] fp32 zero-centred gain
     norm2_w: np.ndarray  # [D] fp32
+    q_norm_w: np.ndarray | None = None  # [head_dim] fp32 zero-centred QKNorm gains (optional prologue)
+    k_norm_w: np.ndarray | None = None
 
 
 def block_weights(cfg: Config, block: int = 0) -> BlockWeights:
@@ -174,6 +180,13 @@ def block_weights(cfg: Config, block: int = 0) -> BlockWeights:
         norm1_w=_normal(cfg, block, TID_NORM1, (d,), cfg.w_std, False),
         norm2_w=_normal(cfg, block, TID_NORM2, (d,), cfg.w_std, False),
     )
+
+
+def qk_norm_weights(cfg: Config, w: BlockWeights, block: int = 0) -> BlockWeights:
+    """The same weights with QKNorm gains w_q, w_k [head_dim] ~ N(0, w_std) fp32."""
+    return dataclasses.replace(
+        w, q_norm_w=_normal(cfg, block, TID_QNORM, (cfg.head_dim,), cfg.w_std, False),
+        k_norm_w=_normal(cfg, block, TID_KNORM, (cfg.head_dim,), cfg.w_std, False))
 
 
 def activations(cfg: Config) -> np.ndarray:

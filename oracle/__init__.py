@@ -24,6 +24,14 @@ Parity status (what pins each function; see the tests under
   give the shared map from t to the modulation vector; the oracle's
   two-layer bias-free MLP is a reading, and the HIP path implements the
   same reading.
+* ``qk_rmsnorm``, ``rope_positions``, ``rope_angles``, ``apply_rope``,
+  ``attention_prologue`` (the optional QKNorm + 3D axial RoPE): pinned by
+  the scalar-loop brute force, by torch's float64 ``rms_norm``, by the
+  rotation's closed forms (one pair turned by a known angle, norms kept,
+  position 0 and text tokens unchanged, scores depending only on position
+  differences along an axis) and by planted mistakes.  The axis split
+  (32, 48, 48), the adjacent-pair convention and the base 10000 are
+  readings: parity of those conventions is unpinned by the pages.
 * The zero-centred gain form ``(1 + w)`` of the RMSNorm is a reading of
   the pages (weight decay on a zero-centred parameter); parity of that
   convention is unpinned by the pages, though the arithmetic under it is
@@ -31,6 +39,12 @@ Parity status (what pins each function; see the tests under
 """
 from .dit_oracle import (  # noqa: F401
     OracleConfig,
+    Prologue,
+    apply_rope,
+    attention_prologue,
+    qk_rmsnorm,
+    rope_angles,
+    rope_positions,
     block_forward,
     block_forward_rows,
     gated_gqa_attention,

@@ -20,9 +20,37 @@ def _vec(a):
     return [float(v) for v in a]
 
 
-def block(x, mod, wts, n_heads, n_kv_heads, head_dim, ffn, eps):
+def _prologue_row(vec, gain, pos, qk_norm, rope, axes, theta, eps):
+    """One head vector of one token: zero-centred RMSNorm, then the pairs
+    (2j, 2j+1) turned by pos[axis] * theta^(-2i/d_axis)."""
+    d = len(vec)
+    v = list(vec)
+    if qk_norm:
+        ss = 0.0
+        for c in range(d):
+            ss += v[c] * v[c]
+        inv = 1.0 / math.sqrt(ss / d + eps)
+        v = [v[c] * inv * (1.0 + (gain[c] if gain is not None else 0.0)) for c in range(d)]
+    if rope:
+        out = list(v)
+        j = 0
+        for a, da in enumerate(axes):
+            for i in range(da // 2):
+                ang = pos[a] * theta ** (-(2.0 * i) / da)
+                c0, c1 = v[2 * j], v[2 * j + 1]
+                out[2 * j] = c0 * math.cos(ang) - c1 * math.sin(ang)
+                out[2 * j + 1] = c0 * math.sin(ang) + c1 * math.cos(ang)
+                j += 1
+        v = out
+    return v
+
+
+def block(x, mod, wts, n_heads, n_kv_heads, head_dim, ffn, eps, prologue=None):
     """x: nested lists [B][L][D]; mod [B][6][D]; wts has the same fields as
-    ``datagen.BlockWeights``.  Returns nested lists [B][L][D]."""
+    ``datagen.BlockWeights``.  prologue: None, or a dict with keys qk_norm,
+    rope, grid_h, grid_w, axes, theta (QKNorm and 3D axial RoPE on Q and K;
+    image tokens first in raster order, text tokens at position 0).
+    Returns nested lists [B][L][D]."""
     w_qkvg = _rows(wts.w_qkvg)
     w_o = _rows(wts.w_o)
     w_13 = _rows(wts.w_13)
@@ -56,6 +84,20 @@ def block(x, mod, wts, n_heads, n_kv_heads, head_dim, ffn, eps):
         h1 = [norm(xs[t], n1, m[0], m[1]) for t in range(L)]
         z = [lin(h1[t], w_qkvg) for t in range(L)]
         H, Hk, d = n_heads, n_kv_heads, head_dim
+        if prologue is not None:
+            gq = getattr(wts, "q_norm_w", None)
+            gk = getattr(wts, "k_norm_w", None)
+            gq = None if gq is None else _vec(gq)
+            gk = None if gk is None else _vec(gk)
+            gw = prologue["grid_w"]
+            n_img = prologue["grid_h"] * gw
+            for t in range(L):
+                pos = (0, t // gw, t % gw) if t < n_img else (0, 0, 0)
+                for hh in range(H + Hk):  # query heads, then key heads
+                    lo = hh * d
+                    z[t][lo:lo + d] = _prologue_row(z[t][lo:lo + d], gq if hh < H else gk, pos,
+                                                    prologue["qk_norm"], prologue["rope"], prologue["axes"],
+                                                    prologue["theta"], eps)
         og = [[0.0] * (H * d) for _ in range(L)]
         for h in range(H):
             j = (h * Hk) // H  # contiguous groups of H/Hk query heads

@@ -44,6 +44,25 @@ Readings where the pages leave a step open (each is also a test):
 * Timestep map (parity unpinned): e = [cos(1000 t f_i), sin(1000 t f_i)],
   f_i = 10000^(-i/(n/2)), m = W_t2 silu(W_t1 e), bias-free, shared by all
   blocks.
+
+Optional attention prologue (``Prologue``; off in the block the benchmark
+measures, which has no positional terms).  Page "Krea 2 技术报告", 架构 ›
+归一化: RMSNorm is also the QKNorm; 架构 › 位置编码: 3D axial RoPE with the
+head dimensions assigned to frame, height and width, RoPE indices of text
+tokens set to zero (the Indonesian and Korean pages list the same).
+Readings where the pages are silent:
+
+* QKNorm: zero-centred RMSNorm over head_dim of every query and key head,
+  x / sqrt(mean(x^2) + eps) * (1 + w), one gain vector w [head_dim] per
+  block for queries and one for keys, shared by the heads; applied to the
+  projections before RoPE, not to V or the gate.
+* RoPE: head_dim split into (frame, height, width) = axes (32, 48, 48 at
+  head_dim 128), each even; rotation pairs are adjacent dimensions
+  (2j, 2j+1); pair i of an axis with d_a dimensions turns by
+  pos_a * theta^(-2i/d_a), theta = 10000; image token l (raster order on
+  the grid_h x grid_w latent grid) has position (0, l // grid_w,
+  l % grid_w), text tokens (0, 0, 0).  Parity unpinned: the split, the
+  pairing and the base are conventions the pages do not give.
 """
 from __future__ import annotations
 
@@ -182,8 +201,81 @@ def gated_residual(x, gate, y) -> np.ndarray:
     return _f64(x) + _f64(gate) * _f64(y)
 
 
+# ------------------------------------------------------------------ prologue
+@dataclasses.dataclass(frozen=True)
+class Prologue:
+    """QKNorm and 3D axial RoPE in front of the attention (see the module
+    docstring for the readings)."""
+
+    qk_norm: bool = True
+    rope: bool = True
+    grid_h: int = 0
+    grid_w: int = 0
+    axes: tuple = (32, 48, 48)
+    theta: float = 10000.0
+
+
+def qk_rmsnorm(x, w, eps: float) -> np.ndarray:
+    """Zero-centred RMSNorm over the last axis (head_dim):
+    x / sqrt(mean(x^2) + eps) * (1 + w) (page "Krea 2 技术报告", 架构 ›
+    归一化: RMSNorm as the QKNorm, zero-centred gain)."""
+    x = _f64(x)
+    w = np.zeros(x.shape[-1]) if w is None else _f64(w)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps) * (1.0 + w)
+
+
+def rope_positions(seq_len: int, grid_h: int, grid_w: int) -> np.ndarray:
+    """[L, 3] (frame, height, width) index of every token: image tokens
+    first, in raster order on the grid_h x grid_w latent grid, frame 0;
+    text tokens all zero (page "Krea 2 技术报告", 架构 › 位置编码)."""
+    pos = np.zeros((seq_len, 3), dtype=np.int64)
+    n_img = min(seq_len, grid_h * grid_w)
+    l = np.arange(n_img)
+    pos[:n_img, 1] = l // grid_w
+    pos[:n_img, 2] = l % grid_w
+    return pos
+
+
+def rope_angles(pos, axes, theta: float) -> np.ndarray:
+    """[L, sum(axes)/2] rotation angle of every dimension pair: the pairs of
+    axis a (d_a dimensions, in the order frame, height, width) turn by
+    pos[:, a] * theta^(-2i/d_a), i < d_a/2."""
+    pos = np.asarray(pos, dtype=F64)
+    cols = []
+    for a, da in enumerate(axes):
+        freq = theta ** (-np.arange(0, da, 2, dtype=F64) / da)
+        cols.append(pos[:, a:a + 1] * freq[None, :])
+    return np.concatenate(cols, axis=1)
+
+
+def apply_rope(x, ang) -> np.ndarray:
+    """Rotate the adjacent pairs (2j, 2j+1) of x [L, heads, d] by ang [L, d/2]."""
+    x = _f64(x)
+    c, sn = np.cos(ang)[:, None, :], np.sin(ang)[:, None, :]
+    x0, x1 = x[..., 0::2], x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = x0 * c - x1 * sn
+    out[..., 1::2] = x0 * sn + x1 * c
+    return out
+
+
+def attention_prologue(q, k, pro: Prologue, wts, eps: float, q_rows=None):
+    """QKNorm then RoPE on q [Lq, H, d] (tokens q_rows of the sample, all if
+    None) and k [L, Hkv, d] (all tokens)."""
+    L, d = k.shape[0], k.shape[-1]
+    if pro.qk_norm:
+        q = qk_rmsnorm(q, getattr(wts, "q_norm_w", None), eps)
+        k = qk_rmsnorm(k, getattr(wts, "k_norm_w", None), eps)
+    if pro.rope:
+        assert sum(pro.axes) == d and all(a % 2 == 0 for a in pro.axes)
+        ang = rope_angles(rope_positions(L, pro.grid_h, pro.grid_w), pro.axes, pro.theta)
+        q = apply_rope(q, ang if q_rows is None else ang[q_rows])
+        k = apply_rope(k, ang)
+    return q, k
+
+
 # ------------------------------------------------------------------ block
-def _sample_forward(x, mod_b, wts, oc: OracleConfig, rows=None):
+def _sample_forward(x, mod_b, wts, oc: OracleConfig, rows=None, pro: Prologue | None = None):
     """Block forward of one sample x [L, D]; outputs for ``rows`` (all if None)."""
     shift1, scale1, gate1, shift2, scale2, gate2 = split_modulation(mod_b, wts.mod_bias)
     x = _f64(x)
@@ -198,6 +290,8 @@ def _sample_forward(x, mod_b, wts, oc: OracleConfig, rows=None):
     hr = h1 if rows is None else h1[rows]
     q = (hr @ w_qkvg[: H * d].T).reshape(-1, H, d)
     g = (hr @ w_qkvg[(H + 2 * Hk) * d :].T).reshape(-1, H, d)
+    if pro is not None:
+        q, k = attention_prologue(q, k, pro, wts, oc.eps, q_rows=rows)
     og = gated_gqa_attention(q, k, v, g)
     a = og @ _f64(wts.w_o).T
     x1 = gated_residual(xr, gate1, a)
@@ -206,19 +300,20 @@ def _sample_forward(x, mod_b, wts, oc: OracleConfig, rows=None):
     return gated_residual(x1, gate2, mlp)
 
 
-def block_forward(x, mod, wts, oc: OracleConfig) -> np.ndarray:
+def block_forward(x, mod, wts, oc: OracleConfig, pro: Prologue | None = None) -> np.ndarray:
     """x [B, L, D], mod [B, 6, D] -> [B, L, D]; samples are independent."""
     x = _f64(x)
-    return np.stack([_sample_forward(x[b], mod[b], wts, oc) for b in range(x.shape[0])])
+    return np.stack([_sample_forward(x[b], mod[b], wts, oc, pro=pro) for b in range(x.shape[0])])
 
 
-def block_forward_rows(x, mod, wts, oc: OracleConfig, b: int, rows: Sequence[int]) -> np.ndarray:
+def block_forward_rows(x, mod, wts, oc: OracleConfig, b: int, rows: Sequence[int],
+                       pro: Prologue | None = None) -> np.ndarray:
     """The same definition evaluated only at query tokens ``rows`` of sample b."""
-    return _sample_forward(_f64(x[b]), mod[b], wts, oc, rows=np.asarray(rows))
+    return _sample_forward(_f64(x[b]), mod[b], wts, oc, rows=np.asarray(rows), pro=pro)
 
 
 def stack_forward(x, mod, weights: Iterable | Callable[[int], object], n_blocks: int,
-                  oc: OracleConfig) -> np.ndarray:
+                  oc: OracleConfig, pro: Prologue | None = None) -> np.ndarray:
     """Apply blocks 0..n_blocks-1 in order with one shared modulation m.
 
     ``weights`` is either a sequence of per-block weights or a function
@@ -227,5 +322,5 @@ def stack_forward(x, mod, weights: Iterable | Callable[[int], object], n_blocks:
     get = weights if callable(weights) else (lambda i, _w=list(weights): _w[i])
     y = _f64(x)
     for i in range(n_blocks):
-        y = block_forward(y, mod, get(i), oc)
+        y = block_forward(y, mod, get(i), oc, pro)
     return y

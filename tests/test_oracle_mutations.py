@@ -111,3 +111,92 @@ def test_planted_mistake_is_caught(name, monkeypatch):
     bad = O.block_forward(x, mod, w, oc)
     # the pin tolerates 1e-12 relative; every mutant must exceed it by a wide margin
     assert np.max(np.abs(bad - bf)) > 1e-9 * np.max(np.abs(bf)), name
+
+
+# ------------------------------------------------------------------ attention prologue mutants
+_ROPE = O.apply_rope
+_ANGLES = O.rope_angles
+_POS = O.rope_positions
+_QKN = O.qk_rmsnorm
+
+
+def _rope_negative_turn(x, ang):
+    return _ROPE(x, -np.asarray(ang))
+
+
+def _rope_half_split_pairs(x, ang):  # pairs (j, j + d/2) instead of adjacent dimensions
+    x = np.asarray(x, float)
+    h = x.shape[-1] // 2
+    c, s = np.cos(ang)[:, None, :], np.sin(ang)[:, None, :]
+    out = np.empty_like(x)
+    out[..., :h] = x[..., :h] * c - x[..., h:] * s
+    out[..., h:] = x[..., :h] * s + x[..., h:] * c
+    return out
+
+
+def _angles_axes_reversed(pos, axes, theta):
+    return _ANGLES(np.asarray(pos)[:, ::-1], axes[::-1], theta)
+
+
+def _angles_freq_without_2(pos, axes, theta):
+    pos = np.asarray(pos, float)
+    cols = [pos[:, a:a + 1] * (theta ** (-np.arange(da // 2) / da))[None, :] for a, da in enumerate(axes)]
+    return np.concatenate(cols, axis=1)
+
+
+def _positions_text_continue(seq_len, grid_h, grid_w):
+    pos = _POS(seq_len, grid_h, grid_w)
+    l = np.arange(grid_h * grid_w, seq_len)
+    pos[grid_h * grid_w:, 1] = l // grid_w  # text tokens continue the raster instead of sitting at 0
+    pos[grid_h * grid_w:, 2] = l % grid_w
+    return pos
+
+
+def _positions_grid_transposed(seq_len, grid_h, grid_w):
+    pos = _POS(seq_len, grid_h, grid_w)
+    l = np.arange(grid_h * grid_w)
+    pos[:grid_h * grid_w, 1] = l % grid_h
+    pos[:grid_h * grid_w, 2] = l // grid_h
+    return pos
+
+
+def _qkn_gain_not_centred(x, w, eps):
+    return _QKN(x, None, eps) * (0.0 if w is None else np.asarray(w, float))
+
+
+def _qkn_eps_outside(x, w, eps):
+    x = np.asarray(x, float)
+    w = np.zeros(x.shape[-1]) if w is None else np.asarray(w, float)
+    return x / (np.sqrt(np.mean(x * x, axis=-1, keepdims=True)) + 0.3) * (1 + w)
+
+
+PRO_MUTANTS = {
+    "rope turns the other way": ("apply_rope", _rope_negative_turn),
+    "rope pairs half-split": ("apply_rope", _rope_half_split_pairs),
+    "rope axes reversed": ("rope_angles", _angles_axes_reversed),
+    "rope frequency exponent": ("rope_angles", _angles_freq_without_2),
+    "text tokens not at zero": ("rope_positions", _positions_text_continue),
+    "grid transposed": ("rope_positions", _positions_grid_transposed),
+    "qk gain w instead of 1+w": ("qk_rmsnorm", _qkn_gain_not_centred),
+    "qk eps outside sqrt": ("qk_rmsnorm", _qkn_eps_outside),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PRO_MUTANTS))
+def test_planted_prologue_mistake_is_caught(name, monkeypatch):
+    cfg = datagen.Config("tiny-pro", batch=1, n_image=6, n_text=2, hidden=24, n_heads=2, n_kv_heads=1,
+                         head_dim=12, ffn=16, dtype="f32", seed=23, w_std=0.5, out_std=0.5, mod_std=1.0,
+                         grid_h=2, grid_w=3)
+    x = datagen.activations(cfg)
+    w = datagen.qk_norm_weights(cfg, datagen.block_weights(cfg))
+    mod = datagen.block_mod(cfg, strong=True)
+    kw = dict(qk_norm=True, rope=True, grid_h=2, grid_w=3, axes=(2, 4, 6), theta=10.0)
+    bf = np.array(bruteforce.block(x, mod, w, 2, 1, 12, 16, cfg.eps, prologue=kw))
+    oc = O.OracleConfig.of(cfg)
+    pro = O.Prologue(**kw)
+    good = O.block_forward(x, mod, w, oc, pro)
+    assert np.max(np.abs(good - bf)) <= 1e-12 * np.max(np.abs(bf))
+    attr, fn = PRO_MUTANTS[name]
+    monkeypatch.setattr(O, attr, fn)
+    bad = O.block_forward(x, mod, w, oc, pro)
+    assert np.max(np.abs(bad - bf)) > 1e-9 * np.max(np.abs(bf)), name

@@ -318,3 +318,91 @@ def test_parameter_count_pins_elementwise_gate():
     # SwiGLU width: 2/3 * 4 * D rounded up to a multiple of 256
     assert c4.ffn == int(math.ceil(2 / 3 * 4 * 4096 / 256) * 256)
     assert datagen.get_config("c0").ffn == int(math.ceil(2 / 3 * 4 * 256 / 16) * 16)
+
+
+# ------------------------------------------------------------------ attention prologue
+def prologue_cfg(batch=1, n_image=6, n_text=2, hkv=1, seed=3, gh=2, gw=3):
+    return datagen.Config("tiny-pro", batch=batch, n_image=n_image, n_text=n_text, hidden=24, n_heads=2,
+                          n_kv_heads=hkv, head_dim=12, ffn=16, dtype="f32", seed=seed, w_std=0.5,
+                          out_std=0.5, mod_std=1.0, grid_h=gh, grid_w=gw)
+
+
+@pytest.mark.parametrize("qk_norm,rope", [(True, True), (True, False), (False, True)])
+@pytest.mark.parametrize("batch,hkv", [(1, 1), (2, 2)])
+def test_prologue_matches_bruteforce(qk_norm, rope, batch, hkv):
+    """QKNorm + 3D axial RoPE in the block: vectorised oracle = scalar loops,
+    text tokens after the image grid, two heads per KV group or one."""
+    cfg = prologue_cfg(batch=batch, hkv=hkv, seed=40 + batch + hkv)
+    x = datagen.activations(cfg)
+    w = datagen.qk_norm_weights(cfg, datagen.block_weights(cfg))
+    mod = datagen.block_mod(cfg, strong=True)
+    pro = O.Prologue(qk_norm=qk_norm, rope=rope, grid_h=2, grid_w=3, axes=(2, 4, 6), theta=10.0)
+    ref = O.block_forward(x, mod, w, oc(cfg), pro)
+    bf = np.array(bruteforce.block(x, mod, w, 2, hkv, 12, 16, cfg.eps,
+                                   prologue=dict(qk_norm=qk_norm, rope=rope, grid_h=2, grid_w=3,
+                                                 axes=(2, 4, 6), theta=10.0)))
+    assert np.max(np.abs(ref - bf)) <= 1e-12 * np.max(np.abs(bf))
+    assert np.max(np.abs(ref - O.block_forward(x, mod, w, oc(cfg)))) > 1e-3  # the prologue did something
+
+
+def test_rope_closed_form_one_pair():
+    """A unit vector on the first dimension of height pair i = 1 (axes
+    (4, 4, 4), theta 100) at height position 3 turns by 3 * 100^(-2/4) = 0.3
+    rad into that pair: (cos 0.3, sin 0.3), nothing elsewhere."""
+    x = np.zeros((1, 1, 12))
+    x[0, 0, 6] = 1.0  # pairs: frame 0,1 | height 2,3 | width 4,5 -> dims 6,7 = height pair i = 1
+    ang = O.rope_angles(np.array([[0, 3, 5]]), (4, 4, 4), 100.0)
+    y = O.apply_rope(x, ang)[0, 0]
+    want = np.zeros(12)
+    want[6], want[7] = math.cos(0.3), math.sin(0.3)
+    assert np.max(np.abs(y - want)) < 1e-15
+    # width pair i = 0 at position 5 turns by 5 rad
+    assert abs(ang[0, 4] - 5.0) < 1e-15 and abs(ang[0, 5] - 5.0 * 0.1) < 1e-15
+    assert ang[0, 0] == 0.0 and ang[0, 1] == 0.0  # frame axis: position 0
+
+
+def test_rope_scores_depend_on_position_differences():
+    """Along any one axis, <rope(q, p), rope(k, p')> depends only on p - p'
+    (the defining property of rotary embeddings); norms are kept."""
+    r = np.random.default_rng(5)
+    q, k = r.standard_normal((1, 1, 16)), r.standard_normal((1, 1, 16))
+    axes = (4, 6, 6)
+    for axis in (1, 2):
+        def score(pq, pk):
+            a = np.zeros((1, 3)); a[0, axis] = pq
+            b = np.zeros((1, 3)); b[0, axis] = pk
+            return float(np.sum(O.apply_rope(q, O.rope_angles(a, axes, 10000.0)) *
+                                O.apply_rope(k, O.rope_angles(b, axes, 10000.0))))
+        for pq, pk in ((0, 3), (7, 2), (40, 41)):
+            for delta in (1, 5, 23):
+                assert abs(score(pq, pk) - score(pq + delta, pk + delta)) < 1e-12
+        a = np.zeros((1, 3)); a[0, axis] = 13
+        y = O.apply_rope(q, O.rope_angles(a, axes, 10000.0))
+        assert abs(np.linalg.norm(y) - np.linalg.norm(q)) < 1e-12
+        pairs_in, pairs_out = q[0, 0].reshape(-1, 2), y[0, 0].reshape(-1, 2)
+        assert np.allclose(np.linalg.norm(pairs_in, axis=1), np.linalg.norm(pairs_out, axis=1), atol=1e-13)
+
+
+def test_rope_positions_text_and_origin_unchanged():
+    """Image tokens in raster order (row l // grid_w, column l % grid_w), frame
+    0; text tokens at (0, 0, 0); the rotation leaves position 0 alone."""
+    pos = O.rope_positions(14, 3, 4)
+    assert pos[5].tolist() == [0, 1, 1] and pos[11].tolist() == [0, 2, 3]
+    assert (pos[12:] == 0).all() and (pos[0] == 0).all() and (pos[:, 0] == 0).all()
+    x = np.random.default_rng(1).standard_normal((14, 2, 12))
+    y = O.apply_rope(x, O.rope_angles(pos, (4, 4, 4), 10000.0))
+    assert np.array_equal(y[12:], x[12:]) and np.array_equal(y[0], x[0])
+    assert not np.allclose(y[5], x[5])
+
+
+def test_qk_norm_is_torch_rms_norm():
+    """QKNorm = torch's float64 rms_norm over head_dim with gain 1 + w."""
+    r = np.random.default_rng(9)
+    x = r.standard_normal((5, 3, 16)) * 3.0
+    w = r.standard_normal(16) * 0.1
+    got = O.qk_rmsnorm(x, w, 1e-6)
+    want = F.rms_norm(torch.from_numpy(x), (16,), weight=torch.from_numpy(1.0 + w), eps=1e-6).numpy()
+    assert np.max(np.abs(got - want)) < 1e-13
+    unit = O.qk_rmsnorm(x, None, 0.0)
+    assert np.allclose(np.sqrt(np.mean(unit ** 2, axis=-1)), 1.0, atol=1e-14)
+    assert np.allclose(O.qk_rmsnorm(7.5 * x, w, 0.0), O.qk_rmsnorm(x, w, 0.0), atol=1e-13)
