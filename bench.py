@@ -134,6 +134,40 @@ def bench_stack(dit, torch, steps: int, warmup: int) -> dict:
     return out
 
 
+def bench_prologue(dit, torch, cfg, c, W, X, Y, M, ws, step, steps: int, warmup: int) -> dict:
+    """The same step with the attention prologue on (QKNorm on Q and K with
+    seeded gains, 3D axial RoPE on the 64 x 64 image grid, text at 0):
+    ms per step, and the prologue kernel's own time and bandwidth
+    (algorithmic bytes: the Q and K heads read and written once)."""
+    import datagen
+    from datagen import device
+    wq = datagen.qk_norm_weights(cfg, datagen.block_weights(cfg))
+    Wp = dict(W, q_norm_w=device.to_device(wq.q_norm_w, "f32"), k_norm_w=device.to_device(wq.k_norm_w, "f32"))
+    pro = dit.make_prologue(grid_h=cfg.grid_h, grid_w=cfg.grid_w, axes=(32, 48, 48), theta=10000.0)
+    def pstep():
+        step(timestep_only=True)
+        dit.block_fwd_ex(c, pro, Wp, X, Y, M, ws)
+
+    for _ in range(warmup):
+        pstep()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        pstep()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    dit.timer_start("prologue", steps)
+    for _ in range(steps):
+        pstep()
+    torch.cuda.synchronize()
+    ms, n = dit.timer_stop()
+    per = ms / max(n, 1)
+    nbytes = 2 * cfg.tokens * (cfg.n_heads + cfg.n_kv_heads) * cfg.head_dim * 2
+    return {"ms_per_step": dt * 1e3, "tokens_per_s": cfg.tokens / dt, "prologue_ms_per_launch": per,
+            "prologue_gbs": nbytes / (per * 1e-3) / 1e9, "prologue_hbm_frac": nbytes / (per * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "axes": [32, 48, 48], "grid": [cfg.grid_h, cfg.grid_w], "theta": 10000.0}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -169,9 +203,10 @@ def main() -> int:
     M = torch.empty((cfg.batch, 6, cfg.hidden), dtype=torch.float32, device="cuda")
     ws = torch.empty(dit.workspace_size(c), dtype=torch.uint8, device="cuda")
 
-    def step():
+    def step(timestep_only=False):
         dit.timestep_mod(c, Tt, W1, W2, M, ws)
-        dit.block_fwd(c, W, X, Y, M, ws)
+        if not timestep_only:
+            dit.block_fwd(c, W, X, Y, M, ws)
 
     for _ in range(args.warmup):
         step()
@@ -237,6 +272,7 @@ def main() -> int:
         "mfma_frac": step_flops / (elapsed / args.steps) / 1e12 / PEAK_BF16_TFLOPS,
         "kernels": kernels, "roofline": roofline,
     }
+    out["with_prologue"] = bench_prologue(dit, torch, cfg, c, W, X, Y, M, ws, step, args.steps, args.warmup)
     if not args.no_stack:
         out["stack"] = bench_stack(dit, torch, args.stack_steps, 2)
     if not args.no_cpu_baseline:

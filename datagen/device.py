@@ -37,4 +37,6 @@ def weights_to_device(w, dtype: str, device="cuda") -> dict:
         "mod_bias": to_device(w.mod_bias, "f32", device),
         "norm1_w": to_device(w.norm1_w, "f32", device),
         "norm2_w": to_device(w.norm2_w, "f32", device),
+        **({"q_norm_w": to_device(w.q_norm_w, "f32", device)} if getattr(w, "q_norm_w", None) is not None else {}),
+        **({"k_norm_w": to_device(w.k_norm_w, "f32", device)} if getattr(w, "k_norm_w", None) is not None else {}),
     }

@@ -11,10 +11,12 @@ from ._lib import (  # noqa: F401
     KERNEL_KINDS,
     LIB_PATH,
     BlockWeights,
+    Prologue,
     Config,
     DitError,
     attention,
     block_fwd,
+    block_fwd_ex,
     config_of,
     gated_residual,
     gemm,
@@ -24,9 +26,12 @@ from ._lib import (  # noqa: F401
     gemm_variant,
     lib,
     make_config,
+    make_prologue,
     make_weights,
     modnorm,
+    qk_prologue,
     stack_fwd,
+    stack_fwd_ex,
     stack_workspace_size,
     timer_start,
     timer_stop,

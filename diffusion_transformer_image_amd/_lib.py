@@ -19,13 +19,14 @@ DIT_F32, DIT_BF16 = 0, 1
 STATUS = {0: "DIT_OK", 1: "DIT_ERR_NULL", 2: "DIT_ERR_SHAPE", 3: "DIT_ERR_UNSUPPORTED",
           4: "DIT_ERR_ALIGN", 5: "DIT_ERR_WORKSPACE", 6: "DIT_ERR_DTYPE", 7: "DIT_ERR_HIP"}
 KERNEL_KINDS = {"modnorm": 0, "gemm_qkvg": 1, "attn": 2, "gemm_o": 3, "resid": 4,
-                "gemm_w13": 5, "gemm_w2": 6, "tmod": 7}
+                "gemm_w13": 5, "gemm_w2": 6, "tmod": 7, "prologue": 8}
 
 EXPORTS = (
     "dit_workspace_size", "dit_stack_workspace_size", "dit_block_fwd", "dit_stack_fwd",
     "dit_timestep_mod", "dit_modnorm", "dit_gemm", "dit_gemm_swiglu", "dit_gemm_variant", "dit_attention",
     "dit_gated_residual", "dit_status_str", "dit_last_hip_error", "dit_timer_start",
-    "dit_timer_stop", "dit_gemm_splitk", "dit_gemm_plan",
+    "dit_timer_stop", "dit_gemm_splitk", "dit_gemm_plan", "dit_block_fwd_ex", "dit_stack_fwd_ex",
+    "dit_qk_prologue",
 )
 
 
@@ -49,7 +50,14 @@ class Config(ctypes.Structure):
 class BlockWeights(ctypes.Structure):
     _fields_ = [("w_qkvg", ctypes.c_void_p), ("w_o", ctypes.c_void_p), ("w_13", ctypes.c_void_p),
                 ("w_2", ctypes.c_void_p), ("mod_bias", ctypes.c_void_p),
-                ("norm1_w", ctypes.c_void_p), ("norm2_w", ctypes.c_void_p)]
+                ("norm1_w", ctypes.c_void_p), ("norm2_w", ctypes.c_void_p),
+                ("q_norm_w", ctypes.c_void_p), ("k_norm_w", ctypes.c_void_p)]
+
+
+class Prologue(ctypes.Structure):
+    """dit_prologue: QKNorm and 3D axial RoPE on Q and K."""
+    _fields_ = [("qk_norm", ctypes.c_int32), ("rope", ctypes.c_int32), ("grid_h", ctypes.c_int32),
+                ("grid_w", ctypes.c_int32), ("axes", ctypes.c_int32 * 3), ("theta", ctypes.c_float)]
 
 
 _LIB = None
@@ -69,6 +77,9 @@ def lib() -> ctypes.CDLL:
             "dit_workspace_size": (sz, [cfgp]),
             "dit_stack_workspace_size": (sz, [cfgp]),
             "dit_block_fwd": (i32, [cfgp, wp, vp, vp, vp, vp, sz, vp]),
+            "dit_block_fwd_ex": (i32, [cfgp, ctypes.POINTER(Prologue), wp, vp, vp, vp, vp, sz, vp]),
+            "dit_stack_fwd_ex": (i32, [cfgp, ctypes.POINTER(Prologue), i32, wp, vp, vp, vp, vp, sz, vp]),
+            "dit_qk_prologue": (i32, [cfgp, ctypes.POINTER(Prologue), vp, vp, vp, vp]),
             "dit_stack_fwd": (i32, [cfgp, i32, wp, vp, vp, vp, vp, sz, vp]),
             "dit_timestep_mod": (i32, [cfgp, i32, vp, vp, vp, vp, vp, sz, vp]),
             "dit_modnorm": (i32, [cfgp, vp, i32, vp, vp, vp, vp, i32, vp]),
@@ -141,7 +152,13 @@ def config_of(c, batch: int | None = None, seq_len: int | None = None) -> Config
 
 def make_weights(w: Mapping) -> BlockWeights:
     return BlockWeights(_ptr(w["w_qkvg"]), _ptr(w["w_o"]), _ptr(w["w_13"]), _ptr(w["w_2"]),
-                        _ptr(w["mod_bias"]), _ptr(w.get("norm1_w")), _ptr(w.get("norm2_w")))
+                        _ptr(w["mod_bias"]), _ptr(w.get("norm1_w")), _ptr(w.get("norm2_w")),
+                        _ptr(w.get("q_norm_w")), _ptr(w.get("k_norm_w")))
+
+
+def make_prologue(qk_norm: bool = True, rope: bool = True, grid_h: int = 0, grid_w: int = 0,
+                  axes=(32, 48, 48), theta: float = 10000.0) -> Prologue:
+    return Prologue(int(qk_norm), int(rope), grid_h, grid_w, (ctypes.c_int32 * 3)(*axes), theta)
 
 
 # ------------------------------------------------------------------ entry points
@@ -158,6 +175,29 @@ def block_fwd(cfg: Config, w: Mapping, x_in, x_out, mod, ws, stream=None) -> Non
     nbytes = ws.numel() * ws.element_size() if hasattr(ws, "numel") else 0
     _check(lib().dit_block_fwd(ctypes.byref(cfg), ctypes.byref(bw), _ptr(x_in), _ptr(x_out),
                                _ptr(mod), _ptr(ws), nbytes, _stream(stream)), "dit_block_fwd")
+
+
+def block_fwd_ex(cfg: Config, pro: Prologue | None, w: Mapping, x_in, x_out, mod, ws, stream=None) -> None:
+    bw = make_weights(w)
+    nbytes = ws.numel() * ws.element_size() if hasattr(ws, "numel") else 0
+    _check(lib().dit_block_fwd_ex(ctypes.byref(cfg), None if pro is None else ctypes.byref(pro),
+                                  ctypes.byref(bw), _ptr(x_in), _ptr(x_out), _ptr(mod), _ptr(ws), nbytes,
+                                  _stream(stream)), "dit_block_fwd_ex")
+
+
+def stack_fwd_ex(cfg: Config, pro: Prologue | None, blocks: Sequence[Mapping], x_in, x_out, mod, ws,
+                 stream=None) -> None:
+    arr = (BlockWeights * len(blocks))(*[make_weights(b) for b in blocks])
+    nbytes = ws.numel() * ws.element_size() if hasattr(ws, "numel") else 0
+    _check(lib().dit_stack_fwd_ex(ctypes.byref(cfg), None if pro is None else ctypes.byref(pro), len(blocks),
+                                  arr, _ptr(x_in), _ptr(x_out), _ptr(mod), _ptr(ws), nbytes, _stream(stream)),
+           "dit_stack_fwd_ex")
+
+
+def qk_prologue(cfg: Config, pro: Prologue, qkvg, q_norm_w=None, k_norm_w=None, stream=None) -> None:
+    """QKNorm + RoPE in place on the Q and K heads of qkvg [T, (2H+2Hkv)*d]."""
+    _check(lib().dit_qk_prologue(ctypes.byref(cfg), ctypes.byref(pro), _ptr(q_norm_w), _ptr(k_norm_w),
+                                 _ptr(qkvg), _stream(stream)), "dit_qk_prologue")
 
 
 def stack_fwd(cfg: Config, blocks: Sequence[Mapping], x_in, x_out, mod, ws, stream=None) -> None:

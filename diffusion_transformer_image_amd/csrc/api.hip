@@ -145,10 +145,28 @@ dit_status check_weights(const dit_block_weights *w) {
   if (!w) return DIT_ERR_NULL;
   if (!w->w_qkvg || !w->w_o || !w->w_13 || !w->w_2 || !w->mod_bias) return DIT_ERR_NULL;
   if (!aligned(w->w_qkvg) || !aligned(w->w_o) || !aligned(w->w_13) || !aligned(w->w_2) ||
-      !aligned(w->mod_bias) || !aligned(w->norm1_w) || !aligned(w->norm2_w))
+      !aligned(w->mod_bias) || !aligned(w->norm1_w) || !aligned(w->norm2_w) || !aligned(w->q_norm_w) ||
+      !aligned(w->k_norm_w))
     return DIT_ERR_ALIGN;
   return DIT_OK;
 }
+
+// NULL is valid (no prologue)
+dit_status check_prologue(const dit_config *c, const dit_prologue *p) {
+  if (!p) return DIT_OK;
+  if ((p->qk_norm != 0 && p->qk_norm != 1) || (p->rope != 0 && p->rope != 1)) return DIT_ERR_SHAPE;
+  if (p->rope) {
+    if (p->grid_h < 1 || p->grid_w < 1 || (int64_t)p->grid_h * p->grid_w > c->seq_len) return DIT_ERR_SHAPE;
+    int64_t sum = 0;
+    for (int i = 0; i < 3; ++i) {
+      if (p->axes[i] < 0 || (p->axes[i] & 1)) return DIT_ERR_SHAPE;
+      sum += p->axes[i];
+    }
+    if (sum != c->head_dim || !(p->theta > 0.f)) return DIT_ERR_SHAPE;
+  }
+  return DIT_OK;
+}
+bool prologue_on(const dit_prologue *p) { return p && (p->qk_norm || p->rope); }
 
 #define DIT_TRY(expr)                     \
   do {                                    \
@@ -158,8 +176,8 @@ dit_status check_weights(const dit_block_weights *w) {
 
 // One block, on the carved workspace.  x_in has dtype xin_f32 ? f32 : dtype;
 // x_out has xout_f32 ? f32 : dtype; x1 (fp32) is stored in x1buf.
-dit_status run_block(const dit_config *c, const dit_block_weights *w, const void *x_in,
-                     bool xin_f32, void *x_out, bool xout_f32, const float *mod,
+dit_status run_block(const dit_config *c, const dit_prologue *pro, const dit_block_weights *w,
+                     const void *x_in, bool xin_f32, void *x_out, bool xout_f32, const float *mod,
                      const BlockWs &ws, void *x1buf, hipStream_t s) {
   const bool x1_f32 = true;
   const Dims d = dims(c);
@@ -171,6 +189,13 @@ dit_status run_block(const dit_config *c, const dit_block_weights *w, const void
   DIT_TRY(timed(DIT_K_GEMM_QKVG, s, [&] {
     return launch_gemm(f32, ws.h, w->w_qkvg, ws.qkvg, T, (int)d.nqkvg, D, s, -1, 0, ws.part, ws.part_bytes);
   }));
+  if (prologue_on(pro)) {
+    DIT_TRY(timed(DIT_K_PROLOGUE, s, [&] {
+      return launch_qk_prologue(f32, c->head_dim, ws.qkvg, w->q_norm_w, w->k_norm_w, T, L, c->n_heads,
+                                c->n_kv_heads, pro->qk_norm, pro->rope, pro->grid_h, pro->grid_w, pro->axes,
+                                pro->theta, c->eps, s);
+    }));
+  }
   DIT_TRY(timed(DIT_K_ATTN, s, [&] {
     return launch_attention(f32, c->head_dim, ws.qkvg, ws.vt, ws.og, c->batch, L, c->n_heads, c->n_kv_heads, s);
   }));
@@ -234,10 +259,12 @@ size_t dit_stack_workspace_size(const dit_config *cfg) {
   return carve(cfg, nullptr).bytes + round_up(d.T * d.D * 4);
 }
 
-dit_status dit_block_fwd(const dit_config *cfg, const dit_block_weights *w, const void *x_in,
-                         void *x_out, const float *mod, void *ws, size_t ws_bytes, void *stream) {
+dit_status dit_block_fwd_ex(const dit_config *cfg, const dit_prologue *pro, const dit_block_weights *w,
+                            const void *x_in, void *x_out, const float *mod, void *ws, size_t ws_bytes,
+                            void *stream) {
   dit_status st = check_cfg(cfg);
   if (st != DIT_OK) return st;
+  if ((st = check_prologue(cfg, pro)) != DIT_OK) return st;
   if ((st = check_weights(w)) != DIT_OK) return st;
   if (!x_in || !x_out || !mod) return DIT_ERR_NULL;
   if (!ws) return DIT_ERR_WORKSPACE;
@@ -252,14 +279,20 @@ dit_status dit_block_fwd(const dit_config *cfg, const dit_block_weights *w, cons
     return DIT_ERR_SHAPE;
   const BlockWs bw = carve(cfg, ws);
   const bool f32 = cfg->dtype == DIT_F32;
-  return run_block(cfg, w, x_in, f32, x_out, f32, mod, bw, bw.x1, (hipStream_t)stream);
+  return run_block(cfg, pro, w, x_in, f32, x_out, f32, mod, bw, bw.x1, (hipStream_t)stream);
 }
 
-dit_status dit_stack_fwd(const dit_config *cfg, int32_t n_blocks, const dit_block_weights *blocks,
-                         const void *x_in, void *x_out, const float *mod, void *ws, size_t ws_bytes,
-                         void *stream) {
+dit_status dit_block_fwd(const dit_config *cfg, const dit_block_weights *w, const void *x_in,
+                         void *x_out, const float *mod, void *ws, size_t ws_bytes, void *stream) {
+  return dit_block_fwd_ex(cfg, nullptr, w, x_in, x_out, mod, ws, ws_bytes, stream);
+}
+
+dit_status dit_stack_fwd_ex(const dit_config *cfg, const dit_prologue *pro, int32_t n_blocks,
+                            const dit_block_weights *blocks, const void *x_in, void *x_out, const float *mod,
+                            void *ws, size_t ws_bytes, void *stream) {
   dit_status st = check_cfg(cfg);
   if (st != DIT_OK) return st;
+  if ((st = check_prologue(cfg, pro)) != DIT_OK) return st;
   if (n_blocks <= 0) return DIT_ERR_SHAPE;
   if (!blocks) return DIT_ERR_NULL;
   for (int i = 0; i < n_blocks; ++i)
@@ -281,11 +314,38 @@ dit_status dit_stack_fwd(const dit_config *cfg, int32_t n_blocks, const dit_bloc
   hipStream_t s = (hipStream_t)stream;
   for (int i = 0; i < n_blocks; ++i) {
     const bool first = i == 0, last = i == n_blocks - 1;
-    st = run_block(cfg, &blocks[i], first ? x_in : xa, first ? f32 : true, last ? x_out : xa,
+    st = run_block(cfg, pro, &blocks[i], first ? x_in : xa, first ? f32 : true, last ? x_out : xa,
                    last ? f32 : true, mod, bw, bw.x1, s);
     if (st != DIT_OK) return st;
   }
   return DIT_OK;
+}
+
+dit_status dit_stack_fwd(const dit_config *cfg, int32_t n_blocks, const dit_block_weights *blocks,
+                         const void *x_in, void *x_out, const float *mod, void *ws, size_t ws_bytes,
+                         void *stream) {
+  return dit_stack_fwd_ex(cfg, nullptr, n_blocks, blocks, x_in, x_out, mod, ws, ws_bytes, stream);
+}
+
+dit_status dit_qk_prologue(const dit_config *cfg, const dit_prologue *pro, const float *q_norm_w,
+                           const float *k_norm_w, void *qkvg, void *stream) {
+  dit_status st = check_cfg(cfg);
+  if (st != DIT_OK) return st;
+  if (!pro || !qkvg) return DIT_ERR_NULL;
+  if ((st = check_prologue(cfg, pro)) != DIT_OK) return st;
+  if (!aligned(qkvg) || !aligned(q_norm_w) || !aligned(k_norm_w)) return DIT_ERR_ALIGN;
+  const Dims d = dims(cfg);
+  if (overlap(qkvg, d.T * d.nqkvg * d.es, q_norm_w, q_norm_w ? cfg->head_dim * 4 : 0) ||
+      overlap(qkvg, d.T * d.nqkvg * d.es, k_norm_w, k_norm_w ? cfg->head_dim * 4 : 0))
+    return DIT_ERR_SHAPE;
+  if (!prologue_on(pro)) return DIT_OK;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = timed(DIT_K_PROLOGUE, s, [&] {
+    return launch_qk_prologue(cfg->dtype == DIT_F32, cfg->head_dim, qkvg, q_norm_w, k_norm_w, (int)d.T,
+                              cfg->seq_len, cfg->n_heads, cfg->n_kv_heads, pro->qk_norm, pro->rope, pro->grid_h,
+                              pro->grid_w, pro->axes, pro->theta, cfg->eps, s);
+  });
+  return e == hipSuccess ? DIT_OK : hip_fail(e);
 }
 
 dit_status dit_timestep_mod(const dit_config *cfg, int32_t t_dim, const float *t, const float *w_t1,

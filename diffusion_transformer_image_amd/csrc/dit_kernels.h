@@ -43,4 +43,9 @@ size_t attention_vt_bytes(bool f32, int B, int L, int Hkv, int head_dim);
 hipError_t launch_attention(bool f32, int head_dim, const void *qkvg, void *vt, void *og, int B,
                             int L, int H, int Hkv, hipStream_t s);
 
+// QKNorm and 3D axial RoPE in place on the Q and K heads of qkvg rows
+hipError_t launch_qk_prologue(bool f32, int head_dim, void *qkvg, const float *wq, const float *wk, int T,
+                              int L, int H, int Hkv, int qk_norm, int rope, int grid_h, int grid_w,
+                              const int axes[3], float theta, float eps, hipStream_t s);
+
 }  // namespace dit

@@ -1,0 +1,162 @@
+// Attention prologue: QKNorm and 3D axial RoPE on the query and key heads
+// (page "Krea 2 技术报告", 架构 › 归一化: RMSNorm as the QKNorm, zero-centred
+// gain; 架构 › 位置编码: 3D axial RoPE over frame, height and width, text
+// tokens at index zero).
+//
+// In place on the Q | K column blocks of the QKVG projection rows.  One
+// wave per token row; a head of d dimensions is handled by d/8 lanes with
+// 16-byte accesses (4 rotation pairs each).  The angles of a lane's pairs
+// depend only on the token and the pair index: they are computed once per
+// token (fp32 frequency and angle, accurate sincosf) and reused for every
+// head.  The head's mean square is a shuffle reduction
+// over its d/8 lanes.
+#include <cmath>
+
+#include "dit_common.h"
+#include "dit_kernels.h"
+
+namespace dit {
+
+// 8 consecutive elements (4 rotation pairs) of one head per lane.
+template <typename T> struct Oct;
+template <> struct Oct<bf16> {
+  static __device__ __forceinline__ void load(const bf16 *p, float (&v)[8]) {
+    const bf16x8 b = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(p));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (float)b[i];
+  }
+  static __device__ __forceinline__ void store(bf16 *p, const float (&v)[8]) {
+    bf16x8 b;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) b[i] = (bf16)v[i];
+    *reinterpret_cast<u32x4 *>(p) = __builtin_bit_cast(u32x4, b);
+  }
+};
+template <> struct Oct<float> {
+  static __device__ __forceinline__ void load(const float *p, float (&v)[8]) {
+    const f32x4 a = *reinterpret_cast<const f32x4 *>(p), b = *reinterpret_cast<const f32x4 *>(p + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { v[i] = a[i]; v[4 + i] = b[i]; }
+  }
+  static __device__ __forceinline__ void store(float *p, const float (&v)[8]) {
+    *reinterpret_cast<f32x4 *>(p) = f32x4{v[0], v[1], v[2], v[3]};
+    *reinterpret_cast<f32x4 *>(p + 4) = f32x4{v[4], v[5], v[6], v[7]};
+  }
+};
+
+// Sum over the G consecutive lanes of a group (G a power of two <= 64).
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int o = G / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// One wave per token row.  A head of HD dimensions is HD/8 lanes holding 8
+// consecutive elements (4 rotation pairs) each, so a wave covers 64 / (HD/8)
+// heads per step; U steps' loads are issued before the first is used.
+template <typename T, int HD>
+__global__ __launch_bounds__(256) void qk_prologue_kernel(T *__restrict__ qkvg, const float *__restrict__ wq,
+                                                          const float *__restrict__ wk, int T_rows, int L,
+                                                          int H, int Hkv, int qk_norm, int rope, int grid_h,
+                                                          int grid_w, int ax0, int ax1, float theta, float eps) {
+  constexpr int LPH = HD / 8;    // lanes per head
+  constexpr int HPW = 64 / LPH;  // heads per wave step
+  constexpr int U = 4;           // wave steps in flight together
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= T_rows) return;
+  const int e0 = (lane % LPH) * 8, hsub = lane / LPH;  // first element of this lane in its head
+  T *base = qkvg + (size_t)row * (2 * H + 2 * Hkv) * HD + e0;
+  const int nh = H + Hkv;  // query heads, then key heads
+  float x[U][8];
+  auto load_step = [&](int h0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int h = h0 + u * HPW + hsub;
+      if (h < nh) Oct<T>::load(base + h * HD, x[u]);
+      else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[u][i] = 0.f;
+      }
+    }
+  };
+  load_step(0);  // in flight while the angles are computed
+  // ---- rotations of this lane's 4 pairs j = e0/2 .. e0/2 + 3 at this token
+  float c[4] = {1.f, 1.f, 1.f, 1.f}, s[4] = {0.f, 0.f, 0.f, 0.f};
+  if (rope) {
+    const int l = row % L;
+    if (l < grid_h * grid_w) {
+      const float l2t = log2f(theta);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int j = e0 / 2 + k;
+        int pos = 0, i = 0, da = 1;
+        if (2 * j >= ax0 && 2 * j < ax0 + ax1) {
+          pos = l / grid_w; i = j - ax0 / 2; da = ax1;
+        } else if (2 * j >= ax0 + ax1) {
+          pos = l % grid_w; i = j - (ax0 + ax1) / 2; da = HD - ax0 - ax1;
+        }  // frame axis: position 0 for an image
+        if (pos != 0) {
+          // fp32 is enough: the exponent's rounding moves the angle by at
+          // most ~2e-6 rad at position 84, the product by ~5e-6 rad, and
+          // sincosf reduces its argument exactly
+          const float a = (float)pos * exp2f(-(2.0f * (float)i / (float)da) * l2t);
+          sincosf(a, &s[k], &c[k]);
+        }
+      }
+    }
+  }
+  float gq[8], gk[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    gq[i] = (qk_norm && wq) ? 1.f + wq[e0 + i] : 1.f;
+    gk[i] = (qk_norm && wk) ? 1.f + wk[e0 + i] : 1.f;
+  }
+  for (int h0 = 0; h0 < nh; h0 += U * HPW) {
+    if (h0 > 0) load_step(h0);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int h = h0 + u * HPW + hsub;
+      float v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = x[u][i];
+      if (qk_norm) {
+        float ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ss += v[i] * v[i];
+        const float inv = rsqrtf(group_sum<LPH>(ss) / (float)HD + eps);
+        const bool isq = h < H;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] *= inv * (isq ? gq[i] : gk[i]);
+      }
+      float o[8];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        o[2 * k] = v[2 * k] * c[k] - v[2 * k + 1] * s[k];
+        o[2 * k + 1] = v[2 * k] * s[k] + v[2 * k + 1] * c[k];
+      }
+      if (h < nh) Oct<T>::store(base + h * HD, o);
+    }
+  }
+}
+
+hipError_t launch_qk_prologue(bool f32, int head_dim, void *qkvg, const float *wq, const float *wk, int T,
+                              int L, int H, int Hkv, int qk_norm, int rope, int grid_h, int grid_w,
+                              const int axes[3], float theta, float eps, hipStream_t s) {
+  const dim3 grid((T + 3) / 4), block(256);
+#define DIT_QP(TT, HDV)                                                                                \
+  hipLaunchKernelGGL((qk_prologue_kernel<TT, HDV>), grid, block, 0, s, (TT *)qkvg, wq, wk, T, L, H, Hkv, \
+                     qk_norm, rope, grid_h, grid_w, axes[0], axes[1], theta, eps)
+  if (head_dim == 128) {
+    if (f32) DIT_QP(float, 128); else DIT_QP(bf16, 128);
+  } else if (head_dim == 64) {
+    if (f32) DIT_QP(float, 64); else DIT_QP(bf16, 64);
+  } else {
+    return hipErrorInvalidValue;
+  }
+#undef DIT_QP
+  return hipGetLastError();
+}
+
+}  // namespace dit

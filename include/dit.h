@@ -11,7 +11,9 @@
  *     single-stream (one set of weights over the joint text+image sequence),
  *     and a SwiGLU MLP;
  *   - 架构 › 残差设计: standard (here: gated) residual connections.
- * Positional terms and QKNorm are not part of this path.
+ * Positional terms and QKNorm are off by default; the *_ex entry points
+ * add the pages' attention prologue (QKNorm and 3D axial RoPE, see
+ * dit_prologue).
  *
  * Conventions shared by every entry point
  *   - Every pointer argument is a DEVICE pointer unless marked (host).
@@ -91,7 +93,37 @@ typedef struct {
                          /* scale2, gate2                                       */
   const float *norm1_w;  /* [D] fp32 zero-centred gain w (gain = 1 + w);        */
   const float *norm2_w;  /* NULL means w = 0                                    */
+  const float *q_norm_w; /* [d] fp32 zero-centred QKNorm gains of the query and */
+  const float *k_norm_w; /* key heads (used only with dit_prologue.qk_norm);    */
+                         /* NULL means w = 0                                    */
 } dit_block_weights;
+
+/* Optional attention prologue (page "Krea 2 技术报告", 架构 › 归一化:
+ * RMSNorm also as the QKNorm; 架构 › 位置编码: 3D axial RoPE with the head
+ * dimensions assigned to frame, height and width, text tokens at RoPE index
+ * zero).  Applied to every query and key head right after the QKVG
+ * projection, before attention; V and the gate are untouched:
+ *   qk_norm: q = q / sqrt(mean_d(q^2) + eps) * (1 + q_norm_w), k likewise
+ *            with k_norm_w;
+ *   rope:    the dimension pairs (2j, 2j+1) are rotated,
+ *            (x0, x1) -> (x0 cos a - x1 sin a, x0 sin a + x1 cos a), where
+ *            pair i of axis A (axes[A] dimensions, axes in the order frame,
+ *            height, width) has a = pos_A * theta^(-2i / axes[A]).  Image
+ *            token l < grid_h * grid_w of a sample (raster order) has
+ *            pos = (0, l / grid_w, l % grid_w); every later token (text)
+ *            has pos = (0, 0, 0).
+ * The axis split, the adjacent-pair convention and theta are this library's
+ * readings (the pages do not give them).  Requirements: qk_norm, rope in
+ * {0, 1}; with rope: grid_h, grid_w >= 1, grid_h * grid_w <= seq_len, each
+ * axes[i] >= 0 and even, axes[0] + axes[1] + axes[2] == head_dim, theta > 0
+ * (else DIT_ERR_SHAPE). */
+typedef struct {
+  int32_t qk_norm;
+  int32_t rope;
+  int32_t grid_h, grid_w;
+  int32_t axes[3];
+  float theta;
+} dit_prologue;
 
 /* Kernel classes, for the timing hook. */
 typedef enum {
@@ -103,7 +135,8 @@ typedef enum {
   DIT_K_GEMM_W13 = 5,  /* h2 * W_13^T with SwiGLU epilogue     */
   DIT_K_GEMM_W2 = 6,   /* U * W_2^T                            */
   DIT_K_TMOD = 7,      /* timestep embedding + modulation MLP  */
-  DIT_K_COUNT = 8
+  DIT_K_PROLOGUE = 8,  /* QKNorm + RoPE on Q and K (if enabled) */
+  DIT_K_COUNT = 9
 } dit_kernel_kind;
 
 /* Workspace bytes needed by dit_block_fwd for this configuration
@@ -147,6 +180,24 @@ dit_status dit_block_fwd(const dit_config *cfg /* host */, const dit_block_weigh
 dit_status dit_stack_fwd(const dit_config *cfg /* host */, int32_t n_blocks,
                          const dit_block_weights *blocks /* host [n_blocks] */, const void *x_in,
                          void *x_out, const float *mod, void *ws, size_t ws_bytes, void *stream);
+
+/* dit_block_fwd / dit_stack_fwd with the attention prologue `pro` (host;
+ * NULL = none, the same as the plain entry points) applied to Q and K
+ * after every block's QKVG projection, with that block's q_norm_w and
+ * k_norm_w.  Same workspace sizes. */
+dit_status dit_block_fwd_ex(const dit_config *cfg /* host */, const dit_prologue *pro /* host */,
+                            const dit_block_weights *w /* host */, const void *x_in, void *x_out,
+                            const float *mod, void *ws, size_t ws_bytes, void *stream);
+dit_status dit_stack_fwd_ex(const dit_config *cfg /* host */, const dit_prologue *pro /* host */,
+                            int32_t n_blocks, const dit_block_weights *blocks /* host [n_blocks] */,
+                            const void *x_in, void *x_out, const float *mod, void *ws, size_t ws_bytes,
+                            void *stream);
+
+/* The prologue as a step: transforms the Q and K column blocks of qkvg
+ * [T, (2H+2Hkv)*d] (dtype, as produced by the QKVG projection) in place;
+ * V and G are not touched.  q_norm_w, k_norm_w [d] fp32 or NULL. */
+dit_status dit_qk_prologue(const dit_config *cfg /* host */, const dit_prologue *pro /* host */,
+                           const float *q_norm_w, const float *k_norm_w, void *qkvg, void *stream);
 
 /* Shared timestep modulation of every sample:
  *   e = [cos(1000 t f_i), sin(1000 t f_i)], f_i = 10000^(-i/(t_dim/2)),

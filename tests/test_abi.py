@@ -183,3 +183,27 @@ def test_gemm_plan_choices():
             assert p["sk_tiles"] == 0 or 2 <= p["segs"] <= 8
     with pytest.raises(dit.DitError):
         dit.gemm_plan(0, 16, 16)
+
+
+def test_prologue_argument_checks():
+    """dit_prologue validation happens before anything is enqueued."""
+    L = dit.lib()
+    c = cfg()
+    G = 1 << 30
+    S = lambda st: _lib.STATUS[st]
+    good = dit.make_prologue(grid_h=2, grid_w=3, axes=(16, 24, 24))  # head_dim 64
+    assert S(L.dit_qk_prologue(ctypes.byref(c), None, 0, 0, P, None)) == "DIT_ERR_NULL"
+    assert S(L.dit_qk_prologue(ctypes.byref(c), ctypes.byref(good), 0, 0, 0, None)) == "DIT_ERR_NULL"
+    assert S(L.dit_qk_prologue(ctypes.byref(c), ctypes.byref(good), P + 4, 0, P + G, None)) == "DIT_ERR_ALIGN"
+    for bad in (dit.make_prologue(grid_h=2, grid_w=3, axes=(16, 24, 16)),        # sum != head_dim
+                dit.make_prologue(grid_h=2, grid_w=3, axes=(15, 25, 24)),        # odd
+                dit.make_prologue(grid_h=0, grid_w=3, axes=(16, 24, 24)),        # empty grid
+                dit.make_prologue(grid_h=2, grid_w=3, axes=(16, 24, 24), theta=0.0),
+                dit.make_prologue(grid_h=9, grid_w=9, axes=(16, 24, 24)),        # more tokens than seq_len
+                _lib.Prologue(2, 0, 0, 0, (ctypes.c_int32 * 3)(0, 0, 0), 1.0)):
+        assert S(L.dit_qk_prologue(ctypes.byref(c), ctypes.byref(bad), 0, 0, P, None)) == "DIT_ERR_SHAPE"
+        assert S(L.dit_block_fwd_ex(ctypes.byref(c), ctypes.byref(bad), None, P, P + G, P + 2 * G, P + 3 * G,
+                                    1 << 40, None)) == "DIT_ERR_SHAPE"
+    # rope off: the grid and axes are not looked at
+    off = _lib.Prologue(1, 0, 0, 0, (ctypes.c_int32 * 3)(0, 0, 0), 0.0)
+    assert S(L.dit_qk_prologue(ctypes.byref(c), ctypes.byref(off), 0, 0, 0, None)) == "DIT_ERR_NULL"
