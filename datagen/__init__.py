@@ -34,13 +34,15 @@ import numpy as np
 __all__ = [
     "Config", "CONFIGS", "get_config", "bf16_bits", "bf16_round", "bits_to_f32",
     "BlockWeights", "block_weights", "activations", "block_mod", "timestep_inputs",
-    "qkvg_activations", "rng", "qk_norm_weights",
+    "qkvg_activations", "rng", "qk_norm_weights", "ModelWeights", "model_weights", "latent_noise",
+    "text_features",
 ]
 
 # tensor ids used in the spawn keys (stable: changing one changes the data)
 TID_X, TID_T, TID_WT1, TID_WT2, TID_MOD = 0, 1, 2, 3, 4
 TID_WQKVG, TID_WO, TID_W13, TID_W2, TID_MODBIAS, TID_NORM1, TID_NORM2 = 10, 11, 12, 13, 14, 15, 16
 TID_QNORM, TID_KNORM = 17, 18
+TID_WIN, TID_WTXT, TID_WTF, TID_NORMF, TID_WOUT, TID_Z, TID_TXT = 40, 41, 42, 43, 44, 45, 46
 TID_QKVG_ACT = 20
 TID_GEMM_A, TID_GEMM_W = 30, 31
 
@@ -68,6 +70,8 @@ class Config:
     t_dim: int = 256  # sinusoidal timestep-embedding width
     grid_h: int = 0  # latent patch grid of the image tokens (grid_h * grid_w = n_image)
     grid_w: int = 0
+    latent_ch: int = 16  # autoencoder latent channels C; 2 x 2 patches -> 4C per token
+    txt_dim: int = 4096  # width of the text-encoder features
 
     @property
     def seq_len(self) -> int:
@@ -223,3 +227,40 @@ def gemm_operands(cfg: Config, m: int, n: int, k: int, tag: int = 0):
     a = _normal(cfg, 1000 + tag, TID_GEMM_A, (m, k), 1.0, True)
     w = _normal(cfg, 1000 + tag, TID_GEMM_W, (n, k), cfg.w_std, True)
     return a, w
+
+
+# ---------------------------------------------------------------- boundary layers and sampler inputs
+@dataclasses.dataclass
+class ModelWeights:
+    """The layers around the block stack (float32 arrays; model-dtype ones bf16-exact)."""
+
+    w_in: np.ndarray  # [D, 4C] patch embedding
+    w_txt: np.ndarray  # [D, txt_dim] text-feature projection
+    w_t1: np.ndarray  # [D, t_dim] fp32 timestep MLP, first layer
+    w_t2: np.ndarray  # [6D, D] fp32 shared block modulation
+    w_tf: np.ndarray  # [2D, D] fp32 final-norm shift / scale
+    norm_f_w: np.ndarray  # [D] fp32 zero-centred gain of the final norm
+    w_out: np.ndarray  # [4C, D] output projection to the patch vector
+
+
+def model_weights(cfg: Config) -> ModelWeights:
+    d, p = cfg.hidden, 4 * cfg.latent_ch
+    _, w_t1, w_t2 = timestep_inputs(cfg)
+    return ModelWeights(
+        w_in=_normal(cfg, 0, TID_WIN, (d, p), cfg.w_std, True),
+        w_txt=_normal(cfg, 0, TID_WTXT, (d, cfg.txt_dim), cfg.w_std, True),
+        w_t1=w_t1, w_t2=w_t2,
+        w_tf=_normal(cfg, 0, TID_WTF, (2 * d, d), cfg.w_std, False),
+        norm_f_w=_normal(cfg, 0, TID_NORMF, (d,), cfg.w_std, False),
+        w_out=_normal(cfg, 0, TID_WOUT, (p, d), cfg.w_std, True),
+    )
+
+
+def latent_noise(cfg: Config) -> np.ndarray:
+    """Starting latent z ~ N(0, 1) [B, C, 2 grid_h, 2 grid_w] fp32."""
+    return _normal(cfg, 0, TID_Z, (cfg.batch, cfg.latent_ch, 2 * cfg.grid_h, 2 * cfg.grid_w), 1.0, False)
+
+
+def text_features(cfg: Config) -> np.ndarray:
+    """Text-encoder features ~ N(0, 1) [B, n_text, txt_dim], model dtype."""
+    return _normal(cfg, 0, TID_TXT, (cfg.batch, cfg.n_text, cfg.txt_dim), 1.0, True)

@@ -32,6 +32,15 @@ Parity status (what pins each function; see the tests under
   differences along an axis) and by planted mistakes.  The axis split
   (32, 48, 48), the adjacent-pair convention and the base 10000 are
   readings: parity of those conventions is unpinned by the pages.
+* ``patchify``/``unpatchify``, ``embed_tokens``, ``final_mod``,
+  ``final_layer``, ``flow_schedule``, ``euler_sample``,
+  ``model_velocity`` (the stack's boundary layers and the rectified-flow
+  sampler): pinned by explicit index loops for the patch layout and its
+  round trip, by the schedule's closed forms, by exact integration of a
+  straight-path velocity field (Euler lands on x0), and by torch routines
+  for the norm; the layer conventions (16-channel latent, 2 x 2 patches,
+  bias-free embeddings, the final modulation map, the shift form) are
+  readings: parity of those conventions is unpinned by the pages.
 * The zero-centred gain form ``(1 + w)`` of the RMSNorm is a reading of
   the pages (weight decay on a zero-centred parameter); parity of that
   convention is unpinned by the pages, though the arithmetic under it is
@@ -41,6 +50,14 @@ from .dit_oracle import (  # noqa: F401
     OracleConfig,
     Prologue,
     apply_rope,
+    embed_tokens,
+    euler_sample,
+    final_layer,
+    final_mod,
+    flow_schedule,
+    model_velocity,
+    patchify,
+    unpatchify,
     attention_prologue,
     qk_rmsnorm,
     rope_angles,

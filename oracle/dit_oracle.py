@@ -324,3 +324,90 @@ def stack_forward(x, mod, weights: Iterable | Callable[[int], object], n_blocks:
     for i in range(n_blocks):
         y = block_forward(y, mod, get(i), oc, pro)
     return y
+
+
+# ------------------------------------------------------------------ boundary layers and sampler
+# Page "Krea 2 技术报告": 架构 (the DiT over latent tokens of an autoencoder,
+# Qwen-Image / FLUX 2 VAE, text features from Qwen3-VL); 训练 › 预训练: the
+# model is trained with the standard rectified-flow loss and
+# v-parameterization, and training and inference use a shifted sampling
+# schedule whose inference shift is kept constant.  Readings where the
+# pages are silent (parity unpinned: conventions of the boundary layers):
+#
+# * latent z [B, C, Hl, Wl]; 2 x 2 patches in raster order, patch vector
+#   index c * 4 + dy * 2 + dx; image tokens first, then text tokens;
+# * bias-free linear embeddings: image token = W_in p, text token = W_txt f;
+# * final layer on the image tokens: zero-centred RMSNorm with adaLN
+#   shift/scale (mod_f = W_tf silu(W_t1 e(t)), [B, 2, D]: shift, scale),
+#   then v_patch = W_out h, unpatchified to [B, C, Hl, Wl];
+# * velocity v = eps - x0 on the path z_t = (1 - t) x0 + t eps, sampled from
+#   t = 1 to 0 with Euler steps z <- z + (t_next - t) v(z, t);
+# * schedule t_i = s u_i / (1 + (s - 1) u_i), u_i = 1 - i / N, shift s.
+def patchify(z) -> np.ndarray:
+    """[B, C, Hl, Wl] -> [B, (Hl/2)(Wl/2), 4C]: 2 x 2 patches in raster order,
+    vector index c * 4 + dy * 2 + dx."""
+    z = _f64(z)
+    B, C, Hl, Wl = z.shape
+    t = z.reshape(B, C, Hl // 2, 2, Wl // 2, 2)          # b c py dy px dx
+    t = t.transpose(0, 2, 4, 1, 3, 5)                    # b py px c dy dx
+    return t.reshape(B, (Hl // 2) * (Wl // 2), C * 4)
+
+
+def unpatchify(p, C: int, Hl: int, Wl: int) -> np.ndarray:
+    """Inverse of patchify: [B, (Hl/2)(Wl/2), 4C] -> [B, C, Hl, Wl]."""
+    p = _f64(p)
+    B = p.shape[0]
+    t = p.reshape(B, Hl // 2, Wl // 2, C, 2, 2).transpose(0, 3, 1, 4, 2, 5)
+    return t.reshape(B, C, Hl, Wl)
+
+
+def embed_tokens(z, txt, w_in, w_txt) -> np.ndarray:
+    """Joint token sequence [B, n_img + n_txt, D]: W_in applied to the
+    patches of z, then W_txt applied to the text features txt [B, n_txt, D_txt]."""
+    img = patchify(z) @ _f64(w_in).T
+    return np.concatenate([img, _f64(txt) @ _f64(w_txt).T], axis=1)
+
+
+def final_mod(t, w_t1, w_tf, hidden: int) -> np.ndarray:
+    """[B, 2, D] shift and scale of the final norm: W_tf silu(W_t1 e(t))."""
+    e = time_embedding(t, dim=_f64(w_t1).shape[1])
+    return (silu(e @ _f64(w_t1).T) @ _f64(w_tf).T).reshape(-1, 2, hidden)
+
+
+def final_layer(x_img, modf, norm_w, w_out, eps: float) -> np.ndarray:
+    """v tokens [B, n_img, 4C] = W_out (rmsnorm(x) (1 + w) (1 + scale) + shift)."""
+    x_img = _f64(x_img)
+    out = []
+    for b in range(x_img.shape[0]):
+        h = modulated_rmsnorm(x_img[b], norm_w, modf[b, 0], modf[b, 1], eps)
+        out.append(h @ _f64(w_out).T)
+    return np.stack(out)
+
+
+def flow_schedule(n_steps: int, shift: float) -> np.ndarray:
+    """n_steps + 1 times from 1 to 0: s u / (1 + (s - 1) u), u = 1 - i / n_steps."""
+    u = 1.0 - np.arange(n_steps + 1, dtype=F64) / n_steps
+    return shift * u / (1.0 + (shift - 1.0) * u)
+
+
+def euler_sample(z, times, velocity: Callable) -> np.ndarray:
+    """z <- z + (t_{i+1} - t_i) velocity(z, t_i) over the schedule."""
+    z = _f64(z)
+    for i in range(len(times) - 1):
+        z = z + (times[i + 1] - times[i]) * velocity(z, times[i])
+    return z
+
+
+def model_velocity(z, t, txt, model, blocks, n_blocks: int, oc: OracleConfig, pro=None) -> np.ndarray:
+    """The DiT as a velocity field: embed, the block stack with the shared
+    timestep modulation, final layer, unpatchify.  ``model`` carries w_in,
+    w_txt, w_t1, w_t2, w_tf, norm_f_w, w_out; t is one time for every sample."""
+    B, C, Hl, Wl = np.shape(z)
+    tb = np.full(B, t)
+    x = embed_tokens(z, txt, model.w_in, model.w_txt)
+    mod = timestep_modulation(tb, model.w_t1, model.w_t2, oc.hidden)
+    y = stack_forward(x, mod, blocks, n_blocks, oc, pro)
+    n_img = (Hl // 2) * (Wl // 2)
+    v = final_layer(y[:, :n_img], final_mod(tb, model.w_t1, model.w_tf, oc.hidden), model.norm_f_w,
+                    model.w_out, oc.eps)
+    return unpatchify(v, C, Hl, Wl)

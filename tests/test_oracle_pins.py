@@ -406,3 +406,94 @@ def test_qk_norm_is_torch_rms_norm():
     unit = O.qk_rmsnorm(x, None, 0.0)
     assert np.allclose(np.sqrt(np.mean(unit ** 2, axis=-1)), 1.0, atol=1e-14)
     assert np.allclose(O.qk_rmsnorm(7.5 * x, w, 0.0), O.qk_rmsnorm(x, w, 0.0), atol=1e-13)
+
+
+# ------------------------------------------------------------------ boundary layers and sampler
+def test_patchify_layout_and_round_trip():
+    """Token (py, px) in raster order holds z[c, 2py+dy, 2px+dx] at c*4 + dy*2 + dx;
+    unpatchify inverts it."""
+    B, C, Hl, Wl = 2, 3, 4, 6
+    z = np.arange(B * C * Hl * Wl, dtype=np.float64).reshape(B, C, Hl, Wl)
+    p = O.patchify(z)
+    assert p.shape == (B, (Hl // 2) * (Wl // 2), 4 * C)
+    for b in range(B):
+        for py in range(Hl // 2):
+            for px in range(Wl // 2):
+                for c in range(C):
+                    for dy in range(2):
+                        for dx in range(2):
+                            assert p[b, py * (Wl // 2) + px, c * 4 + dy * 2 + dx] == z[b, c, 2 * py + dy, 2 * px + dx]
+    assert np.array_equal(O.unpatchify(p, C, Hl, Wl), z)
+
+
+def test_flow_schedule_closed_forms():
+    t = O.flow_schedule(8, 3.0)
+    assert t[0] == 1.0 and t[-1] == 0.0 and np.all(np.diff(t) < 0)
+    assert np.allclose(O.flow_schedule(4, 1.0), [1.0, 0.75, 0.5, 0.25, 0.0], atol=0, rtol=0)
+    assert abs(O.flow_schedule(2, 3.0)[1] - 0.75) < 1e-15  # s u / (1 + (s-1) u) at u = 1/2: 3/4
+
+
+def test_euler_integrates_a_straight_path_exactly():
+    """For the straight path z_t = (1-t) x0 + t eps the velocity is eps - x0 at
+    every point, so the sampler must land on x0 for any schedule (signs and
+    step direction pinned)."""
+    r = np.random.default_rng(2)
+    x0, eps = r.standard_normal((2, 3, 4, 4)), r.standard_normal((2, 3, 4, 4))
+    for n, s in ((1, 1.0), (8, 3.0), (28, 6.0)):
+        out = O.euler_sample(eps, O.flow_schedule(n, s), lambda z, t: (z - x0) / t)
+        assert np.max(np.abs(out - x0)) < 1e-12
+
+
+def test_embed_and_final_layer_against_torch_and_loops():
+    """Embedding = torch linear on patches / text features; the final layer =
+    torch rms_norm with the adaLN terms, then linear; scale = -1 gives W_out shift."""
+    cfg = datagen.Config("tiny-model", batch=2, n_image=6, n_text=3, hidden=8, n_heads=2, n_kv_heads=1,
+                         head_dim=4, ffn=8, dtype="f32", seed=9, w_std=0.5, out_std=0.5, grid_h=2, grid_w=3,
+                         latent_ch=2, txt_dim=5, t_dim=8)
+    mw = datagen.model_weights(cfg)
+    z = datagen.latent_noise(cfg)
+    txt = datagen.text_features(cfg)
+    x = O.embed_tokens(z, txt, mw.w_in, mw.w_txt)
+    pt = torch.from_numpy(O.patchify(z))
+    assert np.allclose(x[:, :6], F.linear(pt, torch.from_numpy(mw.w_in).double()).numpy(), atol=1e-13)
+    assert np.allclose(x[:, 6:], F.linear(torch.from_numpy(txt).double(), torch.from_numpy(mw.w_txt).double()).numpy(),
+                       atol=1e-13)
+    modf = O.final_mod(np.array([0.3, 0.8]), mw.w_t1, mw.w_tf, 8)
+    v = O.final_layer(x[:, :6], modf, mw.norm_f_w, mw.w_out, 1e-6)
+    xt = torch.from_numpy(x[:, :6])
+    h = F.rms_norm(xt, (8,), weight=torch.from_numpy(1.0 + mw.norm_f_w).double(), eps=1e-6)
+    h = h * (1 + torch.from_numpy(modf[:, 1:2])) + torch.from_numpy(modf[:, 0:1])
+    assert np.allclose(v, F.linear(h, torch.from_numpy(mw.w_out).double()).numpy(), atol=1e-12)
+    m2 = modf.copy()
+    m2[:, 1] = -1.0
+    v2 = O.final_layer(x[:, :6], m2, mw.norm_f_w, mw.w_out, 1e-6)
+    assert np.allclose(v2, (m2[:, 0] @ mw.w_out.astype(np.float64).T)[:, None, :], atol=1e-13)
+
+
+def test_model_velocity_with_no_blocks_matches_per_token_loops():
+    """With an empty stack the velocity is the boundary layers alone: check
+    every latent element against scalar loops (text tokens do not reach the
+    output; image token order = patch order)."""
+    cfg = datagen.Config("tiny-model", batch=1, n_image=4, n_text=2, hidden=4, n_heads=1, n_kv_heads=1,
+                         head_dim=4, ffn=4, dtype="f32", seed=11, w_std=0.5, out_std=0.5, grid_h=2, grid_w=2,
+                         latent_ch=1, txt_dim=3, t_dim=4)
+    mw = datagen.model_weights(cfg)
+    z = datagen.latent_noise(cfg)
+    txt = datagen.text_features(cfg)
+    oc_ = O.OracleConfig.of(cfg)
+    v = O.model_velocity(z, 0.6, txt, mw, [], 0, oc_)
+    e = bruteforce.time_embedding([0.6], dim=4)[0]
+    zs = [sum(float(mw.w_t1[r][k]) * e[k] for k in range(4)) for r in range(4)]
+    zs = [a / (1 + math.exp(-a)) for a in zs]
+    fm = [sum(float(mw.w_tf[o][r]) * zs[r] for r in range(4)) for o in range(8)]
+    shift, scale = fm[:4], fm[4:]
+    for py in range(2):
+        for px in range(2):
+            patch = [float(z[0, 0, 2 * py + dy, 2 * px + dx]) for dy in range(2) for dx in range(2)]
+            tok = [sum(float(mw.w_in[o][i]) * patch[i] for i in range(4)) for o in range(4)]
+            rms = math.sqrt(sum(a * a for a in tok) / 4 + cfg.eps)
+            h = [tok[c] / rms * (1 + float(mw.norm_f_w[c])) * (1 + scale[c]) + shift[c] for c in range(4)]
+            out = [sum(float(mw.w_out[o][c]) * h[c] for c in range(4)) for o in range(4)]
+            for dy in range(2):
+                for dx in range(2):
+                    assert abs(v[0, 0, 2 * py + dy, 2 * px + dx] - out[dy * 2 + dx]) < 1e-12
