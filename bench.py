@@ -129,9 +129,41 @@ def bench_stack(dit, torch, steps: int, warmup: int) -> dict:
            "block_tokens_per_s": cfg.n_blocks * cfg.tokens / dt, "tflops": fl / dt / 1e12,
            "mfma_frac": fl / dt / 1e12 / PEAK_BF16_TFLOPS, "steps": steps, "warmup": warmup,
            "weights_gb": sum(t.numel() * t.element_size() for b in blocks for t in b.values()) / 1e9}
+    out["sample"] = bench_sample(dit, torch, cfg, c, blocks, randn)
     del blocks
     torch.cuda.empty_cache()
     return out
+
+
+def bench_sample(dit, torch, cfg, c, blocks, randn, n_steps: int = 8, shift: float = 3.0, reps: int = 2) -> dict:
+    """One image's denoising at 1024 px, batch 1: n_steps Euler steps of the
+    rectified-flow sampler, each the full model (patch and text embeddings,
+    the 60-block stack, final layer).  The pages' Turbo checkpoint is said
+    to make an image in under a second (hardware not stated; with 8 steps
+    per a commenter); this measures the DiT part of that, not the text
+    encoder or the autoencoder.  Random-init weights of the same shapes."""
+    d, C, txt_dim = cfg.hidden, cfg.latent_ch, cfg.txt_dim
+    mw = {"w_in": randn((d, 4 * C), cfg.w_std), "w_txt": randn((d, txt_dim), cfg.w_std),
+          "w_t1": randn((d, cfg.t_dim), cfg.w_std, torch.float32), "w_t2": randn((6 * d, d), cfg.w_std, torch.float32),
+          "w_tf": randn((2 * d, d), cfg.w_std, torch.float32), "norm_f_w": randn((d,), cfg.w_std, torch.float32),
+          "w_out": randn((4 * C, d), cfg.w_std)}
+    mc = dit.make_model_config(C, cfg.grid_h, cfg.grid_w, cfg.n_text, txt_dim, cfg.t_dim)
+    z0 = randn((1, C, 2 * cfg.grid_h, 2 * cfg.grid_w), 1.0, torch.float32)
+    txt = randn((1, cfg.n_text, txt_dim), 1.0)
+    ws = torch.empty(dit.model_workspace_size(c, mc), dtype=torch.uint8, device="cuda")
+    z = z0.clone()
+    dit.sample(c, mc, mw, blocks, z, n_steps, shift, txt, ws)  # warm-up
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        z.copy_(z0)
+        dit.sample(c, mc, mw, blocks, z, n_steps, shift, txt, ws)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / reps
+    return {"workload": "krea2-sample-1024px", "batch": 1, "n_steps": n_steps, "shift": shift,
+            "n_blocks": cfg.n_blocks, "latent": [C, 2 * cfg.grid_h, 2 * cfg.grid_w], "text_tokens": cfg.n_text,
+            "ms_per_image": dt * 1e3, "ms_per_step": dt * 1e3 / n_steps, "reps": reps,
+            "finite": bool(torch.isfinite(z).all().item())}
 
 
 def bench_prologue(dit, torch, cfg, c, W, X, Y, M, ws, step, steps: int, warmup: int) -> dict:

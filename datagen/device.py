@@ -40,3 +40,16 @@ def weights_to_device(w, dtype: str, device="cuda") -> dict:
         **({"q_norm_w": to_device(w.q_norm_w, "f32", device)} if getattr(w, "q_norm_w", None) is not None else {}),
         **({"k_norm_w": to_device(w.k_norm_w, "f32", device)} if getattr(w, "k_norm_w", None) is not None else {}),
     }
+
+
+def model_to_device(mw, dtype: str, device="cuda") -> dict:
+    """datagen.ModelWeights -> dict of device tensors keyed like dit_model_weights."""
+    return {
+        "w_in": to_device(mw.w_in, dtype, device),
+        "w_txt": to_device(mw.w_txt, dtype, device),
+        "w_t1": to_device(mw.w_t1, "f32", device),
+        "w_t2": to_device(mw.w_t2, "f32", device),
+        "w_tf": to_device(mw.w_tf, "f32", device),
+        "norm_f_w": to_device(mw.norm_f_w, "f32", device),
+        "w_out": to_device(mw.w_out, dtype, device),
+    }

@@ -26,7 +26,7 @@ EXPORTS = (
     "dit_timestep_mod", "dit_modnorm", "dit_gemm", "dit_gemm_swiglu", "dit_gemm_variant", "dit_attention",
     "dit_gated_residual", "dit_status_str", "dit_last_hip_error", "dit_timer_start",
     "dit_timer_stop", "dit_gemm_splitk", "dit_gemm_plan", "dit_block_fwd_ex", "dit_stack_fwd_ex",
-    "dit_qk_prologue",
+    "dit_qk_prologue", "dit_model_workspace_size", "dit_model_velocity", "dit_sample",
 )
 
 
@@ -52,6 +52,18 @@ class BlockWeights(ctypes.Structure):
                 ("w_2", ctypes.c_void_p), ("mod_bias", ctypes.c_void_p),
                 ("norm1_w", ctypes.c_void_p), ("norm2_w", ctypes.c_void_p),
                 ("q_norm_w", ctypes.c_void_p), ("k_norm_w", ctypes.c_void_p)]
+
+
+class ModelConfig(ctypes.Structure):
+    """dit_model_config: latent and text shapes around the stack."""
+    _fields_ = [("latent_ch", ctypes.c_int32), ("grid_h", ctypes.c_int32), ("grid_w", ctypes.c_int32),
+                ("n_text", ctypes.c_int32), ("txt_dim", ctypes.c_int32), ("t_dim", ctypes.c_int32)]
+
+
+class ModelWeights(ctypes.Structure):
+    _fields_ = [("w_in", ctypes.c_void_p), ("w_txt", ctypes.c_void_p), ("w_t1", ctypes.c_void_p),
+                ("w_t2", ctypes.c_void_p), ("w_tf", ctypes.c_void_p), ("norm_f_w", ctypes.c_void_p),
+                ("w_out", ctypes.c_void_p)]
 
 
 class Prologue(ctypes.Structure):
@@ -80,6 +92,12 @@ def lib() -> ctypes.CDLL:
             "dit_block_fwd_ex": (i32, [cfgp, ctypes.POINTER(Prologue), wp, vp, vp, vp, vp, sz, vp]),
             "dit_stack_fwd_ex": (i32, [cfgp, ctypes.POINTER(Prologue), i32, wp, vp, vp, vp, vp, sz, vp]),
             "dit_qk_prologue": (i32, [cfgp, ctypes.POINTER(Prologue), vp, vp, vp, vp]),
+            "dit_model_workspace_size": (sz, [cfgp, ctypes.POINTER(ModelConfig)]),
+            "dit_model_velocity": (i32, [cfgp, ctypes.POINTER(ModelConfig), ctypes.POINTER(Prologue),
+                                         ctypes.POINTER(ModelWeights), i32, wp, vp, ctypes.c_float, vp, vp, vp, sz,
+                                         vp]),
+            "dit_sample": (i32, [cfgp, ctypes.POINTER(ModelConfig), ctypes.POINTER(Prologue),
+                                 ctypes.POINTER(ModelWeights), i32, wp, vp, i32, ctypes.c_float, vp, vp, sz, vp]),
             "dit_stack_fwd": (i32, [cfgp, i32, wp, vp, vp, vp, vp, sz, vp]),
             "dit_timestep_mod": (i32, [cfgp, i32, vp, vp, vp, vp, vp, sz, vp]),
             "dit_modnorm": (i32, [cfgp, vp, i32, vp, vp, vp, vp, i32, vp]),
@@ -198,6 +216,41 @@ def qk_prologue(cfg: Config, pro: Prologue, qkvg, q_norm_w=None, k_norm_w=None, 
     """QKNorm + RoPE in place on the Q and K heads of qkvg [T, (2H+2Hkv)*d]."""
     _check(lib().dit_qk_prologue(ctypes.byref(cfg), ctypes.byref(pro), _ptr(q_norm_w), _ptr(k_norm_w),
                                  _ptr(qkvg), _stream(stream)), "dit_qk_prologue")
+
+
+def make_model_config(latent_ch: int, grid_h: int, grid_w: int, n_text: int, txt_dim: int,
+                      t_dim: int = 256) -> ModelConfig:
+    return ModelConfig(latent_ch, grid_h, grid_w, n_text, txt_dim, t_dim)
+
+
+def make_model_weights(m: Mapping) -> ModelWeights:
+    return ModelWeights(_ptr(m["w_in"]), _ptr(m.get("w_txt")), _ptr(m["w_t1"]), _ptr(m["w_t2"]),
+                        _ptr(m["w_tf"]), _ptr(m.get("norm_f_w")), _ptr(m["w_out"]))
+
+
+def model_workspace_size(cfg: Config, mc: ModelConfig) -> int:
+    return lib().dit_model_workspace_size(ctypes.byref(cfg), ctypes.byref(mc))
+
+
+def model_velocity(cfg: Config, mc: ModelConfig, mw: Mapping, blocks: Sequence[Mapping], z, t: float, txt,
+                   v_out, ws, pro: Prologue | None = None, stream=None) -> None:
+    arr = (BlockWeights * len(blocks))(*[make_weights(b) for b in blocks])
+    m = make_model_weights(mw)
+    nbytes = ws.numel() * ws.element_size()
+    _check(lib().dit_model_velocity(ctypes.byref(cfg), ctypes.byref(mc), None if pro is None else ctypes.byref(pro),
+                                    ctypes.byref(m), len(blocks), arr, _ptr(z), float(t), _ptr(txt), _ptr(v_out),
+                                    _ptr(ws), nbytes, _stream(stream)), "dit_model_velocity")
+
+
+def sample(cfg: Config, mc: ModelConfig, mw: Mapping, blocks: Sequence[Mapping], z, n_steps: int, shift: float, txt,
+           ws, pro: Prologue | None = None, stream=None) -> None:
+    """n_steps Euler steps of the rectified-flow sampler, z updated in place."""
+    arr = (BlockWeights * len(blocks))(*[make_weights(b) for b in blocks])
+    m = make_model_weights(mw)
+    nbytes = ws.numel() * ws.element_size()
+    _check(lib().dit_sample(ctypes.byref(cfg), ctypes.byref(mc), None if pro is None else ctypes.byref(pro),
+                            ctypes.byref(m), len(blocks), arr, _ptr(z), n_steps, float(shift), _ptr(txt), _ptr(ws),
+                            nbytes, _stream(stream)), "dit_sample")
 
 
 def stack_fwd(cfg: Config, blocks: Sequence[Mapping], x_in, x_out, mod, ws, stream=None) -> None:

@@ -228,6 +228,102 @@ dit_status run_block(const dit_config *c, const dit_prologue *pro, const dit_blo
   return DIT_OK;
 }
 
+// n_blocks blocks on a stack workspace (dit_stack_workspace_size bytes at ws)
+dit_status run_stack(const dit_config *cfg, const dit_prologue *pro, int n_blocks, const dit_block_weights *blocks,
+                     const void *x_in, void *x_out, const float *mod, void *ws, hipStream_t s) {
+  const BlockWs bw = carve(cfg, ws);
+  char *xa = (char *)ws + bw.bytes;  // fp32 residual stream between blocks
+  const bool f32 = cfg->dtype == DIT_F32;
+  for (int i = 0; i < n_blocks; ++i) {
+    const bool first = i == 0, last = i == n_blocks - 1;
+    dit_status st = run_block(cfg, pro, &blocks[i], first ? x_in : xa, first ? f32 : true, last ? x_out : xa,
+                              last ? f32 : true, mod, bw, bw.x1, s);
+    if (st != DIT_OK) return st;
+  }
+  return DIT_OK;
+}
+
+// ---------------------------------------------------------------- model around the stack
+dit_status check_model(const dit_config *c, const dit_model_config *mc, const dit_model_weights *mw) {
+  if (!mc || !mw) return DIT_ERR_NULL;
+  if (mc->latent_ch < 2 || (mc->latent_ch & 1) || mc->grid_h < 1 || mc->grid_w < 1 || mc->n_text < 0)
+    return DIT_ERR_SHAPE;
+  if ((int64_t)mc->grid_h * mc->grid_w + mc->n_text != c->seq_len) return DIT_ERR_SHAPE;
+  if (mc->n_text > 0 && (mc->txt_dim <= 0 || mc->txt_dim % 8)) return DIT_ERR_SHAPE;
+  if (mc->t_dim < 2 || mc->t_dim > 1024 || (mc->t_dim & 1)) return DIT_ERR_SHAPE;
+  if (!mw->w_in || !mw->w_t1 || !mw->w_t2 || !mw->w_tf || !mw->w_out) return DIT_ERR_NULL;
+  if (mc->n_text > 0 && !mw->w_txt) return DIT_ERR_NULL;
+  if (!aligned(mw->w_in) || !aligned(mw->w_txt) || !aligned(mw->w_t1) || !aligned(mw->w_t2) ||
+      !aligned(mw->w_tf) || !aligned(mw->norm_f_w) || !aligned(mw->w_out))
+    return DIT_ERR_ALIGN;
+  const uint64_t es = esize(c->dtype);
+  if ((uint64_t)6 * c->hidden * c->hidden > 0x7FFFFFFFull) return DIT_ERR_UNSUPPORTED;
+  if ((uint64_t)(c->hidden + 256) * mc->txt_dim * es > kMaxSpan) return DIT_ERR_UNSUPPORTED;
+  if ((uint64_t)c->batch * 4 * mc->latent_ch * mc->grid_h * mc->grid_w > 0x7FFFFFFFull) return DIT_ERR_UNSUPPORTED;
+  return DIT_OK;
+}
+
+struct ModelWs {
+  char *stack, *x, *y, *p, *vt;
+  float *mod, *modf, *zero, *zs, *t;
+  size_t bytes;
+};
+ModelWs carve_model(const dit_config *c, const dit_model_config *mc, void *ws) {
+  const Dims d = dims(c);
+  const size_t nimg = (size_t)c->batch * mc->grid_h * mc->grid_w, pv = 4 * (size_t)mc->latent_ch;
+  ModelWs w;
+  char *p = (char *)ws;
+  size_t off = 0;
+  auto take = [&](size_t n) {
+    char *r = p ? p + off : nullptr;
+    off += round_up(n);
+    return r;
+  };
+  w.stack = take(dit_stack_workspace_size(c));
+  w.x = take(d.T * d.D * d.es);
+  w.y = take(d.T * d.D * d.es);
+  w.p = take(nimg * pv * d.es);
+  w.vt = take(nimg * pv * d.es);
+  w.mod = (float *)take((size_t)c->batch * 6 * d.D * 4);
+  w.modf = (float *)take((size_t)c->batch * 2 * d.D * 4);
+  w.zero = (float *)take(2 * d.D * 4);
+  w.zs = (float *)take((size_t)c->batch * d.D * 4);
+  w.t = (float *)take((size_t)c->batch * 4);
+  w.bytes = off;
+  return w;
+}
+
+// v(z, t) into vtok (token layout) -- everything but the unpatchify
+dit_status model_tokens(const dit_config *c, const dit_model_config *mc, const dit_prologue *pro,
+                        const dit_model_weights *mw, int n_blocks, const dit_block_weights *blocks, const float *z,
+                        float t, const void *txt, const ModelWs &w, hipStream_t s) {
+  const Dims d = dims(c);
+  const bool f32 = c->dtype == DIT_F32;
+  const int B = c->batch, L = c->seq_len, D = (int)d.D, C = mc->latent_ch;
+  const int Hl = 2 * mc->grid_h, Wl = 2 * mc->grid_w, nimg = mc->grid_h * mc->grid_w, pv = 4 * C;
+  DIT_TRY(launch_fill(w.t, t, (size_t)B, s));
+  DIT_TRY(timed(DIT_K_TMOD, s, [&] {
+    hipError_t e = launch_tmod(w.t, mw->w_t1, mw->w_t2, w.mod, w.zs, B, D, mc->t_dim, s);
+    return e != hipSuccess ? e : launch_tmod_map(w.zs, mw->w_tf, w.modf, B, D, 2 * D, s);
+  }));
+  DIT_TRY(launch_patchify(f32, z, w.p, B, C, Hl, Wl, s));
+  for (int b = 0; b < B; ++b) {
+    DIT_TRY(launch_gemm(f32, w.p + (size_t)b * nimg * pv * d.es, mw->w_in, w.x + (size_t)b * L * D * d.es, nimg, D,
+                        pv, s));
+    if (mc->n_text > 0)
+      DIT_TRY(launch_gemm(f32, (const char *)txt + (size_t)b * mc->n_text * mc->txt_dim * d.es, mw->w_txt,
+                          w.x + ((size_t)b * L + nimg) * D * d.es, mc->n_text, D, mc->txt_dim, s));
+  }
+  dit_status st = run_stack(c, pro, n_blocks, blocks, w.x, w.y, w.mod, w.stack, s);
+  if (st != DIT_OK) return st;
+  DIT_TRY(launch_fill(w.zero, 0.f, 2 * d.D, s));
+  for (int b = 0; b < B; ++b)  // final norm on the image rows; its output reuses x
+    DIT_TRY(launch_modnorm(f32, f32, w.y + (size_t)b * L * D * d.es, w.x + (size_t)b * nimg * D * d.es,
+                           w.modf + (size_t)b * 2 * D, w.zero, mw->norm_f_w, nimg, nimg, D, c->eps, 0, s));
+  DIT_TRY(launch_gemm(f32, w.x, mw->w_out, w.vt, B * nimg, pv, D, s));
+  return DIT_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -308,17 +404,7 @@ dit_status dit_stack_fwd_ex(const dit_config *cfg, const dit_prologue *pro, int3
   if (overlap(ws, need, x_in, xb) || overlap(ws, need, x_out, xb) ||
       overlap(ws, need, mod, (size_t)cfg->batch * 6 * cfg->hidden * 4))
     return DIT_ERR_SHAPE;
-  const BlockWs bw = carve(cfg, ws);
-  char *xa = (char *)ws + bw.bytes;  // fp32 residual stream between blocks
-  const bool f32 = cfg->dtype == DIT_F32;
-  hipStream_t s = (hipStream_t)stream;
-  for (int i = 0; i < n_blocks; ++i) {
-    const bool first = i == 0, last = i == n_blocks - 1;
-    st = run_block(cfg, pro, &blocks[i], first ? x_in : xa, first ? f32 : true, last ? x_out : xa,
-                   last ? f32 : true, mod, bw, bw.x1, s);
-    if (st != DIT_OK) return st;
-  }
-  return DIT_OK;
+  return run_stack(cfg, pro, n_blocks, blocks, x_in, x_out, mod, ws, (hipStream_t)stream);
 }
 
 dit_status dit_stack_fwd(const dit_config *cfg, int32_t n_blocks, const dit_block_weights *blocks,
@@ -346,6 +432,77 @@ dit_status dit_qk_prologue(const dit_config *cfg, const dit_prologue *pro, const
                               pro->grid_w, pro->axes, pro->theta, cfg->eps, s);
   });
   return e == hipSuccess ? DIT_OK : hip_fail(e);
+}
+
+size_t dit_model_workspace_size(const dit_config *cfg, const dit_model_config *mc) {
+  if (check_cfg(cfg) != DIT_OK || !mc) return 0;
+  if (mc->latent_ch < 2 || mc->grid_h < 1 || mc->grid_w < 1) return 0;
+  return carve_model(cfg, mc, nullptr).bytes;
+}
+
+static dit_status check_model_call(const dit_config *cfg, const dit_model_config *mc, const dit_prologue *pro,
+                                   const dit_model_weights *mw, int32_t n_blocks, const dit_block_weights *blocks,
+                                   const float *z, const void *txt, void *ws, size_t ws_bytes) {
+  dit_status st = check_cfg(cfg);
+  if (st != DIT_OK) return st;
+  if ((st = check_prologue(cfg, pro)) != DIT_OK) return st;
+  if ((st = check_model(cfg, mc, mw)) != DIT_OK) return st;
+  if (n_blocks < 0) return DIT_ERR_SHAPE;
+  if (n_blocks > 0 && !blocks) return DIT_ERR_NULL;
+  for (int i = 0; i < n_blocks; ++i)
+    if ((st = check_weights(&blocks[i])) != DIT_OK) return st;
+  if (n_blocks == 0) return DIT_ERR_SHAPE;
+  if (!z || (mc->n_text > 0 && !txt)) return DIT_ERR_NULL;
+  if (!ws) return DIT_ERR_WORKSPACE;
+  if (!aligned(z) || !aligned(txt) || !aligned(ws)) return DIT_ERR_ALIGN;
+  const size_t need = carve_model(cfg, mc, nullptr).bytes;
+  if (ws_bytes < need) return DIT_ERR_WORKSPACE;
+  const size_t zb = (size_t)cfg->batch * mc->latent_ch * 4 * mc->grid_h * mc->grid_w * 4;
+  const size_t tb = txt ? (size_t)cfg->batch * mc->n_text * mc->txt_dim * esize(cfg->dtype) : 0;
+  if (overlap(ws, need, z, zb) || overlap(ws, need, txt, tb)) return DIT_ERR_SHAPE;
+  return DIT_OK;
+}
+
+dit_status dit_model_velocity(const dit_config *cfg, const dit_model_config *mc, const dit_prologue *pro,
+                              const dit_model_weights *mw, int32_t n_blocks, const dit_block_weights *blocks,
+                              const float *z, float t, const void *txt, float *v_out, void *ws, size_t ws_bytes,
+                              void *stream) {
+  dit_status st = check_model_call(cfg, mc, pro, mw, n_blocks, blocks, z, txt, ws, ws_bytes);
+  if (st != DIT_OK) return st;
+  if (!v_out) return DIT_ERR_NULL;
+  if (!aligned(v_out)) return DIT_ERR_ALIGN;
+  const size_t zb = (size_t)cfg->batch * mc->latent_ch * 4 * mc->grid_h * mc->grid_w * 4;
+  const size_t tb = mc->n_text ? (size_t)cfg->batch * mc->n_text * mc->txt_dim * esize(cfg->dtype) : 0;
+  if (overlap(v_out, zb, z, zb) || overlap(v_out, zb, txt, tb) || overlap(v_out, zb, ws, ws_bytes))
+    return DIT_ERR_SHAPE;
+  hipStream_t s = (hipStream_t)stream;
+  const ModelWs w = carve_model(cfg, mc, ws);
+  if ((st = model_tokens(cfg, mc, pro, mw, n_blocks, blocks, z, t, txt, w, s)) != DIT_OK) return st;
+  hipError_t e = launch_unpatchify_axpy(cfg->dtype == DIT_F32, w.vt, nullptr, v_out, 1.0f, cfg->batch,
+                                        mc->latent_ch, 2 * mc->grid_h, 2 * mc->grid_w, s);
+  return e == hipSuccess ? DIT_OK : hip_fail(e);
+}
+
+dit_status dit_sample(const dit_config *cfg, const dit_model_config *mc, const dit_prologue *pro,
+                      const dit_model_weights *mw, int32_t n_blocks, const dit_block_weights *blocks, float *z,
+                      int32_t n_steps, float shift, const void *txt, void *ws, size_t ws_bytes, void *stream) {
+  dit_status st = check_model_call(cfg, mc, pro, mw, n_blocks, blocks, z, txt, ws, ws_bytes);
+  if (st != DIT_OK) return st;
+  if (n_steps < 1 || n_steps > 100000 || !(shift > 0.f)) return DIT_ERR_SHAPE;
+  hipStream_t s = (hipStream_t)stream;
+  const ModelWs w = carve_model(cfg, mc, ws);
+  auto sched = [&](int i) {  // s u / (1 + (s - 1) u), u = 1 - i / n
+    const double u = 1.0 - (double)i / n_steps, sh = shift;
+    return sh * u / (1.0 + (sh - 1.0) * u);
+  };
+  for (int i = 0; i < n_steps; ++i) {
+    const double t0 = sched(i), t1 = sched(i + 1);
+    if ((st = model_tokens(cfg, mc, pro, mw, n_blocks, blocks, z, (float)t0, txt, w, s)) != DIT_OK) return st;
+    hipError_t e = launch_unpatchify_axpy(cfg->dtype == DIT_F32, w.vt, z, z, (float)(t1 - t0), cfg->batch,
+                                          mc->latent_ch, 2 * mc->grid_h, 2 * mc->grid_w, s);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  return DIT_OK;
 }
 
 dit_status dit_timestep_mod(const dit_config *cfg, int32_t t_dim, const float *t, const float *w_t1,

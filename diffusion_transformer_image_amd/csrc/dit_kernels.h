@@ -17,6 +17,14 @@ hipError_t launch_resid_modnorm(bool x_f32, bool f32, const void *x, const void 
                                 int seq_len, int D, float eps, hipStream_t s);
 hipError_t launch_tmod(const float *t, const float *w1, const float *w2, float *mod, float *zs,
                        int B, int D, int tdim, hipStream_t s);
+// out[b][o] = sum_r w[o][r] zs[b][r], o < O: a second map of the hidden zs
+hipError_t launch_tmod_map(const float *zs, const float *w, float *out, int B, int D, int O, hipStream_t s);
+// boundary layers of the stack
+hipError_t launch_fill(float *p, float v, size_t n, hipStream_t s);
+hipError_t launch_patchify(bool f32, const float *z, void *p, int B, int C, int Hl, int Wl, hipStream_t s);
+// out = z + dt * unpatchify(vtok) (z may alias out, or be NULL for dt * v)
+hipError_t launch_unpatchify_axpy(bool f32, const void *vtok, const float *z, float *out, float dt, int B, int C,
+                                  int Hl, int Wl, hipStream_t s);
 // variant < 0 picks the default tile configuration for the shape; group_m
 // <= 0 the default tile-grouping width (row tiles per L2 group).  part (fp32,
 // part_bytes) lets the default configuration split the tail tiles along K.

@@ -335,16 +335,16 @@ __global__ __launch_bounds__(256) void tmod_stage1(const float *__restrict__ t,
   }
 }
 
-// Stage 2: mod[b][o] = sum_r W_t2[o][r] zs[b][r], o < 6D.  Each wave owns
+// Stage 2: mod[b][o] = sum_r W[o][r] zs[b][r], o < O (O = 6D for the block
+// modulation, 2D for the final norm's shift and scale).  Each wave owns
 // two output rows; a chunk of zs for up to 32 samples is staged in LDS and
 // W_t2 is streamed from HBM once per 32 samples.
 __global__ __launch_bounds__(256) void tmod_stage2(const float *__restrict__ zs,
                                                    const float *__restrict__ w2,
-                                                   float *__restrict__ mod, int B, int D) {
+                                                   float *__restrict__ mod, int B, int D, int O) {
   constexpr int KC = 256, BMAX = 32, NR = 2;
   __shared__ f32x4 zl[BMAX][KC / 4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int O = 6 * D;
   const int o0 = (blockIdx.x * 4 + wave) * NR;
   for (int b0 = 0; b0 < B; b0 += BMAX) {
     const int nb = min(BMAX, B - b0);
@@ -401,13 +401,12 @@ __global__ __launch_bounds__(256) void tmod_stage2(const float *__restrict__ zs,
 constexpr int TM_NB = 4;
 __global__ __launch_bounds__(256) void tmod_stage2_fewb(const float *__restrict__ zs,
                                                         const float *__restrict__ w2,
-                                                        float *__restrict__ mod, int B, int D) {
+                                                        float *__restrict__ mod, int B, int D, int O) {
   extern __shared__ float zl[];  // [B][D]
   for (int i = threadIdx.x * 4; i < B * D; i += blockDim.x * 4)
     *reinterpret_cast<f32x4 *>(zl + i) = *reinterpret_cast<const f32x4 *>(zs + i);
   __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int O = 6 * D;
   // 64 rows per workgroup (4 passes of 4 rows per wave) amortise the staging
   for (int pass = 0; pass < 4; ++pass) {
   const int o0 = ((blockIdx.x * 4 + pass) * 4 + wave) * 4;
@@ -461,11 +460,15 @@ hipError_t launch_tmod(const float *t, const float *w1, const float *w2, float *
   hipLaunchKernelGGL(tmod_stage1, dim3((D + 15) / 16), dim3(256), 0, s, t, w1, zs, B, D, tdim);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  return launch_tmod_map(zs, w2, mod, B, D, 6 * D, s);
+}
+
+hipError_t launch_tmod_map(const float *zs, const float *w, float *out, int B, int D, int O, hipStream_t s) {
   if (B <= TM_NB && (size_t)B * D * sizeof(float) <= 64 * 1024)
-    hipLaunchKernelGGL(tmod_stage2_fewb, dim3((6 * D + 63) / 64), dim3(256), (size_t)B * D * sizeof(float), s,
-                       zs, w2, mod, B, D);
+    hipLaunchKernelGGL(tmod_stage2_fewb, dim3((O + 63) / 64), dim3(256), (size_t)B * D * sizeof(float), s,
+                       zs, w, out, B, D, O);
   else
-    hipLaunchKernelGGL(tmod_stage2, dim3((6 * D + 7) / 8), dim3(256), 0, s, zs, w2, mod, B, D);
+    hipLaunchKernelGGL(tmod_stage2, dim3((O + 7) / 8), dim3(256), 0, s, zs, w, out, B, D, O);
   return hipGetLastError();
 }
 

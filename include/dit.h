@@ -199,6 +199,61 @@ dit_status dit_stack_fwd_ex(const dit_config *cfg /* host */, const dit_prologue
 dit_status dit_qk_prologue(const dit_config *cfg /* host */, const dit_prologue *pro /* host */,
                            const float *q_norm_w, const float *k_norm_w, void *qkvg, void *stream);
 
+/* ---- The layers around the stack and the sampler (page "Krea 2 技术报告":
+ * the DiT runs on autoencoder latent tokens next to text-encoder features;
+ * 训练 › 预训练: rectified-flow loss with v-parameterization, a shifted
+ * sampling schedule whose inference shift is kept constant).  Readings (the
+ * pages do not give them): latent z [B, C, 2*grid_h, 2*grid_w] fp32; 2 x 2
+ * patches in raster order, patch vector index c*4 + dy*2 + dx; image
+ * tokens first (grid_h * grid_w of them), then n_text text tokens, so
+ * cfg->seq_len == grid_h * grid_w + n_text; bias-free embeddings
+ * x_img = W_in p, x_txt = W_txt f; final layer on the image tokens:
+ * h = rmsnorm(x) (1 + norm_f_w) (1 + scale_f) + shift_f with
+ * [shift_f, scale_f] = W_tf SiLU(W_t1 e(t)), then v = W_out h
+ * unpatchified. */
+typedef struct {
+  int32_t latent_ch;      /* C, even (4C is the patch vector)                  */
+  int32_t grid_h, grid_w; /* latent patch grid, >= 1                           */
+  int32_t n_text;         /* text tokens per sample, >= 0                      */
+  int32_t txt_dim;        /* text feature width, % 8 == 0 (if n_text > 0)      */
+  int32_t t_dim;          /* sinusoidal embedding width, even, 2..1024         */
+} dit_model_config;
+
+typedef struct {
+  const void *w_in;      /* [D, 4C] dtype                                     */
+  const void *w_txt;     /* [D, txt_dim] dtype (may be NULL when n_text == 0)  */
+  const float *w_t1;     /* [D, t_dim] fp32 (as in dit_timestep_mod)          */
+  const float *w_t2;     /* [6D, D] fp32 shared block modulation              */
+  const float *w_tf;     /* [2D, D] fp32 final-norm shift / scale             */
+  const float *norm_f_w; /* [D] fp32 zero-centred gain; NULL means 0          */
+  const void *w_out;     /* [4C, D] dtype                                     */
+} dit_model_weights;
+
+/* Workspace bytes of dit_model_velocity and dit_sample (0 if invalid). */
+size_t dit_model_workspace_size(const dit_config *cfg /* host */, const dit_model_config *mc /* host */);
+
+/* The model as a velocity field at time t (host value, the same for every
+ * sample): embeddings, the n_blocks-block stack (with the optional
+ * prologue `pro`, NULL = none) under the shared modulation W_t2 SiLU(W_t1
+ * e(t)), the final layer; v_out [B, C, Hl, Wl] fp32.  z [B, C, Hl, Wl]
+ * fp32, txt [B, n_text, txt_dim] dtype.  v_out must not overlap z, txt or
+ * ws. */
+dit_status dit_model_velocity(const dit_config *cfg /* host */, const dit_model_config *mc /* host */,
+                              const dit_prologue *pro /* host */, const dit_model_weights *mw /* host */,
+                              int32_t n_blocks, const dit_block_weights *blocks /* host [n_blocks] */,
+                              const float *z, float t, const void *txt, float *v_out, void *ws, size_t ws_bytes,
+                              void *stream);
+
+/* n_steps Euler steps of the rectified-flow sampler on z (in place, fp32):
+ *   t_i = s u_i / (1 + (s - 1) u_i), u_i = 1 - i / n_steps (t_0 = 1, t_n = 0),
+ *   z <- z + (t_{i+1} - t_i) v(z, t_i)
+ * with v as in dit_model_velocity (no classifier-free guidance: the pages
+ * treat it as an optional control).  n_steps >= 1, shift s > 0. */
+dit_status dit_sample(const dit_config *cfg /* host */, const dit_model_config *mc /* host */,
+                      const dit_prologue *pro /* host */, const dit_model_weights *mw /* host */, int32_t n_blocks,
+                      const dit_block_weights *blocks /* host [n_blocks] */, float *z, int32_t n_steps,
+                      float shift, const void *txt, void *ws, size_t ws_bytes, void *stream);
+
 /* Shared timestep modulation of every sample:
  *   e = [cos(1000 t f_i), sin(1000 t f_i)], f_i = 10000^(-i/(t_dim/2)),
  *   mod_out[b] = W_t2 * SiLU(W_t1 * e)  reshaped to [6, D].

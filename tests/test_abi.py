@@ -207,3 +207,31 @@ def test_prologue_argument_checks():
     # rope off: the grid and axes are not looked at
     off = _lib.Prologue(1, 0, 0, 0, (ctypes.c_int32 * 3)(0, 0, 0), 0.0)
     assert S(L.dit_qk_prologue(ctypes.byref(c), ctypes.byref(off), 0, 0, 0, None)) == "DIT_ERR_NULL"
+
+
+def test_model_argument_checks():
+    """dit_model_velocity / dit_sample reject bad shapes before any launch."""
+    L = dit.lib()
+    c = cfg()  # seq_len 80
+    G = 1 << 30
+    S = lambda st: _lib.STATUS[st]
+    mc = dit.make_model_config(4, 8, 8, 16, 32, 256)
+    assert dit.model_workspace_size(c, mc) > 0
+    mw = _lib.ModelWeights(P, P, P, P, P, 0, P)
+    bw = (_lib.BlockWeights * 1)(_lib.BlockWeights(P, P, P, P, P, 0, 0, 0, 0))
+    ws_need = dit.model_workspace_size(c, mc)
+    args = lambda mcx, mwx, nb=1: (ctypes.byref(c), ctypes.byref(mcx), None, ctypes.byref(mwx), nb, bw,
+                                   P + G, ctypes.c_float(0.5), P + 2 * G, P + 3 * G, P + 4 * G, ws_need, None)
+    assert S(L.dit_model_velocity(*args(dit.make_model_config(4, 8, 8, 15, 32, 256), mw))) == "DIT_ERR_SHAPE"  # 64+15 != 80
+    assert S(L.dit_model_velocity(*args(dit.make_model_config(3, 8, 8, 16, 32, 256), mw))) == "DIT_ERR_SHAPE"  # odd C
+    assert S(L.dit_model_velocity(*args(dit.make_model_config(4, 8, 8, 16, 12, 256), mw))) == "DIT_ERR_SHAPE"  # txt_dim
+    assert S(L.dit_model_velocity(*args(dit.make_model_config(4, 8, 8, 16, 32, 255), mw))) == "DIT_ERR_SHAPE"  # t_dim
+    assert S(L.dit_model_velocity(*args(mc, _lib.ModelWeights(P, 0, P, P, P, 0, P)))) == "DIT_ERR_NULL"  # w_txt
+    assert S(L.dit_model_velocity(*args(mc, mw, nb=0))) == "DIT_ERR_SHAPE"
+    a = list(args(mc, mw))
+    a[-2] = ws_need - 16
+    assert S(L.dit_model_velocity(*a)) == "DIT_ERR_WORKSPACE"
+    assert S(L.dit_sample(ctypes.byref(c), ctypes.byref(mc), None, ctypes.byref(mw), 1, bw, P + G, 0,
+                          ctypes.c_float(3.0), P + 2 * G, P + 4 * G, ws_need, None)) == "DIT_ERR_SHAPE"  # 0 steps
+    assert S(L.dit_sample(ctypes.byref(c), ctypes.byref(mc), None, ctypes.byref(mw), 1, bw, P + G, 4,
+                          ctypes.c_float(0.0), P + 2 * G, P + 4 * G, ws_need, None)) == "DIT_ERR_SHAPE"  # shift 0
