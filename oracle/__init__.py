@@ -41,6 +41,12 @@ Parity status (what pins each function; see the tests under
   for the norm; the layer conventions (16-channel latent, 2 x 2 patches,
   bias-free embeddings, the final modulation map, the shift form) are
   readings: parity of those conventions is unpinned by the pages.
+* ``fp8_e4m3_round``, ``quantize_rows_fp8``, ``gemm_fp8``, ``swiglu_fp8``
+  (the 8-bit projections): pinned by an exhaustive nearest-value search over
+  all finite e4m3 codes (ties to even), fixed points at representable
+  values, the row maximum landing on +-448, and float64 products of the
+  decoded values; e4m3 with row-wise scales is a reading of the pages'
+  8-bit training (their scaling schemes, not an inference format).
 * The zero-centred gain form ``(1 + w)`` of the RMSNorm is a reading of
   the pages (weight decay on a zero-centred parameter); parity of that
   convention is unpinned by the pages, though the arithmetic under it is
@@ -52,6 +58,10 @@ from .dit_oracle import (  # noqa: F401
     apply_rope,
     embed_tokens,
     euler_sample,
+    fp8_e4m3_round,
+    gemm_fp8,
+    quantize_rows_fp8,
+    swiglu_fp8,
     final_layer,
     final_mod,
     flow_schedule,

@@ -411,3 +411,58 @@ def model_velocity(z, t, txt, model, blocks, n_blocks: int, oc: OracleConfig, pr
     v = final_layer(y[:, :n_img], final_mod(tb, model.w_t1, model.w_tf, oc.hidden), model.norm_f_w,
                     model.w_out, oc.eps)
     return unpatchify(v, C, Hl, Wl)
+
+
+# ------------------------------------------------------------------ 8-bit projections
+# Page "Krea 2 技术报告", 训练 › 预训练 (and the Indonesian / Korean pages):
+# 8-bit training ran 15-20 % faster than bf16, with tensor-wise scaling at
+# 256 px and row-wise scaling at 512 px.  Here the 8-bit format is OCP FP8
+# e4m3 (largest finite 448) with row-wise scales for both operands of a
+# projection: a row (one token of A, one output channel of W) is divided by
+# s = amax(row) / 448 before rounding to the nearest e4m3 value (ties to
+# even).  The scale and the division are float32 operations so that both
+# implementations take the same rounding decisions; the product is then
+#   C[m, n] = sa[m] sw[n] sum_k qa[m, k] qw[n, k].
+FP8_MAX = 448.0
+
+
+def fp8_e4m3_round(y) -> np.ndarray:
+    """Nearest OCP e4m3 (3 mantissa bits, exponent bias 7, subnormal step
+    2^-9, largest finite 448) to each value, ties to the even mantissa.
+    Inputs must lie within [-464, 464] (they round to at most 448)."""
+    y = _f64(y)
+    a = np.abs(y)
+    assert np.all(a <= 464.0), "outside the e4m3 range"
+    _, ex = np.frexp(np.where(a > 0, a, 1.0))
+    e = np.maximum(ex - 1, -6)              # binade; below 2^-6 the subnormal spacing
+    step = np.ldexp(1.0, e - 3)             # 3 mantissa bits
+    q = np.round(a / step) * step           # numpy rounds halves to even
+    return np.sign(y) * q
+
+
+def quantize_rows_fp8(x):
+    """Row-wise FP8 quantisation of x [m, k] (values exact in float32):
+    returns (q [m, k] float64 holding e4m3 values, s [m] float32) with
+    x ~ q * s.  amax = max |x| per row; s = amax / 448 and the quotient
+    x * (448 / amax) in float32; an all-zero row gets s = 1, q = 0."""
+    x32 = np.asarray(x, dtype=np.float32)
+    amax = np.max(np.abs(x32), axis=1)
+    zero = amax == 0
+    safe = np.where(zero, np.float32(1), amax).astype(np.float32)
+    s = np.where(zero, np.float32(1), safe / np.float32(FP8_MAX)).astype(np.float32)
+    inv = (np.float32(FP8_MAX) / safe).astype(np.float32)
+    y = (x32 * inv[:, None]).astype(np.float32)
+    q = fp8_e4m3_round(y)
+    q[zero] = 0.0
+    return q, s
+
+
+def gemm_fp8(qa, sa, qw, sw) -> np.ndarray:
+    """C = (qa qw^T) * sa[:, None] * sw[None, :] in float64."""
+    return (_f64(qa) @ _f64(qw).T) * _f64(sa)[:, None] * _f64(sw)[None, :]
+
+
+def swiglu_fp8(qa, sa, qw13, sw13, ffn: int) -> np.ndarray:
+    """SiLU(A W1^T) * (A W3^T) with both halves of W13 = [W1; W3] in FP8."""
+    c = gemm_fp8(qa, sa, qw13, sw13)
+    return silu(c[:, :ffn]) * c[:, ffn:]

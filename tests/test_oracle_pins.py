@@ -497,3 +497,66 @@ def test_model_velocity_with_no_blocks_matches_per_token_loops():
             for dy in range(2):
                 for dx in range(2):
                     assert abs(v[0, 0, 2 * py + dy, 2 * px + dx] - out[dy * 2 + dx]) < 1e-12
+
+
+# ------------------------------------------------------------------ 8-bit projections
+def _e4m3_values():
+    """Every finite OCP e4m3 value, decoded from its bit fields."""
+    vals = []
+    for v in range(256):
+        if (v & 0x7F) == 0x7F:
+            continue  # NaN codes
+        s, e, m = v >> 7, (v >> 3) & 15, v & 7
+        x = math.ldexp(m / 8.0, -6) if e == 0 else math.ldexp(1.0 + m / 8.0, e - 7)
+        vals.append((-x if s else x, v))
+    return vals
+
+
+def test_fp8_round_is_nearest_even_over_all_codes():
+    """Against an exhaustive search over the 254 finite codes: nearest value,
+    ties to the code with the even mantissa; covers subnormals, ties, the top."""
+    vals = _e4m3_values()
+    r = np.random.default_rng(4)
+    xs = np.concatenate([r.standard_normal(3000) * 50, r.standard_normal(1000) * 0.01,
+                         np.array([448.0, -448.0, 447.9, 1.0625, 1.1875, 0.0009765625, 3 * 2.0 ** -10, 0.0, 240.0, 464.0])])
+    xs = xs[np.abs(xs) <= 464].astype(np.float32).astype(np.float64)
+    got = O.fp8_e4m3_round(xs)
+    for x, g in zip(xs, got):
+        d = [(abs(v - x), (c & 1), v) for v, c in vals]
+        best = min(d)[0]
+        cands = [v for (dist, odd, v) in d if dist == best]
+        want = [v for (dist, odd, v) in d if dist == best and odd == 0] if len(cands) > 1 else cands
+        assert g in want or (g == 0.0 and 0.0 in [abs(w) for w in want]), (x, g, want)
+
+
+def test_fp8_quantize_rows_properties():
+    """Representable values are fixed points; each row's largest |x| lands on
+    +-448; dequantised rows are within half a step; zero rows give zeros."""
+    r = np.random.default_rng(8)
+    x = (r.standard_normal((6, 64)) * np.array([1e-3, 0.5, 3.0, 40.0, 1.0, 7.0])[:, None]).astype(np.float32)
+    x[4] = 0.0
+    q, s = O.quantize_rows_fp8(x)
+    assert s.dtype == np.float32 and s[4] == 1.0 and np.all(q[4] == 0)
+    for i in (0, 1, 2, 3, 5):
+        j = np.argmax(np.abs(x[i]))
+        assert abs(q[i, j]) == 448.0
+        y = (x[i] * (np.float32(448.0) / np.max(np.abs(x[i])))).astype(np.float64)
+        _, ex = np.frexp(np.maximum(np.abs(y), 2.0 ** -6))
+        assert np.all(np.abs(q[i] - y) <= np.ldexp(1.0, ex - 1 - 4) + 1e-12)  # half a step of the binade
+    fixed = np.array([v for v, c in _e4m3_values()])
+    assert np.array_equal(O.fp8_e4m3_round(fixed), fixed)
+
+
+def test_fp8_gemm_is_the_scaled_product():
+    """gemm_fp8 = decoded operands multiplied in float64 and scaled per row and
+    column; with exactly representable operands it equals the plain product."""
+    r = np.random.default_rng(12)
+    a = O.fp8_e4m3_round(r.integers(-8, 9, (5, 32)).astype(np.float32))
+    w = O.fp8_e4m3_round(r.integers(-8, 9, (7, 32)).astype(np.float32))
+    sa, sw = np.float32(r.random(5) + 0.5), np.float32(r.random(7) + 0.5)
+    c = O.gemm_fp8(a, sa, w, sw)
+    for m in range(5):
+        for n in range(7):
+            assert abs(c[m, n] - sum(float(a[m, k]) * float(w[n, k]) for k in range(32)) * float(sa[m]) * float(sw[n])) < 1e-9
+    u = O.swiglu_fp8(a, sa, np.concatenate([w, w]), np.concatenate([sw, sw]), 7)
+    assert np.allclose(u, c / (1 + np.exp(-c)) * c)
