@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "DiT block tokens/s + attn/GEMM TFLOP/s (% bf16 MFMA peak), 1024px bf16"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0  # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0
 
 
@@ -200,6 +201,51 @@ def bench_prologue(dit, torch, cfg, c, W, X, Y, M, ws, step, steps: int, warmup:
             "axes": [32, 48, 48], "grid": [cfg.grid_h, cfg.grid_w], "theta": 10000.0}
 
 
+def bench_fp8(dit, torch, cfg, reps: int = 10) -> dict:
+    """The 8-bit projections (row-wise e4m3, the pages' 8-bit variant) on the
+    1024 px shapes: each GEMM with its weights quantised once (stored FP8)
+    and the activation quantisation per call, timed separately.  A side
+    measurement: the headline stays the bf16 block."""
+    T, D, F = cfg.tokens, cfg.hidden, cfg.ffn
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    out = {}
+    for name, n, k, sw in (("qkvg", cfg.n_qkvg, D, False), ("o", D, D, False), ("w13", F, D, True),
+                           ("w2", D, F, False)):
+        wrows = 2 * n if sw else n
+        a = torch.randn(T, k, generator=g, device="cuda").to(torch.bfloat16)
+        w = (torch.randn(wrows, k, generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+        qa = torch.empty(T, k, dtype=torch.uint8, device="cuda")
+        qw = torch.empty(wrows, k, dtype=torch.uint8, device="cuda")
+        sa = torch.empty(T, dtype=torch.float32, device="cuda")
+        swt = torch.empty(wrows, dtype=torch.float32, device="cuda")
+        c = torch.empty(T, n, dtype=torch.bfloat16, device="cuda")
+        dit.quantize_fp8(w, qw, swt)
+
+        def timed(fn):
+            for _ in range(3):
+                fn()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / reps
+
+        tq = timed(lambda: dit.quantize_fp8(a, qa, sa))
+        tg = timed(lambda: dit.gemm_fp8(qa, sa, qw, swt, c, swiglu=sw))
+        fl = 2.0 * T * k * wrows
+        out[name] = {"gemm_ms": tg, "tflops": fl / (tg * 1e-3) / 1e12, "fp8_frac": fl / (tg * 1e-3) / 1e12 / PEAK_FP8_TFLOPS,
+                     "quantize_ms": tq, "quantize_gbs": 3.0 * T * k / (tq * 1e-3) / 1e9}
+        del a, w, qa, qw, sa, swt, c
+    tot = sum(v["gemm_ms"] + v["quantize_ms"] for v in out.values())
+    out["all_four_ms"] = tot
+    out["peak_tflops"] = PEAK_FP8_TFLOPS
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -304,6 +350,7 @@ def main() -> int:
         "mfma_frac": step_flops / (elapsed / args.steps) / 1e12 / PEAK_BF16_TFLOPS,
         "kernels": kernels, "roofline": roofline,
     }
+    out["fp8"] = bench_fp8(dit, torch, cfg)
     out["with_prologue"] = bench_prologue(dit, torch, cfg, c, W, X, Y, M, ws, step, args.steps, args.warmup)
     if not args.no_stack:
         out["stack"] = bench_stack(dit, torch, args.stack_steps, 2)

@@ -26,7 +26,8 @@ EXPORTS = (
     "dit_timestep_mod", "dit_modnorm", "dit_gemm", "dit_gemm_swiglu", "dit_gemm_variant", "dit_attention",
     "dit_gated_residual", "dit_status_str", "dit_last_hip_error", "dit_timer_start",
     "dit_timer_stop", "dit_gemm_splitk", "dit_gemm_plan", "dit_block_fwd_ex", "dit_stack_fwd_ex",
-    "dit_qk_prologue", "dit_model_workspace_size", "dit_model_velocity", "dit_sample",
+    "dit_qk_prologue", "dit_model_workspace_size", "dit_model_velocity", "dit_sample", "dit_quantize_fp8",
+    "dit_gemm_fp8", "dit_quantize_fp8_tensor",
 )
 
 
@@ -93,6 +94,9 @@ def lib() -> ctypes.CDLL:
             "dit_stack_fwd_ex": (i32, [cfgp, ctypes.POINTER(Prologue), i32, wp, vp, vp, vp, vp, sz, vp]),
             "dit_qk_prologue": (i32, [cfgp, ctypes.POINTER(Prologue), vp, vp, vp, vp]),
             "dit_model_workspace_size": (sz, [cfgp, ctypes.POINTER(ModelConfig)]),
+            "dit_quantize_fp8": (i32, [i32, i32, i32, vp, vp, vp, vp]),
+            "dit_quantize_fp8_tensor": (i32, [i32, i32, i32, vp, vp, vp, vp, vp]),
+            "dit_gemm_fp8": (i32, [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp]),
             "dit_model_velocity": (i32, [cfgp, ctypes.POINTER(ModelConfig), ctypes.POINTER(Prologue),
                                          ctypes.POINTER(ModelWeights), i32, wp, vp, ctypes.c_float, vp, vp, vp, sz,
                                          vp]),
@@ -309,6 +313,28 @@ def gemm_plan(m: int, n: int, k: int, swiglu: bool = False) -> dict:
     _check(lib().dit_gemm_plan(m, n, k, int(swiglu), ctypes.byref(v), ctypes.byref(t), ctypes.byref(sg),
                                ctypes.byref(pb)), "dit_gemm_plan")
     return {"variant": v.value, "sk_tiles": t.value, "segs": sg.value, "part_bytes": pb.value}
+
+
+def quantize_fp8(x, q, scale, stream=None) -> None:
+    """Row-wise e4m3 quantisation of x [m, k] (bf16 or fp32) into q (uint8) and scale [m] fp32."""
+    m, k = x.shape
+    _check(lib().dit_quantize_fp8(_dtype_code(x.dtype), m, k, _ptr(x), _ptr(q), _ptr(scale), _stream(stream)),
+           "dit_quantize_fp8")
+
+
+def quantize_fp8_tensor(x, q, scale, ws, stream=None) -> None:
+    """Tensor-wise e4m3 quantisation (one scale for all of x, repeated per row)."""
+    m, k = x.shape
+    _check(lib().dit_quantize_fp8_tensor(_dtype_code(x.dtype), m, k, _ptr(x), _ptr(q), _ptr(scale), _ptr(ws),
+                                         _stream(stream)), "dit_quantize_fp8_tensor")
+
+
+def gemm_fp8(qa, sa, qw, sw, c, swiglu: bool = False, stream=None) -> None:
+    """bf16 C = (qa qw^T) sa sw (or the SwiGLU hidden with qw = [W1; W3])."""
+    m, k = qa.shape
+    n = qw.shape[0] // 2 if swiglu else qw.shape[0]
+    _check(lib().dit_gemm_fp8(int(swiglu), m, n, k, _ptr(qa), _ptr(sa), _ptr(qw), _ptr(sw), _ptr(c),
+                              _stream(stream)), "dit_gemm_fp8")
 
 
 def attention(cfg: Config, qkvg, og, ws, stream=None) -> None:

@@ -602,6 +602,53 @@ dit_status dit_gemm_variant(dit_dtype dtype, int32_t variant, int32_t group_m, i
   return e == hipSuccess ? DIT_OK : hip_fail(e);
 }
 
+dit_status dit_quantize_fp8(dit_dtype dtype, int32_t m, int32_t k, const void *x, void *q, float *scale,
+                            void *stream) {
+  if (!dtype_ok(dtype)) return DIT_ERR_DTYPE;
+  if (m <= 0 || k <= 0) return DIT_ERR_SHAPE;
+  if (k % 16) return DIT_ERR_UNSUPPORTED;
+  if (!x || !q || !scale) return DIT_ERR_NULL;
+  if (!aligned(x) || !aligned(q) || !aligned(scale)) return DIT_ERR_ALIGN;
+  const size_t xb = (size_t)m * k * esize(dtype), qb = (size_t)m * k;
+  if (overlap(x, xb, q, qb) || overlap(x, xb, scale, (size_t)m * 4) || overlap(q, qb, scale, (size_t)m * 4))
+    return DIT_ERR_SHAPE;
+  hipError_t e = launch_quantize_fp8(dtype == DIT_F32, x, q, scale, m, k, (hipStream_t)stream);
+  return e == hipSuccess ? DIT_OK : hip_fail(e);
+}
+
+dit_status dit_quantize_fp8_tensor(dit_dtype dtype, int32_t m, int32_t k, const void *x, void *q, float *scale,
+                                   void *ws, void *stream) {
+  if (!dtype_ok(dtype)) return DIT_ERR_DTYPE;
+  if (m <= 0 || k <= 0) return DIT_ERR_SHAPE;
+  if (k % 16) return DIT_ERR_UNSUPPORTED;
+  if (!x || !q || !scale) return DIT_ERR_NULL;
+  if (!ws) return DIT_ERR_WORKSPACE;
+  if (!aligned(x) || !aligned(q) || !aligned(scale) || !aligned(ws)) return DIT_ERR_ALIGN;
+  const size_t xb = (size_t)m * k * esize(dtype), qb = (size_t)m * k, sb = (size_t)m * 4;
+  if (overlap(x, xb, q, qb) || overlap(x, xb, scale, sb) || overlap(q, qb, scale, sb) || overlap(ws, 16, x, xb) ||
+      overlap(ws, 16, q, qb) || overlap(ws, 16, scale, sb))
+    return DIT_ERR_SHAPE;
+  hipError_t e = launch_quantize_fp8_tensor(dtype == DIT_F32, x, q, scale, (float *)ws, m, k, (hipStream_t)stream);
+  return e == hipSuccess ? DIT_OK : hip_fail(e);
+}
+
+dit_status dit_gemm_fp8(int32_t swiglu, int32_t m, int32_t n, int32_t k, const void *qa, const float *sa,
+                        const void *qw, const float *sw, void *c, void *stream) {
+  if (swiglu != 0 && swiglu != 1) return DIT_ERR_SHAPE;
+  if (m <= 0 || n <= 0 || k <= 0) return DIT_ERR_SHAPE;
+  if (k % 16) return DIT_ERR_UNSUPPORTED;
+  if (!qa || !sa || !qw || !sw || !c) return DIT_ERR_NULL;
+  if (!aligned(qa) || !aligned(sa) || !aligned(qw) || !aligned(sw) || !aligned(c)) return DIT_ERR_ALIGN;
+  const uint64_t wrows = swiglu ? 2ull * n : (uint64_t)n;
+  if ((wrows + 256) * k > kMaxSpan || 256ull * k > kMaxSpan) return DIT_ERR_UNSUPPORTED;
+  const size_t cb = (size_t)m * n * 2;
+  if (overlap(c, cb, qa, (size_t)m * k) || overlap(c, cb, qw, wrows * k) || overlap(c, cb, sa, (size_t)m * 4) ||
+      overlap(c, cb, sw, wrows * 4))
+    return DIT_ERR_SHAPE;
+  hipError_t e = launch_gemm_fp8(swiglu == 1, qa, sa, qw, sw, c, m, n, k, (hipStream_t)stream);
+  return e == hipSuccess ? DIT_OK : hip_fail(e);
+}
+
 dit_status dit_gemm_plan(int32_t m, int32_t n, int32_t k, int32_t swiglu, int32_t *variant, int32_t *sk_tiles,
                          int32_t *segs, size_t *part_bytes) {
   if (m <= 0 || n <= 0 || k <= 0 || (swiglu != 0 && swiglu != 1)) return DIT_ERR_SHAPE;

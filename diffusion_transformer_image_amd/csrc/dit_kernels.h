@@ -56,4 +56,12 @@ hipError_t launch_qk_prologue(bool f32, int head_dim, void *qkvg, const float *w
                               int L, int H, int Hkv, int qk_norm, int rope, int grid_h, int grid_w,
                               const int axes[3], float theta, float eps, hipStream_t s);
 
+// FP8 (e4m3) projections with row-wise scales
+hipError_t launch_quantize_fp8(bool f32, const void *x, void *q, float *scale, int M, int K, hipStream_t s);
+// tensor-wise: scale[] receives the common scale for every row; tamax: 1 float
+hipError_t launch_quantize_fp8_tensor(bool f32, const void *x, void *q, float *scale, float *tamax, int M, int K,
+                                      hipStream_t s);
+hipError_t launch_gemm_fp8(bool swiglu, const void *aq, const float *sa, const void *wq, const float *sw, void *c,
+                           int M, int N, int K, hipStream_t s);
+
 }  // namespace dit

@@ -606,6 +606,161 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_ring_kernel(const bf16 *__re
   gemm_epilogue<bf16, BM, BN, NW, WM, WN, EPI, R * STAGE>(acc, smem, C, M, N, m0, n0, wave, lane);
 }
 
+// ---------------------------------------------------------------------------
+// FP8 (OCP e4m3) GEMM with row-wise scales (the pages' 8-bit projections,
+// page "Krea 2 技术报告", 训练 › 预训练: row-wise scaling):
+//   C[m, n] = sa[m] sw[n] sum_k qa[m, k] qw[n, k]      (bf16 out)
+// and the SwiGLU form over W13 = [W1; W3] (sw13 holds both halves' scales).
+// Same tile, waves, LDS-DMA ring and epilogue as the bf16 kernel; a stage
+// is 128 bytes of every row = 128 K elements = one v_mfma 16x16x128 f8
+// k-step, so each lane's fragment is 32 bytes (two 16-byte chunks of its
+// row).  The accumulators are scaled by sa[row] * sw[col] before the
+// shared epilogue.
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+template <int EPI>
+__global__ __launch_bounds__(512) void gemm_fp8_kernel(const uint8_t *__restrict__ A, const float *__restrict__ sa,
+                                                       const uint8_t *__restrict__ W, const float *__restrict__ sw,
+                                                       bf16 *__restrict__ C, int M, int N, int K, int m_tiles,
+                                                       int n_tiles, int gm) {
+  constexpr int BM = 256, BN = 256, WM = 2, WN = 4, NW = 8;
+  constexpr int TM = BM / WM, TN = BN / WN, RB = TM / 16, CB = TN / 16;
+  constexpr int BKB = 128, CPR = 8, RPB = 1024 / BKB;
+  constexpr int ABLK = BM / RPB, BBLK = BN / RPB, STAGE = (BM + BN) * BKB, BPW = (ABLK + BBLK) / NW;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int nwg = m_tiles * n_tiles;
+  int pid = blockIdx.x;
+  if ((nwg & 7) == 0) pid = (pid & 7) * (nwg >> 3) + (pid >> 3);
+  int tm, tn;
+  tile_coords(pid, m_tiles, n_tiles, gm, tm, tn);
+  const int m0 = tm * BM;
+  const int n0 = (EPI == EPI_SWIGLU) ? tn * (BN / 2) : tn * BN;
+  const uint32_t ldb = (uint32_t)K;
+  const rsrc_t ra = make_rsrc(A + (size_t)m0 * K, (uint32_t)min(M - m0, BM) * ldb);
+  const rsrc_t rw = (EPI == EPI_SWIGLU)
+                        ? make_rsrc(W + (size_t)n0 * K, (uint32_t)(N + min(N - n0, BN / 2)) * ldb)
+                        : make_rsrc(W + (size_t)n0 * K, (uint32_t)min(N - n0, BN) * ldb);
+  const int lrow = lane / CPR;
+  const int lchunk = (lane % CPR) ^ (lrow & 7);
+  uint32_t goff[BPW];
+  bool gval[BPW];
+#pragma unroll
+  for (int j = 0; j < BPW; ++j) {
+    const int blk = wave + j * NW;
+    if (blk < ABLK) {
+      const int r = blk * RPB + lrow;
+      gval[j] = (m0 + r) < M;
+      goff[j] = (uint32_t)r * ldb + lchunk * 16;
+    } else {
+      const int r = (blk - ABLK) * RPB + lrow;
+      if (EPI == EPI_SWIGLU) {
+        const int rr = r < BN / 2 ? r : r - BN / 2;
+        gval[j] = n0 + rr < N;
+        goff[j] = (uint32_t)(r < BN / 2 ? rr : N + rr) * ldb + lchunk * 16;
+      } else {
+        gval[j] = (n0 + r) < N;
+        goff[j] = (uint32_t)r * ldb + lchunk * 16;
+      }
+    }
+  }
+  auto issue_stage = [&](int kt, int buf) {
+    const int k0 = kt * BKB;
+    const int kc_ok = (k0 + BKB > K) ? (K - k0) / 16 : CPR;
+    char *base = smem + buf * STAGE;
+#pragma unroll
+    for (int j = 0; j < BPW; ++j) {
+      const int blk = wave + j * NW;
+      const bool ok = gval[j] && (lchunk < kc_ok);
+      load_lds16(blk < ABLK ? ra : rw, base + blk * 1024, ok ? goff[j] + (uint32_t)k0 : kOOB);
+    }
+  };
+  const int g = lane >> 4, r16 = lane & 15, swz = r16 & 7;
+  const int c0 = ((2 * g) ^ swz) * 16, c1 = ((2 * g + 1) ^ swz) * 16;
+  int arow[RB], brow[CB];
+#pragma unroll
+  for (int i = 0; i < RB; ++i) arow[i] = (wm * TM + i * 16 + r16) * BKB;
+#pragma unroll
+  for (int j = 0; j < CB; ++j) {
+    int r;
+    if (EPI == EPI_SWIGLU) {
+      const int half = CB / 2, jj = j % half;
+      r = BM + (j < half ? 0 : BN / 2) + wn * (TN / 2) + jj * 16 + r16;
+    } else {
+      r = BM + wn * TN + j * 16 + r16;
+    }
+    brow[j] = r * BKB;
+  }
+  f32x4 acc[RB][CB];
+#pragma unroll
+  for (int i = 0; i < RB; ++i)
+#pragma unroll
+    for (int j = 0; j < CB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto frag = [&](const char *sb, int row) {
+    const u32x4 lo = *reinterpret_cast<const u32x4 *>(sb + row + c0);
+    const u32x4 hi = *reinterpret_cast<const u32x4 *>(sb + row + c1);
+    return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  };
+
+  const int nk = (K + BKB - 1) / BKB;
+  issue_stage(0, 0);
+  for (int kt = 0; kt < nk; ++kt) {
+    wait_vmcnt<0>();  // this wave's DMA of stage kt
+    __syncthreads();  // stage kt visible to all; every wave is done with stage kt-1
+    if (kt + 1 < nk) issue_stage(kt + 1, (kt + 1) & 1);
+    const char *sb = smem + (kt & 1) * STAGE;
+    i32x8 bf[CB];
+#pragma unroll
+    for (int j = 0; j < CB; ++j) bf[j] = frag(sb, brow[j]);
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+      const i32x8 af = frag(sb, arow[i]);
+#pragma unroll
+      for (int j = 0; j < CB; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[j], acc[i][j], 0, 0, 0, 0, 0, 0);
+    }
+  }
+
+  // ---- row and column scales, then the shared epilogue
+  const int row0 = m0 + wm * TM;
+  float cs[CB];
+#pragma unroll
+  for (int j = 0; j < CB; ++j) {
+    if (EPI == EPI_SWIGLU) {
+      const int nr = n0 + wn * (TN / 2) + (j % (CB / 2)) * 16 + r16;
+      cs[j] = nr < N ? sw[j < CB / 2 ? nr : N + nr] : 0.f;
+    } else {
+      const int nr = n0 + wn * TN + j * 16 + r16;
+      cs[j] = nr < N ? sw[nr] : 0.f;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < RB; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = row0 + i * 16 + 4 * g + e;
+      const float rs = r < M ? sa[r] : 0.f;
+#pragma unroll
+      for (int j = 0; j < CB; ++j) acc[i][j][e] *= rs * cs[j];
+    }
+  gemm_epilogue<bf16, BM, BN, NW, WM, WN, EPI, 2 * STAGE>(acc, smem, C, M, N, m0, n0, wave, lane);
+}
+
+hipError_t launch_gemm_fp8(bool swiglu, const void *aq, const float *sa, const void *wq, const float *sw, void *c,
+                           int M, int N, int K, hipStream_t s) {
+  const int mt = (M + 255) / 256, nt = swiglu ? (N + 127) / 128 : (N + 255) / 256;
+  if (swiglu)
+    hipLaunchKernelGGL(gemm_fp8_kernel<EPI_SWIGLU>, dim3(mt * nt), dim3(512), 0, s, (const uint8_t *)aq, sa,
+                       (const uint8_t *)wq, sw, (bf16 *)c, M, N, K, mt, nt, 8);
+  else
+    hipLaunchKernelGGL(gemm_fp8_kernel<EPI_STORE>, dim3(mt * nt), dim3(512), 0, s, (const uint8_t *)aq, sa,
+                       (const uint8_t *)wq, sw, (bf16 *)c, M, N, K, mt, nt, 8);
+  return hipGetLastError();
+}
+
 template <typename T, int BM, int BN, int BKB, int STAGES, int WM, int WN, int EPI, bool PIPE = false>
 static hipError_t launch_gemm_t(const void *a, const void *w, void *c, int M, int N, int K,
                                 hipStream_t s, int gm, int sk_tiles = 0, int segs = 1, float *part = nullptr) {

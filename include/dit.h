@@ -330,6 +330,35 @@ dit_status dit_gemm_splitk(dit_dtype dtype, int32_t swiglu, int32_t m, int32_t n
                            const void *w, void *c, int32_t sk_tiles, int32_t segs, void *ws, size_t ws_bytes,
                            void *stream);
 
+/* ---- 8-bit projections (page "Krea 2 技术报告", 训练 › 预训练: 8-bit
+ * training with row-wise scaling).  Format: OCP FP8 e4m3 (largest finite
+ * 448), one float32 scale per row.
+ *
+ * Row-wise quantisation: for each row r of x [m, k] (dtype),
+ *   amax = max |x[r, :]|,  scale[r] = amax / 448,
+ *   q[r, c] = e4m3(x[r, c] * (448 / amax))  (round to nearest, ties even);
+ * both divisions and the product are float32; an all-zero row gets
+ * scale 1 and zeros.  q [m, k] bytes.  k % 16 == 0 (else
+ * DIT_ERR_UNSUPPORTED); q and scale must not overlap x. */
+dit_status dit_quantize_fp8(dit_dtype dtype, int32_t m, int32_t k, const void *x, void *q, float *scale,
+                            void *stream);
+
+/* Tensor-wise quantisation (the pages' 256 px scheme): one amax over all of
+ * x, the same float32 scale amax / 448 and quotient x * (448 / amax) for
+ * every element; scale [m] receives that scale for every row (so
+ * dit_gemm_fp8 serves both schemes).  ws: 16 bytes of device scratch.
+ * Three launches: row maxima (into scale), their maximum, the codes. */
+dit_status dit_quantize_fp8_tensor(dit_dtype dtype, int32_t m, int32_t k, const void *x, void *q, float *scale,
+                                   void *ws, void *stream);
+
+/* C = (qa qw^T) * sa[:, None] * sw[None, :] in fp32 accumulation, stored
+ * bf16: qa [m, k], qw [n, k] e4m3 bytes, sa [m], sw [n] fp32 (swiglu = 0);
+ * or, swiglu = 1, the SwiGLU hidden U [m, n] = SiLU(C1) * C3 with
+ * qw = [W1; W3] [2n, k] and sw [2n].  256 x 256 output tiles of
+ * v_mfma_f32_16x16x128 f8 operations.  k % 16 == 0. */
+dit_status dit_gemm_fp8(int32_t swiglu, int32_t m, int32_t n, int32_t k, const void *qa, const float *sa,
+                        const void *qw, const float *sw, void *c, void *stream);
+
 /* Gated grouped-query attention over the rows of qkvg [T, (2H+2Hkv)*d]
  * (column blocks Q | K | V | G, as produced by the QKVG projection):
  *   og[b, l, h*d:(h+1)*d] = softmax_keys(Q_h K_j^T / sqrt(d)) V_j * sigmoid(G_h)

@@ -41,7 +41,7 @@ Parity status (what pins each function; see the tests under
   for the norm; the layer conventions (16-channel latent, 2 x 2 patches,
   bias-free embeddings, the final modulation map, the shift form) are
   readings: parity of those conventions is unpinned by the pages.
-* ``fp8_e4m3_round``, ``quantize_rows_fp8``, ``gemm_fp8``, ``swiglu_fp8``
+* ``fp8_e4m3_round``, ``quantize_rows_fp8``, ``quantize_tensor_fp8``, ``gemm_fp8``, ``swiglu_fp8``
   (the 8-bit projections): pinned by an exhaustive nearest-value search over
   all finite e4m3 codes (ties to even), fixed points at representable
   values, the row maximum landing on +-448, and float64 products of the
@@ -61,6 +61,7 @@ from .dit_oracle import (  # noqa: F401
     fp8_e4m3_round,
     gemm_fp8,
     quantize_rows_fp8,
+    quantize_tensor_fp8,
     swiglu_fp8,
     final_layer,
     final_mod,

@@ -457,6 +457,21 @@ def quantize_rows_fp8(x):
     return q, s
 
 
+def quantize_tensor_fp8(x):
+    """Tensor-wise FP8 quantisation (the pages' 256 px scheme): one scale for
+    all of x, s = amax(x) / 448, the quotient in float32 as in
+    quantize_rows_fp8; returned per row (every row the same) so the same
+    product serves both schemes."""
+    x32 = np.asarray(x, dtype=np.float32)
+    amax = np.float32(np.max(np.abs(x32)))
+    if amax == 0:
+        return np.zeros(x32.shape), np.ones(x32.shape[0], dtype=np.float32)
+    s = np.float32(amax / np.float32(FP8_MAX))
+    inv = np.float32(np.float32(FP8_MAX) / amax)
+    q = fp8_e4m3_round((x32 * inv).astype(np.float32))
+    return q, np.full(x32.shape[0], s, dtype=np.float32)
+
+
 def gemm_fp8(qa, sa, qw, sw) -> np.ndarray:
     """C = (qa qw^T) * sa[:, None] * sw[None, :] in float64."""
     return (_f64(qa) @ _f64(qw).T) * _f64(sa)[:, None] * _f64(sw)[None, :]

@@ -235,3 +235,17 @@ def test_model_argument_checks():
                           ctypes.c_float(3.0), P + 2 * G, P + 4 * G, ws_need, None)) == "DIT_ERR_SHAPE"  # 0 steps
     assert S(L.dit_sample(ctypes.byref(c), ctypes.byref(mc), None, ctypes.byref(mw), 1, bw, P + G, 4,
                           ctypes.c_float(0.0), P + 2 * G, P + 4 * G, ws_need, None)) == "DIT_ERR_SHAPE"  # shift 0
+
+
+def test_fp8_argument_checks():
+    L = dit.lib()
+    G = 1 << 30
+    S = lambda st: _lib.STATUS[st]
+    assert S(L.dit_quantize_fp8(1, 16, 24, P, P + G, P + 2 * G, None)) == "DIT_ERR_UNSUPPORTED"  # k % 16
+    assert S(L.dit_quantize_fp8(7, 16, 32, P, P + G, P + 2 * G, None)) == "DIT_ERR_DTYPE"
+    assert S(L.dit_quantize_fp8(1, 16, 32, P, P + 64, P + 2 * G, None)) == "DIT_ERR_SHAPE"  # q overlaps x
+    assert S(L.dit_quantize_fp8(1, 16, 32, P, P + G, 0, None)) == "DIT_ERR_NULL"
+    assert S(L.dit_gemm_fp8(2, 16, 16, 32, P, P + G, P + 2 * G, P + 3 * G, P + 4 * G, None)) == "DIT_ERR_SHAPE"
+    assert S(L.dit_gemm_fp8(0, 16, 16, 40, P, P + G, P + 2 * G, P + 3 * G, P + 4 * G, None)) == "DIT_ERR_UNSUPPORTED"
+    assert S(L.dit_gemm_fp8(0, 16, 16, 32, P, P + G, P + 2 * G, P + 3 * G, P + 2, None)) == "DIT_ERR_ALIGN"
+    assert S(L.dit_gemm_fp8(0, 16, 16, 32, P, P + G, P + 2 * G, P + 3 * G, P + 64, None)) == "DIT_ERR_SHAPE"

@@ -560,3 +560,13 @@ def test_fp8_gemm_is_the_scaled_product():
             assert abs(c[m, n] - sum(float(a[m, k]) * float(w[n, k]) for k in range(32)) * float(sa[m]) * float(sw[n])) < 1e-9
     u = O.swiglu_fp8(a, sa, np.concatenate([w, w]), np.concatenate([sw, sw]), 7)
     assert np.allclose(u, c / (1 + np.exp(-c)) * c)
+
+
+def test_fp8_tensor_scale_is_row_scale_of_the_whole_tensor():
+    """Tensor-wise quantisation = row-wise quantisation of the flattened tensor."""
+    r = np.random.default_rng(21)
+    x = (r.standard_normal((7, 48)) * np.geomspace(0.01, 9.0, 7)[:, None]).astype(np.float32)
+    q, s = O.quantize_tensor_fp8(x)
+    qf, sf = O.quantize_rows_fp8(x.reshape(1, -1))
+    assert np.array_equal(q, qf.reshape(x.shape)) and np.all(s == sf[0])
+    assert np.max(np.abs(q)) == 448.0
