@@ -155,13 +155,23 @@ __device__ __forceinline__ void gemm_epilogue(const f32x4 (&acc)[BM / WM / 16][B
   }
 }
 
+// 16-byte LDS DMA with the K offset as the scalar offset (part of the
+// descriptor's range check).
+__device__ __forceinline__ void load_lds16_k(rsrc_t r, const void *lds_wave_base, uint32_t voff,
+                                             uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds_wave_base, 16, voff, soff, 0, 0);
+}
+
 // PIPE (two-stage ring only): software-pipelined main loop.  The fragments
 // of k-step ks+1 are read from LDS while the MFMAs of k-step ks run, and the
 // stage barrier sits between the last two MFMA bursts of a stage: the wave
 // first reads its last fragments of stage kt, issues the MFMAs of the
-// previous k-step, then waits for stage kt+1 and the barrier, refills the
-// buffer stage kt used and reads the first fragments of stage kt+1 while its
-// last MFMAs of stage kt execute.
+// previous k-step, then waits for stage kt+1 and the barrier, reads the
+// first fragments of stage kt+1 and refills the buffer stage kt used while
+// its last MFMAs of stage kt execute.  When K is a whole number of stages
+// the refill's DMA loads are spread one per RB*CB/BPW MFMAs instead of
+// leaving as one burst right after the barrier (a burst from all waves
+// queues in the texture path and raises the L2 latency every wave sees).
 template <typename T, int BM, int BN, int BKB, int STAGES, int WM, int WN, int EPI, bool PIPE = false>
 __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(const T *__restrict__ A,
                                                            const T *__restrict__ W,
@@ -300,7 +310,58 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(const T *__restrict__
   };
 
   if constexpr (PIPE) {
-    static_assert(STAGES == 2 && KSTEPS == 2, "pipelined loop: two stages of two k-steps");
+  static_assert(STAGES == 2 && KSTEPS == 2, "pipelined loop: two stages of two k-steps");
+  // PIPE with K a whole number of stages: the K offset of a stage is the
+  // DMA's scalar offset; rows outside the operand carry an out-of-range
+  // vector offset at every stage, and the stage past the end of K gets an
+  // out-of-range scalar offset (zeros into a buffer that is not read again)
+  uint32_t goffs[BPW];
+#pragma unroll
+  for (int j = 0; j < BPW; ++j) goffs[j] = gval[j] ? goff[j] : kOOB;
+  auto issue_spread = [&](int kt, int buf) {
+    const uint32_t soff = kt < nk ? (uint32_t)(kb + kt) * KSTAGE * sizeof(T) : kOOB;
+    char *base = smem + buf * STAGE_BYTES;
+#pragma unroll
+    for (int j = 0; j < BPW; ++j) {
+      const int blk = wave + j * NW;
+      load_lds16_k(blk < ABLK ? ra : rw, base + blk * 1024, goffs[j], soff);
+    }
+  };
+  if (K % KSTAGE == 0) {
+    issue_spread(0, 0);
+    wait_vmcnt<0>();
+    __syncthreads();
+    issue_spread(1, 1);
+    u32x4 a0[RB], b0[CB], a1[RB], b1[CB];
+    load_frags(smem, 0, a0, b0);
+    drain_lgkm();
+    for (int kt = 0; kt < nk - 1; ++kt) {
+      const char *sb = smem + (kt & 1) * STAGE_BYTES;
+      load_frags(sb, 1, a1, b1);
+      __builtin_amdgcn_sched_barrier(0);
+      mmas(a0, b0);
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmcnt<0>();  // this wave's DMA of stage kt+1
+      __syncthreads();  // stage kt+1 visible; every wave holds its stage-kt fragments
+      load_frags(smem + ((kt + 1) & 1) * STAGE_BYTES, 0, a0, b0);
+      issue_spread(kt + 2, kt & 1);
+      mmas(a1, b1);
+      // scheduling groups: the fragment reads first, then BPW times
+      // (RB*CB/BPW MFMAs, one DMA load)
+#pragma unroll
+      for (int q = 0; q < RB + CB; ++q) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+      for (int q = 0; q < BPW; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, (RB * CB) / BPW, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    load_frags(smem + ((nk - 1) & 1) * STAGE_BYTES, 1, a1, b1);
+    mmas(a0, b0);
+    mmas(a1, b1);
+    wait_vmcnt<0>();  // the zero-filled stage past the end has landed before LDS is reused
+  } else {
     issue_stage(0, 0);
     wait_vmcnt<0>();
     __syncthreads();
@@ -330,6 +391,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(const T *__restrict__
     load_frags(smem + ((nk - 1) & 1) * STAGE_BYTES, 1, a1, b1);
     mmas(a0, b0);
     mmas(a1, b1);
+  }
   } else {
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s)
@@ -436,10 +498,6 @@ __device__ __forceinline__ bool static_for(F &&f) {
 //    a fragment read on distinct banks for 8- and 16-lane access groups.
 __device__ __forceinline__ int swz64(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
 
-__device__ __forceinline__ void load_lds16_k(rsrc_t r, const void *lds_wave_base, uint32_t voff,
-                                             uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds_wave_base, 16, voff, soff, 0, 0);
-}
 __device__ __forceinline__ void barrier_only() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();

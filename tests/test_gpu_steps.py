@@ -69,6 +69,7 @@ ATTN_CASES = [
     ("c0", 1, 80), ("c0", 2, 1), ("c0", 1, 65), ("c0", 3, 200),
     ("c1", 1, 1), ("c1", 2, 80), ("c1", 2, 512), ("c1", 1, 130), ("c1", 1, 4544), ("c1", 1, 4608),
     ("c1", 2, 4544), ("c1", 2, 4608),  # 48 queries per wave (fewer rounds on 256 CUs)
+    ("c1", 1, 100), ("c0", 1, 47),  # the last tile ends inside its second 32-key half
 ]
 
 
@@ -117,6 +118,59 @@ def test_attention_one_key_returns_gated_value(dev):
     y = device.to_numpy(OG)
     # only the final bf16 rounding separates the two
     assert np.max(np.abs(y - expect)) <= 2 ** -8 * np.max(np.abs(expect))
+
+
+def _attention_vs_oracle(dev, cfg, z, rows, f32_tol=1e-5):
+    torch, device, dit = dev
+    B, L = cfg.batch, cfg.seq_len
+    Z = device.to_device(z, cfg.dtype)
+    OG = torch.empty((cfg.tokens, cfg.n_heads * cfg.head_dim), dtype=Z.dtype, device="cuda")
+    c = dit.config_of(cfg)
+    dit.attention(c, Z, OG, torch.empty(dit.workspace_size(c), dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    y = device.to_numpy(OG).reshape(B, L, -1)
+    H, Hk, d = cfg.n_heads, cfg.n_kv_heads, cfg.head_dim
+    zz = z.reshape(B, L, -1)
+    for b in range(B):
+        zb = zz[b].astype(np.float64)
+        q = zb[rows, : H * d].reshape(len(rows), H, d)
+        k = zb[:, H * d:(H + Hk) * d].reshape(L, Hk, d)
+        v = zb[:, (H + Hk) * d:(H + 2 * Hk) * d].reshape(L, Hk, d)
+        g = zb[rows, (H + 2 * Hk) * d:].reshape(len(rows), H, d)
+        ref = O.gated_gqa_attention(q, k, v, g)
+        assert_parity(y[b, rows], ref, cfg.dtype, f"attention b={b}", maxabs=f32_tol if cfg.dtype == "f32" else 1e-2,
+                      cos_min=0.99999)
+
+
+@pytest.mark.parametrize("name,B,L", [("c0", 1, 200), ("c1", 1, 300), ("c1", 2, 4608)])
+def test_attention_rising_reference(dev, name, B, L):
+    """Scores that step up by about 30 (natural units) at keys placed in the
+    first and in the second 32-key half of several tiles: the running
+    softmax reference has to be raised again and again after the first tile
+    (queries carry a common component along a fixed direction u, and the key
+    component along u steps up at each of those keys)."""
+    print(f"attention rising reference {name} B={B} L={L}", flush=True)
+    cfg = small_cfg(name, batch=B, n_image=L, n_text=0)
+    H, Hk, d = cfg.n_heads, cfg.n_kv_heads, cfg.head_dim
+    z = datagen.qkvg_activations(cfg).reshape(B, L, -1).astype(np.float64)
+    u = np.ones(d) / np.sqrt(d)
+    steps = [40, 74, 178] + list(range(300, L, 397))  # second, first, second half, then spread out
+    c = np.zeros(L)
+    for p in steps:
+        if p < L:
+            c[p:] += 30.0 * np.sqrt(d) / 2.0  # score step ~ 30 for a query with q.u ~ 2
+    for hh in range(H):
+        z[:, :, hh * d:(hh + 1) * d] += 2.0 * u
+    for j in range(Hk):
+        z[:, :, (H + j) * d:(H + j + 1) * d] += c[None, :, None] * u
+    z = z.reshape(B * L, -1).astype(np.float32)
+    if cfg.dtype != "f32":
+        z = datagen.bf16_round(z)
+    rows = np.arange(L) if L <= 600 else np.unique(np.r_[0, 1, 63, 64, 65, L // 2, L - 65, L - 64, L - 2, L - 1,
+                                                            np.random.default_rng(L).integers(0, L, 24)])
+    # scores of a few hundred: fp32 rounding of the dot products alone moves
+    # them by ~1e-5, so the fp32 bar is the general 1e-4 one here
+    _attention_vs_oracle(dev, cfg, z, rows, f32_tol=1e-4)
 
 
 # ------------------------------------------------------------------ modnorm / residual
@@ -207,12 +261,15 @@ def test_gemm_tile_grouping(dev, variant, group_m):
 
 @pytest.mark.parametrize("variant", list(range(15)))
 @pytest.mark.parametrize("swiglu", [False, True])
-def test_gemm_every_tile_variant(dev, variant, swiglu):
-    """Every compiled tile configuration on ragged M, N and K."""
+@pytest.mark.parametrize("k", [328, 384, 64])
+def test_gemm_every_tile_variant(dev, variant, swiglu, k):
+    """Every compiled tile configuration on ragged M and N, with K ragged
+    against the 64-element stage (328), a whole number of stages (384) and
+    a single stage (64)."""
     torch, device, dit = dev
-    m, n, k = 300, 200 if swiglu else 520, 328
+    m, n = 300, 200 if swiglu else 520
     cfg = datagen.get_config("c1")
-    a, w = datagen.gemm_operands(cfg, m, 2 * n if swiglu else n, k, tag=97 + variant)
+    a, w = datagen.gemm_operands(cfg, m, 2 * n if swiglu else n, k, tag=97 + variant + k)
     A, W = device.to_device(a, "bf16"), device.to_device(w, "bf16")
     C = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
     dit.gemm_variant(variant, A, W, C, swiglu=swiglu)
