@@ -69,8 +69,8 @@ def load_traffic(kernel_file: str):
 
 
 def cpu_baseline(cfg, x, w, t, w_t1, w_t2) -> dict:
-    """The oracle as it stands, on sample 0 (all 4608 tokens) of the workload:
-    its own timestep modulation, then the block."""
+    """The oracle as it stands on the whole workload (every sample of the
+    batch, all tokens): its own timestep modulation, then the block."""
     from oracle import dit_oracle as O
     try:
         from threadpoolctl import threadpool_info
@@ -80,12 +80,12 @@ def cpu_baseline(cfg, x, w, t, w_t1, w_t2) -> dict:
         threads, blas = os.cpu_count(), "?"
     oc = O.OracleConfig.of(cfg)
     t0 = time.perf_counter()
-    mod = O.timestep_modulation(t[:1], w_t1, w_t2, cfg.hidden)
-    O.block_forward(x[:1], mod, w, oc)
+    mod = O.timestep_modulation(t, w_t1, w_t2, cfg.hidden)
+    O.block_forward(x, mod, w, oc)
     dt = time.perf_counter() - t0
-    return {"value": cfg.seq_len / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"sample 0 of the batch: one full {cfg.seq_len}-token sequence, one block, "
-                      f"fp64 numpy ({blas}), {dt:.2f} s",
+    return {"value": cfg.tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"the whole batch: {cfg.batch} x {cfg.seq_len} tokens, one block with its timestep "
+                      f"modulation, fp64 numpy ({blas}), {dt:.2f} s",
             "seconds": dt, "affinity_cpus": len(os.sched_getaffinity(0))}
 
 
