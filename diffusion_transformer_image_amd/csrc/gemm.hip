@@ -764,12 +764,7 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(const uint8_t *__restrict
   };
 
   const int nk = (K + BKB - 1) / BKB;
-  issue_stage(0, 0);
-  for (int kt = 0; kt < nk; ++kt) {
-    wait_vmcnt<0>();  // this wave's DMA of stage kt
-    __syncthreads();  // stage kt visible to all; every wave is done with stage kt-1
-    if (kt + 1 < nk) issue_stage(kt + 1, (kt + 1) & 1);
-    const char *sb = smem + (kt & 1) * STAGE;
+  auto mmas = [&](const char *sb) {
     i32x8 bf[CB];
 #pragma unroll
     for (int j = 0; j < CB; ++j) bf[j] = frag(sb, brow[j]);
@@ -779,6 +774,60 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(const uint8_t *__restrict
 #pragma unroll
       for (int j = 0; j < CB; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[j], acc[i][j], 0, 0, 0, 0, 0, 0);
+    }
+  };
+  if (K % BKB == 0) {
+    // K a whole number of stages: the K offset is the DMA's scalar offset
+    // (rows outside the operand keep an out-of-range vector offset; the
+    // stage past the end gets an out-of-range scalar offset), and the 8
+    // loads of the next stage are spread over the stage's MFMAs, the A
+    // fragment reads of row block i+1 issued beside the MFMAs of block i
+    uint32_t goffs[BPW];
+#pragma unroll
+    for (int j = 0; j < BPW; ++j) goffs[j] = gval[j] ? goff[j] : kOOB;
+    auto issue_spread = [&](int kt, int buf) {
+      const uint32_t soff = kt < nk ? (uint32_t)kt * BKB : kOOB;
+      char *base = smem + buf * STAGE;
+#pragma unroll
+      for (int j = 0; j < BPW; ++j) {
+        const int blk = wave + j * NW;
+        load_lds16_k(blk < ABLK ? ra : rw, base + blk * 1024, goffs[j], soff);
+      }
+    };
+    static_assert(BPW == RB, "one DMA load per row block of MFMAs");
+    issue_spread(0, 0);
+    for (int kt = 0; kt < nk; ++kt) {
+      wait_vmcnt<0>();  // this wave's DMA of stage kt
+      __syncthreads();  // stage kt visible to all; every wave is done with stage kt-1
+      const char *sb = smem + (kt & 1) * STAGE;
+      char *nb = smem + ((kt + 1) & 1) * STAGE;
+      const uint32_t soff = kt + 1 < nk ? (uint32_t)(kt + 1) * BKB : kOOB;
+      // program order: the fragment reads of stage kt, then the DMA loads
+      // of stage kt+1 one per row block (the DMA writes the other buffer;
+      // in this order the compiler may keep the loads beside the MFMAs)
+      i32x8 bf[CB];
+#pragma unroll
+      for (int j = 0; j < CB; ++j) bf[j] = frag(sb, brow[j]);
+      i32x8 af = frag(sb, arow[0]);
+#pragma unroll
+      for (int i = 0; i < RB; ++i) {
+        const i32x8 an = i + 1 < RB ? frag(sb, arow[i + 1]) : af;
+        const int blk = wave + i * NW;
+        load_lds16_k(blk < ABLK ? ra : rw, nb + blk * 1024, goffs[i], soff);
+#pragma unroll
+        for (int j = 0; j < CB; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[j], acc[i][j], 0, 0, 0, 0, 0, 0);
+        af = an;
+      }
+    }
+    wait_vmcnt<0>();  // the zero-filled stage past the end has landed before LDS is reused
+  } else {
+    issue_stage(0, 0);
+    for (int kt = 0; kt < nk; ++kt) {
+      wait_vmcnt<0>();  // this wave's DMA of stage kt
+      __syncthreads();  // stage kt visible to all; every wave is done with stage kt-1
+      if (kt + 1 < nk) issue_stage(kt + 1, (kt + 1) & 1);
+      mmas(smem + (kt & 1) * STAGE);
     }
   }
 
