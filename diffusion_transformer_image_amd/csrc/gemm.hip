@@ -328,10 +328,11 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(const T *__restrict__
     }
   };
   if (K % KSTAGE == 0) {
+    // both buffers are free at the start: stage 1 goes out with stage 0
     issue_spread(0, 0);
-    wait_vmcnt<0>();
-    __syncthreads();
     issue_spread(1, 1);
+    wait_vmcnt<BPW>();  // this wave's loads of stage 0 (they complete in issue order)
+    __syncthreads();
     u32x4 a0[RB], b0[CB], a1[RB], b1[CB];
     load_frags(smem, 0, a0, b0);
     drain_lgkm();
