@@ -109,35 +109,37 @@ __device__ __forceinline__ void gemm_epilogue(const f32x4 (&acc)[BM / WM / 16][B
     else return acc[i][j][e];
   };
   // (the XOR swizzle needs a power-of-two number of 16-byte chunks per row)
-  if constexpr (sizeof(T) == 2 && (TNO * 2) % 64 == 0 && ((TNO / 8) & (TNO / 8 - 1)) == 0 &&
-                NW * TM * TNO * 2 <= SMEM) {
-    // bf16: stage the wave's TM x TNO output tile in LDS (16-byte chunks
-    // XOR-swizzled by row), then write whole 16-byte chunks: each row of the
-    // tile goes out as TNO*2 contiguous bytes instead of 2-byte pieces.
-    constexpr int PITCH = TNO * 2;       // bytes per tile row in LDS
-    constexpr int CPRO = PITCH / 16;     // 16-byte chunks per row (4 or 8)
+  constexpr int BNO = (EPI == EPI_SWIGLU) ? BN / 2 : BN;  // output columns of the tile
+  constexpr int PITCH = BNO * 2;                           // bytes per tile row in LDS
+  constexpr int CPRO = PITCH / 16;                         // 16-byte chunks per row
+  if constexpr (sizeof(T) == 2 && CPRO >= 4 && (CPRO & (CPRO - 1)) == 0 && BM * PITCH <= SMEM &&
+                BM % NW == 0) {
+    // bf16: stage the whole BM x BNO output tile in LDS (16-byte chunks
+    // XOR-swizzled by row), then each wave writes BM/NW whole rows of
+    // PITCH contiguous bytes: every store instruction covers whole cache
+    // lines (a wave's own sub-tile row is only 64 bytes for the SwiGLU
+    // tile, half a line, which costs the L2 a merge per line).
     __syncthreads();  // all waves are done reading the operand stages
-    char *tile = smem + wave * (TM * PITCH);
 #pragma unroll
     for (int j = 0; j < CB / ((EPI == EPI_SWIGLU) ? 2 : 1); ++j) {
-      const int col = j * 16 + r16;  // column inside the wave tile
+      const int col = wn * TNO + j * 16 + r16;  // column inside the tile
 #pragma unroll
       for (int i = 0; i < RB; ++i) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int row = i * 16 + 4 * g + e;
+          const int row = wm * TM + i * 16 + 4 * g + e;
           const int off = row * PITCH + (((col >> 3) ^ (row & (CPRO - 1))) << 4) + (col & 7) * 2;
-          *reinterpret_cast<bf16 *>(tile + off) = (bf16)out_val(i, j, e);
+          *reinterpret_cast<bf16 *>(smem + off) = (bf16)out_val(i, j, e);
         }
       }
     }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_wave_barrier();
+    __syncthreads();  // the whole tile is staged
+    constexpr int RPW = BM / NW;  // rows stored by each wave
 #pragma unroll
-    for (int q = lane; q < TM * CPRO; q += 64) {
-      const int row = q / CPRO, c = q % CPRO;
-      const u32x4 v = *reinterpret_cast<const u32x4 *>(tile + row * PITCH + ((c ^ (row & (CPRO - 1))) << 4));
-      const int gr = row0 + row, gc = col0 + c * 8;
+    for (int q = lane; q < RPW * CPRO; q += 64) {
+      const int row = wave * RPW + q / CPRO, c = q % CPRO;
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(smem + row * PITCH + ((c ^ (row & (CPRO - 1))) << 4));
+      const int gr = m0 + row, gc = n0 + c * 8;
       if (gr < M) {
         T *dst = C + (size_t)gr * N + gc;
         if (gc + 8 <= N && (N & 7) == 0) {
