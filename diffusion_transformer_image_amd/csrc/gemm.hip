@@ -864,7 +864,7 @@ hipError_t launch_gemm_fp8(bool swiglu, const void *aq, const float *sa, const v
   const int mt = (M + 255) / 256, nt = swiglu ? (N + 127) / 128 : (N + 255) / 256;
   if (swiglu)
     hipLaunchKernelGGL(gemm_fp8_kernel<EPI_SWIGLU>, dim3(mt * nt), dim3(512), 0, s, (const uint8_t *)aq, sa,
-                       (const uint8_t *)wq, sw, (bf16 *)c, M, N, K, mt, nt, 8);
+                       (const uint8_t *)wq, sw, (bf16 *)c, M, N, K, mt, nt, 4);
   else
     hipLaunchKernelGGL(gemm_fp8_kernel<EPI_STORE>, dim3(mt * nt), dim3(512), 0, s, (const uint8_t *)aq, sa,
                        (const uint8_t *)wq, sw, (bf16 *)c, M, N, K, mt, nt, 8);
@@ -939,7 +939,9 @@ template <int EPI>
 static hipError_t gemm_dispatch(bool f32, int variant, int gm, const void *a, const void *w,
                                 void *c, int M, int N, int K, hipStream_t s, float *part,
                                 size_t part_bytes) {
-  if (gm <= 0) gm = 8;
+  // L2 grouping width: 4 row tiles for the SwiGLU tile (it reads W1 and W3
+  // rows: measured ~3 % faster than 8 on W13 at 1024 px), else 8
+  if (gm <= 0) gm = (EPI == EPI_SWIGLU) ? 4 : 8;
   if (f32) return launch_gemm_t<float, 256, 256, 128, 2, 2, 4, EPI>(a, w, c, M, N, K, s, gm);
   if (variant < 0) {
     const GemmChoice ch = gemm_choose(M, N, K, EPI == EPI_SWIGLU);
@@ -988,7 +990,7 @@ hipError_t launch_gemm_swiglu(bool f32, const void *a, const void *w13, void *u,
 hipError_t launch_gemm_split(bool swiglu, const void *a, const void *w, void *c, int M, int N, int K,
                              int sk_tiles, int segs, float *part, hipStream_t s) {
   if (swiglu)
-    return launch_gemm_t<bf16, 256, 256, 128, 2, 2, 4, EPI_SWIGLU, true>(a, w, c, M, N, K, s, 8, sk_tiles,
+    return launch_gemm_t<bf16, 256, 256, 128, 2, 2, 4, EPI_SWIGLU, true>(a, w, c, M, N, K, s, 4, sk_tiles,
                                                                          segs, part);
   return launch_gemm_t<bf16, 256, 256, 128, 2, 2, 4, EPI_STORE, true>(a, w, c, M, N, K, s, 8, sk_tiles, segs,
                                                                       part);
