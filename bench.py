@@ -51,8 +51,8 @@ def bytes_per_token(cfg) -> dict:
 
 
 def src_hash(name: str) -> str:
-    p = os.path.join(ROOT, "diffusion_transformer_image_amd", "csrc", name)
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+    from bench_traffic import code_hash
+    return code_hash(os.path.join(ROOT, "diffusion_transformer_image_amd", "csrc", name))
 
 
 def load_traffic(kernel_file: str):

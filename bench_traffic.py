@@ -20,8 +20,9 @@ Two steps:
    two counter CSVs, scales each counter by what it reads for the copy
    (FETCH_SIZE and WRITE_SIZE are in KiB; the copy moves a known byte
    count), and writes profiles/traffic_gemm_w13_1024px.json (+ .md) with
-   the per-launch HBM bytes and the sha256 of gemm.hip, so bench.py
-   reports the figure only while the kernel source is unchanged.
+   the per-launch HBM bytes and a hash of gemm.hip's code (comments and
+   whitespace removed), so bench.py reports the figure only while the
+   kernel code is unchanged.
 
 ``python bench_traffic.py stats <run_kernel_stats.csv> <out.md> <title> <command>``
 renders a rocprofv3 ``--stats`` kernel summary CSV as the markdown table kept
@@ -34,6 +35,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import sys
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -93,14 +95,24 @@ def _counter(d: str, name: str):
     return sum(copy) / len(copy), (sum(gemm) + sum(fix)) / len(gemm), f[0]
 
 
+def code_hash(path: str) -> str:
+    """sha256 prefix of a C++/HIP source with its comments and whitespace
+    removed (string literals kept): the traffic record stays valid across
+    comment-only edits and lapses when the code changes."""
+    text = open(path, encoding="utf-8").read()
+    tok = re.compile(r'"(?:\\.|[^"\\\n])*"|//[^\n]*|/\*.*?\*/', re.S)
+    code = tok.sub(lambda m: m.group(0) if m.group(0).startswith('"') else " ", text)
+    code = " ".join(code.split())
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
+
+
 def summarize(fetch_dir: str, write_dir: str) -> None:
     cf, gf, _ = _counter(fetch_dir, "FETCH_SIZE")
     cw, gw, _ = _counter(write_dir, "WRITE_SIZE")
     kf, kw = cf / COPY_READ, cw / COPY_WRITE  # counter bytes per real byte
     fetch, write = gf / kf, gw / kw
     algorithmic = 2 * (T * D + 2 * F * D + T * F)
-    sha = hashlib.sha256(open(os.path.join(ROOT, "diffusion_transformer_image_amd", "csrc", "gemm.hip"),
-                              "rb").read()).hexdigest()[:16]
+    sha = code_hash(os.path.join(ROOT, "diffusion_transformer_image_amd", "csrc", "gemm.hip"))
     rec = {"kernel": "gemm_kernel + gemm_sk_fixup (h2 * W13^T with the SwiGLU epilogue, split tail as in "
                      "the block), 1024 px shapes",
            "bytes_per_launch": fetch + write, "fetch_bytes": fetch, "write_bytes": write,
@@ -121,7 +133,7 @@ def summarize(fetch_dir: str, write_dir: str) -> None:
           f"| total | {fetch + write:.4g} |\n| algorithmic (h2 + W13 + U) | {algorithmic:.4g} |\n\n",
           f"Copy calibration (float32 -> bf16 elementwise copy, {COPY_READ >> 20} MiB read, "
           f"{COPY_WRITE >> 20} MiB written): FETCH_SIZE reads {kf:.3f} and WRITE_SIZE {kw:.3f} "
-          f"counter-bytes per byte.  gemm.hip sha256 prefix {sha}.\n"]
+          f"counter-bytes per byte.  gemm.hip code hash {sha} (comments and whitespace removed).\n"]
     open(out + ".md", "w").write("".join(md))
     print(json.dumps(rec, indent=1))
 

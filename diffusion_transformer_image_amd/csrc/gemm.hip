@@ -11,7 +11,9 @@
 //    staging) through a STAGES-deep ring: the loads of stage kt+STAGES-1 are
 //    issued while stage kt is multiplied, and each wave waits only for its
 //    own loads of the stage it is about to read (partial vmcnt), so one
-//    barrier per stage is the only synchronisation;
+//    barrier per stage is the only synchronisation; in the pipelined
+//    two-stage loop the refill of a stage is spread over the MFMAs (one
+//    load every few MFMAs) instead of leaving as a burst after the barrier;
 //  * 16-byte chunk c of LDS row r sits at chunk c ^ swz(r), which spreads
 //    the fragment reads (16 rows x one chunk per lane group) over all banks;
 //  * tails in M, N and K are zero-filled by the buffer descriptor's range
@@ -19,7 +21,10 @@
 //  * workgroup ids are remapped so that each XCD (dispatch is round-robin
 //    over the 8 XCDs) walks a contiguous band of tiles, grouped gm row
 //    tiles at a time, so tiles sharing A rows or W rows meet in one L2
-//    (gm is chosen per shape by the host).
+//    (gm = 4 row tiles for the SwiGLU tile, 8 otherwise, unless the caller
+//    sets it);
+//  * the bf16 epilogue stages the whole output tile in LDS and each wave
+//    stores whole rows (full cache lines).
 #include <cmath>
 #include <type_traits>
 
