@@ -8,8 +8,7 @@
 // 16-byte accesses (4 rotation pairs each).  The angles of a lane's pairs
 // depend only on the token and the pair index: they are computed once per
 // token (fp32 frequency and angle, accurate sincosf) and reused for every
-// head.  The head's mean square is a shuffle reduction
-// over its d/8 lanes.
+// head.  The head's mean square is a DPP reduction over its d/8 lanes.
 #include <cmath>
 
 #include "dit_common.h"
@@ -44,12 +43,35 @@ template <> struct Oct<float> {
   }
 };
 
-// Sum over the G consecutive lanes of a group (G a power of two <= 64).
+// DPP lane moves inside a row of 16 lanes (no LDS round trip, unlike a
+// shuffle through ds_bpermute): rotate right by N, mirror each half row,
+// swap neighbours / pairs in each quad.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, true));
+}
+constexpr int DPP_ROW_ROR = 0x120, DPP_ROW_HALF_MIRROR = 0x141, DPP_QUAD_XOR1 = 0xb1, DPP_QUAD_XOR2 = 0x4e;
+
+// Sum over the G consecutive lanes of a group (G a power of two <= 64),
+// the result in every lane of the group.
 template <int G>
 __device__ __forceinline__ float group_sum(float v) {
+  if constexpr (G == 16) {  // rotations within the row: pairs, fours, eights, all
+    v += dpp<DPP_ROW_ROR + 8>(v);
+    v += dpp<DPP_ROW_ROR + 4>(v);
+    v += dpp<DPP_ROW_ROR + 2>(v);
+    v += dpp<DPP_ROW_ROR + 1>(v);
+    return v;
+  } else if constexpr (G == 8) {  // lane i + lane 7-i, then the quad's four
+    v += dpp<DPP_ROW_HALF_MIRROR>(v);
+    v += dpp<DPP_QUAD_XOR1>(v);
+    v += dpp<DPP_QUAD_XOR2>(v);
+    return v;
+  } else {
 #pragma unroll
-  for (int o = G / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+    for (int o = G / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+  }
 }
 
 // One wave per token row.  A head of HD dimensions is HD/8 lanes holding 8
@@ -81,6 +103,23 @@ __global__ __launch_bounds__(256) void qk_prologue_kernel(T *__restrict__ qkvg, 
       }
     }
   };
+  // the lane's 8 gains of each norm (16-byte loads, issued with the first
+  // data loads so the two latencies overlap)
+  float gq[8], gk[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) gq[i] = gk[i] = 0.f;
+  if (qk_norm) {
+    if (wq) {
+      const f32x4 a = *reinterpret_cast<const f32x4 *>(wq + e0), b = *reinterpret_cast<const f32x4 *>(wq + e0 + 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { gq[i] = a[i]; gq[4 + i] = b[i]; }
+    }
+    if (wk) {
+      const f32x4 a = *reinterpret_cast<const f32x4 *>(wk + e0), b = *reinterpret_cast<const f32x4 *>(wk + e0 + 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { gk[i] = a[i]; gk[4 + i] = b[i]; }
+    }
+  }
   load_step(0);  // in flight while the angles are computed
   // ---- rotations of this lane's 4 pairs j = e0/2 .. e0/2 + 3 at this token
   float c[4] = {1.f, 1.f, 1.f, 1.f}, s[4] = {0.f, 0.f, 0.f, 0.f};
@@ -107,12 +146,6 @@ __global__ __launch_bounds__(256) void qk_prologue_kernel(T *__restrict__ qkvg, 
       }
     }
   }
-  float gq[8], gk[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    gq[i] = (qk_norm && wq) ? 1.f + wq[e0 + i] : 1.f;
-    gk[i] = (qk_norm && wk) ? 1.f + wk[e0 + i] : 1.f;
-  }
   for (int h0 = 0; h0 < nh; h0 += U * HPW) {
     if (h0 > 0) load_step(h0);
 #pragma unroll
@@ -128,7 +161,7 @@ __global__ __launch_bounds__(256) void qk_prologue_kernel(T *__restrict__ qkvg, 
         const float inv = rsqrtf(group_sum<LPH>(ss) / (float)HD + eps);
         const bool isq = h < H;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] *= inv * (isq ? gq[i] : gk[i]);
+        for (int i = 0; i < 8; ++i) v[i] *= inv * (1.f + (isq ? gq[i] : gk[i]));
       }
       float o[8];
 #pragma unroll
