@@ -42,11 +42,16 @@ template <> struct Vec8<float> {
 __device__ __forceinline__ void load8f(const float *p, float (&v)[8]) { Vec8<float>::load(p, v); }
 
 // ----------------------------------------------------------------- layout
-// Every elementwise kernel runs one workgroup per (sample b, 16 token rows):
+// Every elementwise kernel runs one workgroup per (sample b, 8 token rows):
 // the per-sample modulation vectors it needs (combined with the block bias
 // and the norm gain) are computed once into LDS, then each of the 4 waves
-// streams 4 rows, one row per wave at a time, 8 elements per lane-chunk.
-constexpr int EW_ROWS = 16;  // rows per workgroup
+// streams 2 rows, one row per wave at a time, 8 elements per lane-chunk;
+// the first row's loads go out before the staging and the second row's
+// before the first is computed.  8 rows rather than 16 give twice the
+// workgroups (about 4.5 waves per SIMD at 1024 px instead of 2.25), which
+// the memory latency needs: 1024 px modnorm 41 -> 37.6 us, the residual
+// kernels 80 -> 72 us each, the 60-block stack 115.0 -> 113.5 ms.
+constexpr int EW_ROWS = 8;  // rows per workgroup
 constexpr int EW_WAVES = 4;
 
 __device__ __forceinline__ void lds8(const float *p, float (&v)[8]) {
@@ -55,6 +60,36 @@ __device__ __forceinline__ void lds8(const float *p, float (&v)[8]) {
   v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
   v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
+
+// One row's NCH chunks of 8 elements per lane (chunk ch = lane + 64 c), held
+// as raw 16-byte words so a row can be in flight while the previous one is
+// computed: loads are issued by load(), converted by get().
+template <typename T, int NCH>
+struct RowBuf {
+  static constexpr int W = sizeof(T) == 2 ? 1 : 2;  // 16-byte words per chunk
+  u32x4 r[NCH][W];
+  __device__ __forceinline__ void load(const T *row, int lane, int nch) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int ch = lane + 64 * c;
+      if (ch < nch) {
+#pragma unroll
+        for (int w = 0; w < W; ++w) r[c][w] = *reinterpret_cast<const u32x4 *>(row + ch * 8 + w * 4);
+      }
+    }
+  }
+  __device__ __forceinline__ void get(int c, float (&v)[8]) const {
+    if constexpr (W == 1) {
+      const bf16x8 b = __builtin_bit_cast(bf16x8, r[c][0]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = (float)b[i];
+    } else {
+      const f32x4 a = __builtin_bit_cast(f32x4, r[c][0]), b = __builtin_bit_cast(f32x4, r[c][1]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { v[i] = a[i]; v[4 + i] = b[i]; }
+    }
+  }
+};
 
 // A = (1 + gain) * (1 + scale), S = shift of norm `which`; G = gate of
 // residual `which` (all with the per-block bias added to m[b]).
@@ -90,22 +125,30 @@ __global__ __launch_bounds__(256) void modnorm_kernel(const Tx *__restrict__ x, 
   extern __shared__ float ew_lds[];
   float *A = ew_lds, *S = ew_lds + D;
   const int b = blockIdx.y;
-  stage_norm_vectors(A, S, mod, bias, gain, b, D, which);
-  __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nch = D >> 3;
-  for (int rr = 0; rr < EW_ROWS / EW_WAVES; ++rr) {
-    const int l = blockIdx.x * EW_ROWS + rr * EW_WAVES + wave;
+  constexpr int RPW = EW_ROWS / EW_WAVES;  // rows per wave
+  auto row_at = [&](int rr) { return blockIdx.x * EW_ROWS + rr * EW_WAVES + wave; };
+  // the first row's loads go out before the staging of the vectors, and
+  // row rr+1's before row rr is computed (two memory latencies overlap)
+  RowBuf<Tx, NCH> buf[2];
+  if (row_at(0) < seq_len) buf[0].load(x + ((size_t)b * seq_len + row_at(0)) * D, lane, nch);
+  stage_norm_vectors(A, S, mod, bias, gain, b, D, which);
+  __syncthreads();
+#pragma unroll
+  for (int rr = 0; rr < RPW; ++rr) {
+    const int l = row_at(rr);
     if (l >= seq_len) break;
+    if (rr + 1 < RPW && row_at(rr + 1) < seq_len)
+      buf[(rr + 1) & 1].load(x + ((size_t)b * seq_len + row_at(rr + 1)) * D, lane, nch);
     const size_t row = (size_t)b * seq_len + l;
-    const Tx *xr = x + row * D;
     float v[NCH][8];
     float ss = 0.f;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       const int ch = lane + 64 * c;
       if (ch < nch) {
-        Vec8<Tx>::load(xr + ch * 8, v[c]);
+        buf[rr & 1].get(c, v[c]);
 #pragma unroll
         for (int i = 0; i < 8; ++i) ss += v[c][i] * v[c][i];
       }
@@ -173,22 +216,52 @@ __global__ __launch_bounds__(256) void resid_kernel(const Tx *__restrict__ x, co
   extern __shared__ float ew_lds[];
   float *G = ew_lds;
   const int b = blockIdx.y;
-  stage_gate_vector(G, mod, bias, b, D, which);
-  __syncthreads();
   const int nch = D >> 3;
   const int l0 = blockIdx.x * EW_ROWS;
   const int nrows = min(EW_ROWS, seq_len - l0);
-  // flat walk over (row, chunk) of this workgroup's rows: fully coalesced
-  for (int idx = threadIdx.x; idx < nrows * nch; idx += blockDim.x) {
-    const int r = idx / nch, ch = idx - r * nch;
-    const size_t off = ((size_t)b * seq_len + l0 + r) * D + ch * 8;
-    float xv[8], yv[8], gv[8], o[8];
-    Vec8<Tx>::load(x + off, xv);
-    Vec8<Ty>::load(y + off, yv);
-    lds8(G + ch * 8, gv);
+  const int n = nrows * nch;
+  // flat walk over (row, chunk) of this workgroup's rows, fully coalesced,
+  // UR chunks per thread at a time with all their loads issued first (the
+  // first batch before the gate vector is staged)
+  constexpr int UR = 4;
+  const size_t base = ((size_t)b * seq_len + l0) * D;
+  auto batch = [&](int idx0, RowBuf<Tx, UR> &bx, RowBuf<Ty, UR> &by) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] = xv[i] + gv[i] * yv[i];
-    Vec8<To>::store(out + off, o);
+    for (int u = 0; u < UR; ++u) {
+      const int idx = idx0 + u * blockDim.x;
+      if (idx < n) {
+        const int r = idx / nch, ch = idx - r * nch;
+        const size_t off = base + (size_t)r * D + ch * 8;
+#pragma unroll
+        for (int w = 0; w < RowBuf<Tx, UR>::W; ++w) bx.r[u][w] = *reinterpret_cast<const u32x4 *>(x + off + w * 4);
+#pragma unroll
+        for (int w = 0; w < RowBuf<Ty, UR>::W; ++w) by.r[u][w] = *reinterpret_cast<const u32x4 *>(y + off + w * 4);
+      }
+    }
+  };
+  RowBuf<Tx, UR> bx;
+  RowBuf<Ty, UR> by;
+  int idx0 = threadIdx.x;
+  batch(idx0, bx, by);
+  stage_gate_vector(G, mod, bias, b, D, which);
+  __syncthreads();
+  for (; idx0 < n; idx0 += UR * blockDim.x) {
+#pragma unroll
+    for (int u = 0; u < UR; ++u) {
+      const int idx = idx0 + u * blockDim.x;
+      if (idx < n) {
+        const int r = idx / nch, ch = idx - r * nch;
+        const size_t off = base + (size_t)r * D + ch * 8;
+        float xv[8], yv[8], gv[8], o[8];
+        bx.get(u, xv);
+        by.get(u, yv);
+        lds8(G + ch * 8, gv);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[i] = xv[i] + gv[i] * yv[i];
+        Vec8<To>::store(out + off, o);
+      }
+    }
+    if (idx0 + UR * blockDim.x < n) batch(idx0 + UR * blockDim.x, bx, by);
   }
 }
 
@@ -231,14 +304,31 @@ __global__ __launch_bounds__(256) void resid_modnorm_kernel(const Tx *__restrict
   extern __shared__ float ew_lds[];
   float *G = ew_lds, *A = ew_lds + D, *S = ew_lds + 2 * D;
   const int b = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nch = D >> 3;
+  constexpr int RPW = EW_ROWS / EW_WAVES;  // rows per wave
+  auto row_at = [&](int rr) { return blockIdx.x * EW_ROWS + rr * EW_WAVES + wave; };
+  // the first row's loads go out before the staging of the vectors, and
+  // row rr+1's before row rr is computed (two memory latencies overlap)
+  RowBuf<Tx, NCH> bx[2];
+  RowBuf<Ty, NCH> by[2];
+  if (row_at(0) < seq_len) {
+    const size_t r0 = ((size_t)b * seq_len + row_at(0)) * D;
+    bx[0].load(x + r0, lane, nch);
+    by[0].load(y + r0, lane, nch);
+  }
   stage_gate_vector(G, mod, bias, b, D, 0);
   stage_norm_vectors(A, S, mod, bias, gain2, b, D, 1);
   __syncthreads();
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int nch = D >> 3;
-  for (int rr = 0; rr < EW_ROWS / EW_WAVES; ++rr) {
-    const int l = blockIdx.x * EW_ROWS + rr * EW_WAVES + wave;
+#pragma unroll
+  for (int rr = 0; rr < RPW; ++rr) {
+    const int l = row_at(rr);
     if (l >= seq_len) break;
+    if (rr + 1 < RPW && row_at(rr + 1) < seq_len) {
+      const size_t rn = ((size_t)b * seq_len + row_at(rr + 1)) * D;
+      bx[(rr + 1) & 1].load(x + rn, lane, nch);
+      by[(rr + 1) & 1].load(y + rn, lane, nch);
+    }
     const size_t row = (size_t)b * seq_len + l;
     float v[NCH][8];
     float ss = 0.f;
@@ -247,8 +337,8 @@ __global__ __launch_bounds__(256) void resid_modnorm_kernel(const Tx *__restrict
       const int ch = lane + 64 * c;
       if (ch < nch) {
         float xv[8], yv[8], gv[8];
-        Vec8<Tx>::load(x + row * D + ch * 8, xv);
-        Vec8<Ty>::load(y + row * D + ch * 8, yv);
+        bx[rr & 1].get(c, xv);
+        by[rr & 1].get(c, yv);
         lds8(G + ch * 8, gv);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
