@@ -321,7 +321,10 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(const T *__restrict__
   // PIPE with K a whole number of stages: the K offset of a stage is the
   // DMA's scalar offset; rows outside the operand carry an out-of-range
   // vector offset at every stage, and the stage past the end of K gets an
-  // out-of-range scalar offset (zeros into a buffer that is not read again)
+  // out-of-range scalar offset: its loads land in a buffer that is not read
+  // again (zeros, or for a row outside the operand, whose two out-of-range
+  // offsets may wrap to offset 0 in 32 bits, bytes from the start of the
+  // operand: in bounds either way)
   uint32_t goffs[BPW];
 #pragma unroll
   for (int j = 0; j < BPW; ++j) goffs[j] = gval[j] ? goff[j] : kOOB;
@@ -368,7 +371,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(const T *__restrict__
     load_frags(smem + ((nk - 1) & 1) * STAGE_BYTES, 1, a1, b1);
     mmas(a0, b0);
     mmas(a1, b1);
-    wait_vmcnt<0>();  // the zero-filled stage past the end has landed before LDS is reused
+    wait_vmcnt<0>();  // the stage past the end has landed before LDS is reused
   } else {
     issue_stage(0, 0);
     wait_vmcnt<0>();
@@ -828,7 +831,7 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(const uint8_t *__restrict
         af = an;
       }
     }
-    wait_vmcnt<0>();  // the zero-filled stage past the end has landed before LDS is reused
+    wait_vmcnt<0>();  // the stage past the end has landed before LDS is reused
   } else {
     issue_stage(0, 0);
     for (int kt = 0; kt < nk; ++kt) {
