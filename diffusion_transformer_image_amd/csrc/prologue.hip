@@ -13,6 +13,7 @@
 
 #include "dit_common.h"
 #include "dit_kernels.h"
+#include "qk_rope.h"
 
 namespace dit {
 
@@ -122,29 +123,12 @@ __global__ __launch_bounds__(256) void qk_prologue_kernel(T *__restrict__ qkvg, 
   }
   load_step(0);  // in flight while the angles are computed
   // ---- rotations of this lane's 4 pairs j = e0/2 .. e0/2 + 3 at this token
-  float c[4] = {1.f, 1.f, 1.f, 1.f}, s[4] = {0.f, 0.f, 0.f, 0.f};
-  if (rope) {
-    const int l = row % L;
-    if (l < grid_h * grid_w) {
-      const float l2t = log2f(theta);
+  float c[4], s[4];
+  {
+    const QkParams p{qk_norm, rope, grid_h, grid_w, ax0, ax1, theta, eps, wq, wk};
+    const float l2t = log2f(theta);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int j = e0 / 2 + k;
-        int pos = 0, i = 0, da = 1;
-        if (2 * j >= ax0 && 2 * j < ax0 + ax1) {
-          pos = l / grid_w; i = j - ax0 / 2; da = ax1;
-        } else if (2 * j >= ax0 + ax1) {
-          pos = l % grid_w; i = j - (ax0 + ax1) / 2; da = HD - ax0 - ax1;
-        }  // frame axis: position 0 for an image
-        if (pos != 0) {
-          // fp32 is enough: the exponent's rounding moves the angle by at
-          // most ~2e-6 rad at position 84, the product by ~5e-6 rad, and
-          // sincosf reduces its argument exactly
-          const float a = (float)pos * exp2f(-(2.0f * (float)i / (float)da) * l2t);
-          sincosf(a, &s[k], &c[k]);
-        }
-      }
-    }
+    for (int k = 0; k < 4; ++k) rope_cs<HD>(p, l2t, row % L, e0 / 2 + k, c[k], s[k]);
   }
   for (int h0 = 0; h0 < nh; h0 += U * HPW) {
     if (h0 > 0) load_step(h0);
@@ -158,18 +142,13 @@ __global__ __launch_bounds__(256) void qk_prologue_kernel(T *__restrict__ qkvg, 
         float ss = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) ss += v[i] * v[i];
-        const float inv = rsqrtf(group_sum<LPH>(ss) / (float)HD + eps);
+        const float inv = qk_inv_rms<HD>(group_sum<LPH>(ss), eps);
         const bool isq = h < H;
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[i] *= inv * (1.f + (isq ? gq[i] : gk[i]));
       }
-      float o[8];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        o[2 * k] = v[2 * k] * c[k] - v[2 * k + 1] * s[k];
-        o[2 * k + 1] = v[2 * k] * s[k] + v[2 * k + 1] * c[k];
-      }
-      if (h < nh) Oct<T>::store(base + h * HD, o);
+      rope_apply<4>(v, c, s);
+      if (h < nh) Oct<T>::store(base + h * HD, v);
     }
   }
 }

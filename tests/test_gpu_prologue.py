@@ -111,6 +111,20 @@ def test_block_prologue_small_bf16_full(dev):
         check(y, ref, r.x, "bf16", f"small bf16 + prologue strong={strong}")
 
 
+@pytest.mark.parametrize("qk_norm,rope", [(True, False), (False, True)])
+@pytest.mark.parametrize("heads,kv", [(4, 4), (4, 2), (8, 2)])
+def test_block_prologue_parts_and_groups(dev, qk_norm, rope, heads, kv):
+    """Each half of the prologue alone, at query-head groups of 1, 2 and 4 per
+    key head (every attention launch shape that takes the prologue on its
+    way in), every output of a small bf16 block with a ragged length."""
+    cfg = datagen.get_config("c1").replace(batch=2, n_image=54, n_text=21, hidden=heads * 128, n_heads=heads,
+                                            n_kv_heads=kv, ffn=688, grid_h=6, grid_w=9, seed=80 + heads + kv)
+    r = ProRun(dev, cfg, strong=True, qk_norm=qk_norm, rope=rope)
+    y = r.forward()
+    ref = O.block_forward(r.x, r.mod, r.w, O.OracleConfig.of(cfg), r.pro)
+    check(y, ref, r.x, "bf16", f"H{heads}/{kv} qk_norm={qk_norm} rope={rope}")
+
+
 @pytest.mark.parametrize("name", ["c3", "c3b"])
 def test_block_prologue_full_size_sampled(dev, name):
     """1024 px (64 x 64 grid) and 768 x 1344 (48 x 84) with the prologue: sampled
