@@ -186,18 +186,27 @@ dit_status run_block(const dit_config *c, const dit_prologue *pro, const dit_blo
   DIT_TRY(timed(DIT_K_MODNORM, s, [&] {
     return launch_modnorm(xin_f32, f32, x_in, ws.h, mod, w->mod_bias, w->norm1_w, T, L, D, c->eps, 0, s);
   }));
+  // bf16: the attention's score factor rides on the query heads, applied in
+  // fp32 before their one rounding (by the projection's epilogue, or by the
+  // prologue pass, which would normalise it away), so the attention kernel
+  // spends no per-score multiply
+  const bool pre = !f32;
+  const float qsc = pre ? attn_score_scale(c->head_dim) : 1.f;
+  const bool pro_on = prologue_on(pro);
   DIT_TRY(timed(DIT_K_GEMM_QKVG, s, [&] {
-    return launch_gemm(f32, ws.h, w->w_qkvg, ws.qkvg, T, (int)d.nqkvg, D, s, -1, 0, ws.part, ws.part_bytes);
+    return launch_gemm(f32, ws.h, w->w_qkvg, ws.qkvg, T, (int)d.nqkvg, D, s, -1, 0, ws.part, ws.part_bytes,
+                       pre && !pro_on ? (int)d.hd : 0, qsc);
   }));
-  if (prologue_on(pro)) {
+  if (pro_on) {
     DIT_TRY(timed(DIT_K_PROLOGUE, s, [&] {
       return launch_qk_prologue(f32, c->head_dim, ws.qkvg, w->q_norm_w, w->k_norm_w, T, L, c->n_heads,
                                 c->n_kv_heads, pro->qk_norm, pro->rope, pro->grid_h, pro->grid_w, pro->axes,
-                                pro->theta, c->eps, s);
+                                pro->theta, c->eps, s, qsc);
     }));
   }
   DIT_TRY(timed(DIT_K_ATTN, s, [&] {
-    return launch_attention(f32, c->head_dim, ws.qkvg, ws.vt, ws.og, c->batch, L, c->n_heads, c->n_kv_heads, s);
+    return launch_attention(f32, c->head_dim, ws.qkvg, ws.vt, ws.og, c->batch, L, c->n_heads, c->n_kv_heads, s,
+                            pre);
   }));
   DIT_TRY(timed(DIT_K_GEMM_O, s, [&] {
     return launch_gemm(f32, ws.og, w->w_o, ws.br, T, D, (int)d.hd, s, -1, 0, ws.part, ws.part_bytes);

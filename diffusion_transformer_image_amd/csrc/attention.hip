@@ -105,9 +105,15 @@ __device__ __forceinline__ void att_wait_vmcnt() {
 
 // NW = waves per workgroup (2 per query head of the group); QW = query
 // tokens per wave (32 or 48), so a workgroup covers 2 * QW query tokens.
-template <typename T, int HD, int NW, int QW>
+// PRE: the query heads in qkvg already carry the factor sc = log2(e)/sqrt(d)
+// (applied before their one rounding, by the projection's epilogue or the
+// prologue pass), so scores come out of the MFMAs in base-2 units; each
+// score chain then starts from -reference (the first MFMA reads it as its
+// accumulator input) and a numerator is one exp2, with no per-score FMA.
+template <typename T, int HD, int NW, int QW, bool PRE>
 __global__ __launch_bounds__(NW * 64) void attn_kernel(const T *__restrict__ qkvg, const T *__restrict__ vt,
                                                        T *__restrict__ og, int L, int H, int Hkv, float sc) {
+  static_assert(!PRE || sizeof(T) == 2, "pre-scaled queries: bf16 only");
   constexpr int ES = sizeof(T);
   constexpr int KROW = HD * ES;         // bytes of one K row in LDS
   constexpr int NCK = KROW / 16;        // 16-byte chunks per K row (16 or 32)
@@ -186,9 +192,18 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const T *__restrict__ qkv
   for (int i = 0; i < DB; ++i)
 #pragma unroll
     for (int k = 0; k < QB; ++k) o[i][k] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // mref: the running reference per query column (raw score units, or
+  // base-2 units when PRE); PRE keeps it finite (0 until the first tile,
+  // which always takes the recompute path) and negm = -mref in the layout
+  // of a score accumulator
   float mref[QB], lrow[QB];
+  f32x4 negm[QB];
 #pragma unroll
-  for (int k = 0; k < QB; ++k) { mref[k] = -INFINITY; lrow[k] = 0.f; }
+  for (int k = 0; k < QB; ++k) {
+    mref[k] = PRE ? 0.f : -INFINITY;
+    lrow[k] = 0.f;
+    negm[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   const int nt = (L + ATT_BK - 1) / ATT_BK;
 #pragma unroll
@@ -205,7 +220,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const T *__restrict__ qkv
 
   // S^T[kb][qb] = K Q^T for the tile in buffer kt: lane holds keys
   // kb*16 + 4g + i of query qb*16 + r16 (all K fragments requested first);
-  // keys past the end of the sequence get -inf.
+  // keys past the end of the sequence get -inf.  PRE: S^T - mref.
   auto scores = [&](const char *kt, int t, f32x4(&s)[KB][QB]) {
     u32x4 kf[KB][KS];
 #pragma unroll
@@ -216,7 +231,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const T *__restrict__ qkv
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) s[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int qb = 0; qb < QB; ++qb) s[kb][qb] = PRE ? negm[qb] : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
@@ -236,10 +251,11 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const T *__restrict__ qkv
     }
   };
 
-  // Numerators p = 2^(s*sc - mref*sc) against the running reference, as the
-  // B operand of O^T += V^T P^T (bf16: one 16-byte fragment per pair of
-  // 16-key blocks; fp32: the values themselves), and this lane's partial row
-  // sums, taken from the values the MFMA will use.
+  // Numerators p = 2^(s*sc - mref*sc) against the running reference (PRE:
+  // p = 2^s, the reference already subtracted), as the B operand of
+  // O^T += V^T P^T (bf16: one 16-byte fragment per pair of 16-key blocks;
+  // fp32: the values themselves), and this lane's partial row sums, taken
+  // from the values the MFMA will use.
   constexpr int NPF = (ES == 2) ? KB / 2 : KB;
   auto numerators = [&](f32x4(&s)[KB][QB], u32x4(&pf)[NPF][QB], float (&lp)[QB]) {
 #pragma unroll
@@ -248,7 +264,8 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const T *__restrict__ qkv
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s[kb][qb][i] = __builtin_amdgcn_exp2f(fmaf(s[kb][qb][i], sc, -msc));
+        for (int i = 0; i < 4; ++i)
+          s[kb][qb][i] = __builtin_amdgcn_exp2f(PRE ? s[kb][qb][i] : fmaf(s[kb][qb][i], sc, -msc));
       float sum = 0.f;
       if constexpr (ES == 2) {
 #pragma unroll
@@ -291,16 +308,19 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const T *__restrict__ qkv
     scores(kt, t, s);
     u32x4 pf[NPF][QB];
     float lp[QB];
-    numerators(s, pf, lp);
     // Lazy reference: a lane's partial row sum above 2^30 (or not finite)
     // means a score more than 30 (log2 units) above the reference, or no
-    // reference yet (first tile).  Then the wave recomputes the tile's
-    // scores, raises the reference to the running maximum, rescales the
-    // accumulators and redoes the numerators; O / l does not depend on the
-    // reference, which only keeps the numerators in range.
-    bool big = false;
+    // reference yet (first tile; PRE: always taken there).  Then the wave
+    // recomputes the tile's scores, raises the reference to the running
+    // maximum, rescales the accumulators and redoes the numerators; O / l
+    // does not depend on the reference, which only keeps the numerators in
+    // range.
+    bool big = PRE && t == 0;
+    if (!big) {
+      numerators(s, pf, lp);
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) big |= !(lp[qb] <= 0x1p30f);
+      for (int qb = 0; qb < QB; ++qb) big |= !(lp[qb] <= 0x1p30f);
+    }
     if (__any(big)) {
       scores(kt, t, s);
 #pragma unroll
@@ -312,12 +332,28 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const T *__restrict__ qkv
           for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[kb][qb][i]);
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mnew = fmaxf(mref[qb], mx);
-        const float alpha = __builtin_amdgcn_exp2f((mref[qb] - mnew) * sc);  // 0 when mref = -inf
-        mref[qb] = mnew;
-        lrow[qb] *= alpha;
+        if constexpr (PRE) {
+          // s = score - mref: the new reference is mref + max(mx, 0) (the
+          // first tile: mref + mx); delta <= 0 except on the first tile,
+          // where o and l are still zero
+          const float mnew = mref[qb] + (t == 0 ? mx : fmaxf(mx, 0.f));
+          const float delta = mref[qb] - mnew;
+          const float alpha = __builtin_amdgcn_exp2f(fminf(delta, 0.f));
+          mref[qb] = mnew;
+          negm[qb] = f32x4{-mnew, -mnew, -mnew, -mnew};
+          lrow[qb] *= alpha;
 #pragma unroll
-        for (int db = 0; db < DB; ++db) o[db][qb] *= alpha;
+          for (int db = 0; db < DB; ++db) o[db][qb] *= alpha;
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) s[kb][qb] += delta;
+        } else {
+          const float mnew = fmaxf(mref[qb], mx);
+          const float alpha = __builtin_amdgcn_exp2f((mref[qb] - mnew) * sc);  // 0 when mref = -inf
+          mref[qb] = mnew;
+          lrow[qb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) o[db][qb] *= alpha;
+        }
       }
       numerators(s, pf, lp);
     }
@@ -393,16 +429,19 @@ size_t attention_vt_bytes(bool f32, int B, int L, int Hkv, int head_dim) {
   return (size_t)B * Hkv * head_dim * att_lpad(L) * (f32 ? 4 : 2);
 }
 
-template <typename T, int HD, int QW>
+template <typename T, int HD, int QW, bool PRE>
 static void launch_attn_q(const T *q, const T *v, T *og, int B, int L, int H, int Hkv, float sc,
                           hipStream_t s) {
   const int group = H / Hkv;
   dim3 grid((L + 2 * QW - 1) / (2 * QW), Hkv, B);
+#define DIT_ATT(NWV)                                                                                      \
+  hipLaunchKernelGGL((attn_kernel<T, HD, NWV, QW, PRE>), grid, dim3(NWV * 64), 0, s, q, v, og, L, H, Hkv, sc)
   switch (group) {  // 2 waves per query head of the group
-    case 1: hipLaunchKernelGGL((attn_kernel<T, HD, 2, QW>), grid, dim3(128), 0, s, q, v, og, L, H, Hkv, sc); break;
-    case 2: hipLaunchKernelGGL((attn_kernel<T, HD, 4, QW>), grid, dim3(256), 0, s, q, v, og, L, H, Hkv, sc); break;
-    case 4: hipLaunchKernelGGL((attn_kernel<T, HD, 8, QW>), grid, dim3(512), 0, s, q, v, og, L, H, Hkv, sc); break;
+    case 1: DIT_ATT(2); break;
+    case 2: DIT_ATT(4); break;
+    case 4: DIT_ATT(8); break;
   }
+#undef DIT_ATT
 }
 
 // Work units of a launch, counted in rounds of one workgroup per CU and
@@ -412,7 +451,7 @@ static double attn_rounds(int B, int L, int Hkv, int qw) {
   return std::ceil(wgs / 256.0) * qw;
 }
 
-template <typename T, int HD>
+template <typename T, int HD, bool PRE>
 static hipError_t launch_attn_t(const void *qkvg, void *vt, void *og, int B, int L, int H, int Hkv,
                                 hipStream_t s) {
   const int group = H / Hkv;
@@ -421,24 +460,26 @@ static hipError_t launch_attn_t(const void *qkvg, void *vt, void *og, int B, int
                      (const T *)qkvg, (T *)vt, L, H, Hkv);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // log2(e) / sqrt(d): softmax in base 2 with the score scale in one FMA
-  const float sc = 1.4426950408889634f / sqrtf((float)HD);
+  // softmax in base 2 with the score scale in one FMA (PRE: in the queries)
+  const float sc = attn_score_scale(HD);
   const auto *q = (const T *)qkvg;
   const auto *v = (const T *)vt;
   if (sizeof(T) == 2 && attn_rounds(B, L, Hkv, 48) < attn_rounds(B, L, Hkv, 32))
-    launch_attn_q<T, HD, 48>(q, v, (T *)og, B, L, H, Hkv, sc, s);
+    launch_attn_q<T, HD, 48, PRE>(q, v, (T *)og, B, L, H, Hkv, sc, s);
   else
-    launch_attn_q<T, HD, 32>(q, v, (T *)og, B, L, H, Hkv, sc, s);
+    launch_attn_q<T, HD, 32, PRE>(q, v, (T *)og, B, L, H, Hkv, sc, s);
   return hipGetLastError();
 }
 
 hipError_t launch_attention(bool f32, int head_dim, const void *qkvg, void *vt, void *og, int B,
-                            int L, int H, int Hkv, hipStream_t s) {
+                            int L, int H, int Hkv, hipStream_t s, bool q_prescaled) {
   if (f32) {
-    if (head_dim == 64) return launch_attn_t<float, 64>(qkvg, vt, og, B, L, H, Hkv, s);
-    if (head_dim == 128) return launch_attn_t<float, 128>(qkvg, vt, og, B, L, H, Hkv, s);
-  } else {
-    if (head_dim == 128) return launch_attn_t<bf16, 128>(qkvg, vt, og, B, L, H, Hkv, s);
+    if (q_prescaled) return hipErrorInvalidValue;
+    if (head_dim == 64) return launch_attn_t<float, 64, false>(qkvg, vt, og, B, L, H, Hkv, s);
+    if (head_dim == 128) return launch_attn_t<float, 128, false>(qkvg, vt, og, B, L, H, Hkv, s);
+  } else if (head_dim == 128) {
+    if (q_prescaled) return launch_attn_t<bf16, 128, true>(qkvg, vt, og, B, L, H, Hkv, s);
+    return launch_attn_t<bf16, 128, false>(qkvg, vt, og, B, L, H, Hkv, s);
   }
   return hipErrorInvalidValue;
 }

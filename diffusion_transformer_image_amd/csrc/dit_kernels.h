@@ -3,6 +3,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cmath>
+
 namespace dit {
 
 hipError_t launch_modnorm(bool x_f32, bool h_f32, const void *x, void *h, const float *mod,
@@ -28,9 +30,12 @@ hipError_t launch_unpatchify_axpy(bool f32, const void *vtok, const float *z, fl
 // variant < 0 picks the default tile configuration for the shape; group_m
 // <= 0 the default tile-grouping width (row tiles per L2 group).  part (fp32,
 // part_bytes) lets the default configuration split the tail tiles along K.
+// Columns [0, scale_cols) of C are multiplied by col_scale before rounding
+// (default configuration only; a tuning variant with scale_cols > 0 is an
+// invalid value).
 hipError_t launch_gemm(bool f32, const void *a, const void *w, void *c, int M, int N, int K,
                        hipStream_t s, int variant = -1, int group_m = 0, float *part = nullptr,
-                       size_t part_bytes = 0);
+                       size_t part_bytes = 0, int scale_cols = 0, float col_scale = 1.f);
 hipError_t launch_gemm_swiglu(bool f32, const void *a, const void *w13, void *u, int M, int F,
                               int K, hipStream_t s, int variant = -1, int group_m = 0,
                               float *part = nullptr, size_t part_bytes = 0);
@@ -48,13 +53,18 @@ hipError_t launch_gemm_split(bool swiglu, const void *a, const void *w, void *c,
 constexpr int kGemmVariants = 15;
 // vt: scratch of attention_vt_bytes() for the transposed V of every KV head
 size_t attention_vt_bytes(bool f32, int B, int L, int Hkv, int head_dim);
+// The attention's score factor in base-2 units, log2(e) / sqrt(head_dim).
+inline float attn_score_scale(int head_dim) { return 1.4426950408889634f / sqrtf((float)head_dim); }
+// q_prescaled (bf16 only): the query heads of qkvg already carry the factor
+// attn_score_scale(head_dim), applied before their rounding to bf16.
 hipError_t launch_attention(bool f32, int head_dim, const void *qkvg, void *vt, void *og, int B,
-                            int L, int H, int Hkv, hipStream_t s);
+                            int L, int H, int Hkv, hipStream_t s, bool q_prescaled = false);
 
-// QKNorm and 3D axial RoPE in place on the Q and K heads of qkvg rows
+// QKNorm and 3D axial RoPE in place on the Q and K heads of qkvg rows; the
+// query heads are multiplied by q_scale before they are rounded (1: none)
 hipError_t launch_qk_prologue(bool f32, int head_dim, void *qkvg, const float *wq, const float *wk, int T,
                               int L, int H, int Hkv, int qk_norm, int rope, int grid_h, int grid_w,
-                              const int axes[3], float theta, float eps, hipStream_t s);
+                              const int axes[3], float theta, float eps, hipStream_t s, float q_scale = 1.f);
 
 // FP8 (e4m3) projections with row-wise scales
 hipError_t launch_quantize_fp8(bool f32, const void *x, void *q, float *scale, int M, int K, hipStream_t s);

@@ -59,6 +59,16 @@ struct SkPlan {
   float *part;
 };
 
+// Output columns [0, n) are multiplied by `scale` in fp32 before the one
+// rounding to the output type (the attention score scale folded into the
+// query columns of the QKVG product); n = 0: plain store.  Applies to the
+// store epilogue only.
+struct ColScale {
+  int n = 0;
+  float scale = 1.f;
+  __device__ __forceinline__ float apply(int col, float v) const { return col < n ? v * scale : v; }
+};
+
 // Linear tile id -> (row tile, column tile): walks gm row tiles at a time,
 // column-major inside a group, so tiles sharing operands run together.
 __device__ __forceinline__ void tile_coords(int pid, int m_tiles, int n_tiles, int gm, int &tm, int &tn) {
@@ -74,7 +84,8 @@ __device__ __forceinline__ void tile_coords(int pid, int m_tiles, int n_tiles, i
 // SwiGLU pairing of column blocks j and j + CB/2.
 template <typename T, int TM, int TN, int EPI>
 __device__ __forceinline__ void gemm_store_direct(const f32x4 (&acc)[TM / 16][TN / 16], T *__restrict__ C,
-                                                  int M, int N, int row0, int col0, int lane) {
+                                                  int M, int N, int row0, int col0, int lane,
+                                                  const ColScale &cs) {
   constexpr int RB = TM / 16, CB = TN / 16;
   const int g = lane >> 4, r16 = lane & 15;
 #pragma unroll
@@ -88,7 +99,7 @@ __device__ __forceinline__ void gemm_store_direct(const f32x4 (&acc)[TM / 16][TN
         const int row = row0 + i * 16 + 4 * g + e;
         float v;
         if constexpr (EPI == EPI_SWIGLU) v = silu(acc[i][j][e]) * acc[i][j + CB / 2][e];
-        else v = acc[i][j][e];
+        else v = cs.apply(col, acc[i][j][e]);
         if (row < M) C[(size_t)row * N + col] = from_f32<T>(v);
       }
     }
@@ -101,7 +112,7 @@ __device__ __forceinline__ void gemm_store_direct(const f32x4 (&acc)[TM / 16][TN
 template <typename T, int BM, int BN, int NW, int WM, int WN, int EPI, int SMEM>
 __device__ __forceinline__ void gemm_epilogue(const f32x4 (&acc)[BM / WM / 16][BN / WN / 16], char *smem,
                                               T *__restrict__ C, int M, int N, int m0, int n0,
-                                              int wave, int lane) {
+                                              int wave, int lane, const ColScale &cs) {
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int RB = TM / 16, CB = TN / 16;
   const int wm = wave / WN, wn = wave % WN;
@@ -109,9 +120,9 @@ __device__ __forceinline__ void gemm_epilogue(const f32x4 (&acc)[BM / WM / 16][B
   constexpr int TNO = (EPI == EPI_SWIGLU) ? TN / 2 : TN;  // output columns per wave
   const int col0 = (EPI == EPI_SWIGLU) ? n0 + wn * (TN / 2) : n0 + wn * TN;
   const int row0 = m0 + wm * TM;
-  auto out_val = [&](int i, int j, int e) -> float {
+  auto out_val = [&](int i, int j, int e, int col) -> float {  // col: output column in C
     if constexpr (EPI == EPI_SWIGLU) return silu(acc[i][j][e]) * acc[i][j + CB / 2][e];
-    else return acc[i][j][e];
+    else return cs.apply(col, acc[i][j][e]);
   };
   // (the XOR swizzle needs a power-of-two number of 16-byte chunks per row)
   constexpr int BNO = (EPI == EPI_SWIGLU) ? BN / 2 : BN;  // output columns of the tile
@@ -134,7 +145,7 @@ __device__ __forceinline__ void gemm_epilogue(const f32x4 (&acc)[BM / WM / 16][B
         for (int e = 0; e < 4; ++e) {
           const int row = wm * TM + i * 16 + 4 * g + e;
           const int off = row * PITCH + (((col >> 3) ^ (row & (CPRO - 1))) << 4) + (col & 7) * 2;
-          *reinterpret_cast<bf16 *>(smem + off) = (bf16)out_val(i, j, e);
+          *reinterpret_cast<bf16 *>(smem + off) = (bf16)out_val(i, j, e, n0 + col);
         }
       }
     }
@@ -158,7 +169,7 @@ __device__ __forceinline__ void gemm_epilogue(const f32x4 (&acc)[BM / WM / 16][B
       }
     }
   } else {
-    gemm_store_direct<T, TM, TN, EPI>(acc, C, M, N, row0, col0, lane);
+    gemm_store_direct<T, TM, TN, EPI>(acc, C, M, N, row0, col0, lane, cs);
   }
 }
 
@@ -183,7 +194,8 @@ template <typename T, int BM, int BN, int BKB, int STAGES, int WM, int WN, int E
 __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(const T *__restrict__ A,
                                                            const T *__restrict__ W,
                                                            T *__restrict__ C, int M, int N, int K,
-                                                           int m_tiles, int n_tiles, int gm, SkPlan sk) {
+                                                           int m_tiles, int n_tiles, int gm, SkPlan sk,
+                                                           ColScale cs) {
   constexpr int NW = WM * WN;
   constexpr int CPR = BKB / 16;             // 16-byte chunks per row per stage
   constexpr int RPB = 1024 / BKB;           // rows per 1 KiB DMA block
@@ -441,7 +453,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(const T *__restrict__
     return;
   }
   gemm_epilogue<T, BM, BN, NW, WM, WN, EPI, STAGES * STAGE_BYTES>(acc, smem, C, M, N, m0, n0, wave,
-                                                                 lane);
+                                                                 lane, cs);
 }
 
 // Sums the K-segment partials of each split tile in segment order and
@@ -451,7 +463,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(const T *__restrict__
 template <typename T, int BM, int BN, int WM, int WN, int EPI, int FRB>
 __global__ __launch_bounds__(64) void gemm_sk_fixup(const float *__restrict__ part, T *__restrict__ C,
                                                     int M, int N, int m_tiles, int n_tiles, int gm,
-                                                    int dp_tiles, int segs) {
+                                                    int dp_tiles, int segs, ColScale cs) {
   constexpr int NW = WM * WN, TM = BM / WM, TN = BN / WN, RB = TM / 16, CB = TN / 16;
   static_assert(RB % FRB == 0, "row-block split");
   constexpr int NP = RB / FRB;  // workgroups per wave sub-tile
@@ -475,7 +487,7 @@ __global__ __launch_bounds__(64) void gemm_sk_fixup(const float *__restrict__ pa
   tile_coords(dp_tiles + t, m_tiles, n_tiles, gm, tm, tn);
   const int row0 = tm * BM + wm * TM + piece * FRB * 16;
   const int col0 = (EPI == EPI_SWIGLU) ? tn * (BN / 2) + wn * (TN / 2) : tn * BN + wn * TN;
-  gemm_store_direct<T, FRB * 16, TN, EPI>(acc, C, M, N, row0, col0, lane);
+  gemm_store_direct<T, FRB * 16, TN, EPI>(acc, C, M, N, row0, col0, lane, cs);
 }
 
 // Calls f(integral_constant<I>) for I = B..E-1 in order while f returns true.
@@ -672,7 +684,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_ring_kernel(const bf16 *__re
   }
   wait_vmcnt<0>();
 
-  gemm_epilogue<bf16, BM, BN, NW, WM, WN, EPI, R * STAGE>(acc, smem, C, M, N, m0, n0, wave, lane);
+  gemm_epilogue<bf16, BM, BN, NW, WM, WN, EPI, R * STAGE>(acc, smem, C, M, N, m0, n0, wave, lane, ColScale{});
 }
 
 // ---------------------------------------------------------------------------
@@ -864,7 +876,7 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(const uint8_t *__restrict
 #pragma unroll
       for (int j = 0; j < CB; ++j) acc[i][j][e] *= rs * cs[j];
     }
-  gemm_epilogue<bf16, BM, BN, NW, WM, WN, EPI, 2 * STAGE>(acc, smem, C, M, N, m0, n0, wave, lane);
+  gemm_epilogue<bf16, BM, BN, NW, WM, WN, EPI, 2 * STAGE>(acc, smem, C, M, N, m0, n0, wave, lane, ColScale{});
 }
 
 hipError_t launch_gemm_fp8(bool swiglu, const void *aq, const float *sa, const void *wq, const float *sw, void *c,
@@ -881,19 +893,21 @@ hipError_t launch_gemm_fp8(bool swiglu, const void *aq, const float *sa, const v
 
 template <typename T, int BM, int BN, int BKB, int STAGES, int WM, int WN, int EPI, bool PIPE = false>
 static hipError_t launch_gemm_t(const void *a, const void *w, void *c, int M, int N, int K,
-                                hipStream_t s, int gm, int sk_tiles = 0, int segs = 1, float *part = nullptr) {
+                                hipStream_t s, int gm, int sk_tiles = 0, int segs = 1, float *part = nullptr,
+                                ColScale cs = {}) {
   const int mt = (M + BM - 1) / BM;
   const int nt = (EPI == EPI_SWIGLU) ? (N + BN / 2 - 1) / (BN / 2) : (N + BN - 1) / BN;
   if (segs <= 1 || !part) sk_tiles = 0;
   const SkPlan plan{mt * nt - sk_tiles, sk_tiles ? segs : 1, part};
   hipLaunchKernelGGL((gemm_kernel<T, BM, BN, BKB, STAGES, WM, WN, EPI, PIPE>),
                      dim3(plan.dp_tiles + sk_tiles * plan.segs), dim3(WM * WN * 64), 0, s, (const T *)a,
-                     (const T *)w, (T *)c, M, N, K, mt, nt, gm, plan);
+                     (const T *)w, (T *)c, M, N, K, mt, nt, gm, plan, cs);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || sk_tiles == 0) return e;
   constexpr int FRB = (BM / WM / 16) % 2 == 0 ? 2 : 1;  // row blocks per fixup wave
   hipLaunchKernelGGL((gemm_sk_fixup<T, BM, BN, WM, WN, EPI, FRB>), dim3(sk_tiles * WM * WN * (BM / WM / 16 / FRB)),
-                     dim3(64), 0, s, (const float *)part, (T *)c, M, N, mt, nt, gm, plan.dp_tiles, plan.segs);
+                     dim3(64), 0, s, (const float *)part, (T *)c, M, N, mt, nt, gm, plan.dp_tiles, plan.segs,
+                     cs);
   return hipGetLastError();
 }
 
@@ -946,16 +960,16 @@ GemmChoice gemm_choose(int M, int N, int K, bool swiglu) {
 template <int EPI>
 static hipError_t gemm_dispatch(bool f32, int variant, int gm, const void *a, const void *w,
                                 void *c, int M, int N, int K, hipStream_t s, float *part,
-                                size_t part_bytes) {
+                                size_t part_bytes, ColScale cs = {}) {
   // L2 grouping width: 4 row tiles for the SwiGLU tile (it reads W1 and W3
   // rows: measured ~3 % faster than 8 on W13 at 1024 px), else 8
   if (gm <= 0) gm = (EPI == EPI_SWIGLU) ? 4 : 8;
-  if (f32) return launch_gemm_t<float, 256, 256, 128, 2, 2, 4, EPI>(a, w, c, M, N, K, s, gm);
+  if (f32) return launch_gemm_t<float, 256, 256, 128, 2, 2, 4, EPI>(a, w, c, M, N, K, s, gm, 0, 1, nullptr, cs);
   if (variant < 0) {
     const GemmChoice ch = gemm_choose(M, N, K, EPI == EPI_SWIGLU);
     if (ch.sk_tiles > 0 && part && part_bytes >= ch.part_bytes)
       return launch_gemm_t<bf16, 256, 256, 128, 2, 2, 4, EPI, true>(a, w, c, M, N, K, s, gm, ch.sk_tiles,
-                                                                    ch.segs, part);
+                                                                    ch.segs, part, cs);
     // without the partial buffer: whole tiles, the fuller of 192 / 256 rows
     const int ncols = (EPI == EPI_SWIGLU) ? 128 : 256;
     auto fill = [&](int bm) {
@@ -963,7 +977,11 @@ static hipError_t gemm_dispatch(bool f32, int variant, int gm, const void *a, co
       return tiles / (std::ceil(tiles / 256.0) * 256.0);
     };
     variant = ch.sk_tiles > 0 ? ((fill(192) > fill(256) + 0.02) ? 9 : 8) : ch.variant;
+    if (variant == 8) return launch_gemm_t<bf16, 256, 256, 128, 2, 2, 4, EPI, true>(a, w, c, M, N, K, s, gm, 0, 1,
+                                                                                   nullptr, cs);
+    return launch_gemm_t<bf16, 192, 256, 128, 2, 2, 4, EPI, true>(a, w, c, M, N, K, s, gm, 0, 1, nullptr, cs);
   }
+  if (cs.n > 0) return hipErrorInvalidValue;  // the tuning variants store plainly
   switch (variant) {
     case 0: return launch_gemm_t<bf16, 256, 256, 64, 4, 2, 2, EPI>(a, w, c, M, N, K, s, gm);
     case 1: return launch_gemm_t<bf16, 256, 256, 64, 4, 2, 4, EPI>(a, w, c, M, N, K, s, gm);
@@ -985,8 +1003,10 @@ static hipError_t gemm_dispatch(bool f32, int variant, int gm, const void *a, co
 }
 
 hipError_t launch_gemm(bool f32, const void *a, const void *w, void *c, int M, int N, int K,
-                       hipStream_t s, int variant, int group_m, float *part, size_t part_bytes) {
-  return gemm_dispatch<EPI_STORE>(f32, variant, group_m, a, w, c, M, N, K, s, part, part_bytes);
+                       hipStream_t s, int variant, int group_m, float *part, size_t part_bytes, int scale_cols,
+                       float col_scale) {
+  return gemm_dispatch<EPI_STORE>(f32, variant, group_m, a, w, c, M, N, K, s, part, part_bytes,
+                                  ColScale{scale_cols, col_scale});
 }
 
 hipError_t launch_gemm_swiglu(bool f32, const void *a, const void *w13, void *u, int M, int F,

@@ -82,7 +82,8 @@ template <typename T, int HD>
 __global__ __launch_bounds__(256) void qk_prologue_kernel(T *__restrict__ qkvg, const float *__restrict__ wq,
                                                           const float *__restrict__ wk, int T_rows, int L,
                                                           int H, int Hkv, int qk_norm, int rope, int grid_h,
-                                                          int grid_w, int ax0, int ax1, float theta, float eps) {
+                                                          int grid_w, int ax0, int ax1, float theta, float eps,
+                                                          float q_scale) {
   constexpr int LPH = HD / 8;    // lanes per head
   constexpr int HPW = 64 / LPH;  // heads per wave step
   constexpr int U = 4;           // wave steps in flight together
@@ -148,6 +149,10 @@ __global__ __launch_bounds__(256) void qk_prologue_kernel(T *__restrict__ qkvg, 
         for (int i = 0; i < 8; ++i) v[i] *= inv * (1.f + (isq ? gq[i] : gk[i]));
       }
       rope_apply<4>(v, c, s);
+      if (h < H && q_scale != 1.f) {  // the attention's score factor, before the one rounding
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] *= q_scale;
+      }
       if (h < nh) Oct<T>::store(base + h * HD, v);
     }
   }
@@ -155,11 +160,11 @@ __global__ __launch_bounds__(256) void qk_prologue_kernel(T *__restrict__ qkvg, 
 
 hipError_t launch_qk_prologue(bool f32, int head_dim, void *qkvg, const float *wq, const float *wk, int T,
                               int L, int H, int Hkv, int qk_norm, int rope, int grid_h, int grid_w,
-                              const int axes[3], float theta, float eps, hipStream_t s) {
+                              const int axes[3], float theta, float eps, hipStream_t s, float q_scale) {
   const dim3 grid((T + 3) / 4), block(256);
 #define DIT_QP(TT, HDV)                                                                                \
   hipLaunchKernelGGL((qk_prologue_kernel<TT, HDV>), grid, block, 0, s, (TT *)qkvg, wq, wk, T, L, H, Hkv, \
-                     qk_norm, rope, grid_h, grid_w, axes[0], axes[1], theta, eps)
+                     qk_norm, rope, grid_h, grid_w, axes[0], axes[1], theta, eps, q_scale)
   if (head_dim == 128) {
     if (f32) DIT_QP(float, 128); else DIT_QP(bf16, 128);
   } else if (head_dim == 64) {
