@@ -27,7 +27,7 @@ EXPORTS = (
     "dit_gated_residual", "dit_status_str", "dit_last_hip_error", "dit_timer_start",
     "dit_timer_stop", "dit_gemm_splitk", "dit_gemm_plan", "dit_block_fwd_ex", "dit_stack_fwd_ex",
     "dit_qk_prologue", "dit_model_workspace_size", "dit_model_velocity", "dit_sample", "dit_quantize_fp8",
-    "dit_gemm_fp8", "dit_quantize_fp8_tensor",
+    "dit_gemm_fp8", "dit_quantize_fp8_tensor", "dit_attention_ex",
 )
 
 
@@ -112,6 +112,7 @@ def lib() -> ctypes.CDLL:
             "dit_gemm_plan": (i32, [i32, i32, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32),
                                     ctypes.POINTER(i32), ctypes.POINTER(sz)]),
             "dit_attention": (i32, [cfgp, vp, vp, vp, sz, vp]),
+            "dit_attention_ex": (i32, [cfgp, vp, vp, vp, sz, i32, vp]),
             "dit_gated_residual": (i32, [cfgp, vp, i32, vp, vp, vp, i32, vp, i32, vp]),
             "dit_status_str": (ctypes.c_char_p, [i32]),
             "dit_last_hip_error": (ctypes.c_int, []),
@@ -341,6 +342,12 @@ def attention(cfg: Config, qkvg, og, ws, stream=None) -> None:
     nbytes = ws.numel() * ws.element_size() if hasattr(ws, "numel") else 0
     _check(lib().dit_attention(ctypes.byref(cfg), _ptr(qkvg), _ptr(og), _ptr(ws), nbytes, _stream(stream)),
            "dit_attention")
+
+
+def attention_ex(cfg: Config, qkvg, og, ws, q_prescaled: bool, stream=None) -> None:
+    nbytes = ws.numel() * ws.element_size() if hasattr(ws, "numel") else 0
+    _check(lib().dit_attention_ex(ctypes.byref(cfg), _ptr(qkvg), _ptr(og), _ptr(ws), nbytes, int(q_prescaled),
+                                  _stream(stream)), "dit_attention_ex")
 
 
 def gated_residual(cfg: Config, x, y, mod, bias, which: int, out, stream=None) -> None:

@@ -696,8 +696,15 @@ dit_status dit_gemm_splitk(dit_dtype dtype, int32_t swiglu, int32_t m, int32_t n
 
 dit_status dit_attention(const dit_config *cfg, const void *qkvg, void *og, void *ws, size_t ws_bytes,
                          void *stream) {
+  return dit_attention_ex(cfg, qkvg, og, ws, ws_bytes, 0, stream);
+}
+
+dit_status dit_attention_ex(const dit_config *cfg, const void *qkvg, void *og, void *ws, size_t ws_bytes,
+                            int32_t q_prescaled, void *stream) {
   dit_status st = check_cfg(cfg);
   if (st != DIT_OK) return st;
+  if (q_prescaled != 0 && q_prescaled != 1) return DIT_ERR_SHAPE;
+  if (q_prescaled && cfg->dtype == DIT_F32) return DIT_ERR_UNSUPPORTED;
   if (!qkvg || !og) return DIT_ERR_NULL;
   if (!ws) return DIT_ERR_WORKSPACE;
   if (!aligned(qkvg) || !aligned(og) || !aligned(ws)) return DIT_ERR_ALIGN;
@@ -711,7 +718,7 @@ dit_status dit_attention(const dit_config *cfg, const void *qkvg, void *og, void
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = timed(DIT_K_ATTN, s, [&] {
     return launch_attention(cfg->dtype == DIT_F32, cfg->head_dim, qkvg, ws, og, cfg->batch,
-                            cfg->seq_len, cfg->n_heads, cfg->n_kv_heads, s);
+                            cfg->seq_len, cfg->n_heads, cfg->n_kv_heads, s, q_prescaled == 1);
   });
   return e == hipSuccess ? DIT_OK : hip_fail(e);
 }

@@ -369,6 +369,18 @@ dit_status dit_gemm_fp8(int32_t swiglu, int32_t m, int32_t n, int32_t k, const v
 dit_status dit_attention(const dit_config *cfg /* host */, const void *qkvg, void *og, void *ws,
                          size_t ws_bytes, void *stream);
 
+/* dit_attention with the choice of query scaling.  q_prescaled = 1 (bf16
+ * only): the query columns of qkvg already carry the factor
+ * log2(e)/sqrt(d), applied in fp32 before their rounding to bf16 (this is
+ * what the block path's projection epilogue produces), so the scores are in
+ * base-2 units and the kernel applies no per-score scale:
+ *   og = softmax_keys(2^(Q_h K_j^T) / sum) V_j * sigmoid(G_h),
+ * the same attention as dit_attention's up to the rounding of the scaled Q.
+ * q_prescaled = 0 is dit_attention.  Other values: DIT_ERR_SHAPE;
+ * q_prescaled = 1 with cfg->dtype = DIT_F32: DIT_ERR_UNSUPPORTED. */
+dit_status dit_attention_ex(const dit_config *cfg /* host */, const void *qkvg, void *og, void *ws,
+                            size_t ws_bytes, int32_t q_prescaled, void *stream);
+
 /* out = x + gate * y over rows of [T, D], gate = mod[b][3*which+2] +
  * bias[3*which+2] (page "Krea 2 技术报告", 架构 › 残差设计).
  * x_dtype and out_dtype may be DIT_F32 or cfg->dtype; y has cfg->dtype. */

@@ -138,6 +138,10 @@ def test_step_argument_checks():
     assert S(L.dit_attention(ctypes.byref(c), P, P + 64, P + 2 * G, 1 << 30, None)) == "DIT_ERR_SHAPE"
     assert S(L.dit_attention(ctypes.byref(c), P, P + G, P + 2 * G, 16, None)) == "DIT_ERR_WORKSPACE"
     assert S(L.dit_attention(ctypes.byref(c), P, P + G, 0, 1 << 30, None)) == "DIT_ERR_WORKSPACE"
+    assert S(L.dit_attention_ex(ctypes.byref(c), P, P + G, P + 2 * G, 1 << 30, 2, None)) == "DIT_ERR_SHAPE"
+    assert S(L.dit_attention_ex(ctypes.byref(c), P, P + G, P + 2 * G, 1 << 30, 1, None)) == "DIT_ERR_UNSUPPORTED"
+    cq = cfg(dtype="bf16", hidden=512, n_heads=4, n_kv_heads=1, head_dim=128)
+    assert S(L.dit_attention_ex(ctypes.byref(cq), P, 0, P + 2 * G, 1 << 30, 1, None)) == "DIT_ERR_NULL"
     assert S(L.dit_modnorm(ctypes.byref(c), P, 0, P + G, P + 2 * G, P + 3 * G, 0, 2, None)) == "DIT_ERR_SHAPE"
     assert S(L.dit_modnorm(ctypes.byref(c), P, 9, P + G, P + 2 * G, P + 3 * G, 0, 0, None)) == "DIT_ERR_DTYPE"
     cb = cfg(dtype="f32")

@@ -120,20 +120,41 @@ def test_attention_one_key_returns_gated_value(dev):
     assert np.max(np.abs(y - expect)) <= 2 ** -8 * np.max(np.abs(expect))
 
 
-def _attention_vs_oracle(dev, cfg, z, rows, f32_tol=1e-5):
+def prescale_queries(cfg, z):
+    """The query columns multiplied by log2(e)/sqrt(d) in fp32 and rounded
+    once to bf16 (what the block path's projection epilogue stores), and the
+    queries the oracle must then use: the base-2 scores 2^(q' . k) equal the
+    softmax weights of q = q' ln(2) sqrt(d) in natural units with 1/sqrt(d)."""
+    d, nq = cfg.head_dim, cfg.n_heads * cfg.head_dim
+    zs = z.astype(np.float32).copy()
+    sc = np.float32(1.4426950408889634) / np.sqrt(np.float32(d))
+    zs[:, :nq] = datagen.bf16_round(zs[:, :nq] * sc)
+    q_eff = zs[:, :nq].astype(np.float64) * (np.log(2.0) * np.sqrt(d))
+    return zs, q_eff
+
+
+def _attention_vs_oracle(dev, cfg, z, rows, f32_tol=1e-5, prescaled=False):
     torch, device, dit = dev
     B, L = cfg.batch, cfg.seq_len
+    H, Hk, d = cfg.n_heads, cfg.n_kv_heads, cfg.head_dim
+    q_eff = None
+    if prescaled:
+        z, q_eff = prescale_queries(cfg, z)
+        q_eff = q_eff.reshape(B, L, H * d)
     Z = device.to_device(z, cfg.dtype)
     OG = torch.empty((cfg.tokens, cfg.n_heads * cfg.head_dim), dtype=Z.dtype, device="cuda")
     c = dit.config_of(cfg)
-    dit.attention(c, Z, OG, torch.empty(dit.workspace_size(c), dtype=torch.uint8, device="cuda"))
+    ws = torch.empty(dit.workspace_size(c), dtype=torch.uint8, device="cuda")
+    if prescaled:
+        dit.attention_ex(c, Z, OG, ws, True)
+    else:
+        dit.attention(c, Z, OG, ws)
     torch.cuda.synchronize()
     y = device.to_numpy(OG).reshape(B, L, -1)
-    H, Hk, d = cfg.n_heads, cfg.n_kv_heads, cfg.head_dim
     zz = z.reshape(B, L, -1)
     for b in range(B):
         zb = zz[b].astype(np.float64)
-        q = zb[rows, : H * d].reshape(len(rows), H, d)
+        q = (q_eff[b] if prescaled else zb[:, : H * d])[rows].reshape(len(rows), H, d)
         k = zb[:, H * d:(H + Hk) * d].reshape(L, Hk, d)
         v = zb[:, (H + Hk) * d:(H + 2 * Hk) * d].reshape(L, Hk, d)
         g = zb[rows, (H + 2 * Hk) * d:].reshape(len(rows), H, d)
@@ -171,6 +192,35 @@ def test_attention_rising_reference(dev, name, B, L):
     # scores of a few hundred: fp32 rounding of the dot products alone moves
     # them by ~1e-5, so the fp32 bar is the general 1e-4 one here
     _attention_vs_oracle(dev, cfg, z, rows, f32_tol=1e-4)
+    if cfg.dtype == "bf16":  # the block path's kernel: queries pre-scaled, reference from 0
+        _attention_vs_oracle(dev, cfg, z, rows, prescaled=True)
+
+
+@pytest.mark.parametrize("B,L", [(1, 1), (2, 80), (1, 100), (1, 130), (2, 512), (1, 4544), (2, 4608)])
+def test_attention_prescaled(dev, B, L):
+    """Queries carrying log2(e)/sqrt(d) (the block path's attention): ragged
+    tails in either 32-key half, one key, 32 and 48 queries per wave."""
+    print(f"attention prescaled B={B} L={L}", flush=True)
+    cfg = small_cfg("c1", batch=B, n_image=L, n_text=0)
+    rows = np.arange(L) if L <= 600 else np.unique(np.r_[0, 1, 63, 64, 65, L // 2, L - 65, L - 64, L - 2, L - 1,
+                                                            np.random.default_rng(L).integers(0, L, 24)])
+    _attention_vs_oracle(dev, cfg, datagen.qkvg_activations(cfg), rows, prescaled=True)
+
+
+def test_attention_prescaled_low_scores(dev):
+    """Every score far below zero (about -200 in base-2 units): the
+    reference starts at 0, so the first tile must lower it to the row
+    maximum or every numerator underflows."""
+    cfg = small_cfg("c1", batch=1, n_image=200, n_text=0)
+    H, Hk, d = cfg.n_heads, cfg.n_kv_heads, cfg.head_dim
+    z = datagen.qkvg_activations(cfg).astype(np.float64)
+    u = np.ones(d) / np.sqrt(d)
+    for hh in range(H):
+        z[:, hh * d:(hh + 1) * d] += 2.0 * u
+    for j in range(Hk):
+        z[:, (H + j) * d:(H + j + 1) * d] -= 100.0 * np.sqrt(d) * u / 2.0
+    z = datagen.bf16_round(z.astype(np.float32))
+    _attention_vs_oracle(dev, cfg, z, np.arange(cfg.seq_len), prescaled=True)
 
 
 # ------------------------------------------------------------------ modnorm / residual
