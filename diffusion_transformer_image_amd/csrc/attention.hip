@@ -103,15 +103,20 @@ __device__ __forceinline__ void att_wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// NW = waves per workgroup (2 per query head of the group); QW = query
-// tokens per wave (32 or 48), so a workgroup covers 2 * QW query tokens.
+// NW = waves per workgroup, WPH per query head of the group (NW = group *
+// WPH); QW = query tokens per wave (32 or 48), so a workgroup covers
+// WPH * QW query tokens.  WPH = 2: one workgroup per CU with a 3-deep
+// K / V^T ring; WPH = 1 (bf16, 4 query heads per key head): 4-wave
+// workgroups with a 2-deep ring, two per CU (64 KiB of LDS each), which
+// drift out of phase so one's softmax runs beside the other's MFMAs
+// (1024 px: 626-628 -> 601-605 us, same box, for twice the K / V reads).
 // PRE: the query heads in qkvg already carry the factor sc = log2(e)/sqrt(d)
 // (applied before their one rounding, by the projection's epilogue or the
 // prologue pass), so scores come out of the MFMAs in base-2 units; each
 // score chain then starts from -reference (the first MFMA reads it as its
 // accumulator input) and a numerator is one exp2, with no per-score FMA.
-template <typename T, int HD, int NW, int QW, bool PRE>
-__global__ __launch_bounds__(NW * 64) void attn_kernel(const T *__restrict__ qkvg, const T *__restrict__ vt,
+template <typename T, int HD, int NW, int QW, bool PRE, int WPH>
+__global__ __launch_bounds__(NW * 64, WPH == 1 ? 2 : 1) void attn_kernel(const T *__restrict__ qkvg, const T *__restrict__ vt,
                                                        T *__restrict__ og, int L, int H, int Hkv, float sc) {
   static_assert(!PRE || sizeof(T) == 2, "pre-scaled queries: bf16 only");
   constexpr int ES = sizeof(T);
@@ -126,7 +131,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const T *__restrict__ qkv
   constexpr int DB = HD / 16;           // 16-row blocks of d
   constexpr int QB = QW / 16;           // 16-column blocks of queries per wave
   constexpr int KB = ATT_BK / 16;       // 16-key blocks per tile
-  constexpr int NSTAGE = (3 * STAGE <= 160 * 1024) ? 3 : 2;  // K / V^T ring depth
+  constexpr int NSTAGE = (WPH == 2 && 3 * STAGE <= 160 * 1024) ? 3 : 2;  // K / V^T ring depth
   constexpr int PD = NSTAGE - 1;        // tiles in flight ahead of the one in use
   constexpr int KBLK = KTILE / 1024, VBLK = VTILE / 1024;
   constexpr int DMA_PER_TILE = (KBLK + NW - 1) / NW + (VBLK + NW - 1) / NW;  // per wave
@@ -140,8 +145,8 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(const T *__restrict__ qkv
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
   const int group = H / Hkv;
   const int b = blockIdx.z, j = blockIdx.y;
-  const int h = j * group + (wave >> 1);
-  const int q0 = blockIdx.x * (2 * QW) + (wave & 1) * QW;
+  const int h = j * group + wave / WPH;
+  const int q0 = blockIdx.x * (WPH * QW) + (wave % WPH) * QW;
   const int g = lane >> 4, r16 = lane & 15;
   const int Lp = att_lpad(L);
 
@@ -433,19 +438,24 @@ template <typename T, int HD, int QW, bool PRE>
 static void launch_attn_q(const T *q, const T *v, T *og, int B, int L, int H, int Hkv, float sc,
                           hipStream_t s) {
   const int group = H / Hkv;
-  dim3 grid((L + 2 * QW - 1) / (2 * QW), Hkv, B);
-#define DIT_ATT(NWV)                                                                                      \
-  hipLaunchKernelGGL((attn_kernel<T, HD, NWV, QW, PRE>), grid, dim3(NWV * 64), 0, s, q, v, og, L, H, Hkv, sc)
-  switch (group) {  // 2 waves per query head of the group
-    case 1: DIT_ATT(2); break;
-    case 2: DIT_ATT(4); break;
-    case 4: DIT_ATT(8); break;
+#define DIT_ATT(NWV, WPHV)                                                                             \
+  hipLaunchKernelGGL((attn_kernel<T, HD, NWV, QW, PRE, WPHV>), dim3((L + WPHV * QW - 1) / (WPHV * QW), Hkv, B), \
+                     dim3(NWV * 64), 0, s, q, v, og, L, H, Hkv, sc)
+  switch (group) {
+    case 1: DIT_ATT(2, 2); break;
+    case 2: DIT_ATT(4, 2); break;
+    case 4:
+      if constexpr (sizeof(T) == 2) DIT_ATT(4, 1);  // one wave per head, two workgroups per CU
+      else DIT_ATT(8, 2);
+      break;
   }
 #undef DIT_ATT
 }
 
 // Work units of a launch, counted in rounds of one workgroup per CU and
-// weighted by the queries per wave: picks 32 or 48 queries per wave.
+// weighted by the queries per wave: picks 32 or 48 queries per wave.  (With
+// one wave per head the launch has twice the workgroups and two fit a CU:
+// the same count.)
 static double attn_rounds(int B, int L, int Hkv, int qw) {
   const double wgs = (double)B * Hkv * ((L + 2 * qw - 1) / (2 * qw));
   return std::ceil(wgs / 256.0) * qw;
