@@ -45,9 +45,14 @@ def flops_per_token(cfg) -> dict:
 
 
 def bytes_per_token(cfg) -> dict:
-    """Algorithmic HBM bytes of the elementwise kernels (bf16 path)."""
+    """Algorithmic HBM bytes per token of one launch of the block's
+    elementwise kernels (bf16 path), against which a kind's average launch
+    time is set: the first norm reads x and writes h1 (1 launch); the
+    residual kind is the first residual fused with the second norm (reads x
+    and A, writes x1 in fp32 and h2) and the second residual (reads x1 and
+    M, writes x2): 10 d and 8 d bytes, 9 d per launch on average."""
     d = cfg.hidden
-    return {"modnorm": 2 * (2 * d), "resid": 2 * (3 * d)}  # per launch kind: 2 launches each
+    return {"modnorm": 2 * d + 2 * d, "resid": (10 * d + 8 * d) // 2}
 
 
 def src_hash(name: str) -> str:
