@@ -68,24 +68,38 @@ template <typename T, int HD>
 __global__ __launch_bounds__(256) void vtrans_kernel(const T *__restrict__ qkvg, T *__restrict__ vt,
                                                      int L, int H, int Hkv) {
   constexpr int EPC = 16 / sizeof(T);  // elements per 16-byte chunk
-  __shared__ T tile[ATT_BK][HD + EPC];
+  __shared__ __attribute__((aligned(16))) T tile[ATT_BK][HD + EPC];
   const int l0 = blockIdx.x * ATT_BK, j = blockIdx.y, b = blockIdx.z;
   const int Lp = att_lpad(L);
   const size_t ldq = (size_t)(2 * H + 2 * Hkv) * HD;
   const T *src = qkvg + (size_t)b * L * ldq + (size_t)(H + Hkv + j) * HD;
-  for (int idx = threadIdx.x; idx < ATT_BK * (HD / EPC); idx += blockDim.x) {
-    const int r = idx / (HD / EPC), c = (idx % (HD / EPC)) * EPC;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (l0 + r < L) v = *reinterpret_cast<const u32x4 *>(src + (size_t)(l0 + r) * ldq + c);
-    T pv[EPC];
-    __builtin_memcpy(pv, &v, 16);
+  // all of this thread's row chunks are requested before any is stored;
+  // each lands in the padded tile as one 16-byte write (the row pitch,
+  // (HD + EPC) elements, is a multiple of 16 bytes)
+  constexpr int NLD = ATT_BK * (HD / EPC) / 256;
+  static_assert(NLD * 256 == ATT_BK * (HD / EPC), "whole chunks per thread");
+  u32x4 v[NLD];
 #pragma unroll
-    for (int e = 0; e < EPC; ++e) tile[r][c + e] = pv[e];
+  for (int k = 0; k < NLD; ++k) {
+    const int idx = threadIdx.x + 256 * k;
+    const int r = idx / (HD / EPC), c = (idx % (HD / EPC)) * EPC;
+    v[k] = u32x4{0u, 0u, 0u, 0u};
+    if (l0 + r < L) v[k] = *reinterpret_cast<const u32x4 *>(src + (size_t)(l0 + r) * ldq + c);
+  }
+#pragma unroll
+  for (int k = 0; k < NLD; ++k) {
+    const int idx = threadIdx.x + 256 * k;
+    const int r = idx / (HD / EPC), c = (idx % (HD / EPC)) * EPC;
+    *reinterpret_cast<u32x4 *>(&tile[r][c]) = v[k];
   }
   __syncthreads();
   T *dst = vt + ((size_t)b * Hkv + j) * HD * Lp + l0;
-  for (int idx = threadIdx.x; idx < HD * (ATT_BK / EPC); idx += blockDim.x) {
-    const int dd = idx % HD, pc = idx / HD;  // physical 16-byte chunk of the row
+  static_assert(HD * (ATT_BK / EPC) % 256 == 0, "whole output chunks per thread");
+#pragma unroll
+  for (int idx = threadIdx.x; idx < HD * (ATT_BK / EPC); idx += 256) {
+    // consecutive lanes store consecutive chunks of one V^T row (whole
+    // 128-byte row pieces per 8 lanes for bf16)
+    const int dd = idx / (ATT_BK / EPC), pc = idx % (ATT_BK / EPC);  // physical 16-byte chunk of the row
     const int lc = pc ^ vt_swizzle<T>(dd);   // logical chunk stored there
     T w[EPC];
 #pragma unroll
