@@ -174,18 +174,29 @@ bool prologue_on(const dit_prologue *p) { return p && (p->qk_norm || p->rope); }
     if (e_ != hipSuccess) return hip_fail(e_); \
   } while (0)
 
+// The residual and norm passes can be one kernel (three staged fp32
+// vectors per sample in LDS within the default 64 KiB window).
+bool fused_resid_norm(int D) { return 3 * (size_t)D * sizeof(float) <= 64 * 1024; }
+
 // One block, on the carved workspace.  x_in has dtype xin_f32 ? f32 : dtype;
 // x_out has xout_f32 ? f32 : dtype; x1 (fp32) is stored in x1buf.
+// h1_ready: ws.h already holds this block's first norm of x_in (the previous
+// block of a stack computed it with its second residual).  defer_resid2:
+// the block stops after the W2 product (M in ws.br, x1 in x1buf) and the
+// caller applies the second residual.
 dit_status run_block(const dit_config *c, const dit_prologue *pro, const dit_block_weights *w,
                      const void *x_in, bool xin_f32, void *x_out, bool xout_f32, const float *mod,
-                     const BlockWs &ws, void *x1buf, hipStream_t s) {
+                     const BlockWs &ws, void *x1buf, hipStream_t s, bool h1_ready = false,
+                     bool defer_resid2 = false) {
   const bool x1_f32 = true;
   const Dims d = dims(c);
   const bool f32 = c->dtype == DIT_F32;
   const int T = (int)d.T, D = (int)d.D, L = c->seq_len;
-  DIT_TRY(timed(DIT_K_MODNORM, s, [&] {
-    return launch_modnorm(xin_f32, f32, x_in, ws.h, mod, w->mod_bias, w->norm1_w, T, L, D, c->eps, 0, s);
-  }));
+  if (!h1_ready) {
+    DIT_TRY(timed(DIT_K_MODNORM, s, [&] {
+      return launch_modnorm(xin_f32, f32, x_in, ws.h, mod, w->mod_bias, w->norm1_w, T, L, D, c->eps, 0, s);
+    }));
+  }
   // bf16: the attention's score factor rides on the query heads, applied in
   // fp32 before their one rounding (by the projection's epilogue, or by the
   // prologue pass, which would normalise it away), so the attention kernel
@@ -211,11 +222,11 @@ dit_status run_block(const dit_config *c, const dit_prologue *pro, const dit_blo
   DIT_TRY(timed(DIT_K_GEMM_O, s, [&] {
     return launch_gemm(f32, ws.og, w->w_o, ws.br, T, D, (int)d.hd, s, -1, 0, ws.part, ws.part_bytes);
   }));
-  if (3 * (size_t)D * sizeof(float) <= 64 * 1024) {
+  if (fused_resid_norm(D)) {
     // x1 = x + gate1 * A (fp32) fused with h2 = modnorm(x1; norm 2)
     DIT_TRY(timed(DIT_K_RESID, s, [&] {
-      return launch_resid_modnorm(xin_f32, f32, x_in, ws.br, (float *)x1buf, ws.h, mod, w->mod_bias,
-                                  w->norm2_w, T, L, D, c->eps, s);
+      return launch_resid_modnorm(xin_f32, f32, x_in, ws.br, (float *)x1buf, ws.h, mod, w->mod_bias, 0,
+                                  w->mod_bias, w->norm2_w, 1, T, L, D, c->eps, s);
     }));
   } else {  // the three staged vectors would not fit the default LDS window
     DIT_TRY(timed(DIT_K_RESID, s, [&] {
@@ -231,6 +242,7 @@ dit_status run_block(const dit_config *c, const dit_prologue *pro, const dit_blo
   DIT_TRY(timed(DIT_K_GEMM_W2, s, [&] {
     return launch_gemm(f32, ws.qkvg, w->w_2, ws.br, T, D, (int)d.F, s, -1, 0, ws.part, ws.part_bytes);
   }));
+  if (defer_resid2) return DIT_OK;
   DIT_TRY(timed(DIT_K_RESID, s, [&] {
     return launch_resid(x1_f32, f32, xout_f32, x1buf, ws.br, x_out, mod, w->mod_bias, T, L, D, 1, s);
   }));
@@ -243,11 +255,23 @@ dit_status run_stack(const dit_config *cfg, const dit_prologue *pro, int n_block
   const BlockWs bw = carve(cfg, ws);
   char *xa = (char *)ws + bw.bytes;  // fp32 residual stream between blocks
   const bool f32 = cfg->dtype == DIT_F32;
+  const Dims d = dims(cfg);
+  const int T = (int)d.T, D = (int)d.D, L = cfg->seq_len;
+  // between two blocks, one pass: block i's second residual (x2 -> the fp32
+  // stream) and block i+1's first norm of x2 (-> its h1)
+  const bool chain = fused_resid_norm(D);
   for (int i = 0; i < n_blocks; ++i) {
     const bool first = i == 0, last = i == n_blocks - 1;
     dit_status st = run_block(cfg, pro, &blocks[i], first ? x_in : xa, first ? f32 : true, last ? x_out : xa,
-                              last ? f32 : true, mod, bw, bw.x1, s);
+                              last ? f32 : true, mod, bw, bw.x1, s, chain && !first, chain && !last);
     if (st != DIT_OK) return st;
+    if (chain && !last) {
+      hipError_t e = timed(DIT_K_RESID, s, [&] {
+        return launch_resid_modnorm(true, f32, bw.x1, bw.br, (float *)xa, bw.h, mod, blocks[i].mod_bias, 1,
+                                    blocks[i + 1].mod_bias, blocks[i + 1].norm1_w, 0, T, L, D, cfg->eps, s);
+      });
+      if (e != hipSuccess) return hip_fail(e);
+    }
   }
   return DIT_OK;
 }

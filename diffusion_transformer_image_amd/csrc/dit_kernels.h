@@ -13,10 +13,13 @@ hipError_t launch_modnorm(bool x_f32, bool h_f32, const void *x, void *h, const 
 hipError_t launch_resid(bool x_f32, bool y_f32, bool out_f32, const void *x, const void *y,
                         void *out, const float *mod, const float *bias, int rows, int seq_len,
                         int D, int which, hipStream_t s);
-// x1 = x + gate1 * y (fp32), h = modnorm of x1 with the second norm
+// x1 = x + gate * y (fp32), h = modnorm of x1: the gate of residual gw
+// (0: first, 1: second) with bias gbias, the norm nw with bias nbias and
+// gain ngain (may be NULL)
 hipError_t launch_resid_modnorm(bool x_f32, bool f32, const void *x, const void *y, float *x1, void *h,
-                                const float *mod, const float *bias, const float *gain2, int rows,
-                                int seq_len, int D, float eps, hipStream_t s);
+                                const float *mod, const float *gbias, int gw, const float *nbias,
+                                const float *ngain, int nw, int rows, int seq_len, int D, float eps,
+                                hipStream_t s);
 hipError_t launch_tmod(const float *t, const float *w1, const float *w2, float *mod, float *zs,
                        int B, int D, int tdim, hipStream_t s);
 // out[b][o] = sum_r w[o][r] zs[b][r], o < O: a second map of the hidden zs

@@ -291,16 +291,21 @@ hipError_t launch_resid(bool x_f32, bool y_f32, bool out_f32, const void *x, con
 }
 
 // ----------------------------------------------------------------- residual + norm
-// The first gated residual fused with the second modulated norm:
-//   x1 = x + gate1 * y   (stored fp32),   h2 = modnorm(x1; norm 2).
-// Saves writing x1 and reading it back between two passes.
+// A gated residual fused with the modulated norm that reads its result:
+//   x1 = x + gate * y   (stored fp32),   h = modnorm(x1; norm),
+// gate = residual `gw` with bias gbias, norm = norm `nw` with bias nbias and
+// gain ngain.  Inside a block: the first residual and the second norm (one
+// block's bias for both); between two blocks of a stack: the second
+// residual of one block and the first norm of the next (each its own
+// block's bias).  Saves writing x1 and reading it back between two passes.
 template <typename Tx, typename Ty, typename Th, int NCH>
 __global__ __launch_bounds__(256) void resid_modnorm_kernel(const Tx *__restrict__ x, const Ty *__restrict__ y,
                                                             float *__restrict__ x1, Th *__restrict__ h,
                                                             const float *__restrict__ mod,
-                                                            const float *__restrict__ bias,
-                                                            const float *__restrict__ gain2, int seq_len,
-                                                            int D, float eps) {
+                                                            const float *__restrict__ gbias, int gw,
+                                                            const float *__restrict__ nbias,
+                                                            const float *__restrict__ ngain, int nw,
+                                                            int seq_len, int D, float eps) {
   extern __shared__ float ew_lds[];
   float *G = ew_lds, *A = ew_lds + D, *S = ew_lds + 2 * D;
   const int b = blockIdx.y;
@@ -317,8 +322,8 @@ __global__ __launch_bounds__(256) void resid_modnorm_kernel(const Tx *__restrict
     bx[0].load(x + r0, lane, nch);
     by[0].load(y + r0, lane, nch);
   }
-  stage_gate_vector(G, mod, bias, b, D, 0);
-  stage_norm_vectors(A, S, mod, bias, gain2, b, D, 1);
+  stage_gate_vector(G, mod, gbias, b, D, gw);
+  stage_norm_vectors(A, S, mod, nbias, ngain, b, D, nw);
   __syncthreads();
 #pragma unroll
   for (int rr = 0; rr < RPW; ++rr) {
@@ -366,14 +371,14 @@ __global__ __launch_bounds__(256) void resid_modnorm_kernel(const Tx *__restrict
 
 template <typename Tx, typename Ty, typename Th>
 static hipError_t launch_resid_modnorm_t(const void *x, const void *y, float *x1, void *h, const float *mod,
-                                         const float *bias, const float *gain2, int rows, int seq_len,
-                                         int D, float eps, hipStream_t s) {
+                                         const float *gbias, int gw, const float *nbias, const float *ngain,
+                                         int nw, int rows, int seq_len, int D, float eps, hipStream_t s) {
   const int B = rows / seq_len;
   dim3 grid((seq_len + EW_ROWS - 1) / EW_ROWS, B), block(256);
   const size_t lds = 3 * (size_t)D * sizeof(float);
 #define DIT_RMN(N)                                                                                   \
   hipLaunchKernelGGL((resid_modnorm_kernel<Tx, Ty, Th, N>), grid, block, lds, s, (const Tx *)x,     \
-                     (const Ty *)y, x1, (Th *)h, mod, bias, gain2, seq_len, D, eps)
+                     (const Ty *)y, x1, (Th *)h, mod, gbias, gw, nbias, ngain, nw, seq_len, D, eps)
   switch (nch_bucket(D)) {
     case 1: DIT_RMN(1); break;
     case 2: DIT_RMN(2); break;
@@ -387,12 +392,16 @@ static hipError_t launch_resid_modnorm_t(const void *x, const void *y, float *x1
 }
 
 hipError_t launch_resid_modnorm(bool x_f32, bool f32, const void *x, const void *y, float *x1, void *h,
-                                const float *mod, const float *bias, const float *gain2, int rows,
-                                int seq_len, int D, float eps, hipStream_t s) {
+                                const float *mod, const float *gbias, int gw, const float *nbias,
+                                const float *ngain, int nw, int rows, int seq_len, int D, float eps,
+                                hipStream_t s) {
   // y and h have the compute dtype (f32 ? fp32 : bf16); x is fp32 or that dtype
-  if (f32) return launch_resid_modnorm_t<float, float, float>(x, y, x1, h, mod, bias, gain2, rows, seq_len, D, eps, s);
-  if (x_f32) return launch_resid_modnorm_t<float, bf16, bf16>(x, y, x1, h, mod, bias, gain2, rows, seq_len, D, eps, s);
-  return launch_resid_modnorm_t<bf16, bf16, bf16>(x, y, x1, h, mod, bias, gain2, rows, seq_len, D, eps, s);
+#define DIT_RMNT(TX, TY, TH) \
+  launch_resid_modnorm_t<TX, TY, TH>(x, y, x1, h, mod, gbias, gw, nbias, ngain, nw, rows, seq_len, D, eps, s)
+  if (f32) return DIT_RMNT(float, float, float);
+  if (x_f32) return DIT_RMNT(float, bf16, bf16);
+  return DIT_RMNT(bf16, bf16, bf16);
+#undef DIT_RMNT
 }
 
 // ----------------------------------------------------------------- timestep MLP
