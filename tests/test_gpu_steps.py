@@ -68,7 +68,7 @@ def test_gemm_swiglu(dev, dt, m, f, k):
 ATTN_CASES = [
     ("c0", 1, 80), ("c0", 2, 1), ("c0", 1, 65), ("c0", 3, 200),
     ("c1", 1, 1), ("c1", 2, 80), ("c1", 2, 512), ("c1", 1, 130), ("c1", 1, 4544), ("c1", 1, 4608),
-    ("c1", 2, 4544), ("c1", 2, 4608),  # 48 queries per wave (fewer rounds on 256 CUs)
+    ("c1", 2, 4544), ("c1", 2, 4608),  # the 1024 px and 768 x 1344 launch shapes
     ("c1", 1, 100), ("c0", 1, 47),  # the last tile ends inside its second 32-key half
 ]
 
@@ -199,7 +199,8 @@ def test_attention_rising_reference(dev, name, B, L):
 @pytest.mark.parametrize("B,L", [(1, 1), (2, 80), (1, 100), (1, 130), (2, 512), (1, 4544), (2, 4608)])
 def test_attention_prescaled(dev, B, L):
     """Queries carrying log2(e)/sqrt(d) (the block path's attention): ragged
-    tails in either 32-key half, one key, 32 and 48 queries per wave."""
+    tails in either 32-key half, one key, a query block that ends past the
+    sequence (48 queries per wave), one and two samples."""
     print(f"attention prescaled B={B} L={L}", flush=True)
     cfg = small_cfg("c1", batch=B, n_image=L, n_text=0)
     rows = np.arange(L) if L <= 600 else np.unique(np.r_[0, 1, 63, 64, 65, L // 2, L - 65, L - 64, L - 2, L - 1,
