@@ -934,8 +934,8 @@ static hipError_t launch_ring_t(const void *a, const void *w, void *c, int M, in
 //  * whole 192 x 256 tiles: ceil(tiles192 / 256) rounds of ~0.85 (measured
 //    per-round cost of the smaller tile);
 //  * 256 x 256 tiles with the partial last round split along K into `segs`
-//    segments per tile (segs = 256 / tail tiles, at most 8 and at most
-//    nk / 2): full rounds + 1/segs + the fp32 partials and the fixup pass,
+//    segments per tile (2 <= segs <= min(8, 256 / tail tiles, nk / 2), the
+//    cheapest): full rounds + 1/segs + the fp32 partials and the fixup pass,
 //    ~5 us + 0.13 us per 256 KiB partial (written once, read once), against
 //    a round of ~97 us per 4096 of K (measured on the block's shapes).
 //    Needs the partial buffer (segs * tail * 256 KiB).
@@ -950,12 +950,12 @@ GemmChoice gemm_choose(int M, int N, int K, bool swiglu) {
   const long full = t256 / 256, tail = t256 % 256;
   const int nk = (K + 63) / 64;
   if (full >= 1 && tail > 0) {
-    int segs = (int)std::min<long>(8, 256 / tail);
-    segs = std::min(segs, nk / 2);
-    if (segs >= 2) {
-      const double round_us = 97.0 * K / 4096.0;
+    const int smax = (int)std::min<long>(std::min<long>(8, 256 / tail), nk / 2);
+    const double round_us = 97.0 * K / 4096.0;
+    for (int segs = 2; segs <= smax; ++segs) {
       const double rsk = full + 1.0 / segs + (5.0 + 0.131 * tail * segs) / round_us;
       if (rsk < best) {
+        best = rsk;
         ch = GemmChoice{8, (int)tail, segs, (size_t)tail * segs * 256 * 256 * sizeof(float)};
       }
     }

@@ -176,8 +176,10 @@ def test_gemm_plan_choices():
     a split always fits its stated partial buffer."""
     T, D, F = 9216, 4096, 11008
     w13 = dit.gemm_plan(T, F, D, swiglu=True)
-    assert (w13["sk_tiles"], w13["segs"]) == (24, 8) and w13["part_bytes"] == 24 * 8 * 65536 * 4
-    assert dit.gemm_plan(T, D, F)["sk_tiles"] == 64
+    assert (w13["sk_tiles"], w13["segs"]) == (24, 6) and w13["part_bytes"] == 24 * 6 * 65536 * 4
+    assert (dit.gemm_plan(T, D, F)["sk_tiles"], dit.gemm_plan(T, D, F)["segs"]) == (64, 4)
+    # B = 1: the O product splits its 32 tail tiles 5 ways (8 would write more partials than it saves)
+    assert (dit.gemm_plan(T // 2, D, D)["sk_tiles"], dit.gemm_plan(T // 2, D, D)["segs"]) == (32, 5)
     assert dit.gemm_plan(T, 10240, D) == {"variant": 8, "sk_tiles": 0, "segs": 1, "part_bytes": 0}
     assert dit.gemm_plan(T, D, D)["variant"] == 9 and dit.gemm_plan(T, D, D)["sk_tiles"] == 0
     for m in (80, 1000, 4608, 9088, 16384):
