@@ -10,18 +10,21 @@
 //  * a small pass first writes V^T ([B][Hkv][d][Lp], keys contiguous, Lp =
 //    L rounded up to the key tile, zero padded), so both operand tiles of
 //    the main loop go HBM -> LDS by DMA (buffer_load ... lds) with no VALU
-//    work, through a 3-deep ring (tile t+2 in flight while t is used; each
-//    wave waits only for its own DMA of tile t, then one barrier);
-//  * one workgroup = (sample b, KV head j, 2*QW query tokens) for ALL query
-//    heads of the group: the K / V^T tiles of head j are brought to LDS once
-//    and read by group * 2 waves (each wave: one query head, QW = 32 or 48
-//    queries; 48 when that fills the 256 CUs in fewer weighted rounds, e.g.
-//    4608 tokens: 768 workgroups = 3 full rounds instead of 4.5);
+//    work, through a ring of tiles (each wave waits only for its own DMA
+//    of tile t, then one barrier);
+//  * one workgroup = (sample b, KV head j, WPH*QW query tokens) for ALL
+//    query heads of the group: the K / V^T tiles of head j are brought to
+//    LDS once and read by group * WPH waves (each wave: one query head, QW
+//    queries).  bf16 with 4 query heads per KV head: one wave per head,
+//    QW = 48, a 2-deep ring, two 4-wave workgroups per CU that run out of
+//    phase; otherwise two waves per head, QW = 32, a 3-deep ring;
 //  * scores are computed transposed, S^T = K Q^T (MFMA 16x16), so each
 //    lane owns one query column: the softmax statistics of a query live in
 //    4 lanes (one per lane group) and the probabilities P^T are already in
 //    the register layout of the B operand of O^T = V^T P^T;
-//  * softmax in fp32 base 2 with the 1/sqrt(d) scale folded into one FMA,
+//  * softmax in fp32 base 2 with the 1/sqrt(d) scale folded into one FMA
+//    (or, for queries that carry the factor already, into the queries: then
+//    each score chain starts from -reference and a numerator is one exp2),
 //    against a lazy reference: the numerators of a tile are computed with
 //    the current reference and packed to bf16 (the B operand of P V), and
 //    the row sums are taken from the packed values with v_dot2 (two keys
