@@ -195,6 +195,25 @@ def test_stack_full_dims_three_blocks(dev):
     check_block(y, ref, x, "bf16", "stack3")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_wide_hidden_unfused_passes(dev, dtype):
+    """hidden = 6144: three staged fp32 vectors per sample no longer fit the
+    64 KiB LDS window, so the block runs the residual and the second norm as
+    two passes and the stack does not join blocks; one block and a stack of
+    three, every output against the oracle."""
+    cfg = datagen.get_config("c4" if dtype == "bf16" else "c0").replace(
+        batch=2, n_image=40, n_text=9, hidden=6144, n_heads=48, n_kv_heads=12, head_dim=128, ffn=512,
+        dtype=dtype, n_blocks=3, out_std=0.02 / np.sqrt(6))
+    x = datagen.activations(cfg)
+    mod = datagen.block_mod(cfg, strong=True)
+    blocks = [datagen.block_weights(cfg, i) for i in range(3)]
+    oc = O.OracleConfig.of(cfg)
+    y1 = run_stack(dev, cfg, blocks[:1], x, mod)
+    check_block(y1, O.block_forward(x, mod, blocks[0], oc), x, dtype, "wide block")
+    y3 = run_stack(dev, cfg, blocks, x, mod)
+    check_block(y3, O.stack_forward(x, mod, blocks, 3, oc), x, dtype, "wide stack3")
+
+
 @pytest.mark.parametrize("live", [0, 59])
 def test_stack_c4_full_size_one_live_block(dev, live):
     """The 60-block stack at its full 1024 px shape: 59 blocks run their full
