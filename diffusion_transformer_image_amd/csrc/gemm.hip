@@ -366,14 +366,15 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(const T *__restrict__
       __builtin_amdgcn_sched_barrier(0);
       wait_vmcnt<0>();  // this wave's DMA of stage kt+1
       __syncthreads();  // stage kt+1 visible; every wave holds its stage-kt fragments
+      // the second half of the stage (fragment reads, the refill spread over
+      // the MFMAs) runs at raised wave priority: the SIMD's other wave, in
+      // its first burst or at the barrier, then does not delay this wave's
+      // loads and MFMAs.  The priority is raised before the reads and loads,
+      // not between them and the MFMAs: s_setprio bounds the scheduling
+      // groups, and placed there it leaves the refill as one burst
+      __builtin_amdgcn_s_setprio(1);
       load_frags(smem + ((kt + 1) & 1) * STAGE_BYTES, 0, a0, b0);
       issue_spread(kt + 2, kt & 1);
-      // the burst that carries the refill runs at raised wave priority: the
-      // SIMD's other wave (in its first burst or at the barrier) then does
-      // not delay this wave's loads and MFMAs (W13 at 1024 px: -2 %, W2 -1 %,
-      // the rest unchanged; raising it for both bursts or only the first
-      // gains less)
-      __builtin_amdgcn_s_setprio(1);
       mmas(a1, b1);
       // scheduling groups: the fragment reads first, then BPW times
       // (RB*CB/BPW MFMAs, one DMA load)
