@@ -376,15 +376,19 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_kernel(const T *__restrict__
       load_frags(smem + ((kt + 1) & 1) * STAGE_BYTES, 0, a0, b0);
       issue_spread(kt + 2, kt & 1);
       mmas(a1, b1);
-      // scheduling groups: the fragment reads first, then BPW times
-      // (RB*CB/BPW MFMAs, one DMA load)
+      // scheduling groups: the fragment reads first, then BPW times (two
+      // MFMAs, one DMA load), then the rest of the MFMAs: the refill leaves
+      // within the first 2*BPW MFMAs (one load per 2 MFMAs measured best:
+      // per 1, 3 or 4 MFMAs, or all loads first, were 1-3 % slower on W13)
 #pragma unroll
       for (int q = 0; q < RB + CB; ++q) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
 #pragma unroll
       for (int q = 0; q < BPW; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x008, (RB * CB) / BPW, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
         __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       }
+      static_assert(RB * CB >= 2 * BPW, "two MFMAs per refill load");
+      __builtin_amdgcn_sched_group_barrier(0x008, RB * CB - 2 * BPW, 0);
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_setprio(0);
     }
