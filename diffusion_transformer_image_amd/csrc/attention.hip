@@ -486,7 +486,7 @@ static hipError_t launch_attn_t(const void *qkvg, void *vt, void *og, int B, int
   // workgroups per CU the finer launch balances itself, and 48 measured
   // faster than 32 at every size here (256 px 243 -> 229 us, 512 px 298 ->
   // 283 us, 1024 px equal, the 60-block stack at B = 1 110 -> 108 ms)
-  if (sizeof(T) == 2)
+  if constexpr (sizeof(T) == 2)
     launch_attn_q<T, HD, 48, PRE>(q, v, (T *)og, B, L, H, Hkv, sc, s);
   else
     launch_attn_q<T, HD, 32, PRE>(q, v, (T *)og, B, L, H, Hkv, sc, s);
