@@ -815,8 +815,9 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(const uint8_t *__restrict
     // K a whole number of stages: the K offset is the DMA's scalar offset
     // (rows outside the operand keep an out-of-range vector offset; the
     // stage past the end gets an out-of-range scalar offset), and the 8
-    // loads of the next stage are spread over the stage's MFMAs, the A
-    // fragment reads of row block i+1 issued beside the MFMAs of block i
+    // loads of the next stage are spread over the first half of the
+    // stage's MFMAs, the A fragment reads of row block i+1 issued beside the
+    // MFMAs of block i
     uint32_t goffs[BPW];
 #pragma unroll
     for (int j = 0; j < BPW; ++j) goffs[j] = gval[j] ? goff[j] : kOOB;
@@ -829,7 +830,7 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(const uint8_t *__restrict
         load_lds16_k(blk < ABLK ? ra : rw, base + blk * 1024, goffs[j], soff);
       }
     };
-    static_assert(BPW == RB, "one DMA load per row block of MFMAs");
+    static_assert(BPW == RB && RB % 2 == 0, "two DMA loads per row block over the first half");
     issue_spread(0, 0);
     for (int kt = 0; kt < nk; ++kt) {
       wait_vmcnt<0>();  // this wave's DMA of stage kt
@@ -847,8 +848,16 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(const uint8_t *__restrict
 #pragma unroll
       for (int i = 0; i < RB; ++i) {
         const i32x8 an = i + 1 < RB ? frag(sb, arow[i + 1]) : af;
-        const int blk = wave + i * NW;
-        load_lds16_k(blk < ABLK ? ra : rw, nb + blk * 1024, goffs[i], soff);
+        // the refill leaves two loads per row block over the first half of
+        // the stage (one per block over all of it: the four products 1.83
+        // -> 1.80 ms at 1024 px)
+        if (2 * i < RB) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int blk = wave + (2 * i + h) * NW;
+            load_lds16_k(blk < ABLK ? ra : rw, nb + blk * 1024, goffs[2 * i + h], soff);
+          }
+        }
 #pragma unroll
         for (int j = 0; j < CB; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[j], acc[i][j], 0, 0, 0, 0, 0, 0);
