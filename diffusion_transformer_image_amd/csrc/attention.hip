@@ -17,7 +17,8 @@
 //    LDS once and read by group * WPH waves (each wave: one query head, QW
 //    queries).  bf16 with 4 query heads per KV head: one wave per head,
 //    QW = 48, a 2-deep ring, two 4-wave workgroups per CU that run out of
-//    phase; otherwise two waves per head, QW = 32, a 3-deep ring;
+//    phase; otherwise two waves per head (QW = 48 in bf16, 32 in fp32)
+//    and a 3-deep ring;
 //  * scores are computed transposed, S^T = K Q^T (MFMA 16x16), so each
 //    lane owns one query column: the softmax statistics of a query live in
 //    4 lanes (one per lane group) and the probabilities P^T are already in
