@@ -72,7 +72,9 @@ dit_status check_cfg(const dit_config *c) {
     return DIT_ERR_SHAPE;
   if ((int64_t)c->n_heads * c->head_dim != c->hidden) return DIT_ERR_SHAPE;
   if (c->n_heads % c->n_kv_heads != 0) return DIT_ERR_SHAPE;
-  if (c->n_heads / c->n_kv_heads > 4) return DIT_ERR_UNSUPPORTED;
+  // the attention kernels exist for 1, 2 and 4 query heads per KV head
+  const int group = c->n_heads / c->n_kv_heads;
+  if (group != 1 && group != 2 && group != 4) return DIT_ERR_UNSUPPORTED;
   if (c->dtype == DIT_BF16 ? c->head_dim != 128 : (c->head_dim != 64 && c->head_dim != 128))
     return DIT_ERR_UNSUPPORTED;
   if (c->hidden % 8 || c->ffn % 8) return DIT_ERR_UNSUPPORTED;
@@ -149,6 +151,20 @@ dit_status check_weights(const dit_block_weights *w) {
       !aligned(w->k_norm_w))
     return DIT_ERR_ALIGN;
   return DIT_OK;
+}
+
+// True if [p, p + n) overlaps any buffer of one block's weights (the
+// workspace must not alias an input: it is written before the weights are
+// last read).
+bool overlaps_weights(const dit_config *c, const dit_block_weights *w, const void *p, size_t n) {
+  const Dims d = dims(c);
+  const size_t D = d.D;
+  return overlap(p, n, w->w_qkvg, d.nqkvg * D * d.es) || overlap(p, n, w->w_o, D * d.hd * d.es) ||
+         overlap(p, n, w->w_13, 2 * d.F * D * d.es) || overlap(p, n, w->w_2, D * d.F * d.es) ||
+         overlap(p, n, w->mod_bias, 6 * D * 4) || overlap(p, n, w->norm1_w, w->norm1_w ? D * 4 : 0) ||
+         overlap(p, n, w->norm2_w, w->norm2_w ? D * 4 : 0) ||
+         overlap(p, n, w->q_norm_w, w->q_norm_w ? (size_t)c->head_dim * 4 : 0) ||
+         overlap(p, n, w->k_norm_w, w->k_norm_w ? (size_t)c->head_dim * 4 : 0);
 }
 
 // NULL is valid (no prologue)
@@ -404,7 +420,8 @@ dit_status dit_block_fwd_ex(const dit_config *cfg, const dit_prologue *pro, cons
   const size_t xb = d.T * d.D * d.es;
   if (overlap(x_in, xb, x_out, xb)) return DIT_ERR_SHAPE;
   if (overlap(ws, need.bytes, x_in, xb) || overlap(ws, need.bytes, x_out, xb) ||
-      overlap(ws, need.bytes, mod, (size_t)cfg->batch * 6 * cfg->hidden * 4))
+      overlap(ws, need.bytes, mod, (size_t)cfg->batch * 6 * cfg->hidden * 4) ||
+      overlaps_weights(cfg, w, ws, need.bytes))
     return DIT_ERR_SHAPE;
   const BlockWs bw = carve(cfg, ws);
   const bool f32 = cfg->dtype == DIT_F32;
@@ -437,6 +454,8 @@ dit_status dit_stack_fwd_ex(const dit_config *cfg, const dit_prologue *pro, int3
   if (overlap(ws, need, x_in, xb) || overlap(ws, need, x_out, xb) ||
       overlap(ws, need, mod, (size_t)cfg->batch * 6 * cfg->hidden * 4))
     return DIT_ERR_SHAPE;
+  for (int i = 0; i < n_blocks; ++i)
+    if (overlaps_weights(cfg, &blocks[i], ws, need)) return DIT_ERR_SHAPE;
   return run_stack(cfg, pro, n_blocks, blocks, x_in, x_out, mod, ws, (hipStream_t)stream);
 }
 
@@ -493,6 +512,8 @@ static dit_status check_model_call(const dit_config *cfg, const dit_model_config
   const size_t zb = (size_t)cfg->batch * mc->latent_ch * 4 * mc->grid_h * mc->grid_w * 4;
   const size_t tb = txt ? (size_t)cfg->batch * mc->n_text * mc->txt_dim * esize(cfg->dtype) : 0;
   if (overlap(ws, need, z, zb) || overlap(ws, need, txt, tb)) return DIT_ERR_SHAPE;
+  for (int i = 0; i < n_blocks; ++i)
+    if (overlaps_weights(cfg, &blocks[i], ws, need)) return DIT_ERR_SHAPE;
   return DIT_OK;
 }
 
@@ -773,18 +794,25 @@ dit_status dit_gated_residual(const dit_config *cfg, const void *x, dit_dtype x_
 dit_status dit_timer_start(int32_t kind, int32_t capacity) {
   if (kind < 0 || kind >= DIT_K_COUNT || capacity <= 0 || capacity > 1 << 16) return DIT_ERR_SHAPE;
   std::lock_guard<std::mutex> lk(g_timer.mu);
-  for (size_t i = 0; i < g_timer.ev0.size(); ++i) {
-    (void)hipEventDestroy(g_timer.ev0[i]);
-    (void)hipEventDestroy(g_timer.ev1[i]);
-  }
+  auto release = [] {
+    for (hipEvent_t ev : g_timer.ev0)
+      if (ev) (void)hipEventDestroy(ev);
+    for (hipEvent_t ev : g_timer.ev1)
+      if (ev) (void)hipEventDestroy(ev);
+    g_timer.ev0.clear();
+    g_timer.ev1.clear();
+    g_timer.active = false;
+    g_timer.kind = -1;
+    g_timer.capacity = g_timer.count = 0;
+  };
+  release();
   g_timer.ev0.assign(capacity, nullptr);
   g_timer.ev1.assign(capacity, nullptr);
   for (int i = 0; i < capacity; ++i) {
     hipError_t e = hipEventCreate(&g_timer.ev0[i]);
     if (e == hipSuccess) e = hipEventCreate(&g_timer.ev1[i]);
     if (e != hipSuccess) {
-      g_timer.ev0.resize(i);
-      g_timer.ev1.resize(i);
+      release();  // every event created so far; the timer stays off
       return hip_fail(e);
     }
   }

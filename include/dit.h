@@ -63,7 +63,9 @@ typedef enum {
 typedef enum { DIT_F32 = 0, DIT_BF16 = 1 } dit_dtype;
 
 /* Block dimensions.  Requirements: all sizes > 0; hidden == n_heads*head_dim;
- * n_heads % n_kv_heads == 0 and n_heads / n_kv_heads <= 4; head_dim == 128
+ * n_heads % n_kv_heads == 0; n_heads / n_kv_heads in {1, 2, 4} (other
+ * group sizes return DIT_ERR_UNSUPPORTED: no attention kernel exists for
+ * them); head_dim == 128
  * for bf16, head_dim == 64 or 128 for f32; hidden % 8 == 0, hidden <= 8192;
  * ffn % 8 == 0; eps >= 0. */
 typedef struct {

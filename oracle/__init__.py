@@ -45,8 +45,13 @@ Parity status (what pins each function; see the tests under
   (the 8-bit projections): pinned by an exhaustive nearest-value search over
   all finite e4m3 codes (ties to even), fixed points at representable
   values, the row maximum landing on +-448, and float64 products of the
-  decoded values; e4m3 with row-wise scales is a reading of the pages'
-  8-bit training (their scaling schemes, not an inference format).
+  decoded values; ``swiglu_fp8`` also by a scalar loop with distinct W1 and
+  W3 halves and scales (swapping the SiLU and linear roles fails it); e4m3
+  with row-wise scales is a reading of the pages' 8-bit training (their
+  scaling schemes, not an inference format).
+* ``qkvg_projection`` (the column split Q | K | V | G): pinned by a scalar
+  loop over every head and channel with a distinct value in every row
+  block of W_qkvg.
 * The zero-centred gain form ``(1 + w)`` of the RMSNorm is a reading of
   the pages (weight decay on a zero-centred parameter); parity of that
   convention is unpinned by the pages, though the arithmetic under it is

@@ -49,6 +49,8 @@ def test_status_strings():
     (dict(hidden=255), "DIT_ERR_SHAPE"),          # != H * d
     (dict(n_kv_heads=3), "DIT_ERR_SHAPE"),        # H % Hkv != 0
     (dict(n_heads=8, head_dim=32, n_kv_heads=1), "DIT_ERR_UNSUPPORTED"),  # group 8
+    (dict(n_heads=6, head_dim=64, hidden=384, n_kv_heads=2), "DIT_ERR_UNSUPPORTED"),  # group 3
+    (dict(n_heads=3, head_dim=64, hidden=192, n_kv_heads=1), "DIT_ERR_UNSUPPORTED"),  # group 3
     (dict(head_dim=32, n_heads=8, n_kv_heads=4), "DIT_ERR_UNSUPPORTED"),  # d = 32
     (dict(dtype="bf16"), "DIT_ERR_UNSUPPORTED"),  # bf16 needs d = 128
     (dict(ffn=690), "DIT_ERR_UNSUPPORTED"),       # ffn % 8
@@ -61,6 +63,25 @@ def test_bad_config_is_rejected(kw, expect):
     st = dit.lib().dit_block_fwd(ctypes.byref(c), ctypes.byref(w), P, P + (1 << 30), P + (2 << 30),
                                  P + (3 << 30), 1 << 40, None)
     assert _lib.STATUS[st] == expect
+
+
+@pytest.mark.parametrize("heads,kv", [(6, 2), (3, 1), (12, 4)])
+def test_group_without_attention_kernel_is_rejected_everywhere(heads, kv):
+    """Only 1, 2 and 4 query heads per KV head have attention kernels: any
+    other group is refused by every entry point before anything is enqueued."""
+    c = cfg(n_heads=heads, n_kv_heads=kv, head_dim=64, hidden=64 * heads)
+    L = dit.lib()
+    assert L.dit_workspace_size(ctypes.byref(c)) == 0
+    assert L.dit_stack_workspace_size(ctypes.byref(c)) == 0
+    w = _lib.BlockWeights(P, P, P, P, P, P, P)
+    st = L.dit_block_fwd(ctypes.byref(c), ctypes.byref(w), P, P + (1 << 30), P + (2 << 30),
+                         P + (3 << 30), 1 << 40, None)
+    assert _lib.STATUS[st] == "DIT_ERR_UNSUPPORTED"
+    st = L.dit_attention(ctypes.byref(c), P, P + (1 << 30), P + (2 << 30), 1 << 40, None)
+    assert _lib.STATUS[st] == "DIT_ERR_UNSUPPORTED"
+    st = L.dit_stack_fwd(ctypes.byref(c), 1, ctypes.byref(w), P, P + (1 << 30), P + (2 << 30),
+                         P + (3 << 30), 1 << 40, None)
+    assert _lib.STATUS[st] == "DIT_ERR_UNSUPPORTED"
 
 
 def test_bad_dtype_code():
@@ -93,6 +114,12 @@ def test_block_argument_checks():
     assert call_block(c, _lib.BlockWeights(P + 4, P, P, P, P, 0, 0), X, Y, M, WS, need) == "DIT_ERR_ALIGN"
     assert call_block(c, w, X, X + 64, M, WS, need) == "DIT_ERR_SHAPE"  # x_out overlaps x_in
     assert call_block(c, w, X, Y, M, X, need) == "DIT_ERR_SHAPE"  # workspace overlaps x_in
+    # the workspace must not overlap any weight buffer either
+    for i in range(7):
+        ptrs = [P, P, P, P, P, 0, 0]
+        ptrs[i] = WS + need - 256  # inside the workspace's last bytes
+        assert call_block(c, _lib.BlockWeights(*ptrs), X, Y, M, WS, need) == "DIT_ERR_SHAPE", i
+    assert call_block(c, _lib.BlockWeights(P, P, P, P, P, 0, 0, WS, 0), X, Y, M, WS, need) == "DIT_ERR_SHAPE"
 
 
 def test_stack_argument_checks():

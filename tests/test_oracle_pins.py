@@ -570,3 +570,55 @@ def test_fp8_tensor_scale_is_row_scale_of_the_whole_tensor():
     qf, sf = O.quantize_rows_fp8(x.reshape(1, -1))
     assert np.array_equal(q, qf.reshape(x.shape)) and np.all(s == sf[0])
     assert np.max(np.abs(q)) == 448.0
+
+
+def test_fp8_swiglu_roles_against_scalar_loop():
+    """swiglu_fp8 with distinct W1 and W3 (and distinct scales) against a
+    scalar loop of its definition: u = SiLU(sa sw1 a.w1) * (sa sw3 a.w3),
+    W1 the first ffn rows of W13 (the SiLU branch), W3 the next ffn rows
+    (the linear branch; page "Krea 2 技术报告", 架构 › Transformer块:
+    SwiGLU, the GLU-variants paper's roles).  Swapping the roles must change
+    the result, so the pin tells them apart."""
+    r = np.random.default_rng(44)
+    m, f, k = 4, 5, 32
+    a = O.fp8_e4m3_round(r.integers(-12, 13, (m, k)).astype(np.float32) / 4)
+    w1 = O.fp8_e4m3_round(r.integers(-12, 13, (f, k)).astype(np.float32) / 8)
+    w3 = O.fp8_e4m3_round(r.integers(-12, 13, (f, k)).astype(np.float32) / 8 + 0.5)
+    sa = np.float32(r.random(m) + 0.25)
+    sw1, sw3 = np.float32(r.random(f) + 0.5), np.float32(r.random(f) + 1.5)
+    u = O.swiglu_fp8(a, sa, np.concatenate([w1, w3]), np.concatenate([sw1, sw3]), f)
+    for i in range(m):
+        for n in range(f):
+            z1 = sum(float(a[i, kk]) * float(w1[n, kk]) for kk in range(k)) * float(sa[i]) * float(sw1[n])
+            z3 = sum(float(a[i, kk]) * float(w3[n, kk]) for kk in range(k)) * float(sa[i]) * float(sw3[n])
+            want = z1 / (1.0 + math.exp(-z1)) * z3
+            assert abs(u[i, n] - want) <= 1e-12 * max(1.0, abs(want)), (i, n)
+    swapped = O.swiglu_fp8(a, sa, np.concatenate([w3, w1]), np.concatenate([sw3, sw1]), f)
+    assert np.max(np.abs(swapped - u)) > 1e-3 * np.max(np.abs(u))
+
+
+def test_qkvg_projection_slices_against_scalar_loop():
+    """qkvg_projection's column slices against the row blocks of W_qkvg
+    written out per element: Q head h = rows h d .. h d + d - 1, K head j =
+    rows (H + j) d .., V head j = rows (H + Hkv + j) d .., G head h = rows
+    (H + 2 Hkv + h) d .. (the block's layout); every row block holds
+    different values, so a swapped or shifted slice fails."""
+    r = np.random.default_rng(45)
+    D, H, Hk, d, L = 6, 4, 2, 3, 5
+    oc_ = O.OracleConfig(hidden=D, n_heads=H, n_kv_heads=Hk, head_dim=d, ffn=8)
+    w = r.standard_normal(((2 * H + 2 * Hk) * d, D)) + np.arange((2 * H + 2 * Hk) * d)[:, None]
+    h = r.standard_normal((L, D))
+    q, k, v, g = O.qkvg_projection(h, w, oc_)
+    assert q.shape == (L, H, d) and k.shape == (L, Hk, d) and v.shape == (L, Hk, d) and g.shape == (L, H, d)
+
+    def dot(l, row):
+        return sum(h[l, c] * w[row, c] for c in range(D))
+
+    for l in range(L):
+        for e in range(d):
+            for hh in range(H):
+                assert abs(q[l, hh, e] - dot(l, hh * d + e)) < 1e-9
+                assert abs(g[l, hh, e] - dot(l, (H + 2 * Hk + hh) * d + e)) < 1e-9
+            for j in range(Hk):
+                assert abs(k[l, j, e] - dot(l, (H + j) * d + e)) < 1e-9
+                assert abs(v[l, j, e] - dot(l, (H + Hk + j) * d + e)) < 1e-9
