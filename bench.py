@@ -12,8 +12,13 @@ Prints one JSON line.  ``value`` is tokens/s of the whole step.  The
 ``roofline`` object is for the dominant kernel (the SwiGLU up/gate GEMM:
 the tile kernel and, when the last round of tiles is split along K, its
 fixup pass), timed with HIP events recorded around each of its launches on
-its own stream inside the timed region.  ``cpu_baseline`` times the fp64 oracle on
-one sample of the same workload on the host cores.
+its own stream inside the timed region.  ``cpu_baseline`` times the fp64 oracle
+on the whole benchmarked batch (both samples, all 4608 tokens, with the
+oracle's own timestep modulation) on the host cores; ``parity`` compares
+that oracle output with the GPU output of the benchmarked step, element by
+element.  ``configs`` holds the other synthetic workloads (256 px, 512 px,
+768 x 1344) and ``stack`` the 60-block denoising step, each with a
+per-kernel breakdown.
 """
 from __future__ import annotations
 
@@ -73,6 +78,75 @@ def load_traffic(kernel_file: str):
     return rec.get("bytes_per_launch")
 
 
+def kernel_breakdown(dit, torch, run, cfg, reps: int = 3, per_call: int = 1, resid_bytes=None) -> dict:
+    """Average launch time of each kernel kind over ``reps`` calls of
+    ``run`` (untimed passes, one kind at a time, HIP events around every
+    launch of that kind), with TFLOP/s against the bf16 peak for the MFMA
+    kernels and GB/s against HBM for the elementwise ones.  ``per_call``:
+    blocks per call (60 for the stack)."""
+    fpt, bpt = flops_per_token(cfg), bytes_per_token(cfg)
+    if resid_bytes is not None:
+        bpt["resid"] = resid_bytes
+    out = {}
+    for kind in dit.KERNEL_KINDS:
+        dit.timer_start(kind, 4 * reps * per_call)
+        for _ in range(reps):
+            run()
+        torch.cuda.synchronize()
+        ms, n = dit.timer_stop()
+        if n == 0:
+            continue
+        per_launch = ms / n
+        e = {"launches_per_call": n // reps, "ms_per_launch": per_launch}
+        if kind in fpt:
+            tf = fpt[kind] * cfg.tokens / (per_launch * 1e-3) / 1e12
+            e.update(tflops=tf, mfma_frac=tf / PEAK_BF16_TFLOPS)
+        elif kind in bpt:
+            gbs = bpt[kind] * cfg.tokens / (per_launch * 1e-3) / 1e9
+            e.update(gbs=gbs, hbm_frac=gbs / PEAK_HBM_GBS)
+        out[kind] = e
+    return out
+
+
+def step_stats(ms_list) -> dict:
+    """Median, minimum and mean of per-step times (ms) from stream events."""
+    import statistics
+    return {"median": statistics.median(ms_list), "min": min(ms_list), "mean": sum(ms_list) / len(ms_list),
+            "n": len(ms_list)}
+
+
+def timed_steps(torch, fn, steps: int) -> tuple[float, list]:
+    """Wall time of ``steps`` calls between device synchronisations, and the
+    per-call times from events recorded on the current stream around each."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev[0].record()
+    for i in range(steps):
+        fn()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    return elapsed, [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+
+
+def parity_report(y, ref, x) -> dict:
+    """Element-by-element comparison of the GPU output y with the oracle's
+    ref (both [B, L, D] float64) and of the updates y - x, ref - x, against
+    the bf16 bounds: max-abs <= 2e-2 max|ref|, cosine >= 0.9999."""
+    import numpy as np
+
+    def m(a, b):
+        a, b = a.ravel(), b.ravel()
+        return {"maxabs_rel": float(np.max(np.abs(a - b)) / np.max(np.abs(b))),
+                "cos": float(a @ b / (np.linalg.norm(a) * np.linalg.norm(b)))}
+
+    out = {"output": m(y, ref), "update": m(y - x, ref - x), "elements": int(y.size),
+           "bound": {"maxabs_rel": 2e-2, "cos": 0.9999}}
+    out["output_within_bound"] = out["output"]["maxabs_rel"] <= 2e-2 and out["output"]["cos"] >= 0.9999
+    return out
+
+
 def cpu_baseline(cfg, x, w, t, w_t1, w_t2) -> dict:
     """The oracle as it stands on the whole workload (every sample of the
     batch, all tokens): its own timestep modulation, then the block."""
@@ -86,9 +160,9 @@ def cpu_baseline(cfg, x, w, t, w_t1, w_t2) -> dict:
     oc = O.OracleConfig.of(cfg)
     t0 = time.perf_counter()
     mod = O.timestep_modulation(t, w_t1, w_t2, cfg.hidden)
-    O.block_forward(x, mod, w, oc)
+    ref = O.block_forward(x, mod, w, oc)
     dt = time.perf_counter() - t0
-    return {"value": cfg.tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    return ref, {"value": cfg.tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"the whole batch: {cfg.batch} x {cfg.seq_len} tokens, one block with its timestep "
                       f"modulation, fp64 numpy ({blas}), {dt:.2f} s",
             "seconds": dt, "affinity_cpus": len(os.sched_getaffinity(0))}
@@ -121,20 +195,25 @@ def bench_stack(dit, torch, steps: int, warmup: int) -> dict:
     y = torch.empty_like(x)
     mod = randn((1, 6, d), 0.15, torch.float32)
     ws = torch.empty(dit.stack_workspace_size(c), dtype=torch.uint8, device="cuda")
+    def run():
+        dit.stack_fwd(c, blocks, x, y, mod, ws)
+
     for _ in range(warmup):
-        dit.stack_fwd(c, blocks, x, y, mod, ws)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        dit.stack_fwd(c, blocks, x, y, mod, ws)
-    torch.cuda.synchronize()
-    dt = (time.perf_counter() - t0) / steps
+        run()
+    elapsed, per = timed_steps(torch, run, steps)
+    dt = elapsed / steps
     fl = sum(flops_per_token(cfg).values()) * cfg.tokens * cfg.n_blocks
     out = {"workload": "krea2-dit-stack60-1024px", "batch": 1, "seq_len": cfg.seq_len,
-           "n_blocks": cfg.n_blocks, "ms_per_denoising_step": dt * 1e3,
+           "n_blocks": cfg.n_blocks, "ms_per_denoising_step": dt * 1e3, "step_ms": step_stats(per),
            "block_tokens_per_s": cfg.n_blocks * cfg.tokens / dt, "tflops": fl / dt / 1e12,
            "mfma_frac": fl / dt / 1e12 / PEAK_BF16_TFLOPS, "steps": steps, "warmup": warmup,
            "weights_gb": sum(t.numel() * t.element_size() for b in blocks for t in b.values()) / 1e9}
+    # in the stack the residual kind moves 12 d bytes per token and launch:
+    # the fused first residual + second norm reads the fp32 stream and A,
+    # writes x1 (fp32) and h2; the pass between blocks reads x1 and M and
+    # writes the stream and the next block's h1
+    out["kernels"] = kernel_breakdown(dit, torch, run, cfg, reps=1, per_call=cfg.n_blocks,
+                                      resid_bytes=12 * cfg.hidden)
     out["sample"] = bench_sample(dit, torch, cfg, c, blocks, randn)
     del blocks
     torch.cuda.empty_cache()
@@ -251,6 +330,42 @@ def bench_fp8(dit, torch, cfg, reps: int = 10) -> dict:
     return out
 
 
+def bench_configs(dit, torch, W, W1, W2, steps: int, warmup: int) -> dict:
+    """The other synthetic workloads with the same block weights: 256 px
+    (B = 32, L = 512), 512 px (B = 8, L = 1280) and 768 x 1344 (B = 2, L =
+    4544).  Each: timestep modulation + one block per step, tokens/s,
+    TFLOP/s and the per-kernel breakdown."""
+    import datagen
+    from datagen import device
+    res = {}
+    for name in ("c1", "c2", "c3b"):
+        cfg = datagen.get_config(name)
+        c = dit.config_of(cfg)
+        X = device.to_device(datagen.activations(cfg).reshape(cfg.tokens, cfg.hidden), "bf16")
+        Y = torch.empty_like(X)
+        t = torch.rand(cfg.batch, generator=torch.Generator().manual_seed(cfg.seed)).to("cuda")
+        M = torch.empty((cfg.batch, 6, cfg.hidden), dtype=torch.float32, device="cuda")
+        ws = torch.empty(dit.workspace_size(c), dtype=torch.uint8, device="cuda")
+
+        def step():
+            dit.timestep_mod(c, t, W1, W2, M, ws)
+            dit.block_fwd(c, W, X, Y, M, ws)
+
+        for _ in range(warmup):
+            step()
+        elapsed, per = timed_steps(torch, step, steps)
+        fl = sum(flops_per_token(cfg).values()) * cfg.tokens
+        res[cfg.name] = {"batch": cfg.batch, "seq_len": cfg.seq_len, "image_tokens": cfg.n_image,
+                         "text_tokens": cfg.n_text, "ms_per_step": elapsed / steps * 1e3,
+                         "tokens_per_s": cfg.tokens / (elapsed / steps), "step_ms": step_stats(per),
+                         "tflops": fl / (elapsed / steps) / 1e12,
+                         "mfma_frac": fl / (elapsed / steps) / 1e12 / PEAK_BF16_TFLOPS,
+                         "kernels": kernel_breakdown(dit, torch, step, cfg)}
+        del X, Y, ws
+        torch.cuda.empty_cache()
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -298,40 +413,17 @@ def main() -> int:
     # ---- timed region: K steps, events on the dominant kernel's launches
     dom = "gemm_w13"
     dit.timer_start(dom, args.steps)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    elapsed, per_step = timed_steps(torch, step, args.steps)
     dom_ms, dom_n = dit.timer_stop()
 
     ms_per_step = elapsed / args.steps * 1e3
     tokens_per_s = cfg.tokens / (elapsed / args.steps)
     fpt = flops_per_token(cfg)
     step_flops = sum(fpt.values()) * cfg.tokens
+    y_gpu = device.to_numpy(Y).reshape(x.shape)  # the benchmarked step's output
 
     # ---- per-kernel breakdown (separate, untimed passes; one kind at a time)
-    kernels = {}
-    bpt = bytes_per_token(cfg)
-    for kind in dit.KERNEL_KINDS:
-        reps = 3
-        dit.timer_start(kind, 4 * reps)
-        for _ in range(reps):
-            step()
-        torch.cuda.synchronize()
-        ms, n = dit.timer_stop()
-        if n == 0:
-            continue
-        per_launch = ms / n
-        e = {"launches_per_step": n // reps, "ms_per_launch": per_launch}
-        if kind in fpt:
-            tf = fpt[kind] * cfg.tokens / (per_launch * 1e-3) / 1e12
-            e.update(tflops=tf, mfma_frac=tf / PEAK_BF16_TFLOPS)
-        elif kind in bpt:
-            gbs = bpt[kind] * cfg.tokens / (per_launch * 1e-3) / 1e9
-            e.update(gbs=gbs, hbm_frac=gbs / PEAK_HBM_GBS)
-        kernels[kind] = e
+    kernels = kernel_breakdown(dit, torch, step, cfg)
 
     dom_avg = dom_ms / max(dom_n, 1)
     dom_flops = fpt[dom] * cfg.tokens
@@ -351,16 +443,19 @@ def main() -> int:
                    "image_tokens": cfg.n_image, "text_tokens": cfg.n_text, "hidden": cfg.hidden,
                    "heads": cfg.n_heads, "kv_heads": cfg.n_kv_heads, "head_dim": cfg.head_dim,
                    "ffn": cfg.ffn, "global_batch": cfg.batch, "parallelism": "single GPU"},
+        "step_ms": step_stats(per_step),
         "tflops": step_flops / (elapsed / args.steps) / 1e12,
         "mfma_frac": step_flops / (elapsed / args.steps) / 1e12 / PEAK_BF16_TFLOPS,
         "kernels": kernels, "roofline": roofline,
     }
+    out["configs"] = bench_configs(dit, torch, W, W1, W2, args.steps, args.warmup)
     out["fp8"] = bench_fp8(dit, torch, cfg)
     out["with_prologue"] = bench_prologue(dit, torch, cfg, c, W, X, Y, M, ws, step, args.steps, args.warmup)
     if not args.no_stack:
         out["stack"] = bench_stack(dit, torch, args.stack_steps, 2)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(cfg, x, w, t, w_t1, w_t2)
+        ref, out["cpu_baseline"] = cpu_baseline(cfg, x, w, t, w_t1, w_t2)
+        out["parity"] = parity_report(y_gpu, ref, x.astype(np.float64))
     print(json.dumps(out), flush=True)
     return 0
 

@@ -35,7 +35,7 @@ __all__ = [
     "Config", "CONFIGS", "get_config", "bf16_bits", "bf16_round", "bits_to_f32",
     "BlockWeights", "block_weights", "activations", "block_mod", "timestep_inputs",
     "qkvg_activations", "rng", "qk_norm_weights", "ModelWeights", "model_weights", "latent_noise",
-    "text_features",
+    "text_features", "block_small_weights", "ROLLS", "rolled_block_weights",
 ]
 
 # tensor ids used in the spawn keys (stable: changing one changes the data)
@@ -184,6 +184,39 @@ def block_weights(cfg: Config, block: int = 0) -> BlockWeights:
         norm1_w=_normal(cfg, block, TID_NORM1, (d,), cfg.w_std, False),
         norm2_w=_normal(cfg, block, TID_NORM2, (d,), cfg.w_std, False),
     )
+
+
+def block_small_weights(cfg: Config, block: int):
+    """Block ``block``'s modulation bias and two norm gains alone (the same
+    streams ``block_weights`` draws them from), without drawing its 194 M
+    projection weights."""
+    d = cfg.hidden
+    return (_normal(cfg, block, TID_MODBIAS, (6, d), cfg.w_std, False),
+            _normal(cfg, block, TID_NORM1, (d,), cfg.w_std, False),
+            _normal(cfg, block, TID_NORM2, (d,), cfg.w_std, False))
+
+
+# Row rolls that turn a few drawn projection sets into many distinct blocks:
+# block i uses set i % n_sets with the rows of each matrix rolled by
+# ROLLS[name] * (i // n_sets) (plain re-arrangement of drawn values, so every
+# block of a long full-width stack has its own matrices at the cost of
+# drawing n_sets of them).
+ROLLS = {"w_qkvg": 37, "w_o": 11, "w_13": 53, "w_2": 29}
+
+
+def rolled_block_weights(cfg: Config, block: int, bases) -> BlockWeights:
+    """Block ``block`` of a stack built from the drawn sets ``bases`` (a list
+    of BlockWeights): set block % len(bases), projection rows rolled per
+    ROLLS, and block ``block``'s own modulation bias and norm gains."""
+    n = len(bases)
+    base, k = bases[block % n], block // n
+    mod_bias, n1, n2 = block_small_weights(cfg, block)
+    return BlockWeights(
+        w_qkvg=np.roll(base.w_qkvg, ROLLS["w_qkvg"] * k, axis=0),
+        w_o=np.roll(base.w_o, ROLLS["w_o"] * k, axis=0),
+        w_13=np.roll(base.w_13, ROLLS["w_13"] * k, axis=0),
+        w_2=np.roll(base.w_2, ROLLS["w_2"] * k, axis=0),
+        mod_bias=mod_bias, norm1_w=n1, norm2_w=n2)
 
 
 def qk_norm_weights(cfg: Config, w: BlockWeights, block: int = 0) -> BlockWeights:

@@ -30,20 +30,20 @@ hipError_t launch_patchify(bool f32, const float *z, void *p, int B, int C, int 
 // out = z + dt * unpatchify(vtok) (z may alias out, or be NULL for dt * v)
 hipError_t launch_unpatchify_axpy(bool f32, const void *vtok, const float *z, float *out, float dt, int B, int C,
                                   int Hl, int Wl, hipStream_t s);
-// variant < 0 picks the default tile configuration for the shape; group_m
-// <= 0 the default tile-grouping width (row tiles per L2 group).  part (fp32,
-// part_bytes) lets the default configuration split the tail tiles along K.
-// Columns [0, scale_cols) of C are multiplied by col_scale before rounding
-// (default configuration only; a tuning variant with scale_cols > 0 is an
-// invalid value).
+// variant < 0 picks the default tile configuration for the shape (0 / 1:
+// whole 256- / 192-row tiles); group_m <= 0 the default tile-grouping width
+// (row tiles per L2 group).  part (fp32, part_bytes) lets the default
+// configuration split the tail tiles along K.  Columns [0, scale_cols) of C
+// are multiplied by col_scale before rounding.
 hipError_t launch_gemm(bool f32, const void *a, const void *w, void *c, int M, int N, int K,
                        hipStream_t s, int variant = -1, int group_m = 0, float *part = nullptr,
                        size_t part_bytes = 0, int scale_cols = 0, float col_scale = 1.f);
 hipError_t launch_gemm_swiglu(bool f32, const void *a, const void *w13, void *u, int M, int F,
                               int K, hipStream_t s, int variant = -1, int group_m = 0,
                               float *part = nullptr, size_t part_bytes = 0);
-// The default choice for a bf16 product (256 x 256 tiles, variant 8, when
-// sk_tiles > 0) and the fp32 partial bytes its K split needs.
+// The default choice for a bf16 product (variant 0: 256 x 256 tiles, the
+// only ones split when sk_tiles > 0; 1: 192 x 256 tiles) and the fp32
+// partial bytes its K split needs.
 struct GemmChoice {
   int variant, sk_tiles, segs;
   size_t part_bytes;
@@ -53,7 +53,7 @@ GemmChoice gemm_choose(int M, int N, int K, bool swiglu);
 // segments; part holds sk_tiles * segs * 256 * 256 floats.
 hipError_t launch_gemm_split(bool swiglu, const void *a, const void *w, void *c, int M, int N, int K,
                              int sk_tiles, int segs, float *part, hipStream_t s);
-constexpr int kGemmVariants = 15;
+constexpr int kGemmVariants = 2;
 // vt: scratch of attention_vt_bytes() for the transposed V of every KV head
 size_t attention_vt_bytes(bool f32, int B, int L, int Hkv, int head_dim);
 // The attention's score factor in base-2 units, log2(e) / sqrt(head_dim).

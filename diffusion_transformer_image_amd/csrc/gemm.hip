@@ -502,203 +502,6 @@ __global__ __launch_bounds__(64) void gemm_sk_fixup(const float *__restrict__ pa
   gemm_store_direct<T, FRB * 16, TN, EPI>(acc, C, M, N, row0, col0, lane, cs);
 }
 
-// Calls f(integral_constant<I>) for I = B..E-1 in order while f returns true.
-template <int B, int E, typename F>
-__device__ __forceinline__ bool static_for(F &&f) {
-  if constexpr (B < E) {
-    if (!f(std::integral_constant<int, B>{})) return false;
-    return static_for<B + 1, E>(f);
-  }
-  return true;
-}
-
-// ---------------------------------------------------------------------------
-// Ring kernel (bf16): 8 waves (2 x 4), BM x BN output tile, K advanced 32
-// elements (64 bytes of every row) per stage through an R-deep LDS ring fed
-// by LDS DMA.
-//  * stage s lives in buffer s % R.  At step kt the wave multiplies the
-//    fragments of stage kt (already in registers), reads the fragments of
-//    stage kt+1 from LDS and issues the DMA of stage kt+R into the buffer of
-//    stage kt, so each DMA has R-1 steps to land;
-//  * the one barrier per step sits between the two halves of the step's
-//    MFMAs.  Before it each wave waits only for its own DMA of stage kt+1
-//    (partial vmcnt: the later stages stay in flight) and for its own LDS
-//    reads of stage kt; a bare s_barrier follows (no memory fence, which
-//    would wait for every DMA in flight);
-//  * the K offset of a stage is the scalar soffset of the DMA, so the loop
-//    does no per-lane address arithmetic; the LDS addresses of a buffer are
-//    fixed because the step loop is unrolled over the R buffers;
-//  * a 64-byte LDS row holds 4 chunks; chunk c of row r sits at
-//    c ^ (((r >> 1) ^ (r >> 2)) & 3), which keeps the 16 rows x one chunk of
-//    a fragment read on distinct banks for 8- and 16-lane access groups.
-__device__ __forceinline__ int swz64(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
-
-__device__ __forceinline__ void barrier_only() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-
-template <int BM, int BN, int R, int WM, int WN, int EPI>
-__global__ __launch_bounds__(WM *WN * 64) void gemm_ring_kernel(const bf16 *__restrict__ A,
-                                                        const bf16 *__restrict__ W,
-                                                        bf16 *__restrict__ C, int M, int N, int K,
-                                                        int m_tiles, int n_tiles, int gm) {
-  constexpr int NW = WM * WN;
-  constexpr int TM = BM / WM, TN = BN / WN;
-  constexpr int RB = TM / 16, CB = TN / 16;
-  constexpr int ABLK = BM / 16, BBLK = BN / 16, NBLK = ABLK + BBLK;  // 1 KiB blocks per stage
-  constexpr int STAGE = NBLK * 1024;
-  constexpr int LPW = (NBLK + NW - 1) / NW;  // DMA loads per wave per stage (waves >= NBLK % NW: one less)
-  constexpr bool EVEN = (NBLK % NW) == 0;
-  static_assert(R >= 3 && LPW * (R - 1) < 64, "ring depth / vmcnt range");
-  static_assert(R * STAGE <= 160 * 1024, "LDS");
-  static_assert(RB % 2 == 0, "two MFMA halves");
-  static_assert(EPI != EPI_SWIGLU || (CB % 2 == 0), "SwiGLU pairs column blocks");
-
-  __shared__ __attribute__((aligned(1024))) char smem[R * STAGE];
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / WN, wn = wave % WN;
-
-  const int nwg = m_tiles * n_tiles;
-  int pid = blockIdx.x;
-  if ((nwg & 7) == 0) pid = (pid & 7) * (nwg >> 3) + (pid >> 3);
-  const int group = pid / (gm * n_tiles);
-  const int first_m = group * gm;
-  const int gsz = min(m_tiles - first_m, gm);
-  const int in_g = pid - group * gm * n_tiles;
-  const int tm = first_m + in_g % gsz, tn = in_g / gsz;
-  const int m0 = tm * BM;
-  const int n0 = (EPI == EPI_SWIGLU) ? tn * (BN / 2) : tn * BN;
-
-  const uint32_t ldb = (uint32_t)K * 2;
-  const rsrc_t ra = make_rsrc(A + (size_t)m0 * K, (uint32_t)min(M - m0, BM) * ldb);
-  const rsrc_t rw = (EPI == EPI_SWIGLU)
-                        ? make_rsrc(W + (size_t)n0 * K, (uint32_t)(N + min(N - n0, BN / 2)) * ldb)
-                        : make_rsrc(W + (size_t)n0 * K, (uint32_t)min(N - n0, BN) * ldb);
-
-  // ---- DMA: lane fills slot `lane` of a 1 KiB block = row lane / 4 of the
-  // block, physical chunk lane % 4, which holds logical chunk (lane % 4) ^ swz
-  const int lrow = lane >> 2;
-  const int lchunk = (lane & 3) ^ swz64(lrow);
-  const bool full = EVEN || wave < NBLK % NW;  // this wave issues LPW loads per stage (else LPW - 1)
-  uint32_t goff[LPW];
-#pragma unroll
-  for (int j = 0; j < LPW; ++j) {
-    const int blk = wave + j * NW;
-    bool ok = false;
-    uint32_t off = 0;
-    if (blk < ABLK) {
-      const int r = blk * 16 + lrow;
-      ok = (m0 + r) < M;
-      off = (uint32_t)r * ldb;
-    } else if (blk < NBLK) {
-      const int r = (blk - ABLK) * 16 + lrow;
-      if (EPI == EPI_SWIGLU) {
-        const int rr = r < BN / 2 ? r : r - BN / 2;
-        ok = n0 + rr < N;
-        off = (uint32_t)(r < BN / 2 ? rr : N + rr) * ldb;
-      } else {
-        ok = (n0 + r) < N;
-        off = (uint32_t)r * ldb;
-      }
-    }
-    // rows outside the operand keep an out-of-range offset at every stage
-    goff[j] = ok ? off + lchunk * 16 : kOOB;
-  }
-  const int nk = K / 32;  // the host guarantees K % (32 R) == 0
-  // Stage s >= nk (past the end of K) is issued too, with an out-of-range
-  // scalar offset: its loads return zeros into a buffer nobody reads, which
-  // keeps every step identical (no branches, constant wait counts).
-  auto issue = [&](int s, char *buf) {
-    const uint32_t kb = s < nk ? (uint32_t)s * 64 : kOOB;
-#pragma unroll
-    for (int j = 0; j < LPW; ++j) {
-      const int blk = wave + j * NW;
-      if (j < LPW - 1 || full) load_lds16_k(blk < ABLK ? ra : rw, buf + blk * 1024, goff[j], kb);
-    }
-  };
-  // this wave's DMA of a stage is complete once at most P later stages are in flight
-  auto wait_stages = [&](auto Pc) {
-    constexpr int P = decltype(Pc)::value;
-    if (EVEN || full) wait_vmcnt<LPW * P>();
-    else wait_vmcnt<(LPW - 1) * P>();
-  };
-
-  // ---- fragment addresses: row r16 of each 16-row block, chunk g ^ swz
-  const int g = lane >> 4, r16 = lane & 15;
-  const int fch = (g ^ swz64(r16)) * 16;
-  const int aoff = (wm * TM + r16) * 64 + fch;
-  const int boff = (BM + wn * ((EPI == EPI_SWIGLU) ? TN / 2 : TN) + r16) * 64 + fch;
-  auto bblk = [](int j) {  // 1 KiB offset of column block j from boff
-    if (EPI == EPI_SWIGLU) return (j < CB / 2 ? j : (BN / 2) / 16 + j - CB / 2) * 1024;
-    return j * 1024;
-  };
-
-  f32x4 acc[RB][CB];
-#pragma unroll
-  for (int i = 0; i < RB; ++i)
-#pragma unroll
-    for (int j = 0; j < CB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  u32x4 fa0[RB], fb0[CB], fa1[RB], fb1[CB];
-  auto load_frags = [&](const char *sb, u32x4(&af)[RB], u32x4(&bf)[CB]) {
-#pragma unroll
-    for (int i = 0; i < RB; ++i) af[i] = *reinterpret_cast<const u32x4 *>(sb + aoff + i * 1024);
-#pragma unroll
-    for (int j = 0; j < CB; ++j) bf[j] = *reinterpret_cast<const u32x4 *>(sb + boff + bblk(j));
-  };
-  auto mmas = [&](const u32x4(&af)[RB], const u32x4(&bf)[CB], auto I0) {
-    constexpr int i0 = decltype(I0)::value;
-#pragma unroll
-    for (int i = i0; i < i0 + RB / 2; ++i)
-#pragma unroll
-      for (int j = 0; j < CB; ++j) acc[i][j] = mma16<bf16>(af[i], bf[j], acc[i][j]);
-  };
-
-  // prologue: stages 0 .. R-1 in flight, stage 0 in registers
-#pragma unroll
-  for (int st = 0; st < R; ++st) issue(st, smem + st * STAGE);
-  wait_stages(std::integral_constant<int, R - 1>{});
-  barrier_only();
-  load_frags(smem, fa0, fb0);
-  drain_lgkm();
-
-  // step kt: multiply stage kt (register set cur), fetch stage kt+1 (set nxt)
-  // from buffer (kt+1) % R, refill buffer kt % R with stage kt+R
-  auto step = [&](int kt, auto Uc, u32x4(&ca)[RB], u32x4(&cb)[CB], u32x4(&na)[RB], u32x4(&nb)[CB]) {
-    constexpr int u = decltype(Uc)::value;  // kt % R
-    mmas(ca, cb, std::integral_constant<int, 0>{});
-    __builtin_amdgcn_sched_barrier(0);
-    wait_stages(std::integral_constant<int, R - 2>{});
-    wait_lgkm0();
-    barrier_only();
-    issue(kt + R, smem + u * STAGE);
-    load_frags(smem + ((u + 1) % R) * STAGE, na, nb);
-    __builtin_amdgcn_sched_barrier(0);
-    mmas(ca, cb, std::integral_constant<int, RB / 2>{});
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  // unrolled over R steps (R even) so buffer offsets and register sets are
-  // constants; one loop exit keeps the accumulators in registers (the host
-  // guarantees nk % R == 0)
-  static_assert(R % 2 == 0, "register sets alternate with the buffer index");
-  for (int kt0 = 0; kt0 < nk; kt0 += R) {
-    static_for<0, R>([&](auto V) {
-      constexpr int v = decltype(V)::value;
-      if constexpr (v % 2 == 0) step(kt0 + v, std::integral_constant<int, v>{}, fa0, fb0, fa1, fb1);
-      else step(kt0 + v, std::integral_constant<int, v>{}, fa1, fb1, fa0, fb0);
-      return true;
-    });
-  }
-  wait_vmcnt<0>();
-
-  gemm_epilogue<bf16, BM, BN, NW, WM, WN, EPI, R * STAGE>(acc, smem, C, M, N, m0, n0, wave, lane, ColScale{});
-}
-
 // ---------------------------------------------------------------------------
 // FP8 (OCP e4m3) GEMM with row-wise scales (the pages' 8-bit projections,
 // page "Krea 2 技术报告", 训练 › 预训练: row-wise scaling):
@@ -932,16 +735,6 @@ static hipError_t launch_gemm_t(const void *a, const void *w, void *c, int M, in
   return hipGetLastError();
 }
 
-template <int BM, int BN, int R, int WM, int WN, int EPI>
-static hipError_t launch_ring_t(const void *a, const void *w, void *c, int M, int N, int K,
-                                hipStream_t s, int gm) {
-  const int mt = (M + BM - 1) / BM;
-  const int nt = (EPI == EPI_SWIGLU) ? (N + BN / 2 - 1) / (BN / 2) : (N + BN - 1) / BN;
-  hipLaunchKernelGGL((gemm_ring_kernel<BM, BN, R, WM, WN, EPI>), dim3(mt * nt), dim3(WM * WN * 64), 0, s,
-                     (const bf16 *)a, (const bf16 *)w, (bf16 *)c, M, N, K, mt, nt, gm);
-  return hipGetLastError();
-}
-
 // Default configuration of a bf16 product, in units of one round of
 // 256 x 256 tiles over the 256 CUs:
 //  * whole 256 x 256 tiles: ceil(tiles / 256) rounds;
@@ -954,13 +747,13 @@ static hipError_t launch_ring_t(const void *a, const void *w, void *c, int M, in
 //    a round of ~97 us per 4096 of K (measured on the block's shapes).
 //    Needs the partial buffer (segs * tail * 256 KiB).
 GemmChoice gemm_choose(int M, int N, int K, bool swiglu) {
-  GemmChoice ch{8, 0, 1, 0};
+  GemmChoice ch{0, 0, 1, 0};
   const int ncols = swiglu ? 128 : 256;  // output columns per tile
   const long nt = (N + ncols - 1) / ncols;
   const long t256 = (long)((M + 255) / 256) * nt, t192 = (long)((M + 191) / 192) * nt;
   const double r256 = std::ceil(t256 / 256.0), r192 = std::ceil(t192 / 256.0) * 0.85;
   double best = r256;
-  if (r192 < best) { best = r192; ch.variant = 9; }
+  if (r192 < best) { best = r192; ch.variant = 1; }
   const long full = t256 / 256, tail = t256 % 256;
   const int nk = (K + 63) / 64;
   if (full >= 1 && tail > 0) {
@@ -970,14 +763,15 @@ GemmChoice gemm_choose(int M, int N, int K, bool swiglu) {
       const double rsk = full + 1.0 / segs + (5.0 + 0.131 * tail * segs) / round_us;
       if (rsk < best) {
         best = rsk;
-        ch = GemmChoice{8, (int)tail, segs, (size_t)tail * segs * 256 * 256 * sizeof(float)};
+        ch = GemmChoice{0, (int)tail, segs, (size_t)tail * segs * 256 * 256 * sizeof(float)};
       }
     }
   }
   return ch;
 }
 
-// Tile configurations, selectable for tuning (variant < 0: the default).
+// Tile configurations: variant < 0 picks the default plan; 0 / 1 force whole
+// 256 x 256 / 192 x 256 tiles.
 template <int EPI>
 static hipError_t gemm_dispatch(bool f32, int variant, int gm, const void *a, const void *w,
                                 void *c, int M, int N, int K, hipStream_t s, float *part,
@@ -997,28 +791,14 @@ static hipError_t gemm_dispatch(bool f32, int variant, int gm, const void *a, co
       const double tiles = (double)((M + bm - 1) / bm) * ((N + ncols - 1) / ncols);
       return tiles / (std::ceil(tiles / 256.0) * 256.0);
     };
-    variant = ch.sk_tiles > 0 ? ((fill(192) > fill(256) + 0.02) ? 9 : 8) : ch.variant;
-    if (variant == 8) return launch_gemm_t<bf16, 256, 256, 128, 2, 2, 4, EPI, true>(a, w, c, M, N, K, s, gm, 0, 1,
+    variant = ch.sk_tiles > 0 ? ((fill(192) > fill(256) + 0.02) ? 1 : 0) : ch.variant;
+    if (variant == 0) return launch_gemm_t<bf16, 256, 256, 128, 2, 2, 4, EPI, true>(a, w, c, M, N, K, s, gm, 0, 1,
                                                                                    nullptr, cs);
     return launch_gemm_t<bf16, 192, 256, 128, 2, 2, 4, EPI, true>(a, w, c, M, N, K, s, gm, 0, 1, nullptr, cs);
   }
-  if (cs.n > 0) return hipErrorInvalidValue;  // the tuning variants store plainly
-  switch (variant) {
-    case 0: return launch_gemm_t<bf16, 256, 256, 64, 4, 2, 2, EPI>(a, w, c, M, N, K, s, gm);
-    case 1: return launch_gemm_t<bf16, 256, 256, 64, 4, 2, 4, EPI>(a, w, c, M, N, K, s, gm);
-    case 2: return launch_gemm_t<bf16, 256, 256, 128, 2, 2, 4, EPI>(a, w, c, M, N, K, s, gm);
-    case 3: return launch_gemm_t<bf16, 256, 128, 64, 4, 2, 2, EPI>(a, w, c, M, N, K, s, gm);
-    case 4: return launch_gemm_t<bf16, 256, 128, 128, 3, 2, 2, EPI>(a, w, c, M, N, K, s, gm);
-    case 5: return launch_gemm_t<bf16, 128, 128, 128, 4, 2, 2, EPI>(a, w, c, M, N, K, s, gm);
-    case 6: return launch_gemm_t<bf16, 256, 256, 64, 5, 2, 2, EPI>(a, w, c, M, N, K, s, gm);
-    case 7: return launch_gemm_t<bf16, 192, 256, 128, 2, 2, 4, EPI>(a, w, c, M, N, K, s, gm);
-    case 8: return launch_gemm_t<bf16, 256, 256, 128, 2, 2, 4, EPI, true>(a, w, c, M, N, K, s, gm);
-    case 9: return launch_gemm_t<bf16, 192, 256, 128, 2, 2, 4, EPI, true>(a, w, c, M, N, K, s, gm);
-    case 10: return launch_gemm_t<bf16, 256, 256, 128, 2, 2, 2, EPI, true>(a, w, c, M, N, K, s, gm);
-    case 11: return (K % 128) ? launch_gemm_t<bf16, 256, 256, 128, 2, 2, 4, EPI, true>(a, w, c, M, N, K, s, gm) : launch_ring_t<256, 256, 4, 2, 4, EPI>(a, w, c, M, N, K, s, gm);
-    case 12: return (K % 128) ? launch_gemm_t<bf16, 192, 256, 128, 2, 2, 4, EPI, true>(a, w, c, M, N, K, s, gm) : launch_ring_t<192, 256, 4, 2, 4, EPI>(a, w, c, M, N, K, s, gm);
-    case 13: return (K % 128) ? launch_gemm_t<bf16, 256, 256, 128, 2, 2, 4, EPI, true>(a, w, c, M, N, K, s, gm) : launch_ring_t<256, 256, 4, 2, 2, EPI>(a, w, c, M, N, K, s, gm);
-    case 14: return (K % 128) ? launch_gemm_t<bf16, 192, 256, 128, 2, 2, 4, EPI, true>(a, w, c, M, N, K, s, gm) : launch_ring_t<256, 192, 4, 2, 2, EPI>(a, w, c, M, N, K, s, gm);
+  switch (variant) {  // the two whole-tile plans, for tests and tuning
+    case 0: return launch_gemm_t<bf16, 256, 256, 128, 2, 2, 4, EPI, true>(a, w, c, M, N, K, s, gm, 0, 1, nullptr, cs);
+    case 1: return launch_gemm_t<bf16, 192, 256, 128, 2, 2, 4, EPI, true>(a, w, c, M, N, K, s, gm, 0, 1, nullptr, cs);
     default: return hipErrorInvalidValue;
   }
 }

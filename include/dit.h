@@ -291,10 +291,9 @@ dit_status dit_gemm_swiglu(dit_dtype dtype, int32_t m, int32_t f, int32_t k, con
                            const void *w13, void *u, void *stream);
 
 /* The same products with an explicit tile configuration, for tuning and
- * tests: variant 0..14 selects one of the compiled (BM x BN tile, stage
- * depth, wave grid) configurations (11..14: 64-byte stages in a 4-deep LDS
- * ring, used when K % 128 == 0, else the 128-byte two-stage kernel of the
- * same tile); group_m (0 = default, else 1..64) is
+ * tests: variant 0 forces whole 256 x 256 output tiles, 1 whole 192 x 256
+ * tiles (the two whole-tile plans the block chooses from; 2 and above ->
+ * DIT_ERR_UNSUPPORTED); group_m (0 = default, else 1..64) is
  * the number of row tiles walked together so their operands share an L2.
  * Every choice computes the same result up to fp32 summation order.
  * swiglu = 0: C[M, N] = A W^T with W [N, K]; swiglu = 1: as

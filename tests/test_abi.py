@@ -147,10 +147,10 @@ def test_step_argument_checks():
     assert S(L.dit_gemm(1, 16, 16, 16, P + 2, P + G, P + 2 * G, None)) == "DIT_ERR_ALIGN"
     assert S(L.dit_gemm(1, 16, 16, 16, P, P + G, P + 64, None)) == "DIT_ERR_SHAPE"  # C overlaps A
     assert S(L.dit_gemm_swiglu(1, 16, 16, 16, 0, P + G, P + 2 * G, None)) == "DIT_ERR_NULL"
-    assert S(L.dit_gemm_variant(1, 15, 0, 0, 16, 16, 16, P, P + G, P + 2 * G, None)) == "DIT_ERR_UNSUPPORTED"
-    assert S(L.dit_gemm_variant(1, 8, 65, 0, 16, 16, 16, P, P + G, P + 2 * G, None)) == "DIT_ERR_SHAPE"
-    assert S(L.dit_gemm_variant(1, 8, -1, 0, 16, 16, 16, P, P + G, P + 2 * G, None)) == "DIT_ERR_SHAPE"
-    assert S(L.dit_gemm_variant(1, 8, 4, 2, 16, 16, 16, P, P + G, P + 2 * G, None)) == "DIT_ERR_SHAPE"
+    assert S(L.dit_gemm_variant(1, 2, 0, 0, 16, 16, 16, P, P + G, P + 2 * G, None)) == "DIT_ERR_UNSUPPORTED"
+    assert S(L.dit_gemm_variant(1, 0, 65, 0, 16, 16, 16, P, P + G, P + 2 * G, None)) == "DIT_ERR_SHAPE"
+    assert S(L.dit_gemm_variant(1, 0, -1, 0, 16, 16, 16, P, P + G, P + 2 * G, None)) == "DIT_ERR_SHAPE"
+    assert S(L.dit_gemm_variant(1, 0, 4, 2, 16, 16, 16, P, P + G, P + 2 * G, None)) == "DIT_ERR_SHAPE"
     # split-K tail: dtype, tile / segment ranges, workspace size and overlap
     sk = lambda *a: S(L.dit_gemm_splitk(*a))
     assert sk(0, 0, 512, 512, 256, P, P + G, P + 2 * G, 1, 2, P + 3 * G, 1 << 20, None) == "DIT_ERR_UNSUPPORTED"
@@ -207,8 +207,8 @@ def test_gemm_plan_choices():
     assert (dit.gemm_plan(T, D, F)["sk_tiles"], dit.gemm_plan(T, D, F)["segs"]) == (64, 4)
     # B = 1: the O product splits its 32 tail tiles 5 ways (8 would write more partials than it saves)
     assert (dit.gemm_plan(T // 2, D, D)["sk_tiles"], dit.gemm_plan(T // 2, D, D)["segs"]) == (32, 5)
-    assert dit.gemm_plan(T, 10240, D) == {"variant": 8, "sk_tiles": 0, "segs": 1, "part_bytes": 0}
-    assert dit.gemm_plan(T, D, D)["variant"] == 9 and dit.gemm_plan(T, D, D)["sk_tiles"] == 0
+    assert dit.gemm_plan(T, 10240, D) == {"variant": 0, "sk_tiles": 0, "segs": 1, "part_bytes": 0}
+    assert dit.gemm_plan(T, D, D)["variant"] == 1 and dit.gemm_plan(T, D, D)["sk_tiles"] == 0
     for m in (80, 1000, 4608, 9088, 16384):
         for n, k, sw in ((10240, 4096, False), (4096, 11008, False), (11008, 4096, True)):
             p = dit.gemm_plan(m, n, k, swiglu=sw)

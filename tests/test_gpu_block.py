@@ -103,6 +103,37 @@ def test_zero_gates_identity_bitwise(dev):
         np.testing.assert_array_equal(y, r.x.astype(np.float64))
 
 
+@pytest.mark.parametrize("name", ["c0", "c1"])
+def test_gate_logits_far_below_zero_equal_zero_gate1(dev, name):
+    """A block whose gate logits are all far below zero runs its attention
+    branch to exactly zero, so it equals, bitwise, the same block with
+    gate1 = 0.  The logits are driven there through the block's own
+    projection: scale1 = -1 makes h1 = shift1 on every token, and the gate
+    rows of W_qkvg are -sign(h1), so every gate logit is -sum|h1|."""
+    torch, device, dit = dev
+    cfg = datagen.get_config(name).replace(batch=1, n_image=100, n_text=30)
+    r = Run(dev, cfg, strong=True)
+    H, Hk, d, D = cfg.n_heads, cfg.n_kv_heads, cfg.head_dim, cfg.hidden
+    mod = r.mod.copy()
+    mod[0, 1] = -1.0 - r.w.mod_bias[1]  # scale1 = -1 (to within an fp32 ulp)
+    shift1 = mod[0, 0].astype(np.float64) + r.w.mod_bias[0]
+    wq = r.w.w_qkvg.copy()
+    wq[(H + 2 * Hk) * d:] = -np.sign(shift1)[None, :]
+    logit = -np.sum(np.abs(datagen.bf16_round(shift1.astype(np.float32)) if cfg.dtype == "bf16" else shift1))
+    assert logit < -100.0, logit  # sigmoid underflows to exactly 0 in fp32
+    W = dict(r.W)
+    W["w_qkvg"] = device.to_device(wq, cfg.dtype)
+    ya = r.forward(W=W, M=device.to_device(mod, "f32"))
+    mod0 = mod.copy()
+    mod0[0, 2] = -r.w.mod_bias[2]  # m + bias = 0 exactly: gate1 = 0
+    yb = r.forward(W=W, M=device.to_device(mod0, "f32"))
+    np.testing.assert_array_equal(ya, yb)
+    # and the x1 = x shortcut is what the oracle computes too
+    w = datagen.BlockWeights(wq, r.w.w_o, r.w.w_13, r.w.w_2, r.w.mod_bias, r.w.norm1_w, r.w.norm2_w)
+    ref = O.block_forward(r.x, mod0, w, O.OracleConfig.of(cfg))
+    check_block(ya, ref, r.x, cfg.dtype, f"{name} gate logits -> -inf")
+
+
 def test_gqa_equals_mha_with_replicated_kv(dev):
     torch, device, dit = dev
     cfg = datagen.get_config("c1").replace(batch=1, n_image=96, n_text=33, hidden=512, n_heads=4,
@@ -242,3 +273,54 @@ def test_stack_c4_full_size_one_live_block(dev, live):
     rows = sample_rows(cfg.seq_len, 7 + live)
     ref = O.block_forward_rows(x, mod, w, O.OracleConfig.of(cfg), 0, rows)
     check_block(y[0, rows], ref, x[0, rows].astype(np.float64), "bf16", f"c4 live block {live}")
+
+
+@pytest.mark.timeout(900)
+def test_stack_c4_width_60_live_blocks(dev):
+    """The 60-block bf16 forward at the stack's full width (hidden 4096, 32 /
+    8 heads of 128, SwiGLU 11008, W_o and W_2 ~ N(0, 0.02/sqrt(120))) with
+    every block live and its own weights: 4 drawn projection sets, rows
+    rolled per block (datagen.rolled_block_weights), each block's own
+    modulation bias and norm gains.  One sample of 456 image + 64 text
+    tokens (L = 520: eight whole 64-key tiles and a ragged ninth).  Every
+    output and the update are checked against the oracle's stack, which
+    streams the blocks one at a time; this is the error build-up of the
+    fp32 residual stream over 60 live 4096-wide blocks."""
+    import time
+    torch, device, dit = dev
+    cfg = datagen.get_config("c4").replace(n_image=456, n_text=64)
+    n_sets, nb = 4, cfg.n_blocks
+    assert nb == 60
+    t0 = time.time()
+    bases = [datagen.block_weights(cfg, s) for s in range(n_sets)]
+    print(f"drew {n_sets} sets in {time.time() - t0:.1f} s", flush=True)
+    dev_bases = [device.weights_to_device(b, "bf16") for b in bases]
+    blocks = []
+    for i in range(nb):
+        base, k = dev_bases[i % n_sets], i // n_sets
+        mb, n1, n2 = datagen.block_small_weights(cfg, i)
+        blocks.append({name: torch.roll(base[name], datagen.ROLLS[name] * k, dims=0).contiguous()
+                       for name in ("w_qkvg", "w_o", "w_13", "w_2")})
+        blocks[-1].update(mod_bias=device.to_device(mb, "f32"), norm1_w=device.to_device(n1, "f32"),
+                          norm2_w=device.to_device(n2, "f32"))
+    del dev_bases
+    x = datagen.activations(cfg)
+    mod = datagen.block_mod(cfg)
+    c = dit.config_of(cfg)
+    X = device.to_device(x.reshape(cfg.tokens, cfg.hidden), "bf16")
+    Y = torch.empty_like(X)
+    ws = torch.empty(dit.stack_workspace_size(c), dtype=torch.uint8, device="cuda")
+    dit.stack_fwd(c, blocks, X, Y, device.to_device(mod, "f32"), ws)
+    torch.cuda.synchronize()
+    y = device.to_numpy(Y).reshape(x.shape)
+    del blocks, ws
+    torch.cuda.empty_cache()
+    print(f"GPU stack done at {time.time() - t0:.1f} s", flush=True)
+
+    def get(i):
+        if i % 10 == 0:
+            print(f"oracle block {i} at {time.time() - t0:.1f} s", flush=True)
+        return datagen.rolled_block_weights(cfg, i, bases)
+
+    ref = O.stack_forward(x, mod, get, nb, O.OracleConfig.of(cfg))
+    check_block(y, ref, x, "bf16", "stack60 full width, 60 live blocks")

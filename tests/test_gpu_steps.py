@@ -102,6 +102,27 @@ def test_attention(dev, name, B, L):
                       cos_min=0.99999)
 
 
+@pytest.mark.parametrize("name,prescaled", [("c0", False), ("c1", False), ("c1", True)])
+@pytest.mark.parametrize("glogit", [-np.inf, -1e4])
+def test_attention_gate_to_minus_inf_zeroes_the_branch(dev, name, prescaled, glogit):
+    """Gate logits at -inf (or far below zero) make the gated attention
+    output exactly zero, whatever the scores (sigmoid(-inf) = 0; page
+    "Krea 2 技术报告", 架构 › Transformer块: the sigmoid output gate)."""
+    torch, device, dit = dev
+    cfg = small_cfg(name, batch=2, n_image=130, n_text=0)
+    z = datagen.qkvg_activations(cfg).copy()
+    H, Hk, d = cfg.n_heads, cfg.n_kv_heads, cfg.head_dim
+    z[:, (H + 2 * Hk) * d:] = glogit
+    Z = device.to_device(z, cfg.dtype)
+    OG = torch.full((cfg.tokens, H * d), 7.0, dtype=Z.dtype, device="cuda")
+    c = dit.config_of(cfg)
+    ws = torch.empty(dit.workspace_size(c), dtype=torch.uint8, device="cuda")
+    dit.attention_ex(c, Z, OG, ws, prescaled)
+    torch.cuda.synchronize()
+    y = device.to_numpy(OG)
+    assert np.all(y == 0.0), np.max(np.abs(y))
+
+
 def test_attention_one_key_returns_gated_value(dev):
     torch, device, dit = dev
     cfg = small_cfg("c1", batch=3, n_image=1, n_text=0)
@@ -293,7 +314,7 @@ def test_timestep_mod(dev, name, batch):
 
 
 @pytest.mark.parametrize("group_m", [1, 3, 64])
-@pytest.mark.parametrize("variant", [8, 9])
+@pytest.mark.parametrize("variant", [0, 1])
 def test_gemm_tile_grouping(dev, variant, group_m):
     """The L2 grouping width reorders tiles only: ragged M with fewer row
     tiles than one group, and several groups with a partial last one."""
@@ -310,13 +331,13 @@ def test_gemm_tile_grouping(dev, variant, group_m):
                   cos_min=0.99999)
 
 
-@pytest.mark.parametrize("variant", list(range(15)))
+@pytest.mark.parametrize("variant", [0, 1])
 @pytest.mark.parametrize("swiglu", [False, True])
 @pytest.mark.parametrize("k", [328, 384, 64])
-def test_gemm_every_tile_variant(dev, variant, swiglu, k):
-    """Every compiled tile configuration on ragged M and N, with K ragged
-    against the 64-element stage (328), a whole number of stages (384) and
-    a single stage (64)."""
+def test_gemm_whole_tile_variants(dev, variant, swiglu, k):
+    """Both whole-tile plans (256- and 192-row tiles) on ragged M and N, with
+    K ragged against the 64-element stage (328), a whole number of stages
+    (384) and a single stage (64)."""
     torch, device, dit = dev
     m, n = 300, 200 if swiglu else 520
     cfg = datagen.get_config("c1")
@@ -327,25 +348,6 @@ def test_gemm_every_tile_variant(dev, variant, swiglu, k):
     torch.cuda.synchronize()
     ref = O.swiglu_hidden(a, w, n) if swiglu else a.astype(np.float64) @ w.astype(np.float64).T
     assert_parity(device.to_numpy(C), ref, "bf16", f"variant {variant}", maxabs=8e-3, cos_min=0.99999)
-
-
-@pytest.mark.parametrize("k", [128, 384, 1152])
-@pytest.mark.parametrize("variant", [11, 12, 13, 14])
-@pytest.mark.parametrize("swiglu", [False, True])
-def test_gemm_ring_variants(dev, variant, swiglu, k):
-    """The LDS-ring tiles (K a multiple of 128): ragged M and N, K from one
-    ring's worth of stages (every step past the end issues empty loads) to
-    several trips round the ring."""
-    torch, device, dit = dev
-    m, n = 300, 200 if swiglu else 520
-    cfg = datagen.get_config("c1")
-    a, w = datagen.gemm_operands(cfg, m, 2 * n if swiglu else n, k, tag=131 + variant + k)
-    A, W = device.to_device(a, "bf16"), device.to_device(w, "bf16")
-    C = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
-    dit.gemm_variant(variant, A, W, C, swiglu=swiglu)
-    torch.cuda.synchronize()
-    ref = O.swiglu_hidden(a, w, n) if swiglu else a.astype(np.float64) @ w.astype(np.float64).T
-    assert_parity(device.to_numpy(C), ref, "bf16", f"variant {variant} k {k}", maxabs=8e-3, cos_min=0.99999)
 
 
 @pytest.mark.parametrize("swiglu", [False, True])
