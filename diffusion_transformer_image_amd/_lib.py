@@ -27,7 +27,7 @@ EXPORTS = (
     "dit_gated_residual", "dit_status_str", "dit_last_hip_error", "dit_timer_start",
     "dit_timer_stop", "dit_gemm_splitk", "dit_gemm_plan", "dit_block_fwd_ex", "dit_stack_fwd_ex",
     "dit_qk_prologue", "dit_model_workspace_size", "dit_model_velocity", "dit_sample", "dit_quantize_fp8",
-    "dit_gemm_fp8", "dit_quantize_fp8_tensor", "dit_attention_ex",
+    "dit_gemm_fp8", "dit_quantize_fp8_tensor", "dit_attention_ex", "dit_timestep_mod_noalloc",
 )
 
 
@@ -104,6 +104,7 @@ def lib() -> ctypes.CDLL:
                                  ctypes.POINTER(ModelWeights), i32, wp, vp, i32, ctypes.c_float, vp, vp, sz, vp]),
             "dit_stack_fwd": (i32, [cfgp, i32, wp, vp, vp, vp, vp, sz, vp]),
             "dit_timestep_mod": (i32, [cfgp, i32, vp, vp, vp, vp, vp, sz, vp]),
+            "dit_timestep_mod_noalloc": (i32, [cfgp, i32, vp, vp, vp, vp, vp]),
             "dit_modnorm": (i32, [cfgp, vp, i32, vp, vp, vp, vp, i32, vp]),
             "dit_gemm": (i32, [i32, i32, i32, i32, vp, vp, vp, vp]),
             "dit_gemm_swiglu": (i32, [i32, i32, i32, i32, vp, vp, vp, vp]),
@@ -270,6 +271,12 @@ def timestep_mod(cfg: Config, t, w_t1, w_t2, mod_out, ws, t_dim: int = 256, stre
     _check(lib().dit_timestep_mod(ctypes.byref(cfg), t_dim, _ptr(t), _ptr(w_t1), _ptr(w_t2),
                                   _ptr(mod_out), _ptr(ws), nbytes, _stream(stream)),
            "dit_timestep_mod")
+
+
+def timestep_mod_noalloc(cfg: Config, t, w_t1, w_t2, mod_out, t_dim: int = 256, stream=None) -> None:
+    _check(lib().dit_timestep_mod_noalloc(ctypes.byref(cfg), t_dim, _ptr(t), _ptr(w_t1), _ptr(w_t2),
+                                          _ptr(mod_out), _stream(stream)),
+           "dit_timestep_mod_noalloc")
 
 
 def modnorm(cfg: Config, x, h, mod, bias, gain, which: int, stream=None) -> None:

@@ -19,6 +19,39 @@ dit_status hip_fail(hipError_t e) {
   return DIT_ERR_HIP;
 }
 
+// ---------------------------------------------------------------- fixed scratch
+// Scratch of dit_timestep_mod_noalloc: a file-scope device array, one copy
+// per GPU, held until the process ends.  On the host the array's name is
+// only a stand-in symbol, never a device address: host code passes the
+// address hipGetSymbolAddress returns for the current device.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+}  // namespace
+
+static __device__ __align__(256) char scratch[DIT_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+// The current device's copy of `scratch` (looked up once per device).
+dit_status scratch_address(void **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev < 0 || dev >= kMaxDevices) return DIT_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e);
+    if (!p) return hip_fail(hipErrorInvalidSymbol);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DIT_OK;
+}
+
 // ---------------------------------------------------------------- timing hook
 struct Timer {
   std::mutex mu;
@@ -574,6 +607,27 @@ dit_status dit_timestep_mod(const dit_config *cfg, int32_t t_dim, const float *t
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = timed(DIT_K_TMOD, s, [&] {
     return launch_tmod(t, w_t1, w_t2, mod_out, (float *)ws, cfg->batch, cfg->hidden, t_dim, s);
+  });
+  return e == hipSuccess ? DIT_OK : hip_fail(e);
+}
+
+dit_status dit_timestep_mod_noalloc(const dit_config *cfg, int32_t t_dim, const float *t, const float *w_t1,
+                                    const float *w_t2, float *mod_out, void *stream) {
+  dit_status st = check_cfg(cfg);
+  if (st != DIT_OK) return st;
+  if (t_dim < 2 || t_dim > 1024 || (t_dim & 1)) return DIT_ERR_SHAPE;
+  if (!t || !w_t1 || !w_t2 || !mod_out) return DIT_ERR_NULL;
+  if (!aligned(t) || !aligned(w_t1) || !aligned(w_t2) || !aligned(mod_out)) return DIT_ERR_ALIGN;
+  if ((uint64_t)6 * cfg->hidden * cfg->hidden > 0x7FFFFFFFull) return DIT_ERR_UNSUPPORTED;
+  // the hidden activations [B, D] fp32 live in the fixed scratch
+  if ((uint64_t)cfg->batch * cfg->hidden * 4 > DIT_NOALLOC_SCRATCH_BYTES) return DIT_ERR_WORKSPACE;
+  void *zs = nullptr;
+  if ((st = scratch_address(&zs)) != DIT_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  // stage 1 writes every element of zs before stage 2 reads it, so nothing
+  // has to be cleared between calls
+  hipError_t e = timed(DIT_K_TMOD, s, [&] {
+    return launch_tmod(t, w_t1, w_t2, mod_out, (float *)zs, cfg->batch, cfg->hidden, t_dim, s);
   });
   return e == hipSuccess ? DIT_OK : hip_fail(e);
 }

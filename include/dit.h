@@ -268,6 +268,22 @@ dit_status dit_timestep_mod(const dit_config *cfg /* host */, int32_t t_dim, con
                             const float *w_t1, const float *w_t2, float *mod_out, void *ws,
                             size_t ws_bytes, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * dit_timestep_mod without the workspace argument.  Same kernels, same
+ * result as dit_timestep_mod; the hidden activations [B, D] fp32 go to a
+ * fixed scratch array of DIT_NOALLOC_SCRATCH_BYTES that the library holds
+ * on each GPU it runs on until the process ends (looked up on the current
+ * device at the first call there; the stream must belong to the current
+ * device).  Nothing is allocated or freed.  B * hidden * 4 bytes must fit
+ * the scratch (else DIT_ERR_WORKSPACE: e.g. B <= 128 at hidden 4096).
+ * Every call on one GPU shares that GPU's scratch, which keeps the last
+ * call's contents (each call writes all it reads): calls that overlap in
+ * time on one GPU, on any streams, race. */
+#define DIT_NOALLOC_SCRATCH_BYTES (2u << 20)
+dit_status dit_timestep_mod_noalloc(const dit_config *cfg /* host */, int32_t t_dim, const float *t,
+                                    const float *w_t1, const float *w_t2, float *mod_out, void *stream);
+
 /* ---- the individual steps of the block (same kernels dit_block_fwd runs) */
 
 /* Modulated zero-centred RMSNorm over rows of x [T, D] (page
