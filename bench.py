@@ -61,7 +61,7 @@ def bytes_per_token(cfg) -> dict:
 
 
 def src_hash(name: str) -> str:
-    from bench_traffic import code_hash
+    from bench_counters import code_hash
     return code_hash(os.path.join(ROOT, "diffusion_transformer_image_amd", "csrc", name))
 
 
