@@ -253,9 +253,15 @@ dit_status run_block(const dit_config *c, const dit_prologue *pro, const dit_blo
   const bool pre = !f32;
   const float qsc = pre ? attn_score_scale(c->head_dim) : 1.f;
   const bool pro_on = prologue_on(pro);
+  // bf16 with whole 64-key tiles and no K split of the projection: its
+  // epilogue writes the value heads straight into the attention's V^T
+  // layout (no separate transpose pass, and V never reaches the QKVG rows)
+  const int vc0 = (c->n_heads + c->n_kv_heads) * c->head_dim;
+  const GemmVt gvt{ws.vt, vc0, vc0 + c->n_kv_heads * c->head_dim, L};
+  const bool vt_by_gemm = !f32 && L % 64 == 0 && gemm_choose(T, (int)d.nqkvg, D, false).sk_tiles == 0;
   DIT_TRY(timed(DIT_K_GEMM_QKVG, s, [&] {
     return launch_gemm(f32, ws.h, w->w_qkvg, ws.qkvg, T, (int)d.nqkvg, D, s, -1, 0, ws.part, ws.part_bytes,
-                       pre && !pro_on ? (int)d.hd : 0, qsc);
+                       pre && !pro_on ? (int)d.hd : 0, qsc, vt_by_gemm ? &gvt : nullptr);
   }));
   if (pro_on) {
     DIT_TRY(timed(DIT_K_PROLOGUE, s, [&] {
@@ -266,7 +272,7 @@ dit_status run_block(const dit_config *c, const dit_prologue *pro, const dit_blo
   }
   DIT_TRY(timed(DIT_K_ATTN, s, [&] {
     return launch_attention(f32, c->head_dim, ws.qkvg, ws.vt, ws.og, c->batch, L, c->n_heads, c->n_kv_heads, s,
-                            pre);
+                            pre, vt_by_gemm);
   }));
   DIT_TRY(timed(DIT_K_GEMM_O, s, [&] {
     return launch_gemm(f32, ws.og, w->w_o, ws.br, T, D, (int)d.hd, s, -1, 0, ws.part, ws.part_bytes);

@@ -472,13 +472,15 @@ static void launch_attn_q(const T *q, const T *v, T *og, int B, int L, int H, in
 
 template <typename T, int HD, bool PRE>
 static hipError_t launch_attn_t(const void *qkvg, void *vt, void *og, int B, int L, int H, int Hkv,
-                                hipStream_t s) {
+                                hipStream_t s, bool vt_ready) {
   const int group = H / Hkv;
   if (group != 1 && group != 2 && group != 4) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((vtrans_kernel<T, HD>), dim3(att_lpad(L) / ATT_BK, Hkv, B), dim3(256), 0, s,
-                     (const T *)qkvg, (T *)vt, L, H, Hkv);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (!vt_ready) {
+    hipLaunchKernelGGL((vtrans_kernel<T, HD>), dim3(att_lpad(L) / ATT_BK, Hkv, B), dim3(256), 0, s,
+                       (const T *)qkvg, (T *)vt, L, H, Hkv);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   // softmax in base 2 with the score scale in one FMA (PRE: in the queries)
   const float sc = attn_score_scale(HD);
   const auto *q = (const T *)qkvg;
@@ -495,14 +497,15 @@ static hipError_t launch_attn_t(const void *qkvg, void *vt, void *og, int B, int
 }
 
 hipError_t launch_attention(bool f32, int head_dim, const void *qkvg, void *vt, void *og, int B,
-                            int L, int H, int Hkv, hipStream_t s, bool q_prescaled) {
+                            int L, int H, int Hkv, hipStream_t s, bool q_prescaled, bool vt_ready) {
+  if (vt_ready && (f32 || L % ATT_BK)) return hipErrorInvalidValue;  // V^T by the projection: whole key tiles
   if (f32) {
     if (q_prescaled) return hipErrorInvalidValue;
-    if (head_dim == 64) return launch_attn_t<float, 64, false>(qkvg, vt, og, B, L, H, Hkv, s);
-    if (head_dim == 128) return launch_attn_t<float, 128, false>(qkvg, vt, og, B, L, H, Hkv, s);
+    if (head_dim == 64) return launch_attn_t<float, 64, false>(qkvg, vt, og, B, L, H, Hkv, s, false);
+    if (head_dim == 128) return launch_attn_t<float, 128, false>(qkvg, vt, og, B, L, H, Hkv, s, false);
   } else if (head_dim == 128) {
-    if (q_prescaled) return launch_attn_t<bf16, 128, true>(qkvg, vt, og, B, L, H, Hkv, s);
-    return launch_attn_t<bf16, 128, false>(qkvg, vt, og, B, L, H, Hkv, s);
+    if (q_prescaled) return launch_attn_t<bf16, 128, true>(qkvg, vt, og, B, L, H, Hkv, s, vt_ready);
+    return launch_attn_t<bf16, 128, false>(qkvg, vt, og, B, L, H, Hkv, s, vt_ready);
   }
   return hipErrorInvalidValue;
 }

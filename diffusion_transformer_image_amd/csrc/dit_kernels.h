@@ -35,9 +35,18 @@ hipError_t launch_unpatchify_axpy(bool f32, const void *vtok, const float *z, fl
 // (row tiles per L2 group).  part (fp32, part_bytes) lets the default
 // configuration split the tail tiles along K.  Columns [0, scale_cols) of C
 // are multiplied by col_scale before rounding.
+// Value heads of a QKVG product written transposed for the attention
+// kernel (bf16 only, seq_len L % 64 == 0, M a multiple of L): columns [c0,
+// c1) of C go to vt ([B][Hkv][d][L], the layout of the V^T pass) instead of
+// to C.
+struct GemmVt {
+  void *vt;
+  int c0, c1, L;
+};
 hipError_t launch_gemm(bool f32, const void *a, const void *w, void *c, int M, int N, int K,
                        hipStream_t s, int variant = -1, int group_m = 0, float *part = nullptr,
-                       size_t part_bytes = 0, int scale_cols = 0, float col_scale = 1.f);
+                       size_t part_bytes = 0, int scale_cols = 0, float col_scale = 1.f,
+                       const GemmVt *vt = nullptr);
 hipError_t launch_gemm_swiglu(bool f32, const void *a, const void *w13, void *u, int M, int F,
                               int K, hipStream_t s, int variant = -1, int group_m = 0,
                               float *part = nullptr, size_t part_bytes = 0);
@@ -60,8 +69,11 @@ size_t attention_vt_bytes(bool f32, int B, int L, int Hkv, int head_dim);
 inline float attn_score_scale(int head_dim) { return 1.4426950408889634f / sqrtf((float)head_dim); }
 // q_prescaled (bf16 only): the query heads of qkvg already carry the factor
 // attn_score_scale(head_dim), applied before their rounding to bf16.
+// vt_ready: vt already holds V^T (written by the QKVG product's epilogue),
+// so the V^T pass is skipped.
 hipError_t launch_attention(bool f32, int head_dim, const void *qkvg, void *vt, void *og, int B,
-                            int L, int H, int Hkv, hipStream_t s, bool q_prescaled = false);
+                            int L, int H, int Hkv, hipStream_t s, bool q_prescaled = false,
+                            bool vt_ready = false);
 
 // QKNorm and 3D axial RoPE in place on the Q and K heads of qkvg rows; the
 // query heads are multiplied by q_scale before they are rounded (1: none)

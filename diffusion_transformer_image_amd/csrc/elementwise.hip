@@ -44,15 +44,20 @@ __device__ __forceinline__ void load8f(const float *p, float (&v)[8]) { Vec8<flo
 // ----------------------------------------------------------------- layout
 // Every elementwise kernel runs one workgroup per (sample b, 8 token rows):
 // the per-sample modulation vectors it needs (combined with the block bias
-// and the norm gain) are computed once into LDS, then each of the 4 waves
-// streams 2 rows, one row per wave at a time, 8 elements per lane-chunk;
-// the first row's loads go out before the staging and the second row's
-// before the first is computed.  8 rows rather than 16 give twice the
-// workgroups (about 4.5 waves per SIMD at 1024 px instead of 2.25), which
-// the memory latency needs: 1024 px modnorm 41 -> 37.6 us, the residual
-// kernels 80 -> 72 us each, the 60-block stack 115.0 -> 113.5 ms.
+// and the norm gain) are computed once into LDS, then each of the 8 waves
+// streams one row, 8 elements per lane-chunk, its loads issued before the
+// staging.  Timed one launch at a time after a 640 MB read that evicts the
+// last-level cache (1024 px, B = 2): 8 waves of one row each against 4
+// waves of two rows: modnorm 33.7 -> 31.8 us, residual + norm 73.5 -> 72.2
+// us, the stack's residual-and-next-norm pass 49.8 -> 47.7 us, the plain
+// residual unchanged (54 us); a plain copy of modnorm's bytes takes 25 us
+// (6.0 TB/s).  Fewer rows per wave or more rows per workgroup were slower.
 constexpr int EW_ROWS = 8;  // rows per workgroup
-constexpr int EW_WAVES = 4;
+constexpr int EW_WAVES = 8;
+// the plain residual walks its rows flat; 4 rows on 4 waves measured best
+// there (51 us against 54 us with 8 on 8)
+constexpr int RES_ROWS = 4;
+constexpr int RES_WAVES = 4;
 
 __device__ __forceinline__ void lds8(const float *p, float (&v)[8]) {
   const f32x4 a = *reinterpret_cast<const f32x4 *>(p);
@@ -117,7 +122,7 @@ __device__ __forceinline__ void stage_gate_vector(float *G, const float *mod, co
 // h = x * rsqrt(mean(x^2) + eps) * A + S; the row stays in registers
 // (NCH chunks of 8 per lane) between the sum of squares and the output.
 template <typename Tx, typename Th, int NCH>
-__global__ __launch_bounds__(256) void modnorm_kernel(const Tx *__restrict__ x, Th *__restrict__ h,
+__global__ __launch_bounds__(EW_WAVES * 64) void modnorm_kernel(const Tx *__restrict__ x, Th *__restrict__ h,
                                                       const float *__restrict__ mod,
                                                       const float *__restrict__ bias,
                                                       const float *__restrict__ gain, int seq_len, int D,
@@ -180,7 +185,7 @@ static hipError_t launch_modnorm_t(const void *x, void *h, const float *mod, con
                                    const float *gain, int rows, int seq_len, int D, float eps,
                                    int which, hipStream_t s) {
   const int B = rows / seq_len;
-  dim3 grid((seq_len + EW_ROWS - 1) / EW_ROWS, B), block(256);
+  dim3 grid((seq_len + EW_ROWS - 1) / EW_ROWS, B), block(EW_WAVES * 64);
   const size_t lds = 2 * (size_t)D * sizeof(float);
 #define DIT_MN(N)                                                                                  \
   hipLaunchKernelGGL((modnorm_kernel<Tx, Th, N>), grid, block, lds, s, (const Tx *)x, (Th *)h, mod, \
@@ -209,7 +214,7 @@ hipError_t launch_modnorm(bool x_f32, bool h_f32, const void *x, void *h, const 
 // ----------------------------------------------------------------- residual
 // out = x + G * y, G the gate of residual `which`.
 template <typename Tx, typename Ty, typename To>
-__global__ __launch_bounds__(256) void resid_kernel(const Tx *__restrict__ x, const Ty *__restrict__ y,
+__global__ __launch_bounds__(RES_WAVES * 64) void resid_kernel(const Tx *__restrict__ x, const Ty *__restrict__ y,
                                                     To *__restrict__ out, const float *__restrict__ mod,
                                                     const float *__restrict__ bias, int seq_len, int D,
                                                     int which) {
@@ -217,8 +222,8 @@ __global__ __launch_bounds__(256) void resid_kernel(const Tx *__restrict__ x, co
   float *G = ew_lds;
   const int b = blockIdx.y;
   const int nch = D >> 3;
-  const int l0 = blockIdx.x * EW_ROWS;
-  const int nrows = min(EW_ROWS, seq_len - l0);
+  const int l0 = blockIdx.x * RES_ROWS;
+  const int nrows = min(RES_ROWS, seq_len - l0);
   const int n = nrows * nch;
   // flat walk over (row, chunk) of this workgroup's rows, fully coalesced,
   // UR chunks per thread at a time with all their loads issued first (the
@@ -270,8 +275,8 @@ static hipError_t launch_resid_t(const void *x, const void *y, void *out, const 
                                  const float *bias, int rows, int seq_len, int D, int which,
                                  hipStream_t s) {
   const int B = rows / seq_len;
-  dim3 grid((seq_len + EW_ROWS - 1) / EW_ROWS, B);
-  hipLaunchKernelGGL((resid_kernel<Tx, Ty, To>), grid, dim3(256), (size_t)D * sizeof(float), s,
+  dim3 grid((seq_len + RES_ROWS - 1) / RES_ROWS, B);
+  hipLaunchKernelGGL((resid_kernel<Tx, Ty, To>), grid, dim3(RES_WAVES * 64), (size_t)D * sizeof(float), s,
                      (const Tx *)x, (const Ty *)y, (To *)out, mod, bias, seq_len, D, which);
   return hipGetLastError();
 }
@@ -299,7 +304,7 @@ hipError_t launch_resid(bool x_f32, bool y_f32, bool out_f32, const void *x, con
 // residual of one block and the first norm of the next (each its own
 // block's bias).  Saves writing x1 and reading it back between two passes.
 template <typename Tx, typename Ty, typename Th, int NCH>
-__global__ __launch_bounds__(256) void resid_modnorm_kernel(const Tx *__restrict__ x, const Ty *__restrict__ y,
+__global__ __launch_bounds__(EW_WAVES * 64) void resid_modnorm_kernel(const Tx *__restrict__ x, const Ty *__restrict__ y,
                                                             float *__restrict__ x1, Th *__restrict__ h,
                                                             const float *__restrict__ mod,
                                                             const float *__restrict__ gbias, int gw,
@@ -374,7 +379,7 @@ static hipError_t launch_resid_modnorm_t(const void *x, const void *y, float *x1
                                          const float *gbias, int gw, const float *nbias, const float *ngain,
                                          int nw, int rows, int seq_len, int D, float eps, hipStream_t s) {
   const int B = rows / seq_len;
-  dim3 grid((seq_len + EW_ROWS - 1) / EW_ROWS, B), block(256);
+  dim3 grid((seq_len + EW_ROWS - 1) / EW_ROWS, B), block(EW_WAVES * 64);
   const size_t lds = 3 * (size_t)D * sizeof(float);
 #define DIT_RMN(N)                                                                                   \
   hipLaunchKernelGGL((resid_modnorm_kernel<Tx, Ty, Th, N>), grid, block, lds, s, (const Tx *)x,     \

@@ -63,11 +63,55 @@ struct SkPlan {
 // rounding to the output type (the attention score scale folded into the
 // query columns of the QKVG product); n = 0: plain store.  Applies to the
 // store epilogue only.
+//
+// vt != nullptr (bf16 store epilogue, whole tiles, no K split): output
+// columns [vc0, vc1) -- the value heads of the QKVG product -- are written
+// to vt in the transposed, key-permuted layout the attention kernel reads
+// ([B][Hkv][d][L], see attention.hip: key k of a 64-key tile goes to chunk
+// ((k >> 5) * 4 + ((k >> 2) & 3)) ^ (dd & 7), element ((k >> 4) & 1) * 4 +
+// (k & 3)) instead of to C.  Needs L % 64 == 0, so every 32-row pair of
+// 16-row blocks of a tile lies inside one sample and one half of a key
+// tile: a lane then holds, for its column, keys 4g..4g+3 of both 16-key
+// blocks of a chunk -- one 16-byte store.
 struct ColScale {
   int n = 0;
   float scale = 1.f;
+  bf16 *vt = nullptr;
+  int vc0 = 0, vc1 = 0, L = 0;
   __device__ __forceinline__ float apply(int col, float v) const { return col < n ? v * scale : v; }
+  __device__ __forceinline__ bool to_vt(int col) const { return vt && col >= vc0 && col < vc1; }
 };
+
+// The value columns of a wave's TM x TN sub-tile (rows row0.., columns
+// col0..) into the V^T layout described at ColScale.
+template <int TM, int TN>
+__device__ __forceinline__ void store_vt(const f32x4 (&acc)[TM / 16][TN / 16], const ColScale &cs, int M,
+                                         int row0, int col0, int lane) {
+  constexpr int RB = TM / 16, CB = TN / 16;
+  static_assert(RB % 2 == 0, "pairs of 16-row blocks");
+  const int g = lane >> 4, r16 = lane & 15;
+#pragma unroll
+  for (int j = 0; j < CB; ++j) {
+    const int col = col0 + j * 16 + r16;
+    if (!cs.to_vt(col)) continue;
+    const int cv = col - cs.vc0;
+#pragma unroll
+    for (int p = 0; p < RB / 2; ++p) {
+      const int rb = row0 + 2 * p * 16;  // first row of the pair (a multiple of 32 inside its sample)
+      if (rb >= M) continue;
+      const int b = rb / cs.L, l = rb - b * cs.L;
+      const int phys = ((((l >> 5) & 1) * 4) + g) ^ (cv & 7);
+      bf16x8 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[e] = (bf16)acc[2 * p][j][e];
+        v[4 + e] = (bf16)acc[2 * p + 1][j][e];
+      }
+      *reinterpret_cast<u32x4 *>(cs.vt + ((size_t)b * (cs.vc1 - cs.vc0) + cv) * cs.L + (l & ~63) + phys * 8) =
+          __builtin_bit_cast(u32x4, v);
+    }
+  }
+}
 
 // Linear tile id -> (row tile, column tile): walks gm row tiles at a time,
 // column-major inside a group, so tiles sharing operands run together.
@@ -88,10 +132,12 @@ __device__ __forceinline__ void gemm_store_direct(const f32x4 (&acc)[TM / 16][TN
                                                   const ColScale &cs) {
   constexpr int RB = TM / 16, CB = TN / 16;
   const int g = lane >> 4, r16 = lane & 15;
+  if constexpr (EPI == EPI_STORE && is_bf16<T>::value)
+    if (cs.vt) store_vt<TM, TN>(acc, cs, M, row0, col0, lane);
 #pragma unroll
   for (int j = 0; j < CB / ((EPI == EPI_SWIGLU) ? 2 : 1); ++j) {
     const int col = col0 + j * 16 + r16;
-    if (col >= N) continue;
+    if (col >= N || (EPI == EPI_STORE && cs.to_vt(col))) continue;
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
 #pragma unroll
@@ -135,6 +181,8 @@ __device__ __forceinline__ void gemm_epilogue(const f32x4 (&acc)[BM / WM / 16][B
     // PITCH contiguous bytes: every store instruction covers whole cache
     // lines (a wave's own sub-tile row is only 64 bytes for the SwiGLU
     // tile, half a line, which costs the L2 a merge per line).
+    if constexpr (EPI == EPI_STORE)
+      if (cs.vt) store_vt<TM, TN>(acc, cs, M, row0, col0, lane);
     __syncthreads();  // all waves are done reading the operand stages
 #pragma unroll
     for (int j = 0; j < CB / ((EPI == EPI_SWIGLU) ? 2 : 1); ++j) {
@@ -156,7 +204,7 @@ __device__ __forceinline__ void gemm_epilogue(const f32x4 (&acc)[BM / WM / 16][B
       const int row = wave * RPW + q / CPRO, c = q % CPRO;
       const u32x4 v = *reinterpret_cast<const u32x4 *>(smem + row * PITCH + ((c ^ (row & (CPRO - 1))) << 4));
       const int gr = m0 + row, gc = n0 + c * 8;
-      if (gr < M) {
+      if (gr < M && (EPI != EPI_STORE || !cs.to_vt(gc))) {  // value columns went to V^T
         T *dst = C + (size_t)gr * N + gc;
         if (gc + 8 <= N && (N & 7) == 0) {
           *reinterpret_cast<u32x4 *>(dst) = v;
@@ -805,9 +853,18 @@ static hipError_t gemm_dispatch(bool f32, int variant, int gm, const void *a, co
 
 hipError_t launch_gemm(bool f32, const void *a, const void *w, void *c, int M, int N, int K,
                        hipStream_t s, int variant, int group_m, float *part, size_t part_bytes, int scale_cols,
-                       float col_scale) {
-  return gemm_dispatch<EPI_STORE>(f32, variant, group_m, a, w, c, M, N, K, s, part, part_bytes,
-                                  ColScale{scale_cols, col_scale});
+                       float col_scale, const GemmVt *vt) {
+  ColScale cs{scale_cols, col_scale};
+  if (vt) {
+    if (f32 || vt->L <= 0 || vt->L % 64 || M % vt->L || vt->c0 % 16 || vt->c1 % 16 || vt->c0 < 0 ||
+        vt->c1 <= vt->c0 || vt->c1 > N)
+      return hipErrorInvalidValue;
+    cs.vt = (bf16 *)vt->vt;
+    cs.vc0 = vt->c0;
+    cs.vc1 = vt->c1;
+    cs.L = vt->L;
+  }
+  return gemm_dispatch<EPI_STORE>(f32, variant, group_m, a, w, c, M, N, K, s, part, part_bytes, cs);
 }
 
 hipError_t launch_gemm_swiglu(bool f32, const void *a, const void *w13, void *u, int M, int F,

@@ -91,6 +91,29 @@ def test_block_bf16_small_full_output(dev):
         check_block(y, ref, r.x, "bf16", f"small bf16 strong={strong}")
 
 
+@pytest.mark.parametrize("batch,n_image,n_text,hidden,heads,kv", [
+    (2, 100, 28, 512, 4, 1),     # L = 128: a QKVG column tile holds K and V heads side by side
+    (3, 130, 62, 1024, 8, 2),    # L = 192, a ragged last row tile of the projection
+    (1, 4032, 64, 1024, 8, 4),   # L = 4096, one sample, 2 query heads per KV head
+])
+def test_block_bf16_value_heads_from_projection(dev, batch, n_image, n_text, hidden, heads, kv):
+    """With L a multiple of 64 the QKVG product writes the value heads
+    straight into the attention's transposed V layout (no V^T pass); every
+    output of the block against the oracle (the 1024-key case sampled)."""
+    cfg = datagen.get_config("c1").replace(batch=batch, n_image=n_image, n_text=n_text, hidden=hidden,
+                                            n_heads=heads, n_kv_heads=kv, ffn=1368)
+    assert cfg.seq_len % 64 == 0
+    r = Run(dev, cfg, strong=True)
+    y = r.forward()
+    oc = O.OracleConfig.of(cfg)
+    if cfg.seq_len <= 256:
+        check_block(y, O.block_forward(r.x, r.mod, r.w, oc), r.x, "bf16", f"V^T by projection L={cfg.seq_len}")
+    else:
+        rows = sample_rows(cfg.seq_len, 3)
+        ref = O.block_forward_rows(r.x, r.mod, r.w, oc, 0, rows)
+        check_block(y[0, rows], ref, r.x[0, rows].astype(np.float64), "bf16", f"V^T by projection L={cfg.seq_len}")
+
+
 def test_zero_gates_identity_bitwise(dev):
     for name in ("c0", "c1"):
         cfg = datagen.get_config(name).replace(batch=2, n_image=100, n_text=20)
