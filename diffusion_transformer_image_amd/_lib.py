@@ -19,7 +19,7 @@ DIT_F32, DIT_BF16 = 0, 1
 STATUS = {0: "DIT_OK", 1: "DIT_ERR_NULL", 2: "DIT_ERR_SHAPE", 3: "DIT_ERR_UNSUPPORTED",
           4: "DIT_ERR_ALIGN", 5: "DIT_ERR_WORKSPACE", 6: "DIT_ERR_DTYPE", 7: "DIT_ERR_HIP"}
 KERNEL_KINDS = {"modnorm": 0, "gemm_qkvg": 1, "attn": 2, "gemm_o": 3, "resid": 4,
-                "gemm_w13": 5, "gemm_w2": 6, "tmod": 7, "prologue": 8}
+                "gemm_w13": 5, "gemm_w2": 6, "tmod": 7, "prologue": 8, "quant": 9}
 
 EXPORTS = (
     "dit_workspace_size", "dit_stack_workspace_size", "dit_block_fwd", "dit_stack_fwd",
@@ -28,6 +28,7 @@ EXPORTS = (
     "dit_timer_stop", "dit_gemm_splitk", "dit_gemm_plan", "dit_block_fwd_ex", "dit_stack_fwd_ex",
     "dit_qk_prologue", "dit_model_workspace_size", "dit_model_velocity", "dit_sample", "dit_quantize_fp8",
     "dit_gemm_fp8", "dit_quantize_fp8_tensor", "dit_attention_ex", "dit_timestep_mod_noalloc",
+    "dit_workspace_size_fp8", "dit_block_fwd_fp8",
 )
 
 
@@ -53,6 +54,13 @@ class BlockWeights(ctypes.Structure):
                 ("w_2", ctypes.c_void_p), ("mod_bias", ctypes.c_void_p),
                 ("norm1_w", ctypes.c_void_p), ("norm2_w", ctypes.c_void_p),
                 ("q_norm_w", ctypes.c_void_p), ("k_norm_w", ctypes.c_void_p)]
+
+
+class BlockWeightsFp8(ctypes.Structure):
+    _fields_ = [("w_qkvg", ctypes.c_void_p), ("w_o", ctypes.c_void_p), ("w_13", ctypes.c_void_p),
+                ("w_2", ctypes.c_void_p), ("s_qkvg", ctypes.c_void_p), ("s_o", ctypes.c_void_p),
+                ("s_13", ctypes.c_void_p), ("s_2", ctypes.c_void_p), ("mod_bias", ctypes.c_void_p),
+                ("norm1_w", ctypes.c_void_p), ("norm2_w", ctypes.c_void_p)]
 
 
 class ModelConfig(ctypes.Structure):
@@ -88,6 +96,8 @@ def lib() -> ctypes.CDLL:
         wp = ctypes.POINTER(BlockWeights)
         sig = {
             "dit_workspace_size": (sz, [cfgp]),
+            "dit_workspace_size_fp8": (sz, [cfgp]),
+            "dit_block_fwd_fp8": (i32, [cfgp, ctypes.POINTER(BlockWeightsFp8), vp, vp, vp, vp, sz, vp]),
             "dit_stack_workspace_size": (sz, [cfgp]),
             "dit_block_fwd": (i32, [cfgp, wp, vp, vp, vp, vp, sz, vp]),
             "dit_block_fwd_ex": (i32, [cfgp, ctypes.POINTER(Prologue), wp, vp, vp, vp, vp, sz, vp]),
@@ -199,6 +209,25 @@ def block_fwd(cfg: Config, w: Mapping, x_in, x_out, mod, ws, stream=None) -> Non
     nbytes = ws.numel() * ws.element_size() if hasattr(ws, "numel") else 0
     _check(lib().dit_block_fwd(ctypes.byref(cfg), ctypes.byref(bw), _ptr(x_in), _ptr(x_out),
                                _ptr(mod), _ptr(ws), nbytes, _stream(stream)), "dit_block_fwd")
+
+
+def workspace_size_fp8(cfg: Config) -> int:
+    return lib().dit_workspace_size_fp8(ctypes.byref(cfg))
+
+
+def make_weights_fp8(w: Mapping) -> BlockWeightsFp8:
+    return BlockWeightsFp8(*[_ptr(w.get(k)) for k in ("w_qkvg", "w_o", "w_13", "w_2", "s_qkvg", "s_o", "s_13", "s_2",
+                                                       "mod_bias", "norm1_w", "norm2_w")])
+
+
+def block_fwd_fp8(cfg: Config, w: Mapping, x_in, x_out, mod, ws, stream=None) -> None:
+    """The 8-bit block: w holds the e4m3 codes (w_qkvg, w_o, w_13, w_2, uint8)
+    and their row scales (s_qkvg, s_o, s_13, s_2), plus mod_bias, norm1_w,
+    norm2_w as for block_fwd."""
+    bw = make_weights_fp8(w)
+    nbytes = ws.numel() * ws.element_size() if hasattr(ws, "numel") else 0
+    _check(lib().dit_block_fwd_fp8(ctypes.byref(cfg), ctypes.byref(bw), _ptr(x_in), _ptr(x_out), _ptr(mod),
+                                   _ptr(ws), nbytes, _stream(stream)), "dit_block_fwd_fp8")
 
 
 def block_fwd_ex(cfg: Config, pro: Prologue | None, w: Mapping, x_in, x_out, mod, ws, stream=None) -> None:

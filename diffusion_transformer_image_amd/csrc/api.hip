@@ -176,6 +176,77 @@ BlockWs carve(const dit_config *c, void *ws) {
   return w;
 }
 
+// Workspace of the 8-bit block: the bf16 block's buffers but h (QKVG / U,
+// Og, the branch output, x1, V^T; its K-split partials sized for the 8-bit
+// products) plus the codes of one activation matrix [T, max(D, H*d, F)]
+// bytes and its row scales [T] (the norms write their codes there).
+struct Fp8Ws {
+  BlockWs b;
+  uint8_t *codes;
+  float *scales;
+  size_t bytes;
+};
+Fp8Ws carve_fp8(const dit_config *c, void *ws) {
+  const Dims d = dims(c);
+  Fp8Ws w;
+  char *p = (char *)ws;
+  size_t off = 0;
+  auto take = [&](size_t n) {
+    char *r = p ? p + off : nullptr;
+    off += round_up(n);
+    return r;
+  };
+  w.b.h = nullptr;
+  w.b.qkvg = take(d.T * (d.nqkvg > d.F ? d.nqkvg : d.F) * d.es);
+  w.b.og = take(d.T * d.hd * d.es);
+  w.b.br = take(d.T * d.D * d.es);
+  w.b.x1 = take(d.T * d.D * 4);
+  w.b.vt = take(attention_vt_bytes(false, c->batch, c->seq_len, c->n_kv_heads, c->head_dim));
+  const int T = (int)d.T, D = (int)d.D, F = (int)d.F, hd = (int)d.hd, nq = (int)d.nqkvg;
+  size_t pb = gemm_choose_fp8(T, nq, D, false).part_bytes;
+  pb = std::max(pb, gemm_choose_fp8(T, D, hd, false).part_bytes);
+  pb = std::max(pb, gemm_choose_fp8(T, F, D, true).part_bytes);
+  pb = std::max(pb, gemm_choose_fp8(T, D, F, false).part_bytes);
+  w.b.part_bytes = pb;
+  w.b.part = (float *)take(pb);
+  w.codes = (uint8_t *)take(d.T * std::max(std::max(d.D, d.hd), d.F));
+  w.scales = (float *)take(d.T * 4);
+  const size_t tmod = (size_t)c->batch * c->hidden * 4;
+  w.bytes = off > tmod ? off : tmod;
+  w.b.bytes = w.bytes;
+  return w;
+}
+
+dit_status check_cfg_fp8(const dit_config *c) {
+  dit_status st = check_cfg(c);
+  if (st != DIT_OK) return st;
+  if (c->dtype != DIT_BF16) return DIT_ERR_DTYPE;
+  if (c->hidden % 16 || (c->n_heads * c->head_dim) % 16 || c->ffn % 16) return DIT_ERR_UNSUPPORTED;
+  // the 8-bit operands go through 32-bit buffer descriptors too
+  if ((2ull * c->ffn + 256) * c->hidden > kMaxSpan) return DIT_ERR_UNSUPPORTED;
+  return DIT_OK;
+}
+
+dit_status check_weights_fp8(const dit_config *c, const dit_block_weights_fp8 *w, const void *ws, size_t n) {
+  if (!w) return DIT_ERR_NULL;
+  if (!w->w_qkvg || !w->w_o || !w->w_13 || !w->w_2 || !w->s_qkvg || !w->s_o || !w->s_13 || !w->s_2 ||
+      !w->mod_bias)
+    return DIT_ERR_NULL;
+  if (!aligned(w->w_qkvg) || !aligned(w->w_o) || !aligned(w->w_13) || !aligned(w->w_2) || !aligned(w->s_qkvg) ||
+      !aligned(w->s_o) || !aligned(w->s_13) || !aligned(w->s_2) || !aligned(w->mod_bias) || !aligned(w->norm1_w) ||
+      !aligned(w->norm2_w))
+    return DIT_ERR_ALIGN;
+  const Dims d = dims(c);
+  const size_t D = d.D;
+  if (overlap(ws, n, w->w_qkvg, d.nqkvg * D) || overlap(ws, n, w->w_o, D * d.hd) ||
+      overlap(ws, n, w->w_13, 2 * d.F * D) || overlap(ws, n, w->w_2, D * d.F) ||
+      overlap(ws, n, w->s_qkvg, d.nqkvg * 4) || overlap(ws, n, w->s_o, D * 4) || overlap(ws, n, w->s_13, 2 * d.F * 4) ||
+      overlap(ws, n, w->s_2, D * 4) || overlap(ws, n, w->mod_bias, 6 * D * 4) ||
+      overlap(ws, n, w->norm1_w, w->norm1_w ? D * 4 : 0) || overlap(ws, n, w->norm2_w, w->norm2_w ? D * 4 : 0))
+    return DIT_ERR_SHAPE;
+  return DIT_OK;
+}
+
 dit_status check_weights(const dit_block_weights *w) {
   if (!w) return DIT_ERR_NULL;
   if (!w->w_qkvg || !w->w_o || !w->w_13 || !w->w_2 || !w->mod_bias) return DIT_ERR_NULL;
@@ -300,6 +371,59 @@ dit_status run_block(const dit_config *c, const dit_prologue *pro, const dit_blo
   if (defer_resid2) return DIT_OK;
   DIT_TRY(timed(DIT_K_RESID, s, [&] {
     return launch_resid(x1_f32, f32, xout_f32, x1buf, ws.br, x_out, mod, w->mod_bias, T, L, D, 1, s);
+  }));
+  return DIT_OK;
+}
+
+// The 8-bit block: each product's activation rows quantised to e4m3 (one
+// scale per row) and multiplied with the pre-quantised weight rows.
+dit_status run_block_fp8(const dit_config *c, const dit_block_weights_fp8 *w, const void *x_in, void *x_out,
+                         const float *mod, const Fp8Ws &ws, hipStream_t s) {
+  const Dims d = dims(c);
+  const int T = (int)d.T, D = (int)d.D, L = c->seq_len, F = (int)d.F, hd = (int)d.hd, nq = (int)d.nqkvg;
+  const BlockWs &b = ws.b;
+  auto quant = [&](const void *x, int k) {
+    return timed(DIT_K_QUANT, s, [&] { return launch_quantize_fp8(false, x, ws.codes, ws.scales, T, k, s); });
+  };
+  // the norms hand their rows over as codes quantised from fp32 (no bf16 h)
+  DIT_TRY(timed(DIT_K_MODNORM, s, [&] {
+    return launch_modnorm_fp8(false, x_in, ws.codes, ws.scales, mod, w->mod_bias, w->norm1_w, T, L, D, c->eps, 0,
+                              s);
+  }));
+  DIT_TRY(timed(DIT_K_GEMM_QKVG, s, [&] {
+    return launch_gemm_fp8(false, ws.codes, ws.scales, w->w_qkvg, w->s_qkvg, b.qkvg, T, nq, D, s, b.part,
+                           b.part_bytes);
+  }));
+  DIT_TRY(timed(DIT_K_ATTN, s, [&] {
+    return launch_attention(false, c->head_dim, b.qkvg, b.vt, b.og, c->batch, L, c->n_heads, c->n_kv_heads, s);
+  }));
+  DIT_TRY(quant(b.og, hd));
+  DIT_TRY(timed(DIT_K_GEMM_O, s, [&] {
+    return launch_gemm_fp8(false, ws.codes, ws.scales, w->w_o, w->s_o, b.br, T, D, hd, s, b.part, b.part_bytes);
+  }));
+  if (fused_resid_norm(D)) {
+    DIT_TRY(timed(DIT_K_RESID, s, [&] {
+      return launch_resid_modnorm_fp8(false, x_in, b.br, (float *)b.x1, ws.codes, ws.scales, mod, w->mod_bias, 0,
+                                      w->mod_bias, w->norm2_w, 1, T, L, D, c->eps, s);
+    }));
+  } else {
+    DIT_TRY(timed(DIT_K_RESID, s, [&] {
+      return launch_resid(false, false, true, x_in, b.br, b.x1, mod, w->mod_bias, T, L, D, 0, s);
+    }));
+    DIT_TRY(timed(DIT_K_MODNORM, s, [&] {
+      return launch_modnorm_fp8(true, b.x1, ws.codes, ws.scales, mod, w->mod_bias, w->norm2_w, T, L, D, c->eps, 1,
+                                s);
+    }));
+  }
+  DIT_TRY(timed(DIT_K_GEMM_W13, s, [&] {
+    return launch_gemm_fp8(true, ws.codes, ws.scales, w->w_13, w->s_13, b.qkvg, T, F, D, s, b.part, b.part_bytes);
+  }));
+  DIT_TRY(quant(b.qkvg, F));
+  DIT_TRY(timed(DIT_K_GEMM_W2, s, [&] {
+    return launch_gemm_fp8(false, ws.codes, ws.scales, w->w_2, w->s_2, b.br, T, D, F, s, b.part, b.part_bytes);
+  }));
+  DIT_TRY(timed(DIT_K_RESID, s, [&] {
+    return launch_resid(true, false, false, b.x1, b.br, x_out, mod, w->mod_bias, T, L, D, 1, s);
   }));
   return DIT_OK;
 }
@@ -470,6 +594,30 @@ dit_status dit_block_fwd_ex(const dit_config *cfg, const dit_prologue *pro, cons
 dit_status dit_block_fwd(const dit_config *cfg, const dit_block_weights *w, const void *x_in,
                          void *x_out, const float *mod, void *ws, size_t ws_bytes, void *stream) {
   return dit_block_fwd_ex(cfg, nullptr, w, x_in, x_out, mod, ws, ws_bytes, stream);
+}
+
+size_t dit_workspace_size_fp8(const dit_config *cfg) {
+  if (check_cfg_fp8(cfg) != DIT_OK) return 0;
+  return carve_fp8(cfg, nullptr).bytes;
+}
+
+dit_status dit_block_fwd_fp8(const dit_config *cfg, const dit_block_weights_fp8 *w, const void *x_in, void *x_out,
+                             const float *mod, void *ws, size_t ws_bytes, void *stream) {
+  dit_status st = check_cfg_fp8(cfg);
+  if (st != DIT_OK) return st;
+  if (!x_in || !x_out || !mod || !w) return DIT_ERR_NULL;
+  if (!ws) return DIT_ERR_WORKSPACE;
+  if (!aligned(x_in) || !aligned(x_out) || !aligned(mod) || !aligned(ws)) return DIT_ERR_ALIGN;
+  const Dims d = dims(cfg);
+  const size_t need = carve_fp8(cfg, nullptr).bytes;
+  if (ws_bytes < need) return DIT_ERR_WORKSPACE;
+  if ((st = check_weights_fp8(cfg, w, ws, need)) != DIT_OK) return st;
+  const size_t xb = d.T * d.D * d.es;
+  if (overlap(x_in, xb, x_out, xb)) return DIT_ERR_SHAPE;
+  if (overlap(ws, need, x_in, xb) || overlap(ws, need, x_out, xb) ||
+      overlap(ws, need, mod, (size_t)cfg->batch * 6 * cfg->hidden * 4))
+    return DIT_ERR_SHAPE;
+  return run_block_fp8(cfg, w, x_in, x_out, mod, carve_fp8(cfg, ws), (hipStream_t)stream);
 }
 
 dit_status dit_stack_fwd_ex(const dit_config *cfg, const dit_prologue *pro, int32_t n_blocks,

@@ -87,6 +87,27 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// Eight values times inv as OCP e4m3 codes (the hardware conversion rounds
+// to nearest even), packed little-endian: element i is byte i.
+__device__ __forceinline__ u32x2 fp8_pack8(const float (&v)[8], float inv) {
+  int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(v[0] * inv, v[1] * inv, 0, false);
+  w0 = __builtin_amdgcn_cvt_pk_fp8_f32(v[2] * inv, v[3] * inv, w0, true);
+  int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(v[4] * inv, v[5] * inv, 0, false);
+  w1 = __builtin_amdgcn_cvt_pk_fp8_f32(v[6] * inv, v[7] * inv, w1, true);
+  return u32x2{(uint32_t)w0, (uint32_t)w1};
+}
+// The row-wise scale of a row with largest magnitude amax (s = amax / 448,
+// an all-zero row gets s = 1) and the factor its values are multiplied by
+// before the conversion (448 / amax, 0 for an all-zero row).
+__device__ __forceinline__ float fp8_row_scale(float amax) { return amax > 0.f ? amax / 448.0f : 1.0f; }
+__device__ __forceinline__ float fp8_row_inv(float amax) { return amax > 0.f ? 448.0f / amax : 0.0f; }
+
 // z * sigmoid(z) with the hardware reciprocal (~1 ulp) instead of an IEEE
 // division (a ~10-instruction sequence per element in the GEMM epilogues);
 // z -> -inf gives -0, z -> +inf gives z

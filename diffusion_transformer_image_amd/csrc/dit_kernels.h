@@ -20,6 +20,16 @@ hipError_t launch_resid_modnorm(bool x_f32, bool f32, const void *x, const void 
                                 const float *mod, const float *gbias, int gw, const float *nbias,
                                 const float *ngain, int nw, int rows, int seq_len, int D, float eps,
                                 hipStream_t s);
+// The two norms again with h leaving as row-wise e4m3 codes q [rows][D]
+// and row scales qs [rows] (x1 of the fused pass is still stored in fp32;
+// y is bf16)
+hipError_t launch_modnorm_fp8(bool x_f32, const void *x, uint8_t *q, float *qs, const float *mod,
+                              const float *bias, const float *gain, int rows, int seq_len, int D, float eps,
+                              int which, hipStream_t s);
+hipError_t launch_resid_modnorm_fp8(bool x_f32, const void *x, const void *y, float *x1, uint8_t *q, float *qs,
+                                    const float *mod, const float *gbias, int gw, const float *nbias,
+                                    const float *ngain, int nw, int rows, int seq_len, int D, float eps,
+                                    hipStream_t s);
 hipError_t launch_tmod(const float *t, const float *w1, const float *w2, float *mod, float *zs,
                        int B, int D, int tdim, hipStream_t s);
 // out[b][o] = sum_r w[o][r] zs[b][r], o < O: a second map of the hidden zs
@@ -86,7 +96,10 @@ hipError_t launch_quantize_fp8(bool f32, const void *x, void *q, float *scale, i
 // tensor-wise: scale[] receives the common scale for every row; tamax: 1 float
 hipError_t launch_quantize_fp8_tensor(bool f32, const void *x, void *q, float *scale, float *tamax, int M, int K,
                                       hipStream_t s);
+// part (fp32, part_bytes): lets the product split its last round of tiles
+// along K as the bf16 one does (gemm_choose_fp8 says how much it needs)
 hipError_t launch_gemm_fp8(bool swiglu, const void *aq, const float *sa, const void *wq, const float *sw, void *c,
-                           int M, int N, int K, hipStream_t s);
+                           int M, int N, int K, hipStream_t s, float *part = nullptr, size_t part_bytes = 0);
+GemmChoice gemm_choose_fp8(int M, int N, int K, bool swiglu);
 
 }  // namespace dit

@@ -66,6 +66,32 @@ __device__ __forceinline__ void lds8(const float *p, float (&v)[8]) {
   v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
+// Row-wise e4m3 quantisation of one row held in registers (chunk ch = lane
+// + 64 c of NCH per lane): the row's amax is one wave reduction, then the
+// codes go to qr and the scale amax / 448 to *qs.  The same float32
+// decisions as the stand-alone quantiser, from the unrounded values.
+template <typename T> struct is_u8 { static constexpr bool value = false; };
+template <> struct is_u8<uint8_t> { static constexpr bool value = true; };
+template <int NCH>
+__device__ __forceinline__ void quant_row_store(const float (&v)[NCH][8], uint8_t *qr, float *qs, int lane,
+                                                int nch) {
+  float amax = 0.f;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c)
+    if (lane + 64 * c < nch) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[c][i]));
+    }
+  amax = wave_max(amax);
+  const float inv = fp8_row_inv(amax);
+  if (lane == 0) *qs = fp8_row_scale(amax);
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int ch = lane + 64 * c;
+    if (ch < nch) *reinterpret_cast<u32x2 *>(qr + ch * 8) = fp8_pack8(v[c], inv);
+  }
+}
+
 // One row's NCH chunks of 8 elements per lane (chunk ch = lane + 64 c), held
 // as raw 16-byte words so a row can be in flight while the previous one is
 // computed: loads are issued by load(), converted by get().
@@ -121,8 +147,11 @@ __device__ __forceinline__ void stage_gate_vector(float *G, const float *mod, co
 // ----------------------------------------------------------------- modnorm
 // h = x * rsqrt(mean(x^2) + eps) * A + S; the row stays in registers
 // (NCH chunks of 8 per lane) between the sum of squares and the output.
+// Th = uint8_t: h leaves as row-wise e4m3 codes with its row scales in hs
+// (the operand of an 8-bit product, quantised from the fp32 values).
 template <typename Tx, typename Th, int NCH>
 __global__ __launch_bounds__(EW_WAVES * 64) void modnorm_kernel(const Tx *__restrict__ x, Th *__restrict__ h,
+                                                      float *__restrict__ hs,
                                                       const float *__restrict__ mod,
                                                       const float *__restrict__ bias,
                                                       const float *__restrict__ gain, int seq_len, int D,
@@ -164,14 +193,15 @@ __global__ __launch_bounds__(EW_WAVES * 64) void modnorm_kernel(const Tx *__rest
     for (int c = 0; c < NCH; ++c) {
       const int ch = lane + 64 * c;
       if (ch < nch) {
-        float a[8], sh[8], o[8];
+        float a[8], sh[8];
         lds8(A + ch * 8, a);
         lds8(S + ch * 8, sh);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) o[i] = v[c][i] * inv * a[i] + sh[i];
-        Vec8<Th>::store(hr + ch * 8, o);
+        for (int i = 0; i < 8; ++i) v[c][i] = v[c][i] * inv * a[i] + sh[i];
+        if constexpr (!is_u8<Th>::value) Vec8<Th>::store(hr + ch * 8, v[c]);
       }
     }
+    if constexpr (is_u8<Th>::value) quant_row_store<NCH>(v, hr, hs + row, lane, nch);
   }
 }
 
@@ -183,12 +213,12 @@ static int nch_bucket(int D) {
 template <typename Tx, typename Th>
 static hipError_t launch_modnorm_t(const void *x, void *h, const float *mod, const float *bias,
                                    const float *gain, int rows, int seq_len, int D, float eps,
-                                   int which, hipStream_t s) {
+                                   int which, hipStream_t s, float *hs = nullptr) {
   const int B = rows / seq_len;
   dim3 grid((seq_len + EW_ROWS - 1) / EW_ROWS, B), block(EW_WAVES * 64);
   const size_t lds = 2 * (size_t)D * sizeof(float);
 #define DIT_MN(N)                                                                                  \
-  hipLaunchKernelGGL((modnorm_kernel<Tx, Th, N>), grid, block, lds, s, (const Tx *)x, (Th *)h, mod, \
+  hipLaunchKernelGGL((modnorm_kernel<Tx, Th, N>), grid, block, lds, s, (const Tx *)x, (Th *)h, hs, mod, \
                      bias, gain, seq_len, D, eps, which)
   switch (nch_bucket(D)) {
     case 1: DIT_MN(1); break;
@@ -209,6 +239,13 @@ hipError_t launch_modnorm(bool x_f32, bool h_f32, const void *x, void *h, const 
   if (x_f32) return launch_modnorm_t<float, bf16>(x, h, mod, bias, gain, rows, seq_len, D, eps, which, s);
   if (h_f32) return launch_modnorm_t<bf16, float>(x, h, mod, bias, gain, rows, seq_len, D, eps, which, s);
   return launch_modnorm_t<bf16, bf16>(x, h, mod, bias, gain, rows, seq_len, D, eps, which, s);
+}
+
+hipError_t launch_modnorm_fp8(bool x_f32, const void *x, uint8_t *q, float *qs, const float *mod,
+                              const float *bias, const float *gain, int rows, int seq_len, int D, float eps,
+                              int which, hipStream_t s) {
+  if (x_f32) return launch_modnorm_t<float, uint8_t>(x, q, mod, bias, gain, rows, seq_len, D, eps, which, s, qs);
+  return launch_modnorm_t<bf16, uint8_t>(x, q, mod, bias, gain, rows, seq_len, D, eps, which, s, qs);
 }
 
 // ----------------------------------------------------------------- residual
@@ -306,6 +343,7 @@ hipError_t launch_resid(bool x_f32, bool y_f32, bool out_f32, const void *x, con
 template <typename Tx, typename Ty, typename Th, int NCH>
 __global__ __launch_bounds__(EW_WAVES * 64) void resid_modnorm_kernel(const Tx *__restrict__ x, const Ty *__restrict__ y,
                                                             float *__restrict__ x1, Th *__restrict__ h,
+                                                            float *__restrict__ hs,
                                                             const float *__restrict__ mod,
                                                             const float *__restrict__ gbias, int gw,
                                                             const float *__restrict__ nbias,
@@ -363,27 +401,29 @@ __global__ __launch_bounds__(EW_WAVES * 64) void resid_modnorm_kernel(const Tx *
     for (int c = 0; c < NCH; ++c) {
       const int ch = lane + 64 * c;
       if (ch < nch) {
-        float a[8], sh[8], o[8];
+        float a[8], sh[8];
         lds8(A + ch * 8, a);
         lds8(S + ch * 8, sh);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) o[i] = v[c][i] * inv * a[i] + sh[i];
-        Vec8<Th>::store(h + row * D + ch * 8, o);
+        for (int i = 0; i < 8; ++i) v[c][i] = v[c][i] * inv * a[i] + sh[i];
+        if constexpr (!is_u8<Th>::value) Vec8<Th>::store(h + row * D + ch * 8, v[c]);
       }
     }
+    if constexpr (is_u8<Th>::value) quant_row_store<NCH>(v, h + row * D, hs + row, lane, nch);
   }
 }
 
 template <typename Tx, typename Ty, typename Th>
 static hipError_t launch_resid_modnorm_t(const void *x, const void *y, float *x1, void *h, const float *mod,
                                          const float *gbias, int gw, const float *nbias, const float *ngain,
-                                         int nw, int rows, int seq_len, int D, float eps, hipStream_t s) {
+                                         int nw, int rows, int seq_len, int D, float eps, hipStream_t s,
+                                         float *hs = nullptr) {
   const int B = rows / seq_len;
   dim3 grid((seq_len + EW_ROWS - 1) / EW_ROWS, B), block(EW_WAVES * 64);
   const size_t lds = 3 * (size_t)D * sizeof(float);
 #define DIT_RMN(N)                                                                                   \
   hipLaunchKernelGGL((resid_modnorm_kernel<Tx, Ty, Th, N>), grid, block, lds, s, (const Tx *)x,     \
-                     (const Ty *)y, x1, (Th *)h, mod, gbias, gw, nbias, ngain, nw, seq_len, D, eps)
+                     (const Ty *)y, x1, (Th *)h, hs, mod, gbias, gw, nbias, ngain, nw, seq_len, D, eps)
   switch (nch_bucket(D)) {
     case 1: DIT_RMN(1); break;
     case 2: DIT_RMN(2); break;
@@ -407,6 +447,17 @@ hipError_t launch_resid_modnorm(bool x_f32, bool f32, const void *x, const void 
   if (x_f32) return DIT_RMNT(float, bf16, bf16);
   return DIT_RMNT(bf16, bf16, bf16);
 #undef DIT_RMNT
+}
+
+hipError_t launch_resid_modnorm_fp8(bool x_f32, const void *x, const void *y, float *x1, uint8_t *q, float *qs,
+                                    const float *mod, const float *gbias, int gw, const float *nbias,
+                                    const float *ngain, int nw, int rows, int seq_len, int D, float eps,
+                                    hipStream_t s) {
+  if (x_f32)
+    return launch_resid_modnorm_t<float, bf16, uint8_t>(x, y, x1, q, mod, gbias, gw, nbias, ngain, nw, rows,
+                                                        seq_len, D, eps, s, qs);
+  return launch_resid_modnorm_t<bf16, bf16, uint8_t>(x, y, x1, q, mod, gbias, gw, nbias, ngain, nw, rows, seq_len,
+                                                     D, eps, s, qs);
 }
 
 // ----------------------------------------------------------------- timestep MLP

@@ -37,15 +37,14 @@ __global__ __launch_bounds__(256) void quantize_fp8_kernel(const T *__restrict__
 #pragma unroll
     for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+  amax = wave_max(amax);
   if (MODE == 1) {
     if (lane == 0) scale[row] = amax;
     return;
   }
   if (MODE == 2) amax = tamax[0];
-  const float s = amax > 0.f ? amax / 448.0f : 1.0f;
-  const float inv = amax > 0.f ? 448.0f / amax : 0.0f;
+  const float s = fp8_row_scale(amax);
+  const float inv = fp8_row_inv(amax);
   if (lane == 0) scale[row] = s;
   uint8_t *qr = q + (size_t)row * K;
   for (int c = lane; c < nch; c += 64) {
@@ -59,11 +58,7 @@ __global__ __launch_bounds__(256) void quantize_fp8_kernel(const T *__restrict__
 #pragma unroll
       for (int i = 0; i < 4; ++i) { v[i] = a[i]; v[4 + i] = b[i]; }
     }
-    int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(v[0] * inv, v[1] * inv, 0, false);
-    w0 = __builtin_amdgcn_cvt_pk_fp8_f32(v[2] * inv, v[3] * inv, w0, true);
-    int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(v[4] * inv, v[5] * inv, 0, false);
-    w1 = __builtin_amdgcn_cvt_pk_fp8_f32(v[6] * inv, v[7] * inv, w1, true);
-    *reinterpret_cast<u32x2 *>(qr + c * 8) = u32x2{(uint32_t)w0, (uint32_t)w1};
+    *reinterpret_cast<u32x2 *>(qr + c * 8) = fp8_pack8(v, inv);
   }
 }
 

@@ -566,7 +566,7 @@ template <int EPI>
 __global__ __launch_bounds__(512) void gemm_fp8_kernel(const uint8_t *__restrict__ A, const float *__restrict__ sa,
                                                        const uint8_t *__restrict__ W, const float *__restrict__ sw,
                                                        bf16 *__restrict__ C, int M, int N, int K, int m_tiles,
-                                                       int n_tiles, int gm) {
+                                                       int n_tiles, int gm, SkPlan sk) {
   constexpr int BM = 256, BN = 256, WM = 2, WN = 4, NW = 8;
   constexpr int TM = BM / WM, TN = BN / WN, RB = TM / 16, CB = TN / 16;
   constexpr int BKB = 128, CPR = 8, RPB = 1024 / BKB;
@@ -576,9 +576,21 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(const uint8_t *__restrict
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
-  const int nwg = m_tiles * n_tiles;
-  int pid = blockIdx.x;
-  if ((nwg & 7) == 0) pid = (pid & 7) * (nwg >> 3) + (pid >> 3);
+  // whole tiles first (XCD-contiguous remap), then the K segments of the
+  // split tail tiles, as in gemm_kernel (stages of 128 K elements)
+  const int nk_all = (K + BKB - 1) / BKB;
+  int pid, kb = 0, nk = nk_all, slot = -1;
+  if ((int)blockIdx.x < sk.dp_tiles) {
+    const int nwg = sk.dp_tiles;
+    pid = blockIdx.x;
+    if ((nwg & 7) == 0) pid = (pid & 7) * (nwg >> 3) + (pid >> 3);
+  } else {
+    slot = blockIdx.x - sk.dp_tiles;
+    const int seg = slot % sk.segs;
+    pid = sk.dp_tiles + slot / sk.segs;
+    kb = seg * nk_all / sk.segs;
+    nk = (seg + 1) * nk_all / sk.segs - kb;
+  }
   int tm, tn;
   tile_coords(pid, m_tiles, n_tiles, gm, tm, tn);
   const int m0 = tm * BM;
@@ -612,7 +624,7 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(const uint8_t *__restrict
     }
   }
   auto issue_stage = [&](int kt, int buf) {
-    const int k0 = kt * BKB;
+    const int k0 = (kb + kt) * BKB;
     const int kc_ok = (k0 + BKB > K) ? (K - k0) / 16 : CPR;
     char *base = smem + buf * STAGE;
 #pragma unroll
@@ -649,7 +661,6 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(const uint8_t *__restrict
     return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
   };
 
-  const int nk = (K + BKB - 1) / BKB;
   auto mmas = [&](const char *sb) {
     i32x8 bf[CB];
 #pragma unroll
@@ -673,7 +684,7 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(const uint8_t *__restrict
 #pragma unroll
     for (int j = 0; j < BPW; ++j) goffs[j] = gval[j] ? goff[j] : kOOB;
     auto issue_spread = [&](int kt, int buf) {
-      const uint32_t soff = kt < nk ? (uint32_t)kt * BKB : kOOB;
+      const uint32_t soff = kt < nk ? (uint32_t)(kb + kt) * BKB : kOOB;
       char *base = smem + buf * STAGE;
 #pragma unroll
       for (int j = 0; j < BPW; ++j) {
@@ -688,7 +699,7 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(const uint8_t *__restrict
       __syncthreads();  // stage kt visible to all; every wave is done with stage kt-1
       const char *sb = smem + (kt & 1) * STAGE;
       char *nb = smem + ((kt + 1) & 1) * STAGE;
-      const uint32_t soff = kt + 1 < nk ? (uint32_t)(kt + 1) * BKB : kOOB;
+      const uint32_t soff = kt + 1 < nk ? (uint32_t)(kb + kt + 1) * BKB : kOOB;
       // program order: the fragment reads of stage kt, then the DMA loads
       // of stage kt+1 one per row block (the DMA writes the other buffer;
       // in this order the compiler may keep the loads beside the MFMAs)
@@ -748,19 +759,56 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(const uint8_t *__restrict
 #pragma unroll
       for (int j = 0; j < CB; ++j) acc[i][j][e] *= rs * cs[j];
     }
+  if (slot >= 0) {  // a K segment of a split tile: the scaled fp32 partial (the scales are per row and column)
+    float *dst = sk.part + (size_t)slot * BM * BN + (size_t)wave * RB * CB * 256 + lane * 4;
+#pragma unroll
+    for (int i = 0; i < RB; ++i)
+#pragma unroll
+      for (int j = 0; j < CB; ++j) *reinterpret_cast<f32x4 *>(dst + (i * CB + j) * 256) = acc[i][j];
+    return;
+  }
   gemm_epilogue<bf16, BM, BN, NW, WM, WN, EPI, 2 * STAGE>(acc, smem, C, M, N, m0, n0, wave, lane, ColScale{});
 }
 
-hipError_t launch_gemm_fp8(bool swiglu, const void *aq, const float *sa, const void *wq, const float *sw, void *c,
-                           int M, int N, int K, hipStream_t s) {
-  const int mt = (M + 255) / 256, nt = swiglu ? (N + 127) / 128 : (N + 255) / 256;
-  if (swiglu)
-    hipLaunchKernelGGL(gemm_fp8_kernel<EPI_SWIGLU>, dim3(mt * nt), dim3(512), 0, s, (const uint8_t *)aq, sa,
-                       (const uint8_t *)wq, sw, (bf16 *)c, M, N, K, mt, nt, 4);
-  else
-    hipLaunchKernelGGL(gemm_fp8_kernel<EPI_STORE>, dim3(mt * nt), dim3(512), 0, s, (const uint8_t *)aq, sa,
-                       (const uint8_t *)wq, sw, (bf16 *)c, M, N, K, mt, nt, 8);
+template <int EPI>
+static hipError_t launch_fp8_t(const void *aq, const float *sa, const void *wq, const float *sw, void *c, int M,
+                               int N, int K, hipStream_t s, int sk_tiles, int segs, float *part) {
+  const int mt = (M + 255) / 256, nt = (EPI == EPI_SWIGLU) ? (N + 127) / 128 : (N + 255) / 256;
+  const int gm = (EPI == EPI_SWIGLU) ? 4 : 8;
+  if (segs <= 1 || !part) sk_tiles = 0;
+  const SkPlan plan{mt * nt - sk_tiles, sk_tiles ? segs : 1, part};
+  hipLaunchKernelGGL(gemm_fp8_kernel<EPI>, dim3(plan.dp_tiles + sk_tiles * plan.segs), dim3(512), 0, s,
+                     (const uint8_t *)aq, sa, (const uint8_t *)wq, sw, (bf16 *)c, M, N, K, mt, nt, gm, plan);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || sk_tiles == 0) return e;
+  // the partials carry the scales already: the bf16 fixup sums them and
+  // applies the epilogue (same tile and accumulator layout)
+  hipLaunchKernelGGL((gemm_sk_fixup<bf16, 256, 256, 2, 4, EPI, 2>), dim3(sk_tiles * 8 * 4), dim3(64), 0, s,
+                     (const float *)part, (bf16 *)c, M, N, mt, nt, gm, plan.dp_tiles, plan.segs, ColScale{});
   return hipGetLastError();
+}
+
+GemmChoice gemm_choose_fp8(int M, int N, int K, bool swiglu) {
+  // the bf16 cost model on 128-element stages: a round costs about 0.6 of
+  // the bf16 one, so the fixed cost of the partials weighs more; 192-row
+  // tiles do not exist in FP8 (variant 0 only)
+  GemmChoice ch = gemm_choose(M, N, (K + 1) / 2, swiglu);
+  if (ch.sk_tiles == 0) return GemmChoice{0, 0, 1, 0};
+  const int nk = (K + 127) / 128;
+  if (ch.segs > nk / 2) return GemmChoice{0, 0, 1, 0};
+  ch.variant = 0;
+  return ch;
+}
+
+hipError_t launch_gemm_fp8(bool swiglu, const void *aq, const float *sa, const void *wq, const float *sw, void *c,
+                           int M, int N, int K, hipStream_t s, float *part, size_t part_bytes) {
+  GemmChoice ch{0, 0, 1, 0};
+  if (part) {
+    ch = gemm_choose_fp8(M, N, K, swiglu);
+    if (part_bytes < ch.part_bytes) ch = GemmChoice{0, 0, 1, 0};
+  }
+  if (swiglu) return launch_fp8_t<EPI_SWIGLU>(aq, sa, wq, sw, c, M, N, K, s, ch.sk_tiles, ch.segs, part);
+  return launch_fp8_t<EPI_STORE>(aq, sa, wq, sw, c, M, N, K, s, ch.sk_tiles, ch.segs, part);
 }
 
 template <typename T, int BM, int BN, int BKB, int STAGES, int WM, int WN, int EPI, bool PIPE = false>

@@ -138,7 +138,8 @@ typedef enum {
   DIT_K_GEMM_W2 = 6,   /* U * W_2^T                            */
   DIT_K_TMOD = 7,      /* timestep embedding + modulation MLP  */
   DIT_K_PROLOGUE = 8,  /* QKNorm + RoPE on Q and K (if enabled) */
-  DIT_K_COUNT = 9
+  DIT_K_QUANT = 9,     /* row-wise e4m3 quantisation of the activations (8-bit block) */
+  DIT_K_COUNT = 10
 } dit_kernel_kind;
 
 /* Workspace bytes needed by dit_block_fwd for this configuration
@@ -375,6 +376,35 @@ dit_status dit_quantize_fp8_tensor(dit_dtype dtype, int32_t m, int32_t k, const 
  * v_mfma_f32_16x16x128 f8 operations.  k % 16 == 0. */
 dit_status dit_gemm_fp8(int32_t swiglu, int32_t m, int32_t n, int32_t k, const void *qa, const float *sa,
                         const void *qw, const float *sw, void *c, void *stream);
+
+/* One block's weights for the 8-bit block (host struct of device pointers):
+ * each projection matrix as row-wise e4m3 codes with one float32 scale per
+ * row (W ~ codes * scale[row]; dit_quantize_fp8 of the bf16 matrix makes
+ * them, dit_quantize_fp8_tensor the tensor-wise form), in the layouts of
+ * dit_block_weights; the fp32 modulation bias and norm gains as there. */
+typedef struct {
+  const void *w_qkvg, *w_o, *w_13, *w_2;  /* e4m3 bytes                                  */
+  const float *s_qkvg, *s_o, *s_13, *s_2; /* [rows] fp32 scales of the four matrices     */
+  const float *mod_bias;                  /* [6, D]                                      */
+  const float *norm1_w, *norm2_w;         /* [D] or NULL                                 */
+} dit_block_weights_fp8;
+
+/* Workspace bytes of dit_block_fwd_fp8 (0 if cfg is invalid for it). */
+size_t dit_workspace_size_fp8(const dit_config *cfg /* host */);
+
+/* The block with its four projections in 8 bits (page "Krea 2 技术报告",
+ * 训练 › 预训练: 8-bit matrix products with tensor-wise / row-wise
+ * scaling): the activation rows entering each product (h1, Og, h2, U,
+ * stored as bf16 by the kernels that make them) are quantised row-wise to
+ * e4m3 as in dit_quantize_fp8, multiplied with the weight codes as in
+ * dit_gemm_fp8 (fp32 accumulation, both scales applied), and the rest is
+ * the bf16 block of dit_block_fwd (unscaled queries, the V^T pass).
+ * cfg->dtype must be DIT_BF16 (x_in, x_out bf16), head_dim 128, and hidden,
+ * H*d and ffn multiples of 16 (else DIT_ERR_UNSUPPORTED / DIT_ERR_DTYPE).
+ * Other arguments and errors as in dit_block_fwd. */
+dit_status dit_block_fwd_fp8(const dit_config *cfg /* host */, const dit_block_weights_fp8 *w /* host */,
+                             const void *x_in, void *x_out, const float *mod, void *ws, size_t ws_bytes,
+                             void *stream);
 
 /* Gated grouped-query attention over the rows of qkvg [T, (2H+2Hkv)*d]
  * (column blocks Q | K | V | G, as produced by the QKVG projection):

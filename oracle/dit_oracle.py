@@ -481,3 +481,45 @@ def swiglu_fp8(qa, sa, qw13, sw13, ffn: int) -> np.ndarray:
     """SiLU(A W1^T) * (A W3^T) with both halves of W13 = [W1; W3] in FP8."""
     c = gemm_fp8(qa, sa, qw13, sw13)
     return silu(c[:, :ffn]) * c[:, ffn:]
+
+
+def _quant_identity(x):
+    """No quantisation: q = x, s = 1 (the composition then equals the exact
+    block; used to pin its wiring)."""
+    x = _f64(x)
+    return x, np.ones(x.shape[0])
+
+
+def block_forward_fp8(x, mod, wts, oc: OracleConfig, quant: Callable = quantize_rows_fp8) -> np.ndarray:
+    """The block with its four projections in 8 bits (page "Krea 2 技术报告",
+    训练 › 预训练: 8-bit matrix products with row-wise scaling): every
+    product's activation rows and weight rows are quantised with ``quant``
+    (row-wise e4m3 by default: one float32 scale per token row and per weight
+    row) and multiplied as gemm_fp8 / swiglu_fp8 do; everything else is the
+    exact block of _sample_forward.  The activations are quantised from their
+    exact values (h1, Og, h2, U of this oracle)."""
+    H, Hk, d, F = oc.n_heads, oc.n_kv_heads, oc.head_dim, oc.ffn
+    qw = {n: quant(getattr(wts, n)) for n in ("w_qkvg", "w_o", "w_13", "w_2")}
+
+    def prod(a, name):
+        qa, sa = quant(a)
+        return gemm_fp8(qa, sa, *qw[name])
+
+    out = []
+    for b in range(_f64(x).shape[0]):
+        xb = _f64(x[b])
+        shift1, scale1, gate1, shift2, scale2, gate2 = split_modulation(mod[b], wts.mod_bias)
+        h1 = modulated_rmsnorm(xb, wts.norm1_w, shift1, scale1, oc.eps)
+        z = prod(h1, "w_qkvg")
+        L = z.shape[0]
+        q = z[:, : H * d].reshape(L, H, d)
+        k = z[:, H * d:(H + Hk) * d].reshape(L, Hk, d)
+        v = z[:, (H + Hk) * d:(H + 2 * Hk) * d].reshape(L, Hk, d)
+        g = z[:, (H + 2 * Hk) * d:].reshape(L, H, d)
+        og = gated_gqa_attention(q, k, v, g)
+        x1 = gated_residual(xb, gate1, prod(og, "w_o"))
+        h2 = modulated_rmsnorm(x1, wts.norm2_w, shift2, scale2, oc.eps)
+        qa, sa = quant(h2)
+        u = swiglu_fp8(qa, sa, *qw["w_13"], F)
+        out.append(gated_residual(x1, gate2, prod(u, "w_2")))
+    return np.stack(out)

@@ -7,7 +7,7 @@ import pytest
 
 import datagen
 from oracle import dit_oracle as O
-from tests._parity import assert_parity
+from tests._parity import assert_parity, assert_update_parity
 
 pytestmark = pytest.mark.gpu
 
@@ -126,3 +126,93 @@ def test_quantize_fp8_tensor_bit_exact(dev, dtype):
     qw, sw = O.quantize_rows_fp8(w)
     assert_parity(device.to_numpy(C), O.gemm_fp8(q, s, qw, sw), "bf16", "tensor-wise fp8 gemm", maxabs=8e-3,
                   cos_min=0.99999)
+
+
+# ------------------------------------------------------------------ the 8-bit block
+def fp8_block_weights(dev, w, dtype="bf16"):
+    """The block's matrices quantised row-wise on the GPU (codes and scales
+    checked bit for bit against the oracle's quantiser), plus the fp32
+    vectors; returns the device dict for block_fwd_fp8."""
+    torch, device, dit = dev
+    out = {}
+    for name, sname in (("w_qkvg", "s_qkvg"), ("w_o", "s_o"), ("w_13", "s_13"), ("w_2", "s_2")):
+        a = getattr(w, name)
+        Q, S = quantize_on_gpu(dev, a, dtype)
+        q, s = O.quantize_rows_fp8(a)
+        assert np.array_equal(S.cpu().numpy(), s), name
+        assert np.array_equal(decode_e4m3(Q.cpu().numpy()), q), name
+        out[name], out[sname] = Q, S
+    out["mod_bias"] = device.to_device(w.mod_bias, "f32")
+    out["norm1_w"] = device.to_device(w.norm1_w, "f32")
+    out["norm2_w"] = device.to_device(w.norm2_w, "f32")
+    return out
+
+
+# Tolerance of the 8-bit block against the oracle's 8-bit composition.
+# Both sides quantise the same weights to the same codes, and h1, h2 to the
+# same codes too (the norm kernels quantise their fp32 rows, as the oracle
+# quantises its exact rows in float32).  Og and U reach their quantiser as
+# bf16 (their row maximum spans several tiles of the producing kernel),
+# so a few percent of their codes sit one e4m3 step (1/16 - 1/8 of the
+# element) away from the oracle's.  The oracle run with exactly that
+# difference (Og and U rounded to bf16 before quantisation, the output
+# rounded to bf16) departs from the plain one by at most 2.0e-2 of the
+# output and 3.4e-2 of the update on the three shapes below (update
+# cosine 1 - 3e-4); with the bf16 block's own bound for the remaining
+# roundings (2e-2, cos 0.9999): output max-abs <= 4e-2 max|ref|, cos >=
+# 0.9999; update (each element's error less half a bf16 ulp of the
+# output) <= 6e-2 max|dref|, 1 - cos <= 1e-3 + 2 (1 - the exactly rounded
+# oracle output's cosine).
+FP8_OUT, FP8_OUT_COS, FP8_UPD_MAXABS, FP8_UPD_COS = 4e-2, 0.9999, 6e-2, 0.999
+
+
+def check_fp8_block(y, ref, x, what):
+    e, c = assert_parity(y, ref, "bf16", what + " output", maxabs=FP8_OUT, cos_min=FP8_OUT_COS)
+    eu, cu = assert_update_parity(y, ref, x, "bf16", what + " update", maxabs=FP8_UPD_MAXABS, cos_min=FP8_UPD_COS)
+    print(f"{what}: output {e:.2e}/{c:.7f} update {eu:.2e}/{cu:.7f}")
+
+
+@pytest.mark.parametrize("batch,n_image,n_text,strong", [(2, 70, 27, True), (2, 100, 28, False), (1, 250, 6, True)])
+def test_block_fp8_vs_oracle_fp8_composition(dev, batch, n_image, n_text, strong):
+    """Every output of the 8-bit block (d = 128, ragged L and whole key tiles)
+    against the oracle's 8-bit composition of the same block."""
+    torch, device, dit = dev
+    cfg = datagen.get_config("c1").replace(batch=batch, n_image=n_image, n_text=n_text, hidden=512, n_heads=4,
+                                            n_kv_heads=1, ffn=1376)
+    x = datagen.activations(cfg)
+    w = datagen.block_weights(cfg)
+    mod = datagen.block_mod(cfg, strong=strong)
+    c = dit.config_of(cfg)
+    W8 = fp8_block_weights(dev, w)
+    X = device.to_device(x.reshape(cfg.tokens, cfg.hidden), "bf16")
+    Y = torch.empty_like(X)
+    ws = torch.empty(dit.workspace_size_fp8(c), dtype=torch.uint8, device="cuda")
+    dit.block_fwd_fp8(c, W8, X, Y, device.to_device(mod, "f32"), ws)
+    torch.cuda.synchronize()
+    y = device.to_numpy(Y).reshape(x.shape)
+    ref = O.block_forward_fp8(x, mod, w, O.OracleConfig.of(cfg))
+    check_fp8_block(y, ref, x.astype(np.float64), f"fp8 block L={cfg.seq_len} strong={strong}")
+
+
+@pytest.mark.timeout(600)
+def test_block_fp8_full_size_every_output(dev):
+    """The 8-bit block at the stack's per-block shapes (hidden 4096, 32 / 8
+    heads, SwiGLU 11008, one sample of 4096 image + 512 text tokens): every
+    output against the oracle's 8-bit composition (the 256-row tiles, the
+    split tails of the O and down products)."""
+    torch, device, dit = dev
+    cfg = datagen.get_config("c4").replace(ffn=11008)
+    x = datagen.activations(cfg)
+    w = datagen.block_weights(cfg)
+    mod = datagen.block_mod(cfg)
+    c = dit.config_of(cfg)
+    W8 = fp8_block_weights(dev, w)
+    X = device.to_device(x.reshape(cfg.tokens, cfg.hidden), "bf16")
+    Y = torch.empty_like(X)
+    ws = torch.empty(dit.workspace_size_fp8(c), dtype=torch.uint8, device="cuda")
+    dit.block_fwd_fp8(c, W8, X, Y, device.to_device(mod, "f32"), ws)
+    torch.cuda.synchronize()
+    y = device.to_numpy(Y).reshape(x.shape)
+    print("fp8 block full size: GPU done", flush=True)
+    ref = O.block_forward_fp8(x, mod, w, O.OracleConfig.of(cfg))
+    check_fp8_block(y, ref, x.astype(np.float64), "fp8 block 1024 px B=1")

@@ -622,3 +622,28 @@ def test_qkvg_projection_slices_against_scalar_loop():
             for j in range(Hk):
                 assert abs(k[l, j, e] - dot(l, (H + j) * d + e)) < 1e-9
                 assert abs(v[l, j, e] - dot(l, (H + Hk + j) * d + e)) < 1e-9
+
+
+def test_fp8_block_composition_without_quantisation_is_the_block():
+    """block_forward_fp8's wiring: with the quantiser replaced by the identity
+    (codes = values, scales = 1) it must reproduce block_forward (roles of the
+    four products, W1/W3 halves, the residual gates), so only the pinned
+    quantiser and products separate the 8-bit block from the exact one."""
+    for hkv in (1, 2):
+        cfg = tiny_cfg(batch=2, L=5, hkv=hkv, seed=71 + hkv)
+        x, w, mod = inputs(cfg)
+        ref = O.block_forward(x, mod, w, oc(cfg))
+        got = O.block_forward_fp8(x, mod, w, oc(cfg), quant=O._quant_identity)
+        assert np.max(np.abs(got - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+def test_fp8_block_quantises_every_product():
+    """With row-wise e4m3 the 8-bit block differs from the exact block by the
+    quantisation error: a few percent of the update, neither zero (the
+    quantiser is applied) nor of the update's own size."""
+    cfg = tiny_cfg(batch=1, L=6, hkv=1, seed=77)
+    x, w, mod = inputs(cfg)
+    exact = O.block_forward(x, mod, w, oc(cfg))
+    q8 = O.block_forward_fp8(x, mod, w, oc(cfg))
+    du = np.max(np.abs((q8 - x) - (exact - x))) / np.max(np.abs(exact - x))
+    assert 1e-4 < du < 0.5, du
