@@ -390,12 +390,20 @@ dit_status run_block_fp8(const dit_config *c, const dit_block_weights_fp8 *w, co
     return launch_modnorm_fp8(false, x_in, ws.codes, ws.scales, mod, w->mod_bias, w->norm1_w, T, L, D, c->eps, 0,
                               s);
   }));
+  // as in the bf16 block: the query columns leave the product pre-scaled
+  // for the attention, and with whole 64-key tiles and no K split the value
+  // heads go straight to V^T
+  const float qsc = attn_score_scale(c->head_dim);
+  const int vc0 = (c->n_heads + c->n_kv_heads) * c->head_dim;
+  const GemmVt gvt{b.vt, vc0, vc0 + c->n_kv_heads * c->head_dim, L};
+  const bool vt_by_gemm = L % 64 == 0 && gemm_choose_fp8(T, nq, D, false).sk_tiles == 0;
   DIT_TRY(timed(DIT_K_GEMM_QKVG, s, [&] {
     return launch_gemm_fp8(false, ws.codes, ws.scales, w->w_qkvg, w->s_qkvg, b.qkvg, T, nq, D, s, b.part,
-                           b.part_bytes);
+                           b.part_bytes, hd, qsc, vt_by_gemm ? &gvt : nullptr);
   }));
   DIT_TRY(timed(DIT_K_ATTN, s, [&] {
-    return launch_attention(false, c->head_dim, b.qkvg, b.vt, b.og, c->batch, L, c->n_heads, c->n_kv_heads, s);
+    return launch_attention(false, c->head_dim, b.qkvg, b.vt, b.og, c->batch, L, c->n_heads, c->n_kv_heads, s,
+                            true, vt_by_gemm);
   }));
   DIT_TRY(quant(b.og, hd));
   DIT_TRY(timed(DIT_K_GEMM_O, s, [&] {

@@ -97,9 +97,12 @@ hipError_t launch_quantize_fp8(bool f32, const void *x, void *q, float *scale, i
 hipError_t launch_quantize_fp8_tensor(bool f32, const void *x, void *q, float *scale, float *tamax, int M, int K,
                                       hipStream_t s);
 // part (fp32, part_bytes): lets the product split its last round of tiles
-// along K as the bf16 one does (gemm_choose_fp8 says how much it needs)
+// along K as the bf16 one does (gemm_choose_fp8 says how much it needs).
+// scale_cols / col_scale / vt as for launch_gemm (plain product only; vt
+// only when gemm_choose_fp8 gives no split tiles)
 hipError_t launch_gemm_fp8(bool swiglu, const void *aq, const float *sa, const void *wq, const float *sw, void *c,
-                           int M, int N, int K, hipStream_t s, float *part = nullptr, size_t part_bytes = 0);
+                           int M, int N, int K, hipStream_t s, float *part = nullptr, size_t part_bytes = 0,
+                           int scale_cols = 0, float col_scale = 1.f, const GemmVt *vt = nullptr);
 GemmChoice gemm_choose_fp8(int M, int N, int K, bool swiglu);
 
 }  // namespace dit

@@ -62,6 +62,49 @@ __global__ __launch_bounds__(256) void quantize_fp8_kernel(const T *__restrict__
   }
 }
 
+// Row-wise codes of bf16 rows with the whole row held in registers (NCH
+// 16-byte chunks per lane): one read of the row instead of two, every load
+// of it in flight at once.  Same float32 decisions as MODE 0 above.
+template <int NCH>
+__global__ __launch_bounds__(256) void quantize_fp8_rows_reg(const bf16 *__restrict__ x, uint8_t *__restrict__ q,
+                                                             float *__restrict__ scale, int M, int K) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= M) return;
+  const bf16 *xr = x + (size_t)row * K;
+  const int nch = K / 8;
+  u32x4 r[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int ch = lane + 64 * c;
+    if (ch < nch) r[c] = *reinterpret_cast<const u32x4 *>(xr + ch * 8);
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    if (lane + 64 * c < nch) {
+      const bf16x8 b = __builtin_bit_cast(bf16x8, r[c]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf((float)b[i]));
+    }
+  }
+  amax = wave_max(amax);
+  const float inv = fp8_row_inv(amax);
+  if (lane == 0) scale[row] = fp8_row_scale(amax);
+  uint8_t *qr = q + (size_t)row * K;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int ch = lane + 64 * c;
+    if (ch < nch) {
+      const bf16x8 b = __builtin_bit_cast(bf16x8, r[c]);
+      float v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = (float)b[i];
+      *reinterpret_cast<u32x2 *>(qr + ch * 8) = fp8_pack8(v, inv);
+    }
+  }
+}
+
 // max over the M row maxima (one workgroup; the max is exact in any order)
 __global__ __launch_bounds__(1024) void amax_reduce(const float *__restrict__ row_amax, float *__restrict__ out,
                                                     int M) {
@@ -81,6 +124,17 @@ __global__ __launch_bounds__(1024) void amax_reduce(const float *__restrict__ ro
 
 hipError_t launch_quantize_fp8(bool f32, const void *x, void *q, float *scale, int M, int K, hipStream_t s) {
   const dim3 grid((M + 3) / 4), block(256);
+  if (!f32) {  // bf16 rows of up to 16384 elements: one pass from registers
+    const int per = (K / 8 + 63) / 64;
+#define DIT_QR(N)                                                                                                \
+  hipLaunchKernelGGL(quantize_fp8_rows_reg<N>, grid, block, 0, s, (const bf16 *)x, (uint8_t *)q, scale, M, K); \
+  return hipGetLastError()
+    if (per <= 8) { DIT_QR(8); }
+    if (per <= 16) { DIT_QR(16); }
+    if (per <= 24) { DIT_QR(24); }
+    if (per <= 32) { DIT_QR(32); }
+#undef DIT_QR
+  }
   if (f32)
     hipLaunchKernelGGL((quantize_fp8_kernel<float, 0>), grid, block, 0, s, (const float *)x, (uint8_t *)q, scale,
                        nullptr, M, K);

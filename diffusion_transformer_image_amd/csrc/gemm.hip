@@ -566,7 +566,7 @@ template <int EPI>
 __global__ __launch_bounds__(512) void gemm_fp8_kernel(const uint8_t *__restrict__ A, const float *__restrict__ sa,
                                                        const uint8_t *__restrict__ W, const float *__restrict__ sw,
                                                        bf16 *__restrict__ C, int M, int N, int K, int m_tiles,
-                                                       int n_tiles, int gm, SkPlan sk) {
+                                                       int n_tiles, int gm, SkPlan sk, ColScale ocs) {
   constexpr int BM = 256, BN = 256, WM = 2, WN = 4, NW = 8;
   constexpr int TM = BM / WM, TN = BN / WN, RB = TM / 16, CB = TN / 16;
   constexpr int BKB = 128, CPR = 8, RPB = 1024 / BKB;
@@ -767,24 +767,24 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(const uint8_t *__restrict
       for (int j = 0; j < CB; ++j) *reinterpret_cast<f32x4 *>(dst + (i * CB + j) * 256) = acc[i][j];
     return;
   }
-  gemm_epilogue<bf16, BM, BN, NW, WM, WN, EPI, 2 * STAGE>(acc, smem, C, M, N, m0, n0, wave, lane, ColScale{});
+  gemm_epilogue<bf16, BM, BN, NW, WM, WN, EPI, 2 * STAGE>(acc, smem, C, M, N, m0, n0, wave, lane, ocs);
 }
 
 template <int EPI>
 static hipError_t launch_fp8_t(const void *aq, const float *sa, const void *wq, const float *sw, void *c, int M,
-                               int N, int K, hipStream_t s, int sk_tiles, int segs, float *part) {
+                               int N, int K, hipStream_t s, int sk_tiles, int segs, float *part, ColScale cs = {}) {
   const int mt = (M + 255) / 256, nt = (EPI == EPI_SWIGLU) ? (N + 127) / 128 : (N + 255) / 256;
   const int gm = (EPI == EPI_SWIGLU) ? 4 : 8;
   if (segs <= 1 || !part) sk_tiles = 0;
   const SkPlan plan{mt * nt - sk_tiles, sk_tiles ? segs : 1, part};
   hipLaunchKernelGGL(gemm_fp8_kernel<EPI>, dim3(plan.dp_tiles + sk_tiles * plan.segs), dim3(512), 0, s,
-                     (const uint8_t *)aq, sa, (const uint8_t *)wq, sw, (bf16 *)c, M, N, K, mt, nt, gm, plan);
+                     (const uint8_t *)aq, sa, (const uint8_t *)wq, sw, (bf16 *)c, M, N, K, mt, nt, gm, plan, cs);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || sk_tiles == 0) return e;
   // the partials carry the scales already: the bf16 fixup sums them and
   // applies the epilogue (same tile and accumulator layout)
   hipLaunchKernelGGL((gemm_sk_fixup<bf16, 256, 256, 2, 4, EPI, 2>), dim3(sk_tiles * 8 * 4), dim3(64), 0, s,
-                     (const float *)part, (bf16 *)c, M, N, mt, nt, gm, plan.dp_tiles, plan.segs, ColScale{});
+                     (const float *)part, (bf16 *)c, M, N, mt, nt, gm, plan.dp_tiles, plan.segs, cs);
   return hipGetLastError();
 }
 
@@ -800,15 +800,35 @@ GemmChoice gemm_choose_fp8(int M, int N, int K, bool swiglu) {
   return ch;
 }
 
+// A value-head request of launch_gemm (whole tiles only): checked and
+// copied into the epilogue's column settings.
+static bool set_vt(ColScale &cs, const GemmVt *vt, int M, int N) {
+  if (!vt) return true;
+  if (vt->L <= 0 || vt->L % 64 || M % vt->L || vt->c0 % 16 || vt->c1 % 16 || vt->c0 < 0 || vt->c1 <= vt->c0 ||
+      vt->c1 > N)
+    return false;
+  cs.vt = (bf16 *)vt->vt;
+  cs.vc0 = vt->c0;
+  cs.vc1 = vt->c1;
+  cs.L = vt->L;
+  return true;
+}
+
 hipError_t launch_gemm_fp8(bool swiglu, const void *aq, const float *sa, const void *wq, const float *sw, void *c,
-                           int M, int N, int K, hipStream_t s, float *part, size_t part_bytes) {
+                           int M, int N, int K, hipStream_t s, float *part, size_t part_bytes, int scale_cols,
+                           float col_scale, const GemmVt *vt) {
   GemmChoice ch{0, 0, 1, 0};
   if (part) {
     ch = gemm_choose_fp8(M, N, K, swiglu);
     if (part_bytes < ch.part_bytes) ch = GemmChoice{0, 0, 1, 0};
   }
+  ColScale cs{scale_cols, col_scale};
+  // the value heads go to V^T from whole tiles only (the caller checks
+  // gemm_choose_fp8 first); the SwiGLU product has no column settings
+  if (!set_vt(cs, vt, M, N) || (vt && (swiglu || ch.sk_tiles > 0)) || (swiglu && scale_cols))
+    return hipErrorInvalidValue;
   if (swiglu) return launch_fp8_t<EPI_SWIGLU>(aq, sa, wq, sw, c, M, N, K, s, ch.sk_tiles, ch.segs, part);
-  return launch_fp8_t<EPI_STORE>(aq, sa, wq, sw, c, M, N, K, s, ch.sk_tiles, ch.segs, part);
+  return launch_fp8_t<EPI_STORE>(aq, sa, wq, sw, c, M, N, K, s, ch.sk_tiles, ch.segs, part, cs);
 }
 
 template <typename T, int BM, int BN, int BKB, int STAGES, int WM, int WN, int EPI, bool PIPE = false>
@@ -903,15 +923,7 @@ hipError_t launch_gemm(bool f32, const void *a, const void *w, void *c, int M, i
                        hipStream_t s, int variant, int group_m, float *part, size_t part_bytes, int scale_cols,
                        float col_scale, const GemmVt *vt) {
   ColScale cs{scale_cols, col_scale};
-  if (vt) {
-    if (f32 || vt->L <= 0 || vt->L % 64 || M % vt->L || vt->c0 % 16 || vt->c1 % 16 || vt->c0 < 0 ||
-        vt->c1 <= vt->c0 || vt->c1 > N)
-      return hipErrorInvalidValue;
-    cs.vt = (bf16 *)vt->vt;
-    cs.vc0 = vt->c0;
-    cs.vc1 = vt->c1;
-    cs.L = vt->L;
-  }
+  if ((vt && f32) || !set_vt(cs, vt, M, N)) return hipErrorInvalidValue;
   return gemm_dispatch<EPI_STORE>(f32, variant, group_m, a, w, c, M, N, K, s, part, part_bytes, cs);
 }
 

@@ -40,12 +40,16 @@ def quantize_on_gpu(dev, x, dtype):
     return Q, S
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_quantize_fp8_bit_exact(dev, dtype):
+@pytest.mark.parametrize("dtype,k", [("bf16", 4096), ("f32", 4096), ("bf16", 11008), ("bf16", 16384),
+                                     ("bf16", 20480), ("bf16", 272)])
+def test_quantize_fp8_bit_exact(dev, dtype, k):
     """Every code and every scale equal the oracle's (same float32 decisions):
-    rows of very different magnitude, a zero row, a row reaching subnormal codes."""
+    rows of very different magnitude, a zero row, a row reaching subnormal
+    codes; bf16 rows up to 16384 wide take the one-pass kernel (row in
+    registers, partly filled chunks at 11008 and 272), wider ones and fp32
+    the two-pass one."""
     cfg = datagen.get_config("c1")
-    a, _ = datagen.gemm_operands(cfg, 37, 8, 4096, tag=301)
+    a, _ = datagen.gemm_operands(cfg, 37, 8, k, tag=301)
     a = a * np.geomspace(1e-4, 30.0, 37)[:, None].astype(np.float32)
     a[5] = 0.0
     a[9, :100] *= 1e-5
