@@ -420,6 +420,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stack", action="store_true")
     ap.add_argument("--stack-steps", type=int, default=5)
+    ap.add_argument("--only-headline", action="store_true",
+                    help="the 1024 px block step alone (no other workloads, no stack, no CPU baseline): "
+                         "the command the committed kernel-trace summary profiles")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the block's data-parallel "
@@ -494,6 +497,9 @@ def main() -> int:
         "mfma_frac": step_flops / (elapsed / args.steps) / 1e12 / PEAK_BF16_TFLOPS,
         "kernels": kernels, "roofline": roofline,
     }
+    if args.only_headline:
+        print(json.dumps(out), flush=True)
+        return 0
     out["configs"] = bench_configs(dit, torch, W, W1, W2, args.steps, args.warmup)
     out["fp8"] = bench_fp8(dit, torch, cfg)
     out["fp8_block"] = bench_fp8_block(dit, torch, cfg, c, W, X, Tt, W1, W2, M, args.steps, args.warmup)

@@ -8,10 +8,12 @@ Three steps, each a command of its own:
        rocprofv3 --pmc <one pass of counters> --output-format csv -d OUT/<pass> -o p -- python3 bench_counters.py run
 
    It runs, in this order: a calibration copy (128 Mi float32 read = 512
-   MiB, 128 Mi bf16 written = 256 MiB, plain vector loads and stores), two
-   steps of the 1024 px block (timestep modulation + one block, B = 2, L =
-   4608), then two steps of the same block at B = 1 (the per-block shapes
-   of the 60-block stack).  Seeded synthetic inputs, bf16.
+   MiB, 128 Mi bf16 written = 256 MiB, plain vector loads and stores), the
+   row-wise e4m3 quantisation of the four weight matrices (set-up, not
+   reported), two steps of the 1024 px block (timestep modulation + one
+   block, B = 2, L = 4608), two steps of the same block at B = 1 (the
+   per-block shapes of the 60-block stack), then two steps of the 8-bit
+   block at B = 2.  Seeded synthetic inputs, bf16.
 
 2. ``python3 bench_counters.py summarize OUT`` -- reads every pass under
    OUT (one sub-directory per pass, named as in PASSES), labels each
@@ -102,16 +104,26 @@ def run() -> None:
     w = device.weights_to_device(datagen.block_weights(cfg3), "bf16")
     t, w_t1, w_t2 = datagen.timestep_inputs(cfg3)
     W1, W2 = device.to_device(w_t1, "f32"), device.to_device(w_t2, "f32")
-    for cfg in (cfg3, datagen.get_config("c4")):
+    w8 = {n: w[n] for n in ("mod_bias", "norm1_w", "norm2_w")}
+    for name, sname in (("w_qkvg", "s_qkvg"), ("w_o", "s_o"), ("w_13", "s_13"), ("w_2", "s_2")):
+        w8[name] = torch.empty(w[name].shape, dtype=torch.uint8, device="cuda")
+        w8[sname] = torch.empty(w[name].shape[0], dtype=torch.float32, device="cuda")
+        dit.quantize_fp8(w[name], w8[name], w8[sname])
+    torch.cuda.synchronize()
+    for cfg, fp8 in ((cfg3, False), (datagen.get_config("c4"), False), (cfg3, True)):
         c = dit.config_of(cfg)
         X = device.to_device(datagen.activations(cfg).reshape(cfg.tokens, cfg.hidden), "bf16")
         Y = torch.empty_like(X)
         T = device.to_device(t[:cfg.batch], "f32")
         M = torch.empty((cfg.batch, 6, cfg.hidden), dtype=torch.float32, device="cuda")
-        ws = torch.empty(dit.workspace_size(c), dtype=torch.uint8, device="cuda")
+        ws = torch.empty(dit.workspace_size_fp8(c) if fp8 else dit.workspace_size(c), dtype=torch.uint8,
+                         device="cuda")
         for _ in range(2):
             dit.timestep_mod(c, T, W1, W2, M, ws)
-            dit.block_fwd(c, w, X, Y, M, ws)
+            if fp8:
+                dit.block_fwd_fp8(c, w8, X, Y, M, ws)
+            else:
+                dit.block_fwd(c, w, X, Y, M, ws)
         torch.cuda.synchronize()
         del X, Y, ws
     print("done", flush=True)
@@ -124,7 +136,7 @@ def _short(name: str) -> str:
         return "torch"
     for k in ("gemm_sk_fixup", "gemm_kernel", "gemm_pp_kernel", "gemm_fp8_kernel", "attn_kernel", "vtrans_kernel",
               "resid_modnorm_kernel", "resid_kernel", "modnorm_kernel", "tmod_stage1", "tmod_stage2_fewb",
-              "tmod_stage2", "qk_prologue_kernel"):
+              "tmod_stage2", "qk_prologue_kernel", "quantize_fp8_rows_reg", "quantize_fp8_kernel"):
         if k in name:
             return k
     return m.group(1) if m else name[:40]
@@ -146,7 +158,7 @@ def _dispatches(pass_dir: str) -> list[dict]:
 def _label(disp: list[dict]) -> list[tuple[str, str, dict]]:
     """(workload, kernel label, counters) per dispatch of the block steps,
     fixup passes merged into their GEMM; plus ("calib", "copy", ...)."""
-    out, step, gemm_i = [], -1, 0
+    out, step, gemm_i, quant_i = [], -1, 0, 0
     gemm_names = ["gemm_qkvg", "gemm_o", "gemm_w13", "gemm_w2"]
     for d in disp:
         k = _short(d["name"])
@@ -156,12 +168,17 @@ def _label(disp: list[dict]) -> list[tuple[str, str, dict]]:
             continue
         if k == "tmod_stage1":
             step += 1
-            gemm_i = 0
-        wl = "1024px_B2" if step < 2 else "1024px_B1"
+            gemm_i = quant_i = 0
+        if step < 0:  # set-up (the weights' quantisation)
+            continue
+        wl = WORKLOADS[min(step // 2, len(WORKLOADS) - 1)]
         cnt = dict(d["counters"], DURATION_NS=float(d["ns"]))
-        if k in ("gemm_kernel", "gemm_pp_kernel"):
+        if k in ("gemm_kernel", "gemm_pp_kernel", "gemm_fp8_kernel"):
             out.append((wl, gemm_names[min(gemm_i, 3)], cnt))
             gemm_i += 1
+        elif k.startswith("quantize_fp8"):
+            out.append((wl, ("quant_og", "quant_u")[min(quant_i, 1)], cnt))
+            quant_i += 1
         elif k == "gemm_sk_fixup":
             prev = out[-1][2]  # the fixup pass belongs to the GEMM before it (its time too)
             for c, v in dict(d["counters"], DURATION_NS=float(d["ns"])).items():
@@ -174,8 +191,15 @@ def _label(disp: list[dict]) -> list[tuple[str, str, dict]]:
     return out
 
 
+WORKLOADS = ["1024px_B2", "1024px_B1", "1024px_B2_fp8"]
+
+
+def _tokens(wl: str) -> int:
+    return 4608 if wl == "1024px_B1" else 9216
+
+
 def _flops(wl: str, kern: str) -> float | None:
-    T = 9216 if wl == "1024px_B2" else 4608
+    T = _tokens(wl)
     L, D, F, nq = 4608, 4096, 11008, 10240
     per = {"gemm_qkvg": 2 * D * nq, "gemm_o": 2 * D * D, "gemm_w13": 2 * D * 2 * F, "gemm_w2": 2 * F * D,
            "attn": 4 * L * D}
@@ -183,13 +207,19 @@ def _flops(wl: str, kern: str) -> float | None:
 
 
 def _bytes(wl: str, kern: str) -> float | None:
-    T, D = (9216 if wl == "1024px_B2" else 4608), 4096
+    T, D, F = _tokens(wl), 4096, 11008
     # modnorm1: x, h1 bf16; resid1+modnorm2: x, A bf16 in, x1 fp32 and h2
     # bf16 out; resid2: x1 fp32 and M in, x_out bf16 out; the V^T pass: V
-    # in, V^T out; W13: h2, W13 and U once
-    per = {"modnorm1": 4 * D, "resid1+modnorm2": 10 * D, "resid2": 8 * D, "vtrans": 4 * 8 * 128}
-    if kern == "gemm_w13":
-        return 2 * (T * D + 2 * 11008 * D + T * 11008)
+    # in, V^T out; W13: h2, W13 and U once.  8-bit block: h1 and h2 leave
+    # as one-byte codes; the quantiser reads Og or U once and writes codes
+    if wl.endswith("fp8"):
+        per = {"modnorm1": 3 * D, "resid1+modnorm2": 9 * D, "resid2": 8 * D, "quant_og": 3 * D, "quant_u": 3 * F}
+        if kern == "gemm_w13":
+            return T * D + 2 * F * D + 2 * T * F
+    else:
+        per = {"modnorm1": 4 * D, "resid1+modnorm2": 10 * D, "resid2": 8 * D, "vtrans": 4 * 8 * 128}
+        if kern == "gemm_w13":
+            return 2 * (T * D + 2 * F * D + T * F)
     v = per.get(kern)
     return v * T if v else None
 
@@ -226,8 +256,10 @@ def summarize(out_dir: str) -> None:
             r["mfma_busy"] = a["SQ_VALU_MFMA_BUSY_CYCLES"] / (clk * CUS * SIMDS)
         fl = _flops(wl, k)
         if fl and clk:
+            # the 8-bit products against the FP8 peak (twice the bf16 FLOPs per clock)
+            peak = 2 * FLOP_PER_CLK_CU if (wl.endswith("fp8") and k.startswith("gemm")) else FLOP_PER_CLK_CU
             r["flops_per_clk_per_cu"] = fl / clk / CUS
-            r["mfma_frac_of_clock_peak"] = fl / clk / CUS / FLOP_PER_CLK_CU
+            r["mfma_frac_of_clock_peak"] = fl / clk / CUS / peak
         if "SQ_WAVES" in a and a["SQ_WAVES"]:
             w = a["SQ_WAVES"]
             for n, lab in (("SQ_INSTS_VALU", "valu_per_wave"), ("SQ_INSTS_MFMA", "mfma_per_wave"),
@@ -253,7 +285,7 @@ def summarize(out_dir: str) -> None:
         res[f"{wl}/{k}"] = r
     rec = {"kernels": res, "calibration": {n: v for n, v in calib.items()},
            "sources_sha256_16": {f: code_hash(os.path.join(ROOT, "diffusion_transformer_image_amd", "csrc", f))
-                                 for f in ("gemm.hip", "attention.hip", "elementwise.hip")}}
+                                 for f in ("gemm.hip", "attention.hip", "elementwise.hip", "fp8.hip")}}
     base = os.path.join(ROOT, "profiles", "counters_block_1024px")
     json.dump(rec, open(base + ".json", "w"), indent=1)
     cols = [("duration_us", "us", "{:.1f}"), ("clock_ghz", "GHz", "{:.2f}"), ("mfma_busy", "MFMA busy", "{:.3f}"), ("mfma_frac_of_clock_peak", "FLOPs / clock peak", "{:.3f}"),
@@ -269,7 +301,9 @@ def summarize(out_dir: str) -> None:
           "cd /tmp && export TMPDIR=/tmp\n", "\n".join(commands()), "\n",
           "python3 $R/bench_counters.py summarize $R/gpurun_out/counters\n```\n\n",
           "Workloads: `1024px_B2` = the benchmarked block (B = 2, L = 4608); `1024px_B1` = the same block at "
-          "B = 1 (the shapes of each block of the 60-block stack).  Averages of two steps.  MB columns are "
+          "B = 1 (the shapes of each block of the 60-block stack); `1024px_B2_fp8` = the 8-bit block "
+          "(row-wise e4m3 projections) at B = 2, its GEMMs' FLOPs / clock peak against the FP8 rate "
+          "(8192 FLOPs per clock and CU).  Averages of two steps.  MB columns are "
           "per launch (1e6 bytes), scaled by the counters' reading per byte of a calibration copy; "
           "DRAM-side requests include hits in the memory-side last-level cache.\n\n",
           "| kernel | " + " | ".join(c[1] for c in cols) + " |\n", "|---" * (len(cols) + 1) + "|\n"]
