@@ -482,9 +482,11 @@ __global__ __launch_bounds__(256) void tmod_stage1(const float *__restrict__ t,
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int half = tdim / 2;
   const int r0 = blockIdx.x * 16 + wave * 4;
-  for (int b0 = 0; b0 < B; b0 += TM1_NB) {
+  // one chunk of TM1_NB samples per grid row (at 256 px, B = 32, a loop over
+  // the 8 chunks inside 256 workgroups took 59 us, latency-bound)
+  {
+    const int b0 = blockIdx.y * TM1_NB;
     const int nb = min(TM1_NB, B - b0);
-    __syncthreads();  // the previous chunk's embeddings are no longer read
     for (int idx = threadIdx.x; idx < nb * half; idx += blockDim.x) {
       const int bb = idx / half, i = idx - bb * half;
       const double f = exp(-log(10000.0) * (double)i / (double)half);
@@ -536,66 +538,7 @@ __global__ __launch_bounds__(256) void tmod_stage1(const float *__restrict__ t,
 }
 
 // Stage 2: mod[b][o] = sum_r W[o][r] zs[b][r], o < O (O = 6D for the block
-// modulation, 2D for the final norm's shift and scale).  Each wave owns
-// two output rows; a chunk of zs for up to 32 samples is staged in LDS and
-// W_t2 is streamed from HBM once per 32 samples.
-__global__ __launch_bounds__(256) void tmod_stage2(const float *__restrict__ zs,
-                                                   const float *__restrict__ w2,
-                                                   float *__restrict__ mod, int B, int D, int O) {
-  constexpr int KC = 256, BMAX = 32, NR = 2;
-  __shared__ f32x4 zl[BMAX][KC / 4];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int o0 = (blockIdx.x * 4 + wave) * NR;
-  for (int b0 = 0; b0 < B; b0 += BMAX) {
-    const int nb = min(BMAX, B - b0);
-    float acc[NR][BMAX];
-#pragma unroll
-    for (int r = 0; r < NR; ++r)
-#pragma unroll
-      for (int b = 0; b < BMAX; ++b) acc[r][b] = 0.f;
-    for (int k0 = 0; k0 < D; k0 += KC) {
-      __syncthreads();
-      for (int i = threadIdx.x; i < nb * (KC / 4); i += blockDim.x) {
-        const int b = i / (KC / 4), c = i % (KC / 4);
-        const int k = k0 + 4 * c;
-        f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        if (k < D) z = *reinterpret_cast<const f32x4 *>(zs + (size_t)(b0 + b) * D + k);
-        zl[b][c] = z;
-      }
-      __syncthreads();
-      const int k = k0 + 4 * lane;
-      if (k < D) {
-        f32x4 w[NR];
-#pragma unroll
-        for (int r = 0; r < NR; ++r) {
-          const float *wp = w2 + (size_t)(o0 + r) * D + k;
-          // read once when one chunk covers every sample, else once per chunk
-          w[r] = (o0 + r >= O) ? f32x4{0.f, 0.f, 0.f, 0.f}
-                 : (B <= BMAX) ? stream_load(wp) : *reinterpret_cast<const f32x4 *>(wp);
-        }
-#pragma unroll
-        for (int b = 0; b < BMAX; ++b) {
-          if (b < nb) {
-            const f32x4 z = zl[b][lane];
-#pragma unroll
-            for (int r = 0; r < NR; ++r)
-              acc[r][b] += w[r].x * z.x + w[r].y * z.y + w[r].z * z.z + w[r].w * z.w;
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int b = 0; b < BMAX; ++b) {
-      if (b < nb) {
-#pragma unroll
-        for (int r = 0; r < NR; ++r) {
-          const float s = wave_sum(acc[r][b]);
-          if (lane == 0 && o0 + r < O) mod[(size_t)(b0 + b) * O + o0 + r] = s;
-        }
-      }
-    }
-  }
-}
+// modulation, 2D for the final norm's shift and scale).
 
 // Stage 2 for few samples (B <= 4): the whole SiLU'd hidden of every sample
 // sits in LDS, so each wave streams 4 rows of W_t2 at a time over the full K
@@ -657,9 +600,106 @@ __global__ __launch_bounds__(256) void tmod_stage2_fewb(const float *__restrict_
   }
 }
 
+// Stage 2 for more samples (B > 4): the map is a skinny fp32 product
+// mod[B, O] = zs[B, D] W[O, D]^T, streamed once per 16 * NSB samples on
+// the fp32 matrix cores (v_mfma_f32_16x16x4f32: W rows as the 16-row
+// operand, samples as the 16 columns).  A workgroup owns TMM_RB blocks of 16
+// rows; its TMM_W waves split K into contiguous ranges of 64-k chunks and
+// their partial sums are added through LDS.  Each lane loads 16 bytes (4
+// consecutive k) of one W row and of one sample per 16-k step, and the four
+// k of a 16-byte piece feed four MFMAs in the same order on both operands,
+// so every k is summed once.  zs (B * D floats) is read from L2.
+// 4 K ranges per workgroup measured against 8 on one box: 256 px (B = 32)
+// 218 against 227 us, 512 px (B = 8) 128 against 126 us; the previous VALU
+// kernel (hidden vectors staged per 256-k chunk in LDS) took 367 and 144 us
+constexpr int TMM_RB = 2, TMM_U = 4, TMM_W = 4;
+template <int NSB>
+__global__ __launch_bounds__(TMM_W * 64) void tmod_stage2_mfma(const float *__restrict__ zs,
+                                                               const float *__restrict__ w2,
+                                                               float *__restrict__ mod, int B, int D, int O) {
+  __shared__ f32x4 red[TMM_W][TMM_RB * NSB][64];  // per wave: its partial C blocks, lane-major
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int o0 = blockIdx.x * (16 * TMM_RB);
+  const int nc = (D + 16 * TMM_U - 1) / (16 * TMM_U);  // 64-k chunks
+  const int c_beg = wave * nc / TMM_W, c_end = (wave + 1) * nc / TMM_W;
+  for (int b0 = 0; b0 < B; b0 += 16 * NSB) {
+    f32x4 acc[TMM_RB][NSB];
+#pragma unroll
+    for (int rb = 0; rb < TMM_RB; ++rb)
+#pragma unroll
+      for (int sb = 0; sb < NSB; ++sb) acc[rb][sb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // chunk c+1's loads are issued before chunk c's MFMAs (two register sets)
+    f32x4 wv[TMM_U][TMM_RB], zv[TMM_U][NSB], wn[TMM_U][TMM_RB], zn[TMM_U][NSB];
+    auto load_chunk = [&](int c, f32x4 (&w)[TMM_U][TMM_RB], f32x4 (&z)[TMM_U][NSB]) {
+      const int k0 = c * 16 * TMM_U;
+#pragma unroll
+      for (int u = 0; u < TMM_U; ++u) {
+        const int k = k0 + 16 * u + 4 * g;
+        const bool kin = c < c_end && k < D;
+#pragma unroll
+        for (int rb = 0; rb < TMM_RB; ++rb) {
+          const int o = o0 + rb * 16 + r16;
+          w[u][rb] = (kin && o < O) ? stream_load(w2 + (size_t)o * D + k) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int sb = 0; sb < NSB; ++sb) {
+          const int b = b0 + sb * 16 + r16;
+          z[u][sb] = (kin && b < B) ? *reinterpret_cast<const f32x4 *>(zs + (size_t)b * D + k)
+                                    : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+    };
+    load_chunk(c_beg, wn, zn);
+    for (int c = c_beg; c < c_end; ++c) {
+#pragma unroll
+      for (int u = 0; u < TMM_U; ++u) {
+#pragma unroll
+        for (int rb = 0; rb < TMM_RB; ++rb) wv[u][rb] = wn[u][rb];
+#pragma unroll
+        for (int sb = 0; sb < NSB; ++sb) zv[u][sb] = zn[u][sb];
+      }
+      load_chunk(c + 1, wn, zn);
+#pragma unroll
+      for (int u = 0; u < TMM_U; ++u)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int rb = 0; rb < TMM_RB; ++rb)
+#pragma unroll
+            for (int sb = 0; sb < NSB; ++sb)
+              acc[rb][sb] = __builtin_amdgcn_mfma_f32_16x16x4f32(wv[u][rb][j], zv[u][sb][j], acc[rb][sb], 0, 0, 0);
+    }
+    // the K ranges' partial blocks meet in LDS; each thread then adds the
+    // TMM_W partials of (block, lane) slots
+    __syncthreads();  // the previous sample group's slots have been read
+#pragma unroll
+    for (int rb = 0; rb < TMM_RB; ++rb)
+#pragma unroll
+      for (int sb = 0; sb < NSB; ++sb) red[wave][rb * NSB + sb][lane] = acc[rb][sb];
+    __syncthreads();
+    for (int e = threadIdx.x; e < TMM_RB * NSB * 64; e += blockDim.x) {
+      const int blk = e / 64, l = e % 64;
+      const int rb = blk / NSB, sb = blk % NSB;
+      f32x4 v = red[0][blk][l];
+#pragma unroll
+      for (int w = 1; w < TMM_W; ++w) v += red[w][blk][l];
+      // C of a 16x16 block: lane l holds rows 4 (l / 16) + i of column l % 16
+      const int b = b0 + sb * 16 + (l & 15);
+      if (b >= B) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int o = o0 + rb * 16 + 4 * (l >> 4) + i;
+        if (o < O) mod[(size_t)b * O + o] = v[i];
+      }
+    }
+  }
+}
+
 hipError_t launch_tmod(const float *t, const float *w1, const float *w2, float *mod, float *zs,
                        int B, int D, int tdim, hipStream_t s) {
-  hipLaunchKernelGGL(tmod_stage1, dim3((D + 15) / 16), dim3(256), 0, s, t, w1, zs, B, D, tdim);
+  hipLaunchKernelGGL(tmod_stage1, dim3((D + 15) / 16, (B + TM1_NB - 1) / TM1_NB), dim3(256), 0, s, t, w1, zs, B, D,
+                     tdim);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_tmod_map(zs, w2, mod, B, D, 6 * D, s);
@@ -669,8 +709,17 @@ hipError_t launch_tmod_map(const float *zs, const float *w, float *out, int B, i
   if (B <= TM_NB && (size_t)B * D * sizeof(float) <= 64 * 1024)
     hipLaunchKernelGGL(tmod_stage2_fewb, dim3((O + 63) / 64), dim3(256), (size_t)B * D * sizeof(float), s,
                        zs, w, out, B, D, O);
-  else
-    hipLaunchKernelGGL(tmod_stage2, dim3((O + 7) / 8), dim3(256), 0, s, zs, w, out, B, D, O);
+  else {
+    // blocks of 16 samples per pass over W: as many as B needs, at most 4
+    const dim3 grid((O + 16 * TMM_RB - 1) / (16 * TMM_RB)), block(TMM_W * 64);
+    const int nsb = (B + 15) / 16;
+    if (nsb <= 1)
+      hipLaunchKernelGGL(tmod_stage2_mfma<1>, grid, block, 0, s, zs, w, out, B, D, O);
+    else if (nsb <= 2)
+      hipLaunchKernelGGL(tmod_stage2_mfma<2>, grid, block, 0, s, zs, w, out, B, D, O);
+    else
+      hipLaunchKernelGGL(tmod_stage2_mfma<4>, grid, block, 0, s, zs, w, out, B, D, O);
+  }
   return hipGetLastError();
 }
 
