@@ -28,7 +28,7 @@ EXPORTS = (
     "dit_timer_stop", "dit_gemm_splitk", "dit_gemm_plan", "dit_block_fwd_ex", "dit_stack_fwd_ex",
     "dit_qk_prologue", "dit_model_workspace_size", "dit_model_velocity", "dit_sample", "dit_quantize_fp8",
     "dit_gemm_fp8", "dit_quantize_fp8_tensor", "dit_attention_ex", "dit_timestep_mod_noalloc",
-    "dit_workspace_size_fp8", "dit_block_fwd_fp8",
+    "dit_workspace_size_fp8", "dit_block_fwd_fp8", "dit_sample_cfg_workspace_size", "dit_sample_cfg",
 )
 
 
@@ -112,6 +112,10 @@ def lib() -> ctypes.CDLL:
                                          vp]),
             "dit_sample": (i32, [cfgp, ctypes.POINTER(ModelConfig), ctypes.POINTER(Prologue),
                                  ctypes.POINTER(ModelWeights), i32, wp, vp, i32, ctypes.c_float, vp, vp, sz, vp]),
+            "dit_sample_cfg_workspace_size": (sz, [cfgp, ctypes.POINTER(ModelConfig)]),
+            "dit_sample_cfg": (i32, [cfgp, ctypes.POINTER(ModelConfig), ctypes.POINTER(Prologue),
+                                     ctypes.POINTER(ModelWeights), i32, wp, vp, i32, ctypes.c_float, ctypes.c_float,
+                                     vp, vp, vp, sz, vp]),
             "dit_stack_fwd": (i32, [cfgp, i32, wp, vp, vp, vp, vp, sz, vp]),
             "dit_timestep_mod": (i32, [cfgp, i32, vp, vp, vp, vp, vp, sz, vp]),
             "dit_timestep_mod_noalloc": (i32, [cfgp, i32, vp, vp, vp, vp, vp]),
@@ -286,6 +290,21 @@ def sample(cfg: Config, mc: ModelConfig, mw: Mapping, blocks: Sequence[Mapping],
     _check(lib().dit_sample(ctypes.byref(cfg), ctypes.byref(mc), None if pro is None else ctypes.byref(pro),
                             ctypes.byref(m), len(blocks), arr, _ptr(z), n_steps, float(shift), _ptr(txt), _ptr(ws),
                             nbytes, _stream(stream)), "dit_sample")
+
+
+def sample_cfg_workspace_size(cfg: Config, mc: ModelConfig) -> int:
+    return lib().dit_sample_cfg_workspace_size(ctypes.byref(cfg), ctypes.byref(mc))
+
+
+def sample_cfg(cfg: Config, mc: ModelConfig, mw: Mapping, blocks: Sequence[Mapping], z, n_steps: int, shift: float,
+               guidance: float, txt, txt_null, ws, pro: Prologue | None = None, stream=None) -> None:
+    """n_steps Euler steps with classifier-free guidance v_u + g (v_c - v_u), z updated in place."""
+    arr = (BlockWeights * len(blocks))(*[make_weights(b) for b in blocks])
+    m = make_model_weights(mw)
+    nbytes = ws.numel() * ws.element_size()
+    _check(lib().dit_sample_cfg(ctypes.byref(cfg), ctypes.byref(mc), None if pro is None else ctypes.byref(pro),
+                                ctypes.byref(m), len(blocks), arr, _ptr(z), n_steps, float(shift), float(guidance),
+                                _ptr(txt), _ptr(txt_null), _ptr(ws), nbytes, _stream(stream)), "dit_sample_cfg")
 
 
 def stack_fwd(cfg: Config, blocks: Sequence[Mapping], x_in, x_out, mod, ws, stream=None) -> None:

@@ -687,9 +687,13 @@ size_t dit_model_workspace_size(const dit_config *cfg, const dit_model_config *m
   return carve_model(cfg, mc, nullptr).bytes;
 }
 
+// io_batch: samples of z and txt when they differ from cfg->batch (the
+// guided sampler's model call runs 2B samples on B-sample inputs); need:
+// the workspace bytes when more than the model call's own.
 static dit_status check_model_call(const dit_config *cfg, const dit_model_config *mc, const dit_prologue *pro,
                                    const dit_model_weights *mw, int32_t n_blocks, const dit_block_weights *blocks,
-                                   const float *z, const void *txt, void *ws, size_t ws_bytes) {
+                                   const float *z, const void *txt, void *ws, size_t ws_bytes, int io_batch = -1,
+                                   size_t need_total = 0) {
   dit_status st = check_cfg(cfg);
   if (st != DIT_OK) return st;
   if ((st = check_prologue(cfg, pro)) != DIT_OK) return st;
@@ -702,10 +706,11 @@ static dit_status check_model_call(const dit_config *cfg, const dit_model_config
   if (!z || (mc->n_text > 0 && !txt)) return DIT_ERR_NULL;
   if (!ws) return DIT_ERR_WORKSPACE;
   if (!aligned(z) || !aligned(txt) || !aligned(ws)) return DIT_ERR_ALIGN;
-  const size_t need = carve_model(cfg, mc, nullptr).bytes;
+  const size_t need = std::max(carve_model(cfg, mc, nullptr).bytes, need_total);
   if (ws_bytes < need) return DIT_ERR_WORKSPACE;
-  const size_t zb = (size_t)cfg->batch * mc->latent_ch * 4 * mc->grid_h * mc->grid_w * 4;
-  const size_t tb = txt ? (size_t)cfg->batch * mc->n_text * mc->txt_dim * esize(cfg->dtype) : 0;
+  const size_t nb = io_batch >= 0 ? (size_t)io_batch : (size_t)cfg->batch;
+  const size_t zb = nb * mc->latent_ch * 4 * mc->grid_h * mc->grid_w * 4;
+  const size_t tb = txt ? nb * mc->n_text * mc->txt_dim * esize(cfg->dtype) : 0;
   if (overlap(ws, need, z, zb) || overlap(ws, need, txt, tb)) return DIT_ERR_SHAPE;
   for (int i = 0; i < n_blocks; ++i)
     if (overlaps_weights(cfg, &blocks[i], ws, need)) return DIT_ERR_SHAPE;
@@ -749,6 +754,94 @@ dit_status dit_sample(const dit_config *cfg, const dit_model_config *mc, const d
     if ((st = model_tokens(cfg, mc, pro, mw, n_blocks, blocks, z, (float)t0, txt, w, s)) != DIT_OK) return st;
     hipError_t e = launch_unpatchify_axpy(cfg->dtype == DIT_F32, w.vt, z, z, (float)(t1 - t0), cfg->batch,
                                           mc->latent_ch, 2 * mc->grid_h, 2 * mc->grid_w, s);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  return DIT_OK;
+}
+
+// Classifier-free guidance runs the model once on 2B samples: the
+// workspace of that model call, then z twice [2B, C, Hl, Wl] fp32 and the
+// text features of both halves [2B, n_text, txt_dim].
+struct CfgWs {
+  ModelWs m;
+  float *z2;
+  char *txt2;
+  size_t bytes;
+};
+static dit_config doubled(const dit_config *c) {
+  dit_config c2 = *c;
+  c2.batch = 2 * c->batch;
+  return c2;
+}
+static CfgWs carve_cfg(const dit_config *c, const dit_model_config *mc, void *ws) {
+  const dit_config c2 = doubled(c);
+  CfgWs w;
+  w.m = carve_model(&c2, mc, ws);
+  char *p = (char *)ws;
+  size_t off = w.m.bytes;
+  auto take = [&](size_t n) {
+    char *r = p ? p + off : nullptr;
+    off += round_up(n);
+    return r;
+  };
+  w.z2 = (float *)take((size_t)c2.batch * mc->latent_ch * 4 * mc->grid_h * mc->grid_w * 4);
+  w.txt2 = take((size_t)c2.batch * mc->n_text * mc->txt_dim * esize(c->dtype));
+  w.bytes = off;
+  return w;
+}
+
+size_t dit_sample_cfg_workspace_size(const dit_config *cfg, const dit_model_config *mc) {
+  if (check_cfg(cfg) != DIT_OK || !mc || cfg->batch > 0x3FFFFFFF) return 0;
+  const dit_config c2 = doubled(cfg);
+  if (check_cfg(&c2) != DIT_OK) return 0;
+  if (mc->latent_ch < 2 || mc->grid_h < 1 || mc->grid_w < 1) return 0;
+  return carve_cfg(cfg, mc, nullptr).bytes;
+}
+
+dit_status dit_sample_cfg(const dit_config *cfg, const dit_model_config *mc, const dit_prologue *pro,
+                          const dit_model_weights *mw, int32_t n_blocks, const dit_block_weights *blocks, float *z,
+                          int32_t n_steps, float shift, float guidance, const void *txt, const void *txt_null,
+                          void *ws, size_t ws_bytes, void *stream) {
+  dit_status st = check_cfg(cfg);
+  if (st != DIT_OK) return st;
+  if (cfg->batch > 0x3FFFFFFF) return DIT_ERR_SHAPE;
+  if (!mc) return DIT_ERR_NULL;
+  // every kernel runs the doubled batch: the model call is checked at 2B
+  // samples on B-sample inputs, against the whole workspace
+  const dit_config c2 = doubled(cfg);
+  if ((st = check_model_call(&c2, mc, pro, mw, n_blocks, blocks, z, txt, ws, ws_bytes, cfg->batch,
+                             carve_cfg(cfg, mc, nullptr).bytes)) != DIT_OK)
+    return st;
+  const size_t need = carve_cfg(cfg, mc, nullptr).bytes;
+  if (n_steps < 1 || n_steps > 100000 || !(shift > 0.f) || !std::isfinite(guidance)) return DIT_ERR_SHAPE;
+  if (mc->n_text > 0 && !txt_null) return DIT_ERR_NULL;
+  if (!aligned(txt_null)) return DIT_ERR_ALIGN;
+  const size_t zb = (size_t)cfg->batch * mc->latent_ch * 4 * mc->grid_h * mc->grid_w * 4;
+  const size_t tb = mc->n_text ? (size_t)cfg->batch * mc->n_text * mc->txt_dim * esize(cfg->dtype) : 0;
+  if (overlap(ws, need, z, zb) || overlap(ws, need, txt, tb) || overlap(ws, need, txt_null, tb) ||
+      overlap(z, zb, txt_null, tb))
+    return DIT_ERR_SHAPE;
+  hipStream_t s = (hipStream_t)stream;
+  const CfgWs w = carve_cfg(cfg, mc, ws);
+  if (tb) {  // samples 0..B-1 conditional, B..2B-1 unconditional
+    DIT_TRY(hipMemcpyAsync(w.txt2, txt, tb, hipMemcpyDeviceToDevice, s));
+    DIT_TRY(hipMemcpyAsync(w.txt2 + tb, txt_null, tb, hipMemcpyDeviceToDevice, s));
+  }
+  auto sched = [&](int i) {  // s u / (1 + (s - 1) u), u = 1 - i / n
+    const double u = 1.0 - (double)i / n_steps, sh = shift;
+    return sh * u / (1.0 + (sh - 1.0) * u);
+  };
+  const size_t half_tok = (size_t)cfg->batch * mc->grid_h * mc->grid_w * 4 * mc->latent_ch * esize(cfg->dtype);
+  for (int i = 0; i < n_steps; ++i) {
+    const double t0 = sched(i), t1 = sched(i + 1);
+    DIT_TRY(hipMemcpyAsync(w.z2, z, zb, hipMemcpyDeviceToDevice, s));
+    DIT_TRY(hipMemcpyAsync((char *)w.z2 + zb, z, zb, hipMemcpyDeviceToDevice, s));
+    if ((st = model_tokens(&c2, mc, pro, mw, n_blocks, blocks, w.z2, (float)t0, w.txt2, w.m, s)) != DIT_OK)
+      return st;
+    // velocity tokens: the conditional half first, then the unconditional
+    hipError_t e = launch_unpatchify_axpy(cfg->dtype == DIT_F32, w.m.vt, z, z, (float)(t1 - t0), cfg->batch,
+                                          mc->latent_ch, 2 * mc->grid_h, 2 * mc->grid_w, s, w.m.vt + half_tok,
+                                          guidance);
     if (e != hipSuccess) return hip_fail(e);
   }
   return DIT_OK;

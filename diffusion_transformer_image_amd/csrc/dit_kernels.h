@@ -37,9 +37,11 @@ hipError_t launch_tmod_map(const float *zs, const float *w, float *out, int B, i
 // boundary layers of the stack
 hipError_t launch_fill(float *p, float v, size_t n, hipStream_t s);
 hipError_t launch_patchify(bool f32, const float *z, void *p, int B, int C, int Hl, int Wl, hipStream_t s);
-// out = z + dt * unpatchify(vtok) (z may alias out, or be NULL for dt * v)
+// out = z + dt * unpatchify(vtok) (z may alias out, or be NULL for dt * v);
+// with vtok_uncond, the velocity is vu + guidance * (v - vu)
 hipError_t launch_unpatchify_axpy(bool f32, const void *vtok, const float *z, float *out, float dt, int B, int C,
-                                  int Hl, int Wl, hipStream_t s);
+                                  int Hl, int Wl, hipStream_t s, const void *vtok_uncond = nullptr,
+                                  float guidance = 1.f);
 // variant < 0 picks the default tile configuration for the shape (0 / 1:
 // whole 256- / 192-row tiles); group_m <= 0 the default tile-grouping width
 // (row tiles per L2 group).  part (fp32, part_bytes) lets the default

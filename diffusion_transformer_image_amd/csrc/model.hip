@@ -50,11 +50,13 @@ hipError_t launch_patchify(bool f32, const float *z, void *p, int B, int C, int 
 }
 
 // One thread per (token, c, dy): out[b][c][2py+dy][2px + {0,1}] =
-// z + dt * vtok[token][c*4 + dy*2 + {0,1}].
+// z + dt * vtok[token][c*4 + dy*2 + {0,1}].  With vu (the unconditional
+// velocity tokens of classifier-free guidance) the velocity is vu + g (v -
+// vu) instead.
 template <typename T>
 __global__ __launch_bounds__(256) void unpatchify_axpy_kernel(const T *__restrict__ v, const float *z,
                                                                float *out, float dt, int B, int C, int Hl,
-                                                               int Wl) {
+                                                               int Wl, const T *__restrict__ vu, float g) {
   const int gw = Wl / 2, gh = Hl / 2, ntok = gh * gw;
   const size_t n = (size_t)B * ntok * C * 2;
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
@@ -65,7 +67,14 @@ __global__ __launch_bounds__(256) void unpatchify_axpy_kernel(const T *__restric
     const int py = t / gw, px = t % gw;
     const T *src = v + tok * (4 * C) + c * 4 + dy * 2;
     const size_t o = (((size_t)b * C + c) * Hl + 2 * py + dy) * Wl + 2 * px;
-    f32x2 r = {dt * to_f32(src[0]), dt * to_f32(src[1])};
+    float v0 = to_f32(src[0]), v1 = to_f32(src[1]);
+    if (vu) {
+      const T *su = vu + tok * (4 * C) + c * 4 + dy * 2;
+      const float u0 = to_f32(su[0]), u1 = to_f32(su[1]);
+      v0 = u0 + g * (v0 - u0);
+      v1 = u1 + g * (v1 - u1);
+    }
+    f32x2 r = {dt * v0, dt * v1};
     if (z) {
       const f32x2 zz = *reinterpret_cast<const f32x2 *>(z + o);
       r[0] += zz[0];
@@ -76,15 +85,15 @@ __global__ __launch_bounds__(256) void unpatchify_axpy_kernel(const T *__restric
 }
 
 hipError_t launch_unpatchify_axpy(bool f32, const void *vtok, const float *z, float *out, float dt, int B, int C,
-                                  int Hl, int Wl, hipStream_t s) {
+                                  int Hl, int Wl, hipStream_t s, const void *vtok_uncond, float guidance) {
   const size_t n = (size_t)B * (Hl / 2) * (Wl / 2) * C * 2;
   const int grid = (int)std::min<size_t>((n + 255) / 256, 8192);
   if (f32)
     hipLaunchKernelGGL(unpatchify_axpy_kernel<float>, dim3(grid), dim3(256), 0, s, (const float *)vtok, z, out, dt,
-                       B, C, Hl, Wl);
+                       B, C, Hl, Wl, (const float *)vtok_uncond, guidance);
   else
     hipLaunchKernelGGL(unpatchify_axpy_kernel<bf16>, dim3(grid), dim3(256), 0, s, (const bf16 *)vtok, z, out, dt,
-                       B, C, Hl, Wl);
+                       B, C, Hl, Wl, (const bf16 *)vtok_uncond, guidance);
   return hipGetLastError();
 }
 

@@ -250,12 +250,33 @@ dit_status dit_model_velocity(const dit_config *cfg /* host */, const dit_model_
 /* n_steps Euler steps of the rectified-flow sampler on z (in place, fp32):
  *   t_i = s u_i / (1 + (s - 1) u_i), u_i = 1 - i / n_steps (t_0 = 1, t_n = 0),
  *   z <- z + (t_{i+1} - t_i) v(z, t_i)
- * with v as in dit_model_velocity (no classifier-free guidance: the pages
- * treat it as an optional control).  n_steps >= 1, shift s > 0. */
+ * with v as in dit_model_velocity (dit_sample_cfg adds classifier-free
+ * guidance).  n_steps >= 1, shift s > 0. */
 dit_status dit_sample(const dit_config *cfg /* host */, const dit_model_config *mc /* host */,
                       const dit_prologue *pro /* host */, const dit_model_weights *mw /* host */, int32_t n_blocks,
                       const dit_block_weights *blocks /* host [n_blocks] */, float *z, int32_t n_steps,
                       float shift, const void *txt, void *ws, size_t ws_bytes, void *stream);
+
+/* The sampler with classifier-free guidance (page "Krea 2 技术报告",
+ * 训练 › 强化学习: guidance stays an optional control at inference; the
+ * guidance of Ho and Salimans cited there): every step's velocity is
+ *   v = v_u + guidance (v_c - v_u),
+ * v_c the model's velocity under the text features txt, v_u under txt_null
+ * (the caller's unconditional features, e.g. those of the empty prompt; the
+ * pages do not say which), both evaluated as one batch of 2B samples (cfg
+ * describes the B samples of z).  guidance = 1 gives dit_sample's steps
+ * (up to rounding order), 0 the unconditional ones.  z [B, C, Hl, Wl] fp32
+ * in place; txt, txt_null [B, n_text, txt_dim] dtype (txt_null may be NULL
+ * only when n_text == 0).  Workspace: dit_sample_cfg_workspace_size bytes
+ * (the model call at 2B, z twice and both text halves); it must not overlap
+ * z, txt, txt_null or any weight.  Errors as dit_sample, plus DIT_ERR_SHAPE
+ * for a non-finite guidance. */
+size_t dit_sample_cfg_workspace_size(const dit_config *cfg /* host */, const dit_model_config *mc /* host */);
+dit_status dit_sample_cfg(const dit_config *cfg /* host */, const dit_model_config *mc /* host */,
+                          const dit_prologue *pro /* host */, const dit_model_weights *mw /* host */,
+                          int32_t n_blocks, const dit_block_weights *blocks /* host [n_blocks] */, float *z,
+                          int32_t n_steps, float shift, float guidance, const void *txt, const void *txt_null,
+                          void *ws, size_t ws_bytes, void *stream);
 
 /* Shared timestep modulation of every sample:
  *   e = [cos(1000 t f_i), sin(1000 t f_i)], f_i = 10000^(-i/(t_dim/2)),

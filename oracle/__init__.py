@@ -49,6 +49,11 @@ Parity status (what pins each function; see the tests under
   W3 halves and scales (swapping the SiLU and linear roles fails it); e4m3
   with row-wise scales is a reading of the pages' 8-bit training (their
   scaling schemes, not an inference format).
+* ``guided_velocity`` (classifier-free guidance): pinned by its special
+  cases, which reduce to the pinned ``model_velocity`` (g = 1 the
+  conditional, g = 0 the unconditional velocity, text without influence
+  makes g irrelevant) and by a planted swap of the two roles; the use of
+  caller-given unconditional text features is a reading.
 * ``qkvg_projection`` (the column split Q | K | V | G): pinned by a scalar
   loop over every head and channel with a distinct value in every row
   block of W_qkvg.
@@ -65,6 +70,7 @@ from .dit_oracle import (  # noqa: F401
     euler_sample,
     fp8_e4m3_round,
     gemm_fp8,
+    guided_velocity,
     quantize_rows_fp8,
     quantize_tensor_fp8,
     swiglu_fp8,

@@ -413,6 +413,18 @@ def model_velocity(z, t, txt, model, blocks, n_blocks: int, oc: OracleConfig, pr
     return unpatchify(v, C, Hl, Wl)
 
 
+def guided_velocity(z, t, txt, txt_null, guidance: float, model, blocks, n_blocks: int, oc: OracleConfig,
+                    pro=None) -> np.ndarray:
+    """Classifier-free guidance (page "Krea 2 技术报告", 训练 › 强化学习: an
+    optional control at inference; the guidance of Ho and Salimans cited
+    there): v = v_u + g (v_c - v_u), with v_c the velocity under the text
+    features txt and v_u under txt_null (the caller's unconditional
+    features).  g = 1 is the conditional velocity, g = 0 the unconditional."""
+    vc = model_velocity(z, t, txt, model, blocks, n_blocks, oc, pro)
+    vu = model_velocity(z, t, txt_null, model, blocks, n_blocks, oc, pro)
+    return vu + guidance * (vc - vu)
+
+
 # ------------------------------------------------------------------ 8-bit projections
 # Page "Krea 2 技术报告", 训练 › 预训练 (and the Indonesian / Korean pages):
 # 8-bit training ran 15-20 % faster than bf16, with tensor-wise scaling at

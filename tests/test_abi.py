@@ -270,6 +270,35 @@ def test_model_argument_checks():
                           ctypes.c_float(0.0), P + 2 * G, P + 4 * G, ws_need, None)) == "DIT_ERR_SHAPE"  # shift 0
 
 
+def test_sample_cfg_argument_checks():
+    """dit_sample_cfg checks its model call at 2B samples on B-sample inputs
+    and rejects a bad guidance, a missing unconditional text, a short
+    workspace and overlaps before any launch."""
+    L = dit.lib()
+    c = cfg()  # seq_len 80
+    G = 1 << 30
+    S = lambda st: _lib.STATUS[st]
+    mc = dit.make_model_config(4, 8, 8, 16, 32, 256)
+    need = dit.sample_cfg_workspace_size(c, mc)
+    assert need > dit.model_workspace_size(c, mc)
+    assert dit.sample_cfg_workspace_size(c, dit.make_model_config(0, 8, 8, 16, 32, 256)) == 0
+    mw = _lib.ModelWeights(P, P, P, P, P, 0, P)
+    bw = (_lib.BlockWeights * 1)(_lib.BlockWeights(P, P, P, P, P, 0, 0, 0, 0))
+
+    def call(steps=2, shift=3.0, g=4.0, txt=P + 2 * G, txt_null=P + 3 * G, ws=P + 4 * G, nbytes=need):
+        return S(L.dit_sample_cfg(ctypes.byref(c), ctypes.byref(mc), None, ctypes.byref(mw), 1, bw, P + G, steps,
+                                  ctypes.c_float(shift), ctypes.c_float(g), txt, txt_null, ws, nbytes, None))
+    assert call(steps=0) == "DIT_ERR_SHAPE"
+    assert call(shift=0.0) == "DIT_ERR_SHAPE"
+    assert call(g=float("nan")) == "DIT_ERR_SHAPE" and call(g=float("inf")) == "DIT_ERR_SHAPE"
+    assert call(txt_null=0) == "DIT_ERR_NULL"
+    assert call(txt_null=P + 3 * G + 4) == "DIT_ERR_ALIGN"
+    assert call(nbytes=need - 16) == "DIT_ERR_WORKSPACE"
+    assert call(ws=0) == "DIT_ERR_WORKSPACE"
+    assert call(txt_null=P + 4 * G + 1024) == "DIT_ERR_SHAPE"  # inside the workspace
+    assert call(txt_null=P + G) == "DIT_ERR_SHAPE"  # on z
+
+
 def test_fp8_argument_checks():
     L = dit.lib()
     G = 1 << 30

@@ -97,6 +97,45 @@ def test_sampler_small_bf16(dev):
     print(f"sampler bf16 change: {e:.2e} / {c:.7f}")
 
 
+def run_cfg(r, n_steps, shift, g):
+    """dit_sample_cfg on a copy of the run's latent; the unconditional text
+    features are another seeded draw of the same shape."""
+    txt_null = datagen.text_features(r.cfg.replace(seed=r.cfg.seed + 1))
+    ws = r.torch.empty(r.dit.sample_cfg_workspace_size(r.c, r.mc), dtype=r.torch.uint8, device="cuda")
+    Z = r.Z.clone()
+    r.dit.sample_cfg(r.c, r.mc, r.MW, r.BW, Z, n_steps, shift, g, r.TXT, r.device.to_device(txt_null, r.cfg.dtype),
+                     ws)
+    r.torch.cuda.synchronize()
+    ref = O.euler_sample(r.z, O.flow_schedule(n_steps, shift),
+                         lambda z, t: O.guided_velocity(z, t, r.txt, txt_null, g, r.mw, r.blocks, len(r.blocks), r.oc))
+    return r.device.to_numpy(Z), ref
+
+
+@pytest.mark.parametrize("n_steps,g", [(1, 1.0), (2, 3.0), (2, 0.0)])
+def test_sampler_cfg_tiny_f32(dev, n_steps, g):
+    """Classifier-free guidance (conditional and unconditional halves as one
+    batch of 2B) against the oracle's guided Euler steps: g = 1 is the plain
+    sampler, g = 0 the unconditional one, g = 3 extrapolates."""
+    r = ModelRun(dev, tiny_f32(), n_blocks=2)
+    got, ref = run_cfg(r, n_steps, 2.0, g)
+    assert_parity(got, ref, "f32", f"guided sampler g={g}")
+    assert_parity(got - r.z, ref - r.z, "f32", f"guided sampler g={g}, change")
+
+
+def test_sampler_cfg_small_bf16(dev):
+    """bf16 with g = 4.  The guided velocity g v_c + (1 - g) v_u carries up
+    to |g| + |1 - g| = 7 times the error of one bf16 velocity, so the bf16
+    bounds scale by that amplification: max-abs <= 7 * 2e-2 max|ref| and
+    1 - cos <= 7^2 * 1e-4 (the measurement sits far inside both)."""
+    g = 4.0
+    amp = abs(g) + abs(1.0 - g)
+    r = ModelRun(dev, small_bf16(), n_blocks=1)
+    got, ref = run_cfg(r, 2, 3.0, g)
+    e, c = assert_parity(got - r.z, ref - r.z, "bf16", "guided sampler bf16 change", maxabs=amp * 2e-2,
+                         cos_min=1.0 - amp * amp * 1e-4)
+    print(f"guided sampler bf16 change: {e:.2e} / {c:.7f}")
+
+
 def test_velocity_1024px_one_block(dev):
     """The 1024 px shapes (64 x 64 patch grid of a 16-channel latent, 512 text
     tokens of width 4096, hidden 4096), one block, batch 1: every element of

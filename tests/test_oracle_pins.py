@@ -499,6 +499,35 @@ def test_model_velocity_with_no_blocks_matches_per_token_loops():
                     assert abs(v[0, 0, 2 * py + dy, 2 * px + dx] - out[dy * 2 + dx]) < 1e-12
 
 
+def test_guided_velocity_special_cases():
+    """Classifier-free guidance reduces to the pinned model velocity: g = 1
+    gives the conditional velocity, g = 0 the unconditional one (a planted
+    swap of the two roles fails here), and when the text cannot reach the
+    output (no blocks) every g gives the same velocity."""
+    cfg = datagen.Config("tiny-model", batch=2, n_image=6, n_text=3, hidden=8, n_heads=2, n_kv_heads=1,
+                         head_dim=4, ffn=8, dtype="f32", seed=13, w_std=0.5, out_std=0.5, grid_h=2, grid_w=3,
+                         latent_ch=2, txt_dim=5, t_dim=8)
+    mw = datagen.model_weights(cfg)
+    blocks = [datagen.block_weights(cfg, i) for i in range(2)]
+    z = datagen.latent_noise(cfg)
+    txt = datagen.text_features(cfg)
+    txt_null = datagen.text_features(cfg.replace(seed=cfg.seed + 1))
+    oc_ = O.OracleConfig.of(cfg)
+    vc = O.model_velocity(z, 0.4, txt, mw, blocks, 2, oc_)
+    vu = O.model_velocity(z, 0.4, txt_null, mw, blocks, 2, oc_)
+    assert np.max(np.abs(vc - vu)) > 1e-3  # the text matters through the blocks
+    g1 = O.guided_velocity(z, 0.4, txt, txt_null, 1.0, mw, blocks, 2, oc_)
+    g0 = O.guided_velocity(z, 0.4, txt, txt_null, 0.0, mw, blocks, 2, oc_)
+    assert np.max(np.abs(g1 - vc)) < 1e-12 and np.max(np.abs(g0 - vu)) < 1e-12
+
+    def swapped(g):  # the planted mistake: the roles of the two velocities exchanged
+        return vc + g * (vu - vc)
+    assert np.max(np.abs(swapped(0.0) - g0)) > 1e-3
+    e0 = O.model_velocity(z, 0.4, txt, mw, [], 0, oc_)
+    for g in (0.0, 3.5, -1.0):
+        assert np.max(np.abs(O.guided_velocity(z, 0.4, txt, txt_null, g, mw, [], 0, oc_) - e0)) < 1e-12
+
+
 # ------------------------------------------------------------------ 8-bit projections
 def _e4m3_values():
     """Every finite OCP e4m3 value, decoded from its bit fields."""
