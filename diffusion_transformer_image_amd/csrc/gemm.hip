@@ -634,8 +634,12 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(const uint8_t *__restrict
       load_lds16(blk < ABLK ? ra : rw, base + blk * 1024, ok ? goff[j] + (uint32_t)k0 : kOOB);
     }
   };
+  // lane group g supplies the k-chunks g and g + 4 of the 128-byte stage
+  // (any k order works when A and B share it): each of the two reads then
+  // has the bf16 kernel's conflict-free pattern, where chunks 2g and 2g + 1
+  // measured ~3 bank-conflict cycles per LDS instruction cycle
   const int g = lane >> 4, r16 = lane & 15, swz = r16 & 7;
-  const int c0 = ((2 * g) ^ swz) * 16, c1 = ((2 * g + 1) ^ swz) * 16;
+  const int c0 = (g ^ swz) * 16, c1 = ((g + 4) ^ swz) * 16;
   int arow[RB], brow[CB];
 #pragma unroll
   for (int i = 0; i < RB; ++i) arow[i] = (wm * TM + i * 16 + r16) * BKB;
