@@ -91,6 +91,27 @@ def test_block_bf16_small_full_output(dev):
         check_block(y, ref, r.x, "bf16", f"small bf16 strong={strong}")
 
 
+@pytest.mark.parametrize("base,batch,n_image,n_text,hidden,heads,kv,ffn", [
+    ("c0", 5, 1, 0, 256, 4, 2, 688),        # fp32, one token per sample: softmax over one key
+    ("c1", 3, 1, 0, 512, 4, 1, 1368),       # bf16, one token per sample
+    ("c1", 2, 1, 1, 512, 4, 4, 1368),       # bf16, two tokens, MHA
+    ("c1", 1, 60, 10, 8192, 64, 16, 2048),  # bf16 at the widest hidden the norms take (8192)
+])
+def test_block_degenerate_and_widest_shapes(dev, base, batch, n_image, n_text, hidden, heads, kv, ffn):
+    """Every output of blocks at the edges of the supported shapes: a
+    sequence of one token (each query attends only to itself, so the
+    attention branch is sigma(G) V exactly), of two tokens, and hidden 8192
+    (the norms' row of 8192 elements in registers, the residual and second
+    norm as two passes)."""
+    cfg = datagen.get_config(base).replace(batch=batch, n_image=n_image, n_text=n_text, hidden=hidden,
+                                            n_heads=heads, n_kv_heads=kv, ffn=ffn)
+    for strong in (False, True):
+        r = Run(dev, cfg, strong)
+        y = r.forward()
+        ref = O.block_forward(r.x, r.mod, r.w, O.OracleConfig.of(cfg))
+        check_block(y, ref, r.x, cfg.dtype, f"{base} B={batch} L={cfg.seq_len} D={hidden} strong={strong}")
+
+
 @pytest.mark.parametrize("batch,n_image,n_text,hidden,heads,kv", [
     (2, 100, 28, 512, 4, 1),     # L = 128: a QKVG column tile holds K and V heads side by side
     (3, 130, 62, 1024, 8, 2),    # L = 192, a ragged last row tile of the projection
