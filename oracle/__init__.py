@@ -19,11 +19,12 @@ Parity status (what pins each function; see the tests under
   heads, zero gates give the identity, scale = -1 gives h = shift,
   permutation equivariance, batch independence).
 * ``time_embedding``: pinned by closed forms of the sinusoid at chosen t.
-* ``timestep_modulation``: parity unpinned.  The pages name a sinusoidal
-  time embedding and a per-block bias replacing per-block MLPs, but do not
-  give the shared map from t to the modulation vector; the oracle's
-  two-layer bias-free MLP is a reading, and the HIP path implements the
-  same reading.
+* ``timestep_modulation``: its arithmetic pinned by scalar loops over the
+  brute-force embedding (and a zero W_t2 giving zero).  The pages name a
+  sinusoidal time embedding and a per-block bias replacing per-block MLPs,
+  but do not give the shared map from t to the modulation vector: the
+  two-layer bias-free MLP is a reading, so parity of that convention is
+  unpinned by the pages (the HIP path implements the same reading).
 * ``qk_rmsnorm``, ``rope_positions``, ``rope_angles``, ``apply_rope``,
   ``attention_prologue`` (the optional QKNorm + 3D axial RoPE): pinned by
   the scalar-loop brute force, by torch's float64 ``rms_norm``, by the

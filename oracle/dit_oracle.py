@@ -115,8 +115,10 @@ def time_embedding(t, dim: int = 256, t_scale: float = 1000.0, max_period: float
 
 
 def timestep_modulation(t, w_t1, w_t2, hidden: int) -> np.ndarray:
-    """m = W_t2 silu(W_t1 e(t)), reshaped to [B, 6, D] (parity unpinned:
-    the shared map from t to the modulation vector is a reading)."""
+    """m = W_t2 silu(W_t1 e(t)), reshaped to [B, 6, D].  The shared map from
+    t to the modulation vector is a reading (the pages do not give it):
+    parity of the convention is unpinned by the pages, its arithmetic is
+    pinned by scalar loops."""
     w_t1, w_t2 = _f64(w_t1), _f64(w_t2)
     e = time_embedding(t, dim=w_t1.shape[1])
     z = e @ w_t1.T
