@@ -80,6 +80,24 @@ def test_block_full_size_sampled(dev, name, strong):
         check_block(y[b, rows], ref, r.x[b, rows].astype(np.float64), "bf16", f"{name} b={b}")
 
 
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", ["c1", "c2", "c3b"])
+def test_block_full_size_every_output(dev, name):
+    """256 px (B = 32, L = 512), 512 px (B = 8, L = 1280) and 768 x 1344
+    (B = 2, L = 4544) in the launch configuration the benchmark times: every
+    output and the update of the whole batch against the oracle (the 1024 px
+    batch is compared element by element by bench.py's parity report)."""
+    import time
+    cfg = datagen.get_config(name)
+    print(f"block {name} every output", flush=True)
+    r = Run(dev, cfg)
+    y = r.forward()
+    t0 = time.time()
+    ref = O.block_forward(r.x, r.mod, r.w, O.OracleConfig.of(cfg))
+    print(f"oracle {name}: {time.time() - t0:.1f} s", flush=True)
+    check_block(y, ref, r.x, "bf16", f"{name} every output")
+
+
 def test_block_bf16_small_full_output(dev):
     """Every output of a small bf16 block (d = 128, ragged L) against the oracle."""
     cfg = datagen.get_config("c1").replace(batch=2, n_image=70, n_text=27, hidden=512, n_heads=4,
