@@ -415,11 +415,13 @@ size_t dit_workspace_size_fp8(const dit_config *cfg /* host */);
 
 /* The block with its four projections in 8 bits (page "Krea 2 技术报告",
  * 训练 › 预训练: 8-bit matrix products with tensor-wise / row-wise
- * scaling): the activation rows entering each product (h1, Og, h2, U,
- * stored as bf16 by the kernels that make them) are quantised row-wise to
- * e4m3 as in dit_quantize_fp8, multiplied with the weight codes as in
- * dit_gemm_fp8 (fp32 accumulation, both scales applied), and the rest is
- * the bf16 block of dit_block_fwd (unscaled queries, the V^T pass).
+ * scaling): the activation rows entering each product are quantised
+ * row-wise to e4m3 as in dit_quantize_fp8 (h1 and h2 by the norm kernels
+ * from their fp32 rows, Og and U from their bf16 storage) and multiplied
+ * with the weight codes as in dit_gemm_fp8 (fp32 accumulation, both scales
+ * applied); the rest is the bf16 block of dit_block_fwd (queries leave the
+ * QKVG product pre-scaled for the attention; with seq_len a multiple of 64
+ * the value heads go straight to the attention's V^T layout).
  * cfg->dtype must be DIT_BF16 (x_in, x_out bf16), head_dim 128, and hidden,
  * H*d and ffn multiples of 16 (else DIT_ERR_UNSUPPORTED / DIT_ERR_DTYPE).
  * Other arguments and errors as in dit_block_fwd. */
