@@ -743,6 +743,11 @@ dit_status dit_sample(const dit_config *cfg, const dit_model_config *mc, const d
   dit_status st = check_model_call(cfg, mc, pro, mw, n_blocks, blocks, z, txt, ws, ws_bytes);
   if (st != DIT_OK) return st;
   if (n_steps < 1 || n_steps > 100000 || !(shift > 0.f)) return DIT_ERR_SHAPE;
+  {  // z is written in place: it must not overlap the text features
+    const size_t zb = (size_t)cfg->batch * mc->latent_ch * 4 * mc->grid_h * mc->grid_w * 4;
+    const size_t tb = mc->n_text ? (size_t)cfg->batch * mc->n_text * mc->txt_dim * esize(cfg->dtype) : 0;
+    if (overlap(z, zb, txt, tb)) return DIT_ERR_SHAPE;
+  }
   hipStream_t s = (hipStream_t)stream;
   const ModelWs w = carve_model(cfg, mc, ws);
   auto sched = [&](int i) {  // s u / (1 + (s - 1) u), u = 1 - i / n
@@ -819,7 +824,7 @@ dit_status dit_sample_cfg(const dit_config *cfg, const dit_model_config *mc, con
   const size_t zb = (size_t)cfg->batch * mc->latent_ch * 4 * mc->grid_h * mc->grid_w * 4;
   const size_t tb = mc->n_text ? (size_t)cfg->batch * mc->n_text * mc->txt_dim * esize(cfg->dtype) : 0;
   if (overlap(ws, need, z, zb) || overlap(ws, need, txt, tb) || overlap(ws, need, txt_null, tb) ||
-      overlap(z, zb, txt_null, tb))
+      overlap(z, zb, txt, tb) || overlap(z, zb, txt_null, tb))
     return DIT_ERR_SHAPE;
   hipStream_t s = (hipStream_t)stream;
   const CfgWs w = carve_cfg(cfg, mc, ws);

@@ -268,6 +268,8 @@ def test_model_argument_checks():
                           ctypes.c_float(3.0), P + 2 * G, P + 4 * G, ws_need, None)) == "DIT_ERR_SHAPE"  # 0 steps
     assert S(L.dit_sample(ctypes.byref(c), ctypes.byref(mc), None, ctypes.byref(mw), 1, bw, P + G, 4,
                           ctypes.c_float(0.0), P + 2 * G, P + 4 * G, ws_need, None)) == "DIT_ERR_SHAPE"  # shift 0
+    assert S(L.dit_sample(ctypes.byref(c), ctypes.byref(mc), None, ctypes.byref(mw), 1, bw, P + G, 4,
+                          ctypes.c_float(3.0), P + G + 256, P + 4 * G, ws_need, None)) == "DIT_ERR_SHAPE"  # txt on z
 
 
 def test_sample_cfg_argument_checks():
