@@ -165,10 +165,12 @@ def cpu_baseline(cfg, x, w, t, w_t1, w_t2) -> dict:
     mod = O.timestep_modulation(t, w_t1, w_t2, cfg.hidden)
     ref = O.block_forward(x, mod, w, oc)
     dt = time.perf_counter() - t0
+    fl = sum(flops_per_token(cfg).values()) * cfg.tokens  # the block's matrix products and attention
     return ref, {"value": cfg.tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"the whole batch: {cfg.batch} x {cfg.seq_len} tokens, one block with its timestep "
                       f"modulation, fp64 numpy ({blas}), {dt:.2f} s",
-            "seconds": dt, "affinity_cpus": len(os.sched_getaffinity(0))}
+            "seconds": dt, "fp64_gflops": fl / dt / 1e9, "blas": blas,
+            "affinity_cpus": len(os.sched_getaffinity(0)), "cpu_count": os.cpu_count()}
 
 
 def bench_stack(dit, torch, steps: int, warmup: int) -> dict:
