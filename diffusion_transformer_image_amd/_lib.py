@@ -29,6 +29,7 @@ EXPORTS = (
     "dit_qk_prologue", "dit_model_workspace_size", "dit_model_velocity", "dit_sample", "dit_quantize_fp8",
     "dit_gemm_fp8", "dit_quantize_fp8_tensor", "dit_attention_ex", "dit_timestep_mod_noalloc",
     "dit_workspace_size_fp8", "dit_block_fwd_fp8", "dit_sample_cfg_workspace_size", "dit_sample_cfg",
+    "dit_stack_workspace_size_fp8", "dit_stack_fwd_fp8",
 )
 
 
@@ -98,6 +99,8 @@ def lib() -> ctypes.CDLL:
             "dit_workspace_size": (sz, [cfgp]),
             "dit_workspace_size_fp8": (sz, [cfgp]),
             "dit_block_fwd_fp8": (i32, [cfgp, ctypes.POINTER(BlockWeightsFp8), vp, vp, vp, vp, sz, vp]),
+            "dit_stack_workspace_size_fp8": (sz, [cfgp]),
+            "dit_stack_fwd_fp8": (i32, [cfgp, i32, ctypes.POINTER(BlockWeightsFp8), vp, vp, vp, vp, sz, vp]),
             "dit_stack_workspace_size": (sz, [cfgp]),
             "dit_block_fwd": (i32, [cfgp, wp, vp, vp, vp, vp, sz, vp]),
             "dit_block_fwd_ex": (i32, [cfgp, ctypes.POINTER(Prologue), wp, vp, vp, vp, vp, sz, vp]),
@@ -232,6 +235,18 @@ def block_fwd_fp8(cfg: Config, w: Mapping, x_in, x_out, mod, ws, stream=None) ->
     nbytes = ws.numel() * ws.element_size() if hasattr(ws, "numel") else 0
     _check(lib().dit_block_fwd_fp8(ctypes.byref(cfg), ctypes.byref(bw), _ptr(x_in), _ptr(x_out), _ptr(mod),
                                    _ptr(ws), nbytes, _stream(stream)), "dit_block_fwd_fp8")
+
+
+def stack_workspace_size_fp8(cfg: Config) -> int:
+    return lib().dit_stack_workspace_size_fp8(ctypes.byref(cfg))
+
+
+def stack_fwd_fp8(cfg: Config, blocks: Sequence[Mapping], x_in, x_out, mod, ws, stream=None) -> None:
+    """n_blocks 8-bit blocks (each a mapping as for block_fwd_fp8)."""
+    arr = (BlockWeightsFp8 * len(blocks))(*[make_weights_fp8(b) for b in blocks])
+    nbytes = ws.numel() * ws.element_size() if hasattr(ws, "numel") else 0
+    _check(lib().dit_stack_fwd_fp8(ctypes.byref(cfg), len(blocks), arr, _ptr(x_in), _ptr(x_out), _ptr(mod),
+                                   _ptr(ws), nbytes, _stream(stream)), "dit_stack_fwd_fp8")
 
 
 def block_fwd_ex(cfg: Config, pro: Prologue | None, w: Mapping, x_in, x_out, mod, ws, stream=None) -> None:

@@ -377,8 +377,12 @@ dit_status run_block(const dit_config *c, const dit_prologue *pro, const dit_blo
 
 // The 8-bit block: each product's activation rows quantised to e4m3 (one
 // scale per row) and multiplied with the pre-quantised weight rows.
+// x_in / x_out: bf16, or fp32 where xin_f32 / xout_f32 (the stack's
+// residual stream); h1_ready and defer_resid2 as in run_block (h1's codes
+// already in ws.codes; stop after the W2 product).
 dit_status run_block_fp8(const dit_config *c, const dit_block_weights_fp8 *w, const void *x_in, void *x_out,
-                         const float *mod, const Fp8Ws &ws, hipStream_t s) {
+                         const float *mod, const Fp8Ws &ws, hipStream_t s, bool xin_f32 = false,
+                         bool xout_f32 = false, bool h1_ready = false, bool defer_resid2 = false) {
   const Dims d = dims(c);
   const int T = (int)d.T, D = (int)d.D, L = c->seq_len, F = (int)d.F, hd = (int)d.hd, nq = (int)d.nqkvg;
   const BlockWs &b = ws.b;
@@ -386,10 +390,12 @@ dit_status run_block_fp8(const dit_config *c, const dit_block_weights_fp8 *w, co
     return timed(DIT_K_QUANT, s, [&] { return launch_quantize_fp8(false, x, ws.codes, ws.scales, T, k, s); });
   };
   // the norms hand their rows over as codes quantised from fp32 (no bf16 h)
-  DIT_TRY(timed(DIT_K_MODNORM, s, [&] {
-    return launch_modnorm_fp8(false, x_in, ws.codes, ws.scales, mod, w->mod_bias, w->norm1_w, T, L, D, c->eps, 0,
-                              s);
-  }));
+  if (!h1_ready) {
+    DIT_TRY(timed(DIT_K_MODNORM, s, [&] {
+      return launch_modnorm_fp8(xin_f32, x_in, ws.codes, ws.scales, mod, w->mod_bias, w->norm1_w, T, L, D, c->eps,
+                                0, s);
+    }));
+  }
   // as in the bf16 block: the query columns leave the product pre-scaled
   // for the attention, and with whole 64-key tiles and no K split the value
   // heads go straight to V^T
@@ -411,12 +417,12 @@ dit_status run_block_fp8(const dit_config *c, const dit_block_weights_fp8 *w, co
   }));
   if (fused_resid_norm(D)) {
     DIT_TRY(timed(DIT_K_RESID, s, [&] {
-      return launch_resid_modnorm_fp8(false, x_in, b.br, (float *)b.x1, ws.codes, ws.scales, mod, w->mod_bias, 0,
-                                      w->mod_bias, w->norm2_w, 1, T, L, D, c->eps, s);
+      return launch_resid_modnorm_fp8(xin_f32, x_in, b.br, (float *)b.x1, ws.codes, ws.scales, mod, w->mod_bias,
+                                      0, w->mod_bias, w->norm2_w, 1, T, L, D, c->eps, s);
     }));
   } else {
     DIT_TRY(timed(DIT_K_RESID, s, [&] {
-      return launch_resid(false, false, true, x_in, b.br, b.x1, mod, w->mod_bias, T, L, D, 0, s);
+      return launch_resid(xin_f32, false, true, x_in, b.br, b.x1, mod, w->mod_bias, T, L, D, 0, s);
     }));
     DIT_TRY(timed(DIT_K_MODNORM, s, [&] {
       return launch_modnorm_fp8(true, b.x1, ws.codes, ws.scales, mod, w->mod_bias, w->norm2_w, T, L, D, c->eps, 1,
@@ -430,9 +436,37 @@ dit_status run_block_fp8(const dit_config *c, const dit_block_weights_fp8 *w, co
   DIT_TRY(timed(DIT_K_GEMM_W2, s, [&] {
     return launch_gemm_fp8(false, ws.codes, ws.scales, w->w_2, w->s_2, b.br, T, D, F, s, b.part, b.part_bytes);
   }));
+  if (defer_resid2) return DIT_OK;
   DIT_TRY(timed(DIT_K_RESID, s, [&] {
-    return launch_resid(true, false, false, b.x1, b.br, x_out, mod, w->mod_bias, T, L, D, 1, s);
+    return launch_resid(true, false, xout_f32, b.x1, b.br, x_out, mod, w->mod_bias, T, L, D, 1, s);
   }));
+  return DIT_OK;
+}
+
+// n_blocks 8-bit blocks: the fp32 residual stream between blocks after the
+// carved block workspace, each block's second residual joined with the
+// next block's first norm (whose codes the next QKVG product reads)
+dit_status run_stack_fp8(const dit_config *cfg, int n_blocks, const dit_block_weights_fp8 *blocks,
+                         const void *x_in, void *x_out, const float *mod, void *ws, hipStream_t s) {
+  const Fp8Ws fw = carve_fp8(cfg, ws);
+  char *xa = (char *)ws + fw.bytes;
+  const Dims d = dims(cfg);
+  const int T = (int)d.T, D = (int)d.D, L = cfg->seq_len;
+  const bool chain = fused_resid_norm(D);
+  for (int i = 0; i < n_blocks; ++i) {
+    const bool first = i == 0, last = i == n_blocks - 1;
+    dit_status st = run_block_fp8(cfg, &blocks[i], first ? x_in : xa, last ? x_out : xa, mod, fw, s, !first,
+                                  !last, chain && !first, chain && !last);
+    if (st != DIT_OK) return st;
+    if (chain && !last) {
+      hipError_t e = timed(DIT_K_RESID, s, [&] {
+        return launch_resid_modnorm_fp8(true, fw.b.x1, fw.b.br, (float *)xa, fw.codes, fw.scales, mod,
+                                        blocks[i].mod_bias, 1, blocks[i + 1].mod_bias, blocks[i + 1].norm1_w, 0, T,
+                                        L, D, cfg->eps, s);
+      });
+      if (e != hipSuccess) return hip_fail(e);
+    }
+  }
   return DIT_OK;
 }
 
@@ -626,6 +660,34 @@ dit_status dit_block_fwd_fp8(const dit_config *cfg, const dit_block_weights_fp8 
       overlap(ws, need, mod, (size_t)cfg->batch * 6 * cfg->hidden * 4))
     return DIT_ERR_SHAPE;
   return run_block_fp8(cfg, w, x_in, x_out, mod, carve_fp8(cfg, ws), (hipStream_t)stream);
+}
+
+size_t dit_stack_workspace_size_fp8(const dit_config *cfg) {
+  if (check_cfg_fp8(cfg) != DIT_OK) return 0;
+  const Dims d = dims(cfg);
+  return carve_fp8(cfg, nullptr).bytes + round_up(d.T * d.D * 4);
+}
+
+dit_status dit_stack_fwd_fp8(const dit_config *cfg, int32_t n_blocks, const dit_block_weights_fp8 *blocks,
+                             const void *x_in, void *x_out, const float *mod, void *ws, size_t ws_bytes,
+                             void *stream) {
+  dit_status st = check_cfg_fp8(cfg);
+  if (st != DIT_OK) return st;
+  if (n_blocks <= 0) return DIT_ERR_SHAPE;
+  if (!blocks || !x_in || !x_out || !mod) return DIT_ERR_NULL;
+  if (!ws) return DIT_ERR_WORKSPACE;
+  if (!aligned(x_in) || !aligned(x_out) || !aligned(mod) || !aligned(ws)) return DIT_ERR_ALIGN;
+  const Dims d = dims(cfg);
+  const size_t need = dit_stack_workspace_size_fp8(cfg);
+  if (ws_bytes < need) return DIT_ERR_WORKSPACE;
+  for (int i = 0; i < n_blocks; ++i)
+    if ((st = check_weights_fp8(cfg, &blocks[i], ws, need)) != DIT_OK) return st;
+  const size_t xb = d.T * d.D * d.es;
+  if (overlap(x_in, xb, x_out, xb)) return DIT_ERR_SHAPE;
+  if (overlap(ws, need, x_in, xb) || overlap(ws, need, x_out, xb) ||
+      overlap(ws, need, mod, (size_t)cfg->batch * 6 * cfg->hidden * 4))
+    return DIT_ERR_SHAPE;
+  return run_stack_fp8(cfg, n_blocks, blocks, x_in, x_out, mod, ws, (hipStream_t)stream);
 }
 
 dit_status dit_stack_fwd_ex(const dit_config *cfg, const dit_prologue *pro, int32_t n_blocks,

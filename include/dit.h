@@ -429,6 +429,20 @@ dit_status dit_block_fwd_fp8(const dit_config *cfg /* host */, const dit_block_w
                              const void *x_in, void *x_out, const float *mod, void *ws, size_t ws_bytes,
                              void *stream);
 
+/* Workspace bytes of dit_stack_fwd_fp8 (0 if cfg is invalid for it). */
+size_t dit_stack_workspace_size_fp8(const dit_config *cfg /* host */);
+
+/* n_blocks 8-bit blocks in order (blocks: host array of n_blocks weight
+ * structs as for dit_block_fwd_fp8), all under the shared modulation mod:
+ * the stack of dit_stack_fwd with every projection in row-wise e4m3.  The
+ * residual stream between blocks stays fp32 in the workspace; x_in, x_out
+ * bf16.  Arguments, checks and errors as in dit_block_fwd_fp8 and
+ * dit_stack_fwd (n_blocks >= 1; the workspace must not overlap any input or
+ * weight). */
+dit_status dit_stack_fwd_fp8(const dit_config *cfg /* host */, int32_t n_blocks,
+                             const dit_block_weights_fp8 *blocks /* host [n_blocks] */, const void *x_in,
+                             void *x_out, const float *mod, void *ws, size_t ws_bytes, void *stream);
+
 /* Gated grouped-query attention over the rows of qkvg [T, (2H+2Hkv)*d]
  * (column blocks Q | K | V | G, as produced by the QKVG projection):
  *   og[b, l, h*d:(h+1)*d] = softmax_keys(Q_h K_j^T / sqrt(d)) V_j * sigmoid(G_h)

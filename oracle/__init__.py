@@ -42,6 +42,10 @@ Parity status (what pins each function; see the tests under
   for the norm; the layer conventions (16-channel latent, 2 x 2 patches,
   bias-free embeddings, the final modulation map, the shift form) are
   readings: parity of those conventions is unpinned by the pages.
+* ``block_forward_fp8``, ``stack_forward_fp8`` (the 8-bit block and stack):
+  with the quantiser replaced by the identity they reproduce
+  ``block_forward`` / ``stack_forward``; with row-wise e4m3 they depart
+  from them by a few percent of the update.
 * ``fp8_e4m3_round``, ``quantize_rows_fp8``, ``quantize_tensor_fp8``, ``gemm_fp8``, ``swiglu_fp8``
   (the 8-bit projections): pinned by an exhaustive nearest-value search over
   all finite e4m3 codes (ties to even), fixed points at representable
@@ -93,6 +97,7 @@ from .dit_oracle import (  # noqa: F401
     qkvg_projection,
     split_modulation,
     stack_forward,
+    stack_forward_fp8,
     swiglu_mlp,
     time_embedding,
     timestep_modulation,

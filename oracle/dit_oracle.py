@@ -41,7 +41,7 @@ Readings where the pages leave a step open (each is also a test):
 * Softmax scale 1/sqrt(head_dim); query head h reads KV head
   h // (H / Hkv) (contiguous groups); no mask, no positional terms.
 * No linear biases; SwiGLU: silu(h W1^T) * (h W3^T), then W2.
-* Timestep map (parity unpinned): e = [cos(1000 t f_i), sin(1000 t f_i)],
+* Timestep map (a reading; parity of the convention unpinned): e = [cos(1000 t f_i), sin(1000 t f_i)],
   f_i = 10000^(-i/(n/2)), m = W_t2 silu(W_t1 e), bias-free, shared by all
   blocks.
 
@@ -537,3 +537,14 @@ def block_forward_fp8(x, mod, wts, oc: OracleConfig, quant: Callable = quantize_
         u = swiglu_fp8(qa, sa, *qw["w_13"], F)
         out.append(gated_residual(x1, gate2, prod(u, "w_2")))
     return np.stack(out)
+
+
+def stack_forward_fp8(x, mod, weights: Iterable | Callable[[int], object], n_blocks: int, oc: OracleConfig,
+                      quant: Callable = quantize_rows_fp8) -> np.ndarray:
+    """The stack of stack_forward with every block the 8-bit block of
+    block_forward_fp8 (the residual stream exact between blocks)."""
+    get = weights if callable(weights) else (lambda i, _w=list(weights): _w[i])
+    y = _f64(x)
+    for i in range(n_blocks):
+        y = block_forward_fp8(y, mod, get(i), oc, quant)
+    return y

@@ -301,6 +301,27 @@ def test_sample_cfg_argument_checks():
     assert call(txt_null=P + G) == "DIT_ERR_SHAPE"  # on z
 
 
+def test_stack_fp8_argument_checks():
+    L = dit.lib()
+    G = 1 << 30
+    S = lambda st: _lib.STATUS[st]
+    c = dit.make_config(batch=2, seq_len=128, hidden=512, n_heads=4, n_kv_heads=1, head_dim=128, ffn=1376,
+                        eps=1e-6, dtype="bf16")
+    need = dit.stack_workspace_size_fp8(c)
+    assert need > dit.workspace_size_fp8(c) > 0
+    bw = (_lib.BlockWeightsFp8 * 2)(*[_lib.BlockWeightsFp8(P + 5 * G, P + 5 * G, P + 5 * G, P + 5 * G, P + 6 * G,
+                                                           P + 6 * G, P + 6 * G, P + 6 * G, P + 6 * G, 0, 0)] * 2)
+    call = lambda nb=2, ws=P + 3 * G, nbytes=need, xo=P + G: S(L.dit_stack_fwd_fp8(
+        ctypes.byref(c), nb, bw, P, xo, P + 2 * G, ws, nbytes, None))
+    assert call(nb=0) == "DIT_ERR_SHAPE"
+    assert call(nbytes=need - 16) == "DIT_ERR_WORKSPACE"
+    assert call(xo=P) == "DIT_ERR_SHAPE"              # x_out on x_in
+    assert call(ws=P + 5 * G - 1024) == "DIT_ERR_SHAPE"  # workspace over a weight
+    f32 = dit.make_config(batch=2, seq_len=128, hidden=512, n_heads=4, n_kv_heads=1, head_dim=128, ffn=1376,
+                          eps=1e-6, dtype="f32")
+    assert dit.stack_workspace_size_fp8(f32) == 0
+
+
 def test_fp8_argument_checks():
     L = dit.lib()
     G = 1 << 30

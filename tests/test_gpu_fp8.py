@@ -220,3 +220,44 @@ def test_block_fp8_full_size_every_output(dev):
     print("fp8 block full size: GPU done", flush=True)
     ref = O.block_forward_fp8(x, mod, w, O.OracleConfig.of(cfg))
     check_fp8_block(y, ref, x.astype(np.float64), "fp8 block 1024 px B=1")
+
+
+# ------------------------------------------------------------------ the 8-bit stack
+def run_stack_fp8(dev, cfg, n_blocks):
+    torch, device, dit = dev
+    ws_blocks = [datagen.block_weights(cfg, i) for i in range(n_blocks)]
+    W8 = [fp8_block_weights(dev, w) for w in ws_blocks]
+    x = datagen.activations(cfg)
+    mod = datagen.block_mod(cfg)
+    c = dit.config_of(cfg)
+    X = device.to_device(x.reshape(cfg.tokens, cfg.hidden), "bf16")
+    Y = torch.empty_like(X)
+    ws = torch.empty(dit.stack_workspace_size_fp8(c), dtype=torch.uint8, device="cuda")
+    dit.stack_fwd_fp8(c, W8, X, Y, device.to_device(mod, "f32"), ws)
+    torch.cuda.synchronize()
+    y = device.to_numpy(Y).reshape(x.shape)
+    ref = O.stack_forward_fp8(x, mod, ws_blocks, n_blocks, O.OracleConfig.of(cfg))
+    return y, ref, x.astype(np.float64)
+
+
+@pytest.mark.parametrize("n_image,n_text", [(70, 27), (100, 28)])  # ragged keys / V^T by the projection
+def test_stack_fp8_vs_oracle_fp8_composition(dev, n_image, n_text):
+    """8 distinct 8-bit blocks with the fp32 residual stream between them and
+    each block's second residual joined with the next block's first norm:
+    every output against the oracle's 8-bit stack, under the 8-bit block's
+    bound (the oracle run with the GPU's bf16 storage of Og and U moves the
+    8-block update by 2.1-2.7e-2, inside it)."""
+    cfg = datagen.get_config("c1").replace(batch=2, n_image=n_image, n_text=n_text, hidden=512, n_heads=4,
+                                            n_kv_heads=1, ffn=1376)
+    y, ref, x = run_stack_fp8(dev, cfg, 8)
+    check_fp8_block(y, ref, x, f"fp8 stack x8 L={cfg.seq_len}")
+
+
+@pytest.mark.timeout(900)
+def test_stack_fp8_full_width(dev):
+    """4 distinct 8-bit blocks at the stack's width (hidden 4096, 32 / 8 heads,
+    SwiGLU 11008, W_o and W_2 ~ N(0, 0.02/sqrt(120))), one sample of 456
+    image + 64 text tokens: every output against the oracle's 8-bit stack."""
+    cfg = datagen.get_config("c4").replace(n_image=456, n_text=64)
+    y, ref, x = run_stack_fp8(dev, cfg, 4)
+    check_fp8_block(y, ref, x, "fp8 stack x4 full width")

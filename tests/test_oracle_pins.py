@@ -666,6 +666,23 @@ def test_fp8_block_composition_without_quantisation_is_the_block():
         assert np.max(np.abs(got - ref)) <= 1e-12 * np.max(np.abs(ref))
 
 
+def test_fp8_stack_composition_without_quantisation_is_the_stack():
+    """stack_forward_fp8 applies its blocks in order with their own weights:
+    with the identity quantiser it equals stack_forward (three distinct
+    blocks), and with e4m3 each block's quantisation is applied."""
+    cfg = tiny_cfg(batch=2, L=5, hkv=2, seed=83)
+    x, w0, mod = inputs(cfg)
+    blocks = [datagen.block_weights(cfg, i) for i in range(3)]
+    ref = O.stack_forward(x, mod, blocks, 3, oc(cfg))
+    got = O.stack_forward_fp8(x, mod, blocks, 3, oc(cfg), quant=O._quant_identity)
+    assert np.max(np.abs(got - ref)) <= 1e-12 * np.max(np.abs(ref))
+    swapped = O.stack_forward_fp8(x, mod, blocks[::-1], 3, oc(cfg), quant=O._quant_identity)
+    assert np.max(np.abs(swapped - ref)) > 1e-6 * np.max(np.abs(ref))  # the block order matters
+    q8 = O.stack_forward_fp8(x, mod, blocks, 3, oc(cfg))
+    du = np.max(np.abs((q8 - x) - (ref - x))) / np.max(np.abs(ref - x))
+    assert 1e-4 < du < 0.5, du
+
+
 def test_fp8_block_quantises_every_product():
     """With row-wise e4m3 the 8-bit block differs from the exact block by the
     quantisation error: a few percent of the update, neither zero (the
