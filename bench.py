@@ -18,7 +18,8 @@ oracle's own timestep modulation) on the host cores; ``parity`` compares
 that oracle output with the GPU output of the benchmarked step, element by
 element.  ``configs`` holds the other synthetic workloads (256 px, 512 px,
 768 x 1344) and ``stack`` the 60-block denoising step, each with a
-per-kernel breakdown.
+per-kernel breakdown; ``fp8_block`` and ``stack.fp8`` the same block and
+stack with the projections in 8 bits.
 """
 from __future__ import annotations
 
@@ -220,7 +221,39 @@ def bench_stack(dit, torch, steps: int, warmup: int) -> dict:
     out["kernels"] = kernel_breakdown(dit, torch, run, cfg, reps=1, per_call=cfg.n_blocks,
                                       resid_bytes=12 * cfg.hidden)
     out["sample"] = bench_sample(dit, torch, cfg, c, blocks, randn)
+    out["fp8"] = bench_stack_fp8(dit, torch, cfg, c, blocks, x, mod, steps, warmup)
     del blocks
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_stack_fp8(dit, torch, cfg, c, blocks, x, mod, steps: int, warmup: int) -> dict:
+    """The same 60 blocks in 8 bits (dit_stack_fwd_fp8): each block's four
+    matrices quantised row-wise to e4m3 once, before timing; one denoising
+    step per call, B = 1, 1024 px."""
+    blocks8 = []
+    for b in blocks:
+        w8 = {n: b[n] for n in ("mod_bias", "norm1_w", "norm2_w")}
+        for name, sname in (("w_qkvg", "s_qkvg"), ("w_o", "s_o"), ("w_13", "s_13"), ("w_2", "s_2")):
+            w8[name] = torch.empty(b[name].shape, dtype=torch.uint8, device="cuda")
+            w8[sname] = torch.empty(b[name].shape[0], dtype=torch.float32, device="cuda")
+            dit.quantize_fp8(b[name], w8[name], w8[sname])
+        blocks8.append(w8)
+    y = torch.empty_like(x)
+    ws = torch.empty(dit.stack_workspace_size_fp8(c), dtype=torch.uint8, device="cuda")
+
+    def run():
+        dit.stack_fwd_fp8(c, blocks8, x, y, mod, ws)
+
+    for _ in range(warmup):
+        run()
+    elapsed, per = timed_steps(torch, run, steps)
+    dt = elapsed / steps
+    out = {"workload": "krea2-dit-stack60-1024px-fp8", "ms_per_denoising_step": dt * 1e3,
+           "step_ms": step_stats(per), "block_tokens_per_s": cfg.n_blocks * cfg.tokens / dt,
+           "weights_gb": sum(t.numel() * t.element_size() for b in blocks8 for k, t in b.items()
+                             if k.startswith(("w_", "s_"))) / 1e9}
+    del blocks8, ws
     torch.cuda.empty_cache()
     return out
 
