@@ -187,12 +187,15 @@ __global__ __launch_bounds__(NW * 64, WPH == 1 ? 2 : 1) void attn_kernel(const T
     }
   }
 
-  // ---- tile loaders (DMA; each wave writes whole 1 KiB blocks)
+  // ---- tile loaders (DMA; each wave writes whole 1 KiB blocks, blocks
+  // wave, wave + NW, ...: a trip count known at compile time, so the loads
+  // are straight-line code)
   auto issue_tile = [&](int t, int buf) {
     char *kt = smem + buf * STAGE;
     constexpr int KRPB = 1024 / KROW;
 #pragma unroll
-    for (int blk = wave; blk < KBLK; blk += NW) {
+    for (int i = 0; i < KBLK / NW; ++i) {
+      const int blk = wave + i * NW;
       const int row = blk * KRPB + lane / NCK;
       const int lc = (lane % NCK) ^ (row & 15);
       const int key = t * ATT_BK + row;
@@ -202,7 +205,8 @@ __global__ __launch_bounds__(NW * 64, WPH == 1 ? 2 : 1) void attn_kernel(const T
     char *vtl = kt + KTILE;
     constexpr int VRPB = 1024 / VROW;
 #pragma unroll
-    for (int blk = wave; blk < VBLK; blk += NW) {
+    for (int i = 0; i < VBLK / NW; ++i) {
+      const int blk = wave + i * NW;
       // rows of V^T are stored pre-swizzled: copy them verbatim
       const int d = blk * VRPB + lane / VCH;
       const uint32_t off = (uint32_t)d * Lp * ES + (uint32_t)t * VROW + (lane % VCH) * 16;
@@ -242,23 +246,33 @@ __global__ __launch_bounds__(NW * 64, WPH == 1 ? 2 : 1) void attn_kernel(const T
   const int vrow = KTILE + r16 * VROW;
 
   // S^T[kb][qb] = K Q^T for the tile in buffer kt: lane holds keys
-  // kb*16 + 4g + i of query qb*16 + r16 (all K fragments requested first);
-  // keys past the end of the sequence get -inf.  PRE: S^T - mref.
+  // kb*16 + 4g + i of query qb*16 + r16; keys past the end of the sequence
+  // get -inf.  PRE: S^T - mref.  The 16-byte K fragments f = kb*KS + ks are
+  // read KPF ahead of their MFMAs (a rolling window: each read goes out as
+  // soon as the MFMAs of the fragment KPF places earlier are issued, so the
+  // LDS latency runs beside the matrix work instead of after it).
+  constexpr int KPF = 8;
   auto scores = [&](const char *kt, int t, f32x4(&s)[KB][QB]) {
-    u32x4 kf[KB][KS];
+    constexpr int NF = KB * KS;
+    u32x4 kf[NF];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
+    for (int f = 0; f < KPF; ++f)
+      kf[f] = *reinterpret_cast<const u32x4 *>(kt + koff[f % KS] + (f / KS) * 16 * KROW);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        kf[kb][ks] = *reinterpret_cast<const u32x4 *>(kt + koff[ks] + kb * 16 * KROW);
+    for (int f = 0; f < NF; ++f) {
+      const int kb = f / KS, ks = f % KS;
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
+      for (int qb = 0; qb < QB; ++qb)
+        s[kb][qb] = mma16<T>(kf[f], qf[qb][ks], ks ? s[kb][qb] : (PRE ? negm[qb] : f32x4{0.f, 0.f, 0.f, 0.f}));
+      if (f + KPF < NF)
+        kf[f + KPF] = *reinterpret_cast<const u32x4 *>(kt + koff[(f + KPF) % KS] + ((f + KPF) / KS) * 16 * KROW);
+    }
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) s[kb][qb] = PRE ? negm[qb] : f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int f = 0; f < KPF; ++f) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) s[kb][qb] = mma16<T>(kf[kb][ks], qf[qb][ks], s[kb][qb]);
+    for (int f = 0; f < NF; ++f) {
+      __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
+      if (f + KPF < NF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
     if ((t + 1) * ATT_BK > L) {
       // a real branch (the empty volatile asm cannot be speculated): without
@@ -318,6 +332,20 @@ __global__ __launch_bounds__(NW * 64, WPH == 1 ? 2 : 1) void attn_kernel(const T
     }
   };
 
+  // V^T fragments of the P V product: the one of row d = db*16 + r16 for
+  // k-slice c is one 16-byte chunk at c ^ swizzle(d).  bf16: one MFMA
+  // (k = 32) per pair of 16-key blocks, the lane's 8 keys (2pr)*16 + 4g +
+  // {0..3} and (2pr+1)*16 + 4g + {0..3} (chunk pr*4 + g); fp32: four MFMAs
+  // (k = 4 each) per 16-key block, chunk kb*4 + g.
+  constexpr int NVF = NPF * DB;
+  // rolling depth VPF; VPF0 of those are requested before the numerators
+  constexpr int VPF = 6, VPF0 = 2;
+  auto read_vf = [&](const char *kt, int f) {
+    const int ksl = f / DB, db = f % DB;
+    const int cpos = ES == 2 ? ((ksl * 4 + g) ^ (r16 & 7)) * 16 : ((ksl * 4 + g) ^ r16) * 16;
+    return *reinterpret_cast<const u32x4 *>(kt + vrow + db * 16 * VROW + cpos);
+  };
+
   for (int t = 0; t < nt; ++t) {
     // this wave's DMA of tile t is done once only the (up to PD-1) later
     // tiles already issued may be pending
@@ -329,6 +357,13 @@ __global__ __launch_bounds__(NW * 64, WPH == 1 ? 2 : 1) void attn_kernel(const T
 
     f32x4 s[KB][QB];
     scores(kt, t, s);
+    // the first VPF0 V^T fragments of the tile are requested before the
+    // numerators (their LDS latency runs beside the exponentials; more than
+    // two do not fit in the registers left); the rare recompute path reads
+    // them again, so they are not held across it
+    u32x4 vf[NVF];
+#pragma unroll
+    for (int f = 0; f < VPF0; ++f) vf[f] = read_vf(kt, f);
     u32x4 pf[NPF][QB];
     float lp[QB];
     // Lazy reference: a lane's partial row sum above 2^30 (or not finite)
@@ -379,37 +414,27 @@ __global__ __launch_bounds__(NW * 64, WPH == 1 ? 2 : 1) void attn_kernel(const T
         }
       }
       numerators(s, pf, lp);
+#pragma unroll
+      for (int f = 0; f < VPF0; ++f) vf[f] = read_vf(kt, f);
     }
+#pragma unroll
+    for (int f = VPF0; f < VPF; ++f) vf[f] = read_vf(kt, f);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) lrow[qb] += lp[qb];
 
-    // O^T[db][qb] += V^T[db rows] * P^T; the V^T fragment of row
-    // d = db*16 + r16 for k-slice c is one 16-byte chunk at c ^ swizzle(d)
-    if constexpr (ES == 2) {
-      // bf16: one MFMA (k = 32) per pair of 16-key blocks; the lane's 8
-      // keys are (2pr)*16 + 4g + {0..3} and (2pr+1)*16 + 4g + {0..3}
+    // O^T[db][qb] += V^T[db rows] * P^T, fragment f = kslice * DB + db;
+    // the reads roll VPF ahead of the MFMAs
 #pragma unroll
-      for (int pr = 0; pr < KB / 2; ++pr) {
-        const int cpos = ((pr * 4 + g) ^ (r16 & 7)) * 16;
+    for (int f = 0; f < NVF; ++f) {
+      const int ksl = f / DB, db = f % DB;
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const u32x4 vf = *reinterpret_cast<const u32x4 *>(kt + vrow + db * 16 * VROW + cpos);
+      for (int qb = 0; qb < QB; ++qb) o[db][qb] = mma16<T>(vf[f], pf[ksl][qb], o[db][qb]);
+      if (f + VPF < NVF) vf[f + VPF] = read_vf(kt, f + VPF);
+    }
 #pragma unroll
-          for (int qb = 0; qb < QB; ++qb) o[db][qb] = mma16<T>(vf, pf[pr][qb], o[db][qb]);
-        }
-      }
-    } else {
-      // fp32: four MFMAs (k = 4 each) per 16-key block; chunk kb*4 + g
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const int cpos = ((kb * 4 + g) ^ r16) * 16;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const u32x4 vf = *reinterpret_cast<const u32x4 *>(kt + vrow + db * 16 * VROW + cpos);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) o[db][qb] = mma16<T>(vf, pf[kb][qb], o[db][qb]);
-        }
-      }
+    for (int f = 0; f < NVF; ++f) {
+      __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
+      if (f + VPF < NVF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
   }
 
