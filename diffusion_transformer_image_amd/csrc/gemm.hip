@@ -571,7 +571,13 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(const uint8_t *__restrict
   constexpr int TM = BM / WM, TN = BN / WN, RB = TM / 16, CB = TN / 16;
   constexpr int BKB = 128, CPR = 8, RPB = 1024 / BKB;
   constexpr int ABLK = BM / RPB, BBLK = BN / RPB, STAGE = (BM + BN) * BKB, BPW = (ABLK + BBLK) / NW;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+  // the ring, then the tile's row scales (sa of its BM rows) and the scales
+  // of its BN operand rows of W, fetched at the start so their latency
+  // overlaps the main loop instead of preceding the epilogue (one LDS
+  // object: with a second one the compiler no longer keeps the fragment
+  // reads clear of the in-flight DMA and waits for it before each read)
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE + (BM + BN) * 4];
+  float *s_scale = reinterpret_cast<float *>(smem + 2 * STAGE);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -595,6 +601,21 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(const uint8_t *__restrict
   tile_coords(pid, m_tiles, n_tiles, gm, tm, tn);
   const int m0 = tm * BM;
   const int n0 = (EPI == EPI_SWIGLU) ? tn * (BN / 2) : tn * BN;
+  // (called right after the first stage's DMA is issued, so the two
+  // latencies overlap)
+  auto stage_scales = [&]() {
+    static_assert(BM + BN == 512, "one scale per thread");
+    if (tid < BM) {
+      s_scale[tid] = m0 + tid < M ? sa[m0 + tid] : 0.f;
+    } else {
+      // operand row r of the W tile: W1 rows n0.. then W3 rows N + n0..
+      // for the SwiGLU tile, else rows n0..
+      const int r = tid - BM;
+      const int rr = (EPI == EPI_SWIGLU && r >= BN / 2) ? r - BN / 2 : r;
+      const int wr = (EPI == EPI_SWIGLU && r >= BN / 2) ? N + n0 + rr : n0 + rr;
+      s_scale[tid] = n0 + rr < N ? sw[wr] : 0.f;
+    }
+  };
   const uint32_t ldb = (uint32_t)K;
   const rsrc_t ra = make_rsrc(A + (size_t)m0 * K, (uint32_t)min(M - m0, BM) * ldb);
   const rsrc_t rw = (EPI == EPI_SWIGLU)
@@ -698,6 +719,7 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(const uint8_t *__restrict
     };
     static_assert(BPW == RB && RB % 2 == 0, "two DMA loads per row block over the first half");
     issue_spread(0, 0);
+    stage_scales();
     for (int kt = 0; kt < nk; ++kt) {
       wait_vmcnt<0>();  // this wave's DMA of stage kt
       __syncthreads();  // stage kt visible to all; every wave is done with stage kt-1
@@ -733,6 +755,7 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(const uint8_t *__restrict
     wait_vmcnt<0>();  // the stage past the end has landed before LDS is reused
   } else {
     issue_stage(0, 0);
+    stage_scales();
     for (int kt = 0; kt < nk; ++kt) {
       wait_vmcnt<0>();  // this wave's DMA of stage kt
       __syncthreads();  // stage kt visible to all; every wave is done with stage kt-1
@@ -741,25 +764,22 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(const uint8_t *__restrict
     }
   }
 
-  // ---- row and column scales, then the shared epilogue
-  const int row0 = m0 + wm * TM;
+  // ---- row and column scales (staged in LDS at the start; the main
+  // loop's barriers made them visible), then the shared epilogue
+  const float *s_row = s_scale, *s_col = s_scale + BM;
   float cs[CB];
 #pragma unroll
   for (int j = 0; j < CB; ++j) {
-    if (EPI == EPI_SWIGLU) {
-      const int nr = n0 + wn * (TN / 2) + (j % (CB / 2)) * 16 + r16;
-      cs[j] = nr < N ? sw[j < CB / 2 ? nr : N + nr] : 0.f;
-    } else {
-      const int nr = n0 + wn * TN + j * 16 + r16;
-      cs[j] = nr < N ? sw[nr] : 0.f;
-    }
+    if (EPI == EPI_SWIGLU)
+      cs[j] = s_col[(j < CB / 2 ? 0 : BN / 2) + wn * (TN / 2) + (j % (CB / 2)) * 16 + r16];
+    else
+      cs[j] = s_col[wn * TN + j * 16 + r16];
   }
 #pragma unroll
   for (int i = 0; i < RB; ++i)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int r = row0 + i * 16 + 4 * g + e;
-      const float rs = r < M ? sa[r] : 0.f;
+      const float rs = s_row[wm * TM + i * 16 + 4 * g + e];
 #pragma unroll
       for (int j = 0; j < CB; ++j) acc[i][j][e] *= rs * cs[j];
     }
