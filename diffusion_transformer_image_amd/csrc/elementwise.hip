@@ -59,9 +59,17 @@ constexpr int EW_WAVES = 8;
 constexpr int RES_ROWS = 4;
 constexpr int RES_WAVES = 4;
 
-__device__ __forceinline__ void lds8(const float *p, float (&v)[8]) {
-  const f32x4 a = *reinterpret_cast<const f32x4 *>(p);
-  const f32x4 b = *reinterpret_cast<const f32x4 *>(p + 4);
+// Per-sample vectors of length D sit in LDS split in two halves: elements
+// 8c..8c+3 of chunk c at [4c, 4c+4), elements 8c+4..8c+7 at [D/2 + 4c, ...).
+// A wave reading the chunks of 64 consecutive c then makes two reads of
+// 1 KiB each, contiguous over its lanes (with the plain layout each 16-byte
+// read had a 32-byte lane stride: two-way bank conflicts in the counters).
+__device__ __forceinline__ int vec_slot(int i, int D) {  // i: multiple of 4
+  return ((i >> 2) & 1) * (D >> 1) + ((i >> 3) << 2);
+}
+__device__ __forceinline__ void lds8v(const float *vec, int ch, int D, float (&v)[8]) {
+  const f32x4 a = *reinterpret_cast<const f32x4 *>(vec + ch * 4);
+  const f32x4 b = *reinterpret_cast<const f32x4 *>(vec + (D >> 1) + ch * 4);
   v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
   v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
@@ -132,8 +140,8 @@ __device__ __forceinline__ void stage_norm_vectors(float *A, float *S, const flo
     const f32x4 sh = *reinterpret_cast<const f32x4 *>(msh + i) + *reinterpret_cast<const f32x4 *>(bsh + i);
     const f32x4 sc = *reinterpret_cast<const f32x4 *>(msh + D + i) + *reinterpret_cast<const f32x4 *>(bsh + D + i);
     const f32x4 g = gain ? *reinterpret_cast<const f32x4 *>(gain + i) : f32x4{0.f, 0.f, 0.f, 0.f};
-    *reinterpret_cast<f32x4 *>(A + i) = (1.0f + g) * (1.0f + sc);
-    *reinterpret_cast<f32x4 *>(S + i) = sh;
+    *reinterpret_cast<f32x4 *>(A + vec_slot(i, D)) = (1.0f + g) * (1.0f + sc);
+    *reinterpret_cast<f32x4 *>(S + vec_slot(i, D)) = sh;
   }
 }
 __device__ __forceinline__ void stage_gate_vector(float *G, const float *mod, const float *bias, int b, int D,
@@ -141,7 +149,8 @@ __device__ __forceinline__ void stage_gate_vector(float *G, const float *mod, co
   const float *mg = mod + ((size_t)b * 6 + 3 * which + 2) * D;
   const float *bg = bias + (size_t)(3 * which + 2) * D;
   for (int i = threadIdx.x * 4; i < D; i += blockDim.x * 4)
-    *reinterpret_cast<f32x4 *>(G + i) = *reinterpret_cast<const f32x4 *>(mg + i) + *reinterpret_cast<const f32x4 *>(bg + i);
+    *reinterpret_cast<f32x4 *>(G + vec_slot(i, D)) =
+        *reinterpret_cast<const f32x4 *>(mg + i) + *reinterpret_cast<const f32x4 *>(bg + i);
 }
 
 // ----------------------------------------------------------------- modnorm
@@ -194,8 +203,8 @@ __global__ __launch_bounds__(EW_WAVES * 64) void modnorm_kernel(const Tx *__rest
       const int ch = lane + 64 * c;
       if (ch < nch) {
         float a[8], sh[8];
-        lds8(A + ch * 8, a);
-        lds8(S + ch * 8, sh);
+        lds8v(A, ch, D, a);
+        lds8v(S, ch, D, sh);
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[c][i] = v[c][i] * inv * a[i] + sh[i];
         if constexpr (!is_u8<Th>::value) Vec8<Th>::store(hr + ch * 8, v[c]);
@@ -297,7 +306,7 @@ __global__ __launch_bounds__(RES_WAVES * 64) void resid_kernel(const Tx *__restr
         float xv[8], yv[8], gv[8], o[8];
         bx.get(u, xv);
         by.get(u, yv);
-        lds8(G + ch * 8, gv);
+        lds8v(G, ch, D, gv);
 #pragma unroll
         for (int i = 0; i < 8; ++i) o[i] = xv[i] + gv[i] * yv[i];
         Vec8<To>::store(out + off, o);
@@ -387,7 +396,7 @@ __global__ __launch_bounds__(EW_WAVES * 64) void resid_modnorm_kernel(const Tx *
         float xv[8], yv[8], gv[8];
         bx[rr & 1].get(c, xv);
         by[rr & 1].get(c, yv);
-        lds8(G + ch * 8, gv);
+        lds8v(G, ch, D, gv);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           v[c][i] = xv[i] + gv[i] * yv[i];
@@ -402,8 +411,8 @@ __global__ __launch_bounds__(EW_WAVES * 64) void resid_modnorm_kernel(const Tx *
       const int ch = lane + 64 * c;
       if (ch < nch) {
         float a[8], sh[8];
-        lds8(A + ch * 8, a);
-        lds8(S + ch * 8, sh);
+        lds8v(A, ch, D, a);
+        lds8v(S, ch, D, sh);
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[c][i] = v[c][i] * inv * a[i] + sh[i];
         if constexpr (!is_u8<Th>::value) Vec8<Th>::store(h + row * D + ch * 8, v[c]);
