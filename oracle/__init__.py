@@ -23,8 +23,8 @@ Parity status (what pins each function; see the tests under
   brute-force embedding (and a zero W_t2 giving zero).  The pages name a
   sinusoidal time embedding and a per-block bias replacing per-block MLPs,
   but do not give the shared map from t to the modulation vector: the
-  two-layer bias-free MLP is a reading, so parity of that convention is
-  unpinned by the pages (the HIP path implements the same reading).
+  two-layer bias-free MLP is a reading (the HIP path implements the same
+  reading).
 * ``qk_rmsnorm``, ``rope_positions``, ``rope_angles``, ``apply_rope``,
   ``attention_prologue`` (the optional QKNorm + 3D axial RoPE): pinned by
   the scalar-loop brute force, by torch's float64 ``rms_norm``, by the
@@ -32,7 +32,7 @@ Parity status (what pins each function; see the tests under
   position 0 and text tokens unchanged, scores depending only on position
   differences along an axis) and by planted mistakes.  The axis split
   (32, 48, 48), the adjacent-pair convention and the base 10000 are
-  readings: parity of those conventions is unpinned by the pages.
+  readings of conventions the pages do not give.
 * ``patchify``/``unpatchify``, ``embed_tokens``, ``final_mod``,
   ``final_layer``, ``flow_schedule``, ``euler_sample``,
   ``model_velocity`` (the stack's boundary layers and the rectified-flow
@@ -41,7 +41,7 @@ Parity status (what pins each function; see the tests under
   straight-path velocity field (Euler lands on x0), and by torch routines
   for the norm; the layer conventions (16-channel latent, 2 x 2 patches,
   bias-free embeddings, the final modulation map, the shift form) are
-  readings: parity of those conventions is unpinned by the pages.
+  readings of conventions the pages do not give.
 * ``block_forward_fp8``, ``stack_forward_fp8`` (the 8-bit block and stack):
   with the quantiser replaced by the identity they reproduce
   ``block_forward`` / ``stack_forward``; with row-wise e4m3 they depart
@@ -63,9 +63,8 @@ Parity status (what pins each function; see the tests under
   loop over every head and channel with a distinct value in every row
   block of W_qkvg.
 * The zero-centred gain form ``(1 + w)`` of the RMSNorm is a reading of
-  the pages (weight decay on a zero-centred parameter); parity of that
-  convention is unpinned by the pages, though the arithmetic under it is
-  pinned as above.
+  the pages (weight decay on a zero-centred parameter); the arithmetic
+  under it is pinned as above.
 """
 from .dit_oracle import (  # noqa: F401
     OracleConfig,

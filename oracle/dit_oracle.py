@@ -41,7 +41,8 @@ Readings where the pages leave a step open (each is also a test):
 * Softmax scale 1/sqrt(head_dim); query head h reads KV head
   h // (H / Hkv) (contiguous groups); no mask, no positional terms.
 * No linear biases; SwiGLU: silu(h W1^T) * (h W3^T), then W2.
-* Timestep map (a reading; parity of the convention unpinned): e = [cos(1000 t f_i), sin(1000 t f_i)],
+* Timestep map (a reading: the pages do not give the map; its arithmetic is
+  pinned): e = [cos(1000 t f_i), sin(1000 t f_i)],
   f_i = 10000^(-i/(n/2)), m = W_t2 silu(W_t1 e), bias-free, shared by all
   blocks.
 
@@ -61,8 +62,9 @@ Readings where the pages are silent:
   (2j, 2j+1); pair i of an axis with d_a dimensions turns by
   pos_a * theta^(-2i/d_a), theta = 10000; image token l (raster order on
   the grid_h x grid_w latent grid) has position (0, l // grid_w,
-  l % grid_w), text tokens (0, 0, 0).  Parity unpinned: the split, the
-  pairing and the base are conventions the pages do not give.
+  l % grid_w), text tokens (0, 0, 0).  The split, the pairing and the base
+  are readings (the pages do not give them); the rotation's arithmetic is
+  pinned.
 """
 from __future__ import annotations
 
@@ -116,9 +118,8 @@ def time_embedding(t, dim: int = 256, t_scale: float = 1000.0, max_period: float
 
 def timestep_modulation(t, w_t1, w_t2, hidden: int) -> np.ndarray:
     """m = W_t2 silu(W_t1 e(t)), reshaped to [B, 6, D].  The shared map from
-    t to the modulation vector is a reading (the pages do not give it):
-    parity of the convention is unpinned by the pages, its arithmetic is
-    pinned by scalar loops."""
+    t to the modulation vector is a reading (the pages do not give it);
+    its arithmetic is pinned by scalar loops."""
     w_t1, w_t2 = _f64(w_t1), _f64(w_t2)
     e = time_embedding(t, dim=w_t1.shape[1])
     z = e @ w_t1.T
@@ -334,7 +335,8 @@ def stack_forward(x, mod, weights: Iterable | Callable[[int], object], n_blocks:
 # model is trained with the standard rectified-flow loss and
 # v-parameterization, and training and inference use a shifted sampling
 # schedule whose inference shift is kept constant.  Readings where the
-# pages are silent (parity unpinned: conventions of the boundary layers):
+# pages are silent (conventions of the boundary layers; their arithmetic is
+# pinned):
 #
 # * latent z [B, C, Hl, Wl]; 2 x 2 patches in raster order, patch vector
 #   index c * 4 + dy * 2 + dx; image tokens first, then text tokens;
