@@ -37,7 +37,9 @@
 //  * LDS data is XOR-swizzled (K by 16-byte chunk at DMA time, V^T when
 //    the V^T pass writes it, which also groups each lane's keys of one
 //    MFMA into one chunk) so every fragment is one ds_read_b128 and 16
-//    rows hit distinct banks (checked with SQ_LDS_BANK_CONFLICT);
+//    rows hit distinct banks (checked with SQ_LDS_BANK_CONFLICT); both
+//    products read their fragments a rolling window ahead of the MFMAs
+//    that consume them;
 //  * epilogue: divide by the row sum, multiply by sigmoid(G), store.
 #include <cmath>
 
