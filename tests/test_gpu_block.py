@@ -278,6 +278,24 @@ def test_stack_60_blocks_small(dev, dtype):
     check_block(y, ref, x, dtype, "stack60")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_stack_one_block_equals_block(dev, dtype):
+    """A one-block stack runs the block's kernels with the caller's input and
+    output types (no fp32 stream, no join): the outputs equal the block
+    entry point's bit for bit."""
+    torch, device, dit = dev
+    cfg = datagen.get_config("c1" if dtype == "bf16" else "c0").replace(
+        batch=2, n_image=100, n_text=28, hidden=512, n_heads=4, n_kv_heads=1, head_dim=128, ffn=1376,
+        dtype=dtype)
+    r = Run(dev, cfg, strong=True)
+    Yb, Ys = torch.empty_like(r.X), torch.empty_like(r.X)
+    dit.block_fwd(r.c, r.W, r.X, Yb, r.M, r.ws)
+    ws = torch.empty(dit.stack_workspace_size(r.c), dtype=torch.uint8, device="cuda")
+    dit.stack_fwd(r.c, [r.W], r.X, Ys, r.M, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(Yb, Ys)
+
+
 def test_stack_full_dims_three_blocks(dev):
     cfg = datagen.get_config("c4").replace(n_image=200, n_text=56)
     x = datagen.activations(cfg)

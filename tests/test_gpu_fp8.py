@@ -261,3 +261,24 @@ def test_stack_fp8_full_width(dev):
     cfg = datagen.get_config("c4").replace(n_image=456, n_text=64)
     y, ref, x = run_stack_fp8(dev, cfg, 4)
     check_fp8_block(y, ref, x, "fp8 stack x4 full width")
+
+
+def test_stack_fp8_one_block_equals_block(dev):
+    """A one-block 8-bit stack runs the same kernels as the 8-bit block entry
+    point (no residual-stream join, bf16 in and out): the outputs are equal
+    bit for bit."""
+    torch, device, dit = dev
+    cfg = datagen.get_config("c1").replace(batch=2, n_image=100, n_text=28, hidden=512, n_heads=4,
+                                            n_kv_heads=1, ffn=1376)
+    x = datagen.activations(cfg)
+    w = datagen.block_weights(cfg)
+    mod = device.to_device(datagen.block_mod(cfg, strong=True), "f32")
+    c = dit.config_of(cfg)
+    W8 = fp8_block_weights(dev, w)
+    X = device.to_device(x.reshape(cfg.tokens, cfg.hidden), "bf16")
+    Yb, Ys = torch.empty_like(X), torch.empty_like(X)
+    dit.block_fwd_fp8(c, W8, X, Yb, mod, torch.empty(dit.workspace_size_fp8(c), dtype=torch.uint8, device="cuda"))
+    dit.stack_fwd_fp8(c, [W8], X, Ys, mod,
+                      torch.empty(dit.stack_workspace_size_fp8(c), dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    assert torch.equal(Yb, Ys)
