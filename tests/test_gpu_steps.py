@@ -354,6 +354,34 @@ def test_gemm_whole_tile_variants(dev, variant, swiglu, k):
     assert_parity(device.to_numpy(C), ref, "bf16", f"variant {variant}", maxabs=8e-3, cos_min=0.99999)
 
 
+@pytest.mark.parametrize("swiglu,m,n,k,sk_tiles,segs", [
+    (False, 2300, 8200, 192, 0, 1),   # 297 tiles of 3 stages, ragged M
+    (True, 2304, 4224, 128, 0, 1),    # 297 SwiGLU tiles of two stages each
+    (False, 2304, 8192, 256, 32, 2),  # 256 whole tiles (XCD-remapped), then 64 K segments
+    (True, 2100, 4100, 320, 40, 2),   # ragged M and F, segments of 2 and 3 stages
+])
+def test_gemm_more_tiles_than_cus(dev, swiglu, m, n, k, sk_tiles, segs):
+    """More work items than the 256 compute units hold at once: a second
+    round of workgroups, with the grouped tile order, the XCD remap of a
+    whole number of rounds and a split tail after a full round."""
+    torch, device, dit = dev
+    print(f"gemm rounds swiglu={swiglu} M={m} N={n} K={k} split {sk_tiles}x{segs}", flush=True)
+    cfg = datagen.get_config("c1")
+    a, w = datagen.gemm_operands(cfg, m, 2 * n if swiglu else n, k, tag=211 + m + k)
+    A, W = device.to_device(a, "bf16"), device.to_device(w, "bf16")
+    C = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    if sk_tiles:
+        ws = torch.empty(sk_tiles * segs * 65536, dtype=torch.float32, device="cuda")
+        dit.gemm_splitk(A, W, C, sk_tiles, segs, ws, swiglu=swiglu)
+    elif swiglu:
+        dit.gemm_swiglu(A, W, C)
+    else:
+        dit.gemm(A, W, C)
+    torch.cuda.synchronize()
+    ref = O.swiglu_hidden(a, w, n) if swiglu else a.astype(np.float64) @ w.astype(np.float64).T
+    assert_parity(device.to_numpy(C), ref, "bf16", "more tiles than CUs", maxabs=8e-3, cos_min=0.99999)
+
+
 @pytest.mark.parametrize("swiglu", [False, True])
 @pytest.mark.parametrize("m,n,k,sk_tiles,segs", [
     (300, 520, 328, 6, 3),     # every tile split, ragged M, N and K (K tail in the last segment)
