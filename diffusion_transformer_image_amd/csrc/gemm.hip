@@ -21,7 +21,7 @@
 //  * workgroup ids are remapped so that each XCD (dispatch is round-robin
 //    over the 8 XCDs) walks a contiguous band of tiles, grouped gm row
 //    tiles at a time, so tiles sharing A rows or W rows meet in one L2
-//    (gm = 4 row tiles for the SwiGLU tile, 8 otherwise, unless the caller
+//    (gm = 2 row tiles for the SwiGLU tile, 8 otherwise, unless the caller
 //    sets it);
 //  * the bf16 epilogue stages the whole output tile in LDS and each wave
 //    stores whole rows (full cache lines).
@@ -916,9 +916,12 @@ template <int EPI>
 static hipError_t gemm_dispatch(bool f32, int variant, int gm, const void *a, const void *w,
                                 void *c, int M, int N, int K, hipStream_t s, float *part,
                                 size_t part_bytes, ColScale cs = {}) {
-  // L2 grouping width: 4 row tiles for the SwiGLU tile (it reads W1 and W3
-  // rows: measured ~3 % faster than 8 on W13 at 1024 px), else 8
-  if (gm <= 0) gm = (EPI == EPI_SWIGLU) ? 4 : 8;
+  // L2 grouping width: 2 row tiles for the SwiGLU tile (it reads W1 and W3
+  // rows), else 8.  W13 at 1024 px, B = 2, same box: 2 -> 1192, 4 -> 1216,
+  // 8 -> 1200, 16 -> 1250 us; 2 against 4 also 1.7 % faster at 512 px,
+  // 0.7 % at 256 px and within 1 % at B = 1.  (The bf16 tile only: the FP8
+  // SwiGLU tile measured the same with 2 and 4.)
+  if (gm <= 0) gm = (EPI == EPI_SWIGLU) ? 2 : 8;
   if (f32) return launch_gemm_t<float, 256, 256, 128, 2, 2, 4, EPI>(a, w, c, M, N, K, s, gm, 0, 1, nullptr, cs);
   if (variant < 0) {
     const GemmChoice ch = gemm_choose(M, N, K, EPI == EPI_SWIGLU);
