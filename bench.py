@@ -84,8 +84,9 @@ def kernel_breakdown(dit, torch, run, cfg, reps: int = 3, per_call: int = 1, res
     """Average launch time of each kernel kind over ``reps`` calls of
     ``run`` (untimed passes, one kind at a time, HIP events around every
     launch of that kind), with TFLOP/s against ``peak_tflops`` (the bf16
-    peak unless given) for the MFMA kernels and GB/s against HBM for the
-    elementwise ones.  ``per_call``: blocks per call (60 for the stack)."""
+    peak unless given; attention, bf16 in every path, always against the
+    bf16 peak) for the MFMA kernels and GB/s against HBM for the elementwise
+    ones.  ``per_call``: blocks per call (60 for the stack)."""
     fpt, bpt = flops_per_token(cfg), bytes_per_token(cfg)
     if resid_bytes is not None:
         bpt["resid"] = resid_bytes
@@ -104,7 +105,8 @@ def kernel_breakdown(dit, torch, run, cfg, reps: int = 3, per_call: int = 1, res
         e = {"launches_per_call": n // reps, "ms_per_launch": per_launch}
         if kind in fpt:
             tf = fpt[kind] * cfg.tokens / (per_launch * 1e-3) / 1e12
-            e.update(tflops=tf, mfma_frac=tf / peak_tflops)
+            pk = PEAK_BF16_TFLOPS if kind == "attn" else peak_tflops
+            e.update(tflops=tf, mfma_frac=tf / pk, peak_tflops=pk)
         elif kind in bpt:
             gbs = bpt[kind] * cfg.tokens / (per_launch * 1e-3) / 1e9
             e.update(gbs=gbs, hbm_frac=gbs / PEAK_HBM_GBS)
