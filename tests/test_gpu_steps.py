@@ -335,6 +335,31 @@ def test_gemm_tile_grouping(dev, variant, group_m):
                   cos_min=0.99999)
 
 
+@pytest.mark.parametrize("swiglu", [False, True])
+def test_gemm_grouping_changes_order_only(dev, swiglu):
+    """The L2 grouping width and the tile height only reorder whole tiles:
+    every width gives the same bits (each tile's K loop is the same), on a
+    shape with ragged row and column tiles and more tiles than CUs."""
+    torch, device, dit = dev
+    m, n, k = 4100, 2056 if swiglu else 4104, 192  # 289 tiles of 256 rows, 374 of 192
+    print(f"grouping swiglu={swiglu} M={m} N={n} K={k}", flush=True)
+    cfg = datagen.get_config("c1")
+    a, w = datagen.gemm_operands(cfg, m, 2 * n if swiglu else n, k, tag=307 + int(swiglu))
+    A, W = device.to_device(a, "bf16"), device.to_device(w, "bf16")
+    outs = {}
+    for variant in (0, 1):
+        for gm in (1, 2, 3, 8, 64):
+            C = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+            dit.gemm_variant(variant, A, W, C, swiglu=swiglu, group_m=gm)
+            outs[(variant, gm)] = C
+    torch.cuda.synchronize()
+    ref = outs[(0, 1)]
+    for key, c in outs.items():
+        assert torch.equal(c, ref), f"tile height / grouping {key} changed the result"
+    exact = O.swiglu_hidden(a, w, n) if swiglu else a.astype(np.float64) @ w.astype(np.float64).T
+    assert_parity(device.to_numpy(outs[(0, 2)]), exact, "bf16", "grouping", maxabs=8e-3, cos_min=0.99999)
+
+
 @pytest.mark.parametrize("variant", [0, 1])
 @pytest.mark.parametrize("swiglu", [False, True])
 @pytest.mark.parametrize("k", [328, 384, 64])
