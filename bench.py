@@ -24,7 +24,6 @@ stack with the projections in 8 bits.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys

@@ -1,7 +1,6 @@
 """GPU parity of the layers around the stack (patch embedding, text
 projection, final norm and projection, unpatchify) and of the
 rectified-flow Euler sampler against the fp64 oracle, through the C ABI."""
-import numpy as np
 import pytest
 
 import datagen
