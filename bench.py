@@ -175,10 +175,11 @@ def cpu_baseline(cfg, x, w, t, w_t1, w_t2) -> dict:
             "affinity_cpus": len(os.sched_getaffinity(0)), "cpu_count": os.cpu_count()}
 
 
-def bench_stack(dit, torch, steps: int, warmup: int) -> dict:
+def bench_stack(dit, torch, steps: int, warmup: int, extras: bool = True) -> dict:
     """60-block stack at 1024 px, batch 1: one denoising step per call.
     Weights are seeded N(0, 0.02) (N(0, 0.02/sqrt(120)) for W_o, W_2)
-    drawn on the GPU with torch's generator."""
+    drawn on the GPU with torch's generator.  ``extras``: also the
+    per-kernel breakdown, the 8-step image and the 8-bit stack."""
     import datagen
     cfg = datagen.get_config("c4")
     g = torch.Generator(device="cuda")
@@ -215,6 +216,8 @@ def bench_stack(dit, torch, steps: int, warmup: int) -> dict:
            "block_tokens_per_s": cfg.n_blocks * cfg.tokens / dt, "tflops": fl / dt / 1e12,
            "mfma_frac": fl / dt / 1e12 / PEAK_BF16_TFLOPS, "steps": steps, "warmup": warmup,
            "weights_gb": sum(t.numel() * t.element_size() for b in blocks for t in b.values()) / 1e9}
+    if not extras:
+        return out
     # in the stack the residual kind moves 12 d bytes per token and launch:
     # the fused first residual + second norm reads the fp32 stream and A,
     # writes x1 (fp32) and h2; the pass between blocks reads x1 and M and
@@ -456,6 +459,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stack", action="store_true")
     ap.add_argument("--stack-steps", type=int, default=5)
+    ap.add_argument("--only-stack", action="store_true",
+                    help="the bf16 60-block denoising step alone (no per-kernel passes, image or 8-bit "
+                         "stack): the command the committed stack kernel-trace summary profiles")
     ap.add_argument("--only-headline", action="store_true",
                     help="the 1024 px block step alone (no other workloads, no stack, no CPU baseline): "
                          "the command the committed kernel-trace summary profiles")
@@ -465,6 +471,12 @@ def main() -> int:
               "shards need no communication, so N GPUs run N independent copies of this step.",
               file=sys.stderr)
         return 2
+    if args.only_stack:
+        import torch
+        import diffusion_transformer_image_amd as dit
+        torch.cuda.set_device(0)
+        print(json.dumps({"stack": bench_stack(dit, torch, args.stack_steps, 2, extras=False)}), flush=True)
+        return 0
 
     import numpy as np
     import torch
