@@ -19,7 +19,9 @@ that oracle output with the GPU output of the benchmarked step, element by
 element.  ``configs`` holds the other synthetic workloads (256 px, 512 px,
 768 x 1344) and ``stack`` the 60-block denoising step, each with a
 per-kernel breakdown; ``fp8_block`` and ``stack.fp8`` the same block and
-stack with the projections in 8 bits.
+stack with the projections in 8 bits.  ``--only-headline`` and
+``--only-stack`` print the 1024 px step alone or the bf16 60-block step
+alone (the commands the committed kernel traces profile).
 """
 from __future__ import annotations
 
